@@ -1,0 +1,244 @@
+/*
+ * pariskv.h -- C ABI of the ParisKV decode-time KV-cache retrieval path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the path computes (sources are the ParisKV pages, cited by title and
+ * section / equation / frame):
+ *   "README"  = ParisKV: Fast and Drift-Robust KV-Cache Retrieval for
+ *               Long-Context LLMs, the authors' repository README;
+ *   "Slides"  = ParisKV: Fast and Drift-Robust KV-Cache Retrieval, beamer
+ *               slides of the ICML 2026 paper (frames cite paper Sec./Eq.).
+ *
+ * Per (sequence, KV head) "unit", keys are summarised once (pk_encode_keys,
+ * pk_append_keys) and every decode step runs, per query head:
+ *   1. SRHT normalise-rotate of the query and sign-pattern centroid scoring in
+ *      each 8-dim subspace (Slides Eqs. (5)-(6); README "2. Decode");
+ *   2. tier-weighted collision votes S_i over every key's 16 centroid IDs
+ *      (Slides Eq. (15), Sec. 4.2.2);
+ *   3. the C keys with the largest S_i, ties to the lower key index, found by
+ *      histogram + prefix scan instead of a sort (Slides Sec. 4.2.2);
+ *   4. the 4-bit inner-product estimate of each candidate (Slides Eqs. (7)-(10));
+ *   5. the Top-k estimates, ties to the lower key index (Slides Sec. 4.2.3);
+ *   6. softmax attention over the k retrieved full-precision K/V rows only,
+ *      s_i = scale * <k_i, q>, o = sum softmax(s)_i v_i (Slides Sec. 3,
+ *      Eqs. (1)-(3); README "3. Attention"); K/V may sit in pinned host memory
+ *      read through a mapped device pointer (README "Key Insight"; Slides
+ *      Fig. 5, Sec. 4.2.3).
+ *
+ * Conventions for every call:
+ *   - All tensor arguments are raw pointers; "device" pointers are HIP device
+ *     addresses (hipMalloc'd, or device views of mapped pinned host memory from
+ *     pk_host_alloc_mapped).  The caller owns every tensor.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is enqueued and the call returns a negative pk_status;
+ *     pk_last_error() then describes it.
+ *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t, NULL for
+ *     the default stream).  Outputs are valid after the stream synchronises;
+ *     a device fault surfaces at that synchronisation.
+ *   - A context owns scratch memory sized at pk_create; no call allocates
+ *     device memory after that.  One context serves one stream at a time.
+ *   - Outputs must not alias inputs.
+ */
+#ifndef PARISKV_H
+#define PARISKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PK_OK = 0,
+  PK_ERR_INVALID_ARG = -1,   /* bad pointer, size, stride or config field     */
+  PK_ERR_UNSUPPORTED = -2,   /* valid in principle, not supported by this build */
+  PK_ERR_CAPACITY = -3,      /* keys would exceed the summaries' capacity      */
+  PK_ERR_OUT_OF_MEMORY = -4, /* device or pinned host allocation failed        */
+  PK_ERR_HIP = -5            /* a HIP runtime call failed (no GPU, launch error) */
+} pk_status;
+
+typedef enum { PK_F32 = 0, PK_BF16 = 1 } pk_dtype;
+
+/* Fixed geometry of this build. */
+#define PK_HEAD_DIM 128      /* D */
+#define PK_N_SUB 16          /* B subspaces (Slides, App. Table 4: B = 16, m = 8) */
+#define PK_SUB_DIM 8         /* m: one byte of sign bits per subspace          */
+#define PK_N_LEVELS 8        /* 3-bit magnitude index (README "Codebooks")     */
+#define PK_RECORD_BYTES 128  /* 64 B of nibbles + 16 fp32 weights per key      */
+#define PK_MAX_GROUP 4       /* query heads per KV head                        */
+#define PK_MAX_TOPK 256
+#define PK_MAX_CANDIDATES 16384
+
+typedef struct {
+  int32_t head_dim;          /* must be 128                                    */
+  int32_t n_sub;             /* must be 16                                     */
+  int32_t sub_dim;           /* must be 8                                      */
+  uint64_t srht_seed;        /* Philox4x64-10 key for the SRHT sign vector     */
+  int32_t n_tiers;           /* 1..4 */
+  int32_t tier_top[4];       /* strictly increasing centroid-rank cut-offs, <= 256:
+                                a key block whose centroid ranks r < tier_top[t]
+                                (and >= tier_top[t-1]) for the query gets
+                                tier_weight[t]; e.g. {1, 4, 16}               */
+  int32_t tier_weight[4];    /* 0..4 each (n_sub * max weight must be <= 64)   */
+  int32_t n_candidates;      /* C, 1..PK_MAX_CANDIDATES                        */
+  int32_t top_k;             /* k, 1..min(C, PK_MAX_TOPK)                      */
+  float softmax_scale;       /* s_i = scale * <k_i, q>                         */
+  int32_t batch;             /* sequences                                      */
+  int32_t n_kv_heads;        /* KV heads per sequence                          */
+  int32_t n_q_heads;         /* query heads per sequence; query head h reads KV
+                                head h / (n_q_heads / n_kv_heads); the ratio
+                                must be an integer in 1..PK_MAX_GROUP          */
+  int64_t n_capacity;        /* max keys per unit, 1..2^31-1                   */
+} pk_config;
+
+typedef struct pk_context pk_context;   /* opaque */
+
+/* Key summaries of every unit (unit = sequence * n_kv_heads + kv_head), device
+ * memory owned by the caller and sized with pk_summary_bytes:
+ *   codes   u8  [units][n_capacity][16]   centroid ID (sign pattern) per
+ *                                         subspace (README "1. Prefill")
+ *   records u8  [units][n_capacity][128]  bytes 0..63: 4-bit codes, nibble =
+ *                                         (sign << 3) | magnitude index,
+ *                                         coordinate 2p in the low nibble of
+ *                                         byte p; bytes 64..127: 16 fp32
+ *                                         per-subspace weights w_b (Slides
+ *                                         Eq. (9))
+ *   norms   f32 [units][n_capacity]       ||k|| of each key
+ * codes rows must be 16-byte aligned and records 128-byte aligned (true for
+ * hipMalloc'd bases).  `n` is the number of valid keys per unit. */
+typedef struct {
+  uint8_t* codes;
+  uint8_t* records;
+  float* norms;
+  int64_t n;
+  int64_t n_capacity;
+} pk_summaries;
+
+/* Optional copies of intermediate results (device pointers, each nullable),
+ * written by pk_retrieve after its kernels:
+ *   rot_q    f32 [batch][n_q_heads][128]   R q * ||q||-scaled (= fl(H(s*q)/sqrt(D)))
+ *   lut      u32 [units][16][256]          byte g = tier weight of that centroid
+ *                                          for query head g of the unit
+ *   scores   u32 [units][n]                byte g = collision score S of the key
+ *                                          for query head g of the unit
+ *   cand_idx i32 [batch][n_q_heads][C]     candidates, ascending key index;
+ *   cand_est f32 [batch][n_q_heads][C]     their estimates (min(n, C) valid
+ *                                          entries, the rest -1 / -inf)      */
+typedef struct {
+  float* rot_q;
+  uint32_t* lut;
+  uint32_t* scores;
+  int32_t* cand_idx;
+  float* cand_est;
+} pk_debug;
+
+/* Kernels whose launches pk_timing_* can bracket with HIP events. */
+typedef enum {
+  PK_KERNEL_ENCODE = 0,
+  PK_KERNEL_QPREP = 1,
+  PK_KERNEL_COLLIDE = 2,
+  PK_KERNEL_SELECT_RERANK = 3,
+  PK_KERNEL_TOPK = 4,
+  PK_KERNEL_ATTEND = 5,
+  PK_N_KERNELS = 6
+} pk_kernel_id;
+
+typedef struct {
+  int32_t launches;          /* launches recorded                              */
+  double total_ms;           /* summed event-to-event time                     */
+} pk_kernel_timing;
+
+/* ---- configuration and tables (host only, no GPU needed) ---------------- */
+
+/* Check every field of `cfg`; PK_OK or PK_ERR_INVALID_ARG / _UNSUPPORTED. */
+pk_status pk_validate_config(const pk_config* cfg);
+
+/* Bytes of each summary array for `cfg` (units * n_capacity rows). */
+pk_status pk_summary_bytes(const pk_config* cfg, size_t* codes_bytes,
+                           size_t* records_bytes, size_t* norms_bytes);
+
+/* The constant tables a context uses, computed on the host:
+ * signs[128]  +-1, sign j = +1 iff the top bit of the j-th 64-bit output of
+ *             Philox4x64-10 with key (seed, 0) and counters 1, 2, ... is 0
+ *             (the SRHT's random diagonal, Slides Eq. (5), Sec. 4.1.1);
+ * levels[8], thresholds[7]  fp32 Lloyd-Max quantiser of |u_j| under the
+ *             Beta(1/2, (m-1)/2) prior of u_j^2 (Slides Prop. 4.1, App. B.1;
+ *             README "Codebooks"); index = #{thresholds <= |u_j|}. */
+pk_status pk_tables(uint64_t seed, int8_t signs[128], float levels[8], float thresholds[7]);
+
+/* ---- context ------------------------------------------------------------- */
+
+/* Validate `cfg`, compute the tables, allocate the context's device scratch on
+ * the current HIP device.  *out is NULL on error. */
+pk_status pk_create(const pk_config* cfg, pk_context** out);
+void pk_destroy(pk_context* ctx);
+
+/* ---- summaries (Slides Eqs. (5)-(9); README "1. Prefill") ---------------- */
+
+/* Encode keys [batch][n_kv_heads][n][128] (element strides `key_strides` =
+ * {batch, head, token}; the last dimension is contiguous) into rows [0, n) of
+ * every unit and set inout->n = n.  keys: device pointer, PK_F32 or PK_BF16. */
+pk_status pk_encode_keys(pk_context* ctx, const void* keys, pk_dtype key_dtype,
+                         const int64_t key_strides[3], int64_t n,
+                         pk_summaries* inout, void* hip_stream);
+
+/* Encode t new keys per unit ([batch][n_kv_heads][t][128], strides as above)
+ * into rows [inout->n, inout->n + t) and advance inout->n by t.  New keys use
+ * the same fixed analytic codebook, no retraining (Slides, frame "The codebook
+ * is data-independent"). PK_ERR_CAPACITY if n + t > n_capacity. */
+pk_status pk_append_keys(pk_context* ctx, const void* new_keys, pk_dtype key_dtype,
+                         const int64_t key_strides[3], int64_t t,
+                         pk_summaries* inout, void* hip_stream);
+
+/* ---- decode step ------------------------------------------------------------ */
+
+/* Retrieve the Top-k keys of every query head.
+ * q          device [batch][n_q_heads][128], PK_F32 or PK_BF16, contiguous;
+ * sums       summaries with sums->n >= 0 valid keys per unit;
+ * topk_idx   device i32 [batch][n_q_heads][k]: key indices sorted by
+ *            (estimate desc, index asc); -1 pads when fewer than k keys exist;
+ * topk_est   device f32 [batch][n_q_heads][k] estimates (nullable; -inf pads);
+ * dbg        optional intermediate copies (nullable). */
+pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype,
+                      const pk_summaries* sums, int32_t* topk_idx, float* topk_est,
+                      const pk_debug* dbg, void* hip_stream);
+
+/* Sparse attention over the retrieved rows of every query head.
+ * q          device [batch][n_q_heads][128], contiguous;
+ * k, v       [batch][n_kv_heads][n][128] with element strides kv_strides =
+ *            {batch, head, token} shared by K and V, last dim contiguous, rows
+ *            16-byte aligned; device pointers or mapped host pointers;
+ * topk_idx   device i32 [batch][n_q_heads][top_k], entries < 0 are skipped;
+ * out        device [batch][n_q_heads][128] in out_dtype; a head with no
+ *            valid index gets zeros. */
+pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype,
+                           const void* k, const void* v, pk_dtype kv_dtype,
+                           const int64_t kv_strides[3], const int32_t* topk_idx,
+                           void* out, pk_dtype out_dtype, void* hip_stream);
+
+/* ---- host-resident KV tier (README "Key Insight": UVA fetch) -------------- */
+
+/* Pinned, mapped host memory: *host_ptr for the CPU, *device_ptr for kernels.
+ * PK_ERR_OUT_OF_MEMORY if the allocation fails. */
+pk_status pk_host_alloc_mapped(size_t bytes, void** host_ptr, void** device_ptr);
+pk_status pk_host_free(void* host_ptr);
+
+/* ---- timing --------------------------------------------------------------- */
+
+/* Start bracketing each launch of every kernel with HIP events on the stream
+ * it runs on, for at most `max_launches` launches per kernel (allocates the
+ * events).  pk_timing_end synchronises them, fills timings[PK_N_KERNELS] and
+ * stops recording. */
+pk_status pk_timing_begin(pk_context* ctx, int32_t max_launches);
+pk_status pk_timing_end(pk_context* ctx, pk_kernel_timing* timings);
+
+/* ---- diagnostics ---------------------------------------------------------- */
+const char* pk_status_str(pk_status status);
+/* Last error message of `ctx`, or of the calling thread when ctx is NULL. */
+const char* pk_last_error(const pk_context* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PARISKV_H */

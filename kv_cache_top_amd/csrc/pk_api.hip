@@ -1,0 +1,524 @@
+// C ABI of the ParisKV decode path (include/pariskv.h): argument validation,
+// context scratch, launch plans and per-kernel event timing.
+#include "pariskv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "pk_kernels.hpp"
+#include "pk_tables.hpp"
+
+using pk::SelParams;
+
+struct pk_context {
+  pk_config cfg;
+  int group = 1, units = 0, qheads = 0;
+  int device = 0;
+  pk::Tables tb;
+  pk::TierSpec tiers;
+  int64_t max_tiles = 0;
+  // scratch (device)
+  uint32_t* lut = nullptr;        // [units][16][256]
+  float* rq = nullptr;            // [qheads][128]
+  uint32_t* scores = nullptr;     // [units][n_cap]
+  uint32_t* tile_hist = nullptr;  // [units][max_tiles][4][64]
+  SelParams* params = nullptr;    // [units][4]
+  int2* tile_base = nullptr;      // [units][max_tiles][4]
+  uint32_t* tickets = nullptr;    // [units]
+  int32_t* cand_idx = nullptr;    // [qheads][C]
+  float* cand_est = nullptr;      // [qheads][C]
+  std::string err;
+  // timing
+  int timing_cap = 0;
+  std::vector<hipEvent_t> ev[PK_N_KERNELS];
+  int ev_used[PK_N_KERNELS] = {0};
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+pk_status fail(pk_context* ctx, pk_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  if (ctx) ctx->err = buf;
+  return st;
+}
+
+#define PK_HIP(ctx, call)                                                                 \
+  do {                                                                                    \
+    hipError_t e_ = (call);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return fail((ctx), PK_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_));     \
+  } while (0)
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Keys per collide / select workgroup: about 1024 workgroups over all units,
+// 256 threads each doing 1..32 keys.
+int tile_size(int units, int64_t n) {
+  const int64_t want = ((int64_t)units * n + 1024 * 256 - 1) / (1024 * 256);
+  int64_t kpl = want < 1 ? 1 : (want > 32 ? 32 : want);
+  return (int)(256 * kpl);
+}
+
+struct Launch {
+  pk_context* ctx;
+  int kid;
+  hipStream_t s;
+  Launch(pk_context* c, int k, hipStream_t st) : ctx(c), kid(k), s(st) {
+    if (ctx->timing_cap && ctx->ev_used[kid] < ctx->timing_cap)
+      (void)hipEventRecord(ctx->ev[kid][2 * ctx->ev_used[kid]], s);
+  }
+  ~Launch() {
+    if (ctx->timing_cap && ctx->ev_used[kid] < ctx->timing_cap) {
+      (void)hipEventRecord(ctx->ev[kid][2 * ctx->ev_used[kid] + 1], s);
+      ctx->ev_used[kid]++;
+    }
+  }
+};
+
+pk_status check_launch(pk_context* ctx, const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ctx, PK_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return PK_OK;
+}
+
+void free_scratch(pk_context* c) {
+  void* ptrs[] = {c->lut, c->rq, c->scores, c->tile_hist, c->params, c->tile_base, c->tickets,
+                  c->cand_idx, c->cand_est};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+  for (int k = 0; k < PK_N_KERNELS; ++k) {
+    for (hipEvent_t e : c->ev[k]) (void)hipEventDestroy(e);
+    c->ev[k].clear();
+  }
+}
+
+pk_status check_strides(pk_context* ctx, const void* base, pk_dtype dt, const int64_t* st,
+                        const char* what) {
+  if (!base) return fail(ctx, PK_ERR_INVALID_ARG, "%s pointer is NULL", what);
+  if (!st) return fail(ctx, PK_ERR_INVALID_ARG, "%s strides are NULL", what);
+  const int64_t vec = (dt == PK_BF16) ? 8 : 4;   // elements per 16 bytes
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0 || st[i] % vec != 0)
+      return fail(ctx, PK_ERR_INVALID_ARG, "%s stride %d (%lld) must be a non-negative multiple of %lld elements",
+                  what, i, (long long)st[i], (long long)vec);
+  if (st[2] < PK_HEAD_DIM)
+    return fail(ctx, PK_ERR_INVALID_ARG, "%s token stride %lld < 128", what, (long long)st[2]);
+  if (!aligned(base, 16)) return fail(ctx, PK_ERR_INVALID_ARG, "%s must be 16-byte aligned", what);
+  return PK_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+extern "C" {
+
+const char* pk_status_str(pk_status s) {
+  switch (s) {
+    case PK_OK: return "PK_OK";
+    case PK_ERR_INVALID_ARG: return "PK_ERR_INVALID_ARG";
+    case PK_ERR_UNSUPPORTED: return "PK_ERR_UNSUPPORTED";
+    case PK_ERR_CAPACITY: return "PK_ERR_CAPACITY";
+    case PK_ERR_OUT_OF_MEMORY: return "PK_ERR_OUT_OF_MEMORY";
+    case PK_ERR_HIP: return "PK_ERR_HIP";
+  }
+  return "PK_ERR_UNKNOWN";
+}
+
+const char* pk_last_error(const pk_context* ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
+
+pk_status pk_validate_config(const pk_config* c) {
+  if (!c) return fail(nullptr, PK_ERR_INVALID_ARG, "config is NULL");
+  if (c->head_dim != PK_HEAD_DIM || c->n_sub != PK_N_SUB || c->sub_dim != PK_SUB_DIM)
+    return fail(nullptr, PK_ERR_UNSUPPORTED, "geometry must be head_dim 128, n_sub 16, sub_dim 8 (got %d, %d, %d)",
+                c->head_dim, c->n_sub, c->sub_dim);
+  if (c->n_tiers < 1 || c->n_tiers > 4)
+    return fail(nullptr, PK_ERR_INVALID_ARG, "n_tiers must be 1..4 (got %d)", c->n_tiers);
+  int maxw = 0;
+  for (int t = 0; t < c->n_tiers; ++t) {
+    const int top = c->tier_top[t], prev = t ? c->tier_top[t - 1] : 0;
+    if (top <= prev || top > 256)
+      return fail(nullptr, PK_ERR_INVALID_ARG, "tier_top must increase strictly within 1..256 (tier %d: %d)", t, top);
+    if (c->tier_weight[t] < 0 || c->tier_weight[t] > 255)
+      return fail(nullptr, PK_ERR_INVALID_ARG, "tier_weight[%d] = %d out of range", t, c->tier_weight[t]);
+    if (c->tier_weight[t] > maxw) maxw = c->tier_weight[t];
+  }
+  if (maxw * PK_N_SUB > 64)
+    return fail(nullptr, PK_ERR_UNSUPPORTED, "n_sub * max tier weight must be <= 64 (got %d)", maxw * PK_N_SUB);
+  if (c->n_candidates < 1 || c->n_candidates > PK_MAX_CANDIDATES)
+    return fail(nullptr, PK_ERR_INVALID_ARG, "n_candidates must be 1..%d (got %d)", PK_MAX_CANDIDATES, c->n_candidates);
+  if (c->top_k < 1 || c->top_k > PK_MAX_TOPK || c->top_k > c->n_candidates)
+    return fail(nullptr, PK_ERR_INVALID_ARG, "top_k must be 1..min(n_candidates, %d) (got %d)", PK_MAX_TOPK, c->top_k);
+  if (!(std::isfinite(c->softmax_scale)))
+    return fail(nullptr, PK_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1)
+    return fail(nullptr, PK_ERR_INVALID_ARG, "batch, n_kv_heads and n_q_heads must be >= 1");
+  if (c->n_q_heads % c->n_kv_heads != 0)
+    return fail(nullptr, PK_ERR_INVALID_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_q_heads,
+                c->n_kv_heads);
+  if (c->n_q_heads / c->n_kv_heads > PK_MAX_GROUP)
+    return fail(nullptr, PK_ERR_UNSUPPORTED, "at most %d query heads per KV head (got %d)", PK_MAX_GROUP,
+                c->n_q_heads / c->n_kv_heads);
+  if (c->n_capacity < 1 || c->n_capacity > 0x7FFFFFFFll)
+    return fail(nullptr, PK_ERR_INVALID_ARG, "n_capacity must be 1..2^31-1 (got %lld)", (long long)c->n_capacity);
+  if ((int64_t)c->batch * c->n_q_heads > 0x7FFFFFFFll / 2)
+    return fail(nullptr, PK_ERR_INVALID_ARG, "too many heads");
+  return PK_OK;
+}
+
+pk_status pk_summary_bytes(const pk_config* cfg, size_t* codes, size_t* records, size_t* norms) {
+  pk_status st = pk_validate_config(cfg);
+  if (st != PK_OK) return st;
+  const size_t rows = (size_t)cfg->batch * cfg->n_kv_heads * (size_t)cfg->n_capacity;
+  if (codes) *codes = rows * 16;
+  if (records) *records = rows * PK_RECORD_BYTES;
+  if (norms) *norms = rows * sizeof(float);
+  return PK_OK;
+}
+
+pk_status pk_tables(uint64_t seed, int8_t signs[128], float levels[8], float thresholds[7]) {
+  if (!signs || !levels || !thresholds) return fail(nullptr, PK_ERR_INVALID_ARG, "NULL table pointer");
+  pk::srht_signs(seed, signs);
+  static float L[8], T[7];
+  static bool have = false;
+  if (!have) {      // the quantiser does not depend on the seed: compute once
+    pk::magnitude_tables(L, T);
+    have = true;
+  }
+  std::memcpy(levels, L, sizeof(L));
+  std::memcpy(thresholds, T, sizeof(T));
+  return PK_OK;
+}
+
+pk_status pk_create(const pk_config* cfg, pk_context** out) {
+  if (!out) return fail(nullptr, PK_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  pk_status st = pk_validate_config(cfg);
+  if (st != PK_OK) return st;
+  pk_context* c = new (std::nothrow) pk_context();
+  if (!c) return fail(nullptr, PK_ERR_OUT_OF_MEMORY, "host allocation failed");
+  c->cfg = *cfg;
+  c->group = cfg->n_q_heads / cfg->n_kv_heads;
+  c->units = cfg->batch * cfg->n_kv_heads;
+  c->qheads = cfg->batch * cfg->n_q_heads;
+
+  int8_t signs[128];
+  float L[8], T[7];
+  pk_tables(cfg->srht_seed, signs, L, T);
+  std::memset(&c->tb, 0, sizeof(c->tb));
+  for (int j = 0; j < 128; ++j)
+    if (signs[j] < 0) c->tb.neg_bits[j >> 5] |= 1u << (j & 31);
+  std::memcpy(c->tb.levels, L, sizeof(L));
+  std::memcpy(c->tb.thresholds, T, sizeof(T));
+  c->tb.inv_sqrt_d = (float)(1.0 / std::sqrt(128.0));
+  c->tiers.n_tiers = cfg->n_tiers;
+  for (int t = 0; t < 4; ++t) {
+    c->tiers.top[t] = t < cfg->n_tiers ? cfg->tier_top[t] : 0;
+    c->tiers.weight[t] = t < cfg->n_tiers ? cfg->tier_weight[t] : 0;
+  }
+  c->max_tiles = (cfg->n_capacity + 255) / 256;
+
+  hipError_t e = hipGetDevice(&c->device);
+  if (e != hipSuccess) {
+    delete c;
+    return fail(nullptr, PK_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  }
+  struct Alloc { void** p; size_t bytes; };
+  const size_t U = c->units, Q = c->qheads, C = cfg->n_candidates, N = cfg->n_capacity, MT = c->max_tiles;
+  Alloc allocs[] = {
+      {(void**)&c->lut, U * 16 * 256 * 4},
+      {(void**)&c->rq, Q * 128 * 4},
+      {(void**)&c->scores, U * N * 4},
+      {(void**)&c->tile_hist, U * MT * pk::MAXG * pk::NBIN * 4},
+      {(void**)&c->params, U * pk::MAXG * sizeof(SelParams)},
+      {(void**)&c->tile_base, U * MT * pk::MAXG * sizeof(int2)},
+      {(void**)&c->tickets, U * 4},
+      {(void**)&c->cand_idx, Q * C * 4},
+      {(void**)&c->cand_est, Q * C * 4},
+  };
+  for (Alloc& a : allocs) {
+    e = hipMalloc(a.p, a.bytes);
+    if (e != hipSuccess) {
+      *a.p = nullptr;
+      free_scratch(c);
+      delete c;
+      return fail(nullptr, e == hipErrorOutOfMemory ? PK_ERR_OUT_OF_MEMORY : PK_ERR_HIP,
+                  "hipMalloc(%zu) failed: %s", a.bytes, hipGetErrorString(e));
+    }
+  }
+  // LUT bytes of absent query heads stay zero; tickets start at zero
+  if (hipMemset(c->lut, 0, U * 16 * 256 * 4) != hipSuccess || hipMemset(c->tickets, 0, U * 4) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    free_scratch(c);
+    delete c;
+    return fail(nullptr, PK_ERR_HIP, "scratch initialisation failed");
+  }
+  *out = c;
+  return PK_OK;
+}
+
+void pk_destroy(pk_context* ctx) {
+  if (!ctx) return;
+  free_scratch(ctx);
+  delete ctx;
+}
+
+// ---------------------------------------------------------------------------
+static pk_status encode_rows(pk_context* ctx, const void* keys, pk_dtype dt, const int64_t* st,
+                             int64_t t, int64_t row0, pk_summaries* s, hipStream_t stream) {
+  if (t == 0) return PK_OK;
+  const int64_t total = (int64_t)ctx->units * t;
+  const int64_t blocks = (total + 15) / 16;
+  Launch L(ctx, PK_KERNEL_ENCODE, stream);
+  if (dt == PK_BF16)
+    hipLaunchKernelGGL(pk::encode_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t*)keys, st[0], st[1], st[2], ctx->cfg.n_kv_heads, t, total, row0,
+                       s->n_capacity, s->codes, s->records, s->norms, ctx->tb);
+  else
+    hipLaunchKernelGGL(pk::encode_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const float*)keys, st[0], st[1], st[2], ctx->cfg.n_kv_heads, t, total, row0,
+                       s->n_capacity, s->codes, s->records, s->norms, ctx->tb);
+  return check_launch(ctx, "encode");
+}
+
+static pk_status check_summaries(pk_context* ctx, const pk_summaries* s) {
+  if (!s) return fail(ctx, PK_ERR_INVALID_ARG, "summaries pointer is NULL");
+  if (!s->codes || !s->records || !s->norms) return fail(ctx, PK_ERR_INVALID_ARG, "summary array is NULL");
+  if (!aligned(s->codes, 16) || !aligned(s->records, 128) || !aligned(s->norms, 4))
+    return fail(ctx, PK_ERR_INVALID_ARG, "codes must be 16-byte and records 128-byte aligned");
+  if (s->n_capacity != ctx->cfg.n_capacity)
+    return fail(ctx, PK_ERR_INVALID_ARG, "summaries n_capacity (%lld) differs from the context's (%lld)",
+                (long long)s->n_capacity, (long long)ctx->cfg.n_capacity);
+  if (s->n < 0 || s->n > s->n_capacity)
+    return fail(ctx, PK_ERR_INVALID_ARG, "summaries n (%lld) outside 0..n_capacity", (long long)s->n);
+  return PK_OK;
+}
+
+pk_status pk_encode_keys(pk_context* ctx, const void* keys, pk_dtype dt, const int64_t key_strides[3],
+                         int64_t n, pk_summaries* inout, void* hip_stream) {
+  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
+  if (dt != PK_F32 && dt != PK_BF16) return fail(ctx, PK_ERR_UNSUPPORTED, "key dtype %d", (int)dt);
+  pk_status st = check_summaries(ctx, inout);
+  if (st != PK_OK) return st;
+  if (n < 0) return fail(ctx, PK_ERR_INVALID_ARG, "n < 0");
+  if (n > inout->n_capacity)
+    return fail(ctx, PK_ERR_CAPACITY, "n (%lld) exceeds n_capacity (%lld)", (long long)n, (long long)inout->n_capacity);
+  if (n > 0 && (st = check_strides(ctx, keys, dt, key_strides, "keys")) != PK_OK) return st;
+  st = encode_rows(ctx, keys, dt, key_strides, n, 0, inout, (hipStream_t)hip_stream);
+  if (st == PK_OK) inout->n = n;
+  return st;
+}
+
+pk_status pk_append_keys(pk_context* ctx, const void* keys, pk_dtype dt, const int64_t key_strides[3],
+                         int64_t t, pk_summaries* inout, void* hip_stream) {
+  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
+  if (dt != PK_F32 && dt != PK_BF16) return fail(ctx, PK_ERR_UNSUPPORTED, "key dtype %d", (int)dt);
+  pk_status st = check_summaries(ctx, inout);
+  if (st != PK_OK) return st;
+  if (t < 0) return fail(ctx, PK_ERR_INVALID_ARG, "t < 0");
+  if (inout->n + t > inout->n_capacity)
+    return fail(ctx, PK_ERR_CAPACITY, "n + t (%lld) exceeds n_capacity (%lld)", (long long)(inout->n + t),
+                (long long)inout->n_capacity);
+  if (t > 0 && (st = check_strides(ctx, keys, dt, key_strides, "new_keys")) != PK_OK) return st;
+  st = encode_rows(ctx, keys, dt, key_strides, t, inout->n, inout, (hipStream_t)hip_stream);
+  if (st == PK_OK) inout->n += t;
+  return st;
+}
+
+pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s,
+                      int32_t* topk_idx, float* topk_est, const pk_debug* dbg, void* hip_stream) {
+  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
+  pk_status st = check_summaries(ctx, s);
+  if (st != PK_OK) return st;
+  if (!q || !topk_idx) return fail(ctx, PK_ERR_INVALID_ARG, "q and topk_idx must be non-NULL");
+  if (q_dtype != PK_F32 && q_dtype != PK_BF16) return fail(ctx, PK_ERR_UNSUPPORTED, "q dtype %d", (int)q_dtype);
+  if (!aligned(q, q_dtype == PK_BF16 ? 4 : 8) || !aligned(topk_idx, 4) || (topk_est && !aligned(topk_est, 4)))
+    return fail(ctx, PK_ERR_INVALID_ARG, "misaligned q / output pointer");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  const pk_config& cfg = ctx->cfg;
+  const int64_t n = s->n;
+  const int k = cfg.top_k, C = cfg.n_candidates;
+  if (n == 0) {
+    const int64_t cnt = (int64_t)ctx->qheads * k;
+    hipLaunchKernelGGL(pk::fill_empty_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream, topk_idx,
+                       topk_est, cnt);
+    if ((st = check_launch(ctx, "fill")) != PK_OK) return st;
+    if (dbg && dbg->cand_idx) {
+      const int64_t cc = (int64_t)ctx->qheads * C;
+      hipLaunchKernelGGL(pk::fill_empty_kernel, dim3((unsigned)((cc + 255) / 256)), dim3(256), 0, stream,
+                         dbg->cand_idx, dbg->cand_est, cc);
+      if ((st = check_launch(ctx, "fill")) != PK_OK) return st;
+    }
+    return PK_OK;
+  }
+  const int tile = tile_size(ctx->units, n);
+  const int tiles = (int)((n + tile - 1) / tile);
+  const unsigned grid = (unsigned)((int64_t)ctx->units * tiles);
+  const int n_sel = (int)(n < C ? n : C);
+
+  {
+    Launch L(ctx, PK_KERNEL_QPREP, stream);
+    if (q_dtype == PK_BF16)
+      hipLaunchKernelGGL(pk::qprep_kernel<uint16_t>, dim3(ctx->qheads), dim3(1024), 0, stream, (const uint16_t*)q,
+                         cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->rq, (uint8_t*)ctx->lut, ctx->tb, ctx->tiers);
+    else
+      hipLaunchKernelGGL(pk::qprep_kernel<float>, dim3(ctx->qheads), dim3(1024), 0, stream, (const float*)q,
+                         cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->rq, (uint8_t*)ctx->lut, ctx->tb, ctx->tiers);
+  }
+  if ((st = check_launch(ctx, "qprep")) != PK_OK) return st;
+  {
+    Launch L(ctx, PK_KERNEL_COLLIDE, stream);
+    hipLaunchKernelGGL(pk::collide_kernel, dim3(grid), dim3(256), 0, stream, (const uint4*)s->codes, ctx->lut,
+                       ctx->scores, ctx->tile_hist, ctx->params, ctx->tile_base, ctx->tickets, n, s->n_capacity,
+                       tiles, (int)ctx->max_tiles, tile, ctx->group, C);
+  }
+  if ((st = check_launch(ctx, "collide")) != PK_OK) return st;
+  {
+    Launch L(ctx, PK_KERNEL_SELECT_RERANK, stream);
+    hipLaunchKernelGGL(pk::select_rerank_kernel, dim3(grid), dim3(256), 0, stream, ctx->scores, s->records, ctx->rq,
+                       ctx->params, ctx->tile_base, ctx->cand_idx, ctx->cand_est, n, s->n_capacity, tiles,
+                       (int)ctx->max_tiles, tile, ctx->group, cfg.n_q_heads, cfg.n_kv_heads, C, ctx->tb);
+  }
+  if ((st = check_launch(ctx, "select_rerank")) != PK_OK) return st;
+  {
+    Launch L(ctx, PK_KERNEL_TOPK, stream);
+    hipLaunchKernelGGL(pk::topk_kernel, dim3(ctx->qheads), dim3(256), 0, stream, ctx->cand_idx, ctx->cand_est,
+                       n_sel, C, k, topk_idx, topk_est);
+  }
+  if ((st = check_launch(ctx, "topk")) != PK_OK) return st;
+
+  if (dbg) {
+    const size_t U = ctx->units, Q = ctx->qheads;
+    if (dbg->rot_q) PK_HIP(ctx, hipMemcpyAsync(dbg->rot_q, ctx->rq, Q * 128 * 4, hipMemcpyDeviceToDevice, stream));
+    if (dbg->lut) PK_HIP(ctx, hipMemcpyAsync(dbg->lut, ctx->lut, U * 16 * 256 * 4, hipMemcpyDeviceToDevice, stream));
+    if (dbg->scores)
+      PK_HIP(ctx, hipMemcpy2DAsync(dbg->scores, (size_t)n * 4, ctx->scores, (size_t)s->n_capacity * 4, (size_t)n * 4,
+                                   U, hipMemcpyDeviceToDevice, stream));
+    if (dbg->cand_idx)
+      PK_HIP(ctx, hipMemcpyAsync(dbg->cand_idx, ctx->cand_idx, Q * C * 4, hipMemcpyDeviceToDevice, stream));
+    if (dbg->cand_est)
+      PK_HIP(ctx, hipMemcpyAsync(dbg->cand_est, ctx->cand_est, Q * C * 4, hipMemcpyDeviceToDevice, stream));
+  }
+  return PK_OK;
+}
+
+pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, const void* k, const void* v,
+                           pk_dtype kv_dtype, const int64_t kv_strides[3], const int32_t* topk_idx, void* out,
+                           pk_dtype out_dtype, void* hip_stream) {
+  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
+  if (!q || !topk_idx || !out) return fail(ctx, PK_ERR_INVALID_ARG, "q, topk_idx and out must be non-NULL");
+  for (pk_dtype d : {q_dtype, kv_dtype, out_dtype})
+    if (d != PK_F32 && d != PK_BF16) return fail(ctx, PK_ERR_UNSUPPORTED, "dtype %d", (int)d);
+  pk_status st = check_strides(ctx, k, kv_dtype, kv_strides, "k");
+  if (st != PK_OK) return st;
+  if ((st = check_strides(ctx, v, kv_dtype, kv_strides, "v")) != PK_OK) return st;
+  if (!aligned(q, 8) || !aligned(out, 4) || !aligned(topk_idx, 4))
+    return fail(ctx, PK_ERR_INVALID_ARG, "misaligned q / out / topk_idx");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  const pk_config& c = ctx->cfg;
+  const int kk = c.top_k;
+  Launch L(ctx, PK_KERNEL_ATTEND, stream);
+#define PK_ATT(KT, QT, OT, R)                                                                                   \
+  hipLaunchKernelGGL((pk::attend_kernel<KT, QT, OT, R>), dim3(ctx->qheads), dim3(256), 0, stream, (const QT*)q, \
+                     (const KT*)k, (const KT*)v, kv_strides[0], kv_strides[1], kv_strides[2], topk_idx, kk,    \
+                     c.n_q_heads, c.n_kv_heads, ctx->group, c.softmax_scale, (OT*)out)
+#define PK_ATT_R(KT, QT, OT) \
+  do {                       \
+    if (kk <= 128)           \
+      PK_ATT(KT, QT, OT, 32); \
+    else                     \
+      PK_ATT(KT, QT, OT, 64); \
+  } while (0)
+#define PK_ATT_O(KT, QT)                           \
+  do {                                             \
+    if (out_dtype == PK_BF16)                      \
+      PK_ATT_R(KT, QT, uint16_t);                  \
+    else                                           \
+      PK_ATT_R(KT, QT, float);                     \
+  } while (0)
+#define PK_ATT_Q(KT)                               \
+  do {                                             \
+    if (q_dtype == PK_BF16)                        \
+      PK_ATT_O(KT, uint16_t);                      \
+    else                                           \
+      PK_ATT_O(KT, float);                         \
+  } while (0)
+  if (kv_dtype == PK_BF16)
+    PK_ATT_Q(uint16_t);
+  else
+    PK_ATT_Q(float);
+#undef PK_ATT_Q
+#undef PK_ATT_O
+#undef PK_ATT_R
+#undef PK_ATT
+  return check_launch(ctx, "attend");
+}
+
+pk_status pk_host_alloc_mapped(size_t bytes, void** host_ptr, void** device_ptr) {
+  if (!host_ptr || !device_ptr || bytes == 0) return fail(nullptr, PK_ERR_INVALID_ARG, "bad arguments");
+  *host_ptr = *device_ptr = nullptr;
+  void* h = nullptr;
+  hipError_t e = hipHostMalloc(&h, bytes, hipHostMallocMapped);
+  if (e != hipSuccess || !h)
+    return fail(nullptr, PK_ERR_OUT_OF_MEMORY, "hipHostMalloc(%zu, mapped) failed: %s", bytes, hipGetErrorString(e));
+  void* d = nullptr;
+  e = hipHostGetDevicePointer(&d, h, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(h);
+    return fail(nullptr, PK_ERR_HIP, "hipHostGetDevicePointer failed: %s", hipGetErrorString(e));
+  }
+  *host_ptr = h;
+  *device_ptr = d;
+  return PK_OK;
+}
+
+pk_status pk_host_free(void* host_ptr) {
+  if (!host_ptr) return PK_OK;
+  hipError_t e = hipHostFree(host_ptr);
+  if (e != hipSuccess) return fail(nullptr, PK_ERR_HIP, "hipHostFree failed: %s", hipGetErrorString(e));
+  return PK_OK;
+}
+
+pk_status pk_timing_begin(pk_context* ctx, int32_t max_launches) {
+  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
+  if (max_launches < 1 || max_launches > 1000000) return fail(ctx, PK_ERR_INVALID_ARG, "max_launches out of range");
+  for (int k = 0; k < PK_N_KERNELS; ++k) {
+    for (hipEvent_t e : ctx->ev[k]) (void)hipEventDestroy(e);
+    ctx->ev[k].assign(2 * (size_t)max_launches, nullptr);
+    for (auto& e : ctx->ev[k]) PK_HIP(ctx, hipEventCreate(&e));
+    ctx->ev_used[k] = 0;
+  }
+  ctx->timing_cap = max_launches;
+  return PK_OK;
+}
+
+pk_status pk_timing_end(pk_context* ctx, pk_kernel_timing* out) {
+  if (!ctx || !out) return fail(ctx, PK_ERR_INVALID_ARG, "NULL argument");
+  for (int k = 0; k < PK_N_KERNELS; ++k) {
+    out[k].launches = ctx->ev_used[k];
+    out[k].total_ms = 0.0;
+    for (int i = 0; i < ctx->ev_used[k]; ++i) {
+      PK_HIP(ctx, hipEventSynchronize(ctx->ev[k][2 * i + 1]));
+      float ms = 0.0f;
+      PK_HIP(ctx, hipEventElapsedTime(&ms, ctx->ev[k][2 * i], ctx->ev[k][2 * i + 1]));
+      out[k].total_ms += ms;
+    }
+  }
+  ctx->timing_cap = 0;
+  return PK_OK;
+}
+
+}  // extern "C"

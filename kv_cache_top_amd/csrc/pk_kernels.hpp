@@ -1,0 +1,853 @@
+// HIP kernels of the ParisKV decode path for gfx950 (wave64, 160 KiB LDS/CU).
+//
+// Sources: "README" = ParisKV: Fast and Drift-Robust KV-Cache Retrieval for
+// Long-Context LLMs (repository README); "Slides" = ParisKV: Fast and
+// Drift-Robust KV-Cache Retrieval (ICML 2026 paper slides; frames cite the
+// paper's Sec./Eq.).
+//
+// Floating-point operations that decide integers (sign codes, magnitude
+// indices, centroid ranks) or produce the fp32 rerank estimates follow one
+// fixed order, with no contraction into fused multiply-adds (the build passes
+// -ffp-contract=off); division and square root are correctly rounded.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define PK_SORT_N 256          // top-k sort slots (k <= 256)
+#define PK_MAX_TOPK_ATT 256    // rows per attention head (k <= 256)
+
+namespace pk {
+
+constexpr int D = 128;       // head dimension
+constexpr int NSUB = 16;     // subspaces
+constexpr int SUBD = 8;      // coordinates per subspace
+constexpr int NLEV = 8;      // magnitude levels
+constexpr int NBIN = 64;     // collision-score bins 1..64 (0 is derived)
+constexpr int MAXG = 4;      // query heads per KV head
+
+// Constant tables passed by value to every kernel that needs them.
+struct Tables {
+  uint32_t neg_bits[4];      // bit j of the 128-bit mask set <=> SRHT sign j is -1
+  float levels[NLEV];        // Lloyd-Max magnitude levels
+  float thresholds[NLEV - 1];
+  float inv_sqrt_d;          // fl32(1 / sqrt(128))
+};
+
+struct TierSpec {
+  int n_tiers;
+  int top[4];
+  int weight[4];
+};
+
+// per-(unit, head) selection parameters written by the collide kernel
+struct SelParams {
+  int theta;     // threshold score
+  int need_eq;   // keys with S == theta that are taken (lowest indices first)
+  int n_gt;      // keys with S > theta
+  int n_sel;     // n_gt + need_eq = min(n, C)
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// order-preserving map of a float to u32 (larger float -> larger key); -0 == +0
+__device__ __forceinline__ uint32_t orderable(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_orderable(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Correctly rounded fp32 square root.  The hardware estimate s is within one
+// ulp of sqrt(x); the rounded-to-nearest result is s - ulp, s or s + ulp.  For
+// neighbours a < b the midpoint satisfies ((a + b) / 2)^2 = a*b + (b - a)^2 / 4,
+// and x - a*b is an exact multiple of ulp(s)^2 (all three are multiples of it),
+// so sqrt(x) lies below the midpoint iff x - a*b <= 0.  The single-rounding fma
+// gives that sign exactly.
+__device__ __forceinline__ float sqrt_rn(float x) {
+  const float s = sqrtf(x);
+  if (!(x > 0.0f) || !(x < __builtin_inff())) return s;
+  const float sm = __uint_as_float(__float_as_uint(s) - 1u);
+  const float sp = __uint_as_float(__float_as_uint(s) + 1u);
+  const float rm = __builtin_fmaf(-sm, s, x);
+  const float rp = __builtin_fmaf(-s, sp, x);
+  float r = (rm <= 0.0f) ? sm : s;
+  r = (rp > 0.0f) ? sp : r;
+  return r;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint32_t mbcnt(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// ===========================================================================
+// encode: key summaries (Slides Eqs. (5)-(9); README "1. Prefill")
+//
+// 16 lanes per key, lane b owns coordinates 8b..8b+7 (subspace b).  The SRHT
+// is s-flip then an unnormalised 128-point fast Walsh-Hadamard transform with
+// butterfly stages h = 1, 2, 4 inside a lane and h = 8..64 across lanes; the
+// 1/sqrt(128) and the key norm cancel in the codes and are folded into w:
+//   y = H (s * k); rho_b = ||y_b||; bit j = [y_j > 0]; u = y / rho;
+//   idx_j = #{tau_l <= |u_j|}; alpha = sum_j |u_j| L[idx_j];
+//   w_b = rho_b fl(1/sqrt(128)) / alpha  (= ||k|| r_b / alpha_b, Eq. (9)).
+// ===========================================================================
+template <typename KT>
+__global__ void __launch_bounds__(256)
+encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
+              int n_kv_heads, int64_t t, int64_t total, int64_t row0, int64_t n_cap,
+              uint8_t* __restrict__ codes, uint8_t* __restrict__ records,
+              float* __restrict__ norms, Tables tb) {
+  const int64_t key = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int b = threadIdx.x & 15;
+  if (key >= total) return;                 // whole 16-lane groups leave together
+  const int64_t unit = key / t;
+  const int64_t r = key - unit * t;
+  const int64_t seq = unit / n_kv_heads, head = unit - seq * n_kv_heads;
+  const KT* src = keys + seq * sb + head * sh + r * st + b * SUBD;
+
+  float x[SUBD];
+  if constexpr (sizeof(KT) == 2) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src);
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+  } else {
+    const float4 v0 = *reinterpret_cast<const float4*>(src);
+    const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+    x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+    x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+  }
+  float nsq = 0.0f;
+#pragma unroll
+  for (int j = 0; j < SUBD; ++j) nsq += x[j] * x[j];
+
+  const uint32_t neg = (tb.neg_bits[b >> 2] >> ((b & 3) * 8)) & 0xFFu;
+#pragma unroll
+  for (int j = 0; j < SUBD; ++j)
+    x[j] = __uint_as_float(__float_as_uint(x[j]) ^ (((neg >> j) & 1u) << 31));
+
+  // in-lane butterflies
+#pragma unroll
+  for (int h = 1; h < SUBD; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < SUBD; ++j) {
+      if (!(j & h)) {
+        const float a = x[j], c = x[j + h];
+        x[j] = a + c;
+        x[j + h] = a - c;
+      }
+    }
+  }
+  // cross-lane butterflies (partner lane b ^ m holds coordinate +- 8m)
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    const bool upper = (b & m) != 0;
+#pragma unroll
+    for (int j = 0; j < SUBD; ++j) {
+      const float p = __shfl_xor(x[j], m, 16);
+      x[j] = upper ? (p - x[j]) : (x[j] + p);
+    }
+  }
+
+  // per-subspace code, nibbles, weight
+  float e = x[0] * x[0];
+#pragma unroll
+  for (int j = 1; j < SUBD; ++j) e = e + x[j] * x[j];
+  const float rho = sqrt_rn(e);
+  uint32_t code = 0, nib = 0;
+#pragma unroll
+  for (int j = 0; j < SUBD; ++j) {
+    const uint32_t bit = x[j] > 0.0f ? 1u : 0u;
+    code |= bit << j;
+    nib |= (bit << 3) << (4 * j);
+  }
+  float w = 0.0f;
+  if (rho > 0.0f) {
+    float alpha = 0.0f;
+#pragma unroll
+    for (int j = 0; j < SUBD; ++j) {
+      const float a = fabsf(__fdiv_rn(x[j], rho));
+      uint32_t idx = 0;
+      float lv = tb.levels[0];
+#pragma unroll
+      for (int l = 0; l < NLEV - 1; ++l) {
+        const bool ge = a >= tb.thresholds[l];
+        idx += ge ? 1u : 0u;
+        lv = ge ? tb.levels[l + 1] : lv;
+      }
+      const float term = a * lv;
+      alpha = (j == 0) ? term : alpha + term;
+      nib |= idx << (4 * j);
+    }
+    w = __fdiv_rn(rho * tb.inv_sqrt_d, alpha);
+  }
+
+  const int64_t row = unit * n_cap + row0 + r;
+  codes[row * 16 + b] = (uint8_t)code;
+  uint32_t* rec = reinterpret_cast<uint32_t*>(records + row * 128);
+  rec[b] = nib;
+  reinterpret_cast<float*>(rec)[16 + b] = w;
+
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) nsq += __shfl_xor(nsq, m, 16);
+  if (b == 0) norms[row] = sqrt_rn(nsq);
+}
+
+// ===========================================================================
+// qprep: query rotation and centroid activation (README "2. Decode";
+// Slides Eqs. (5)-(6), Eq. (15) tiers).
+//
+// One workgroup of 16 waves per query head; wave b owns subspace b.  Centroid
+// c's score is sum_j (bit_j(c) ? +y_j : -y_j) in fp32, sequential in j.  The
+// centroids ranking r < tier_top[last] by (score desc, c asc) are found with a
+// bitwise threshold search over the order-preserving score keys, then ranked
+// among themselves; each gets its tier weight, every other centroid 0.  The
+// weight is written as byte g (query head g of the unit) of the unit's LUT.
+// ===========================================================================
+template <typename QT>
+__global__ void __launch_bounds__(1024)
+qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
+             float* __restrict__ rot_q, uint8_t* __restrict__ lut_bytes, Tables tb,
+             TierSpec tiers) {
+  __shared__ float y[D];
+  __shared__ uint32_t sel_key[NSUB][256];
+  __shared__ uint32_t sel_c[NSUB][256];
+
+  const int head = blockIdx.x;              // sequence * n_q_heads + query head
+  const int seq = head / n_q_heads, qh = head - seq * n_q_heads;
+  const int unit = seq * n_kv_heads + qh / group, g = qh % group;
+  const int tid = threadIdx.x;
+
+  if (tid < D) {
+    float v;
+    if constexpr (sizeof(QT) == 2) {
+      v = __uint_as_float(((uint32_t)reinterpret_cast<const uint16_t*>(q)[(int64_t)head * D + tid]) << 16);
+    } else {
+      v = q[(int64_t)head * D + tid];
+    }
+    const uint32_t negb = (tb.neg_bits[tid >> 5] >> (tid & 31)) & 1u;
+    y[tid] = __uint_as_float(__float_as_uint(v) ^ (negb << 31));
+  }
+  __syncthreads();
+  for (int h = 1; h < D; h <<= 1) {
+    if (tid < D / 2) {
+      const int lo = (tid / h) * 2 * h + (tid % h), hi = lo + h;
+      const float a = y[lo], c = y[hi];
+      y[lo] = a + c;
+      y[hi] = a - c;
+    }
+    __syncthreads();
+  }
+  if (tid < D) rot_q[(int64_t)head * D + tid] = y[tid] * tb.inv_sqrt_d;
+
+  const int b = tid >> 6, lane = tid & 63;
+  float yb[SUBD];
+#pragma unroll
+  for (int j = 0; j < SUBD; ++j) yb[j] = y[b * SUBD + j];
+  uint32_t key[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t c = lane + 64 * r;
+    float s = (c & 1u) ? yb[0] : -yb[0];
+#pragma unroll
+    for (int j = 1; j < SUBD; ++j) s = s + (((c >> j) & 1u) ? yb[j] : -yb[j]);
+    key[r] = orderable(s);
+  }
+
+  const int T = tiers.top[tiers.n_tiers - 1];
+  // threshold key: the T-th largest score key among the 256 centroids
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cnt += __popcll(__ballot(key[r] >= cand));
+    if (cnt >= T) thr = cand;
+  }
+  int n_gt = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) n_gt += __popcll(__ballot(key[r] > thr));
+  const int need_eq = T - n_gt;
+  // selected centroids, compacted in ascending centroid order
+  int eq_before = 0, sel_before = 0;
+  bool sel[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t eqm = __ballot(key[r] == thr);
+    const int eqrank = eq_before + (int)mbcnt(eqm);
+    sel[r] = key[r] > thr || (key[r] == thr && eqrank < need_eq);
+    const uint64_t sm = __ballot(sel[r]);
+    if (sel[r]) {
+      const int p = sel_before + (int)mbcnt(sm);
+      sel_key[b][p] = key[r];
+      sel_c[b][p] = lane + 64 * r;
+    }
+    eq_before += __popcll(eqm);
+    sel_before += __popcll(sm);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t c = lane + 64 * r;
+    uint32_t wgt = 0;
+    if (sel[r]) {
+      int rank = 0;
+      for (int p = 0; p < sel_before; ++p) {
+        const uint32_t k2 = sel_key[b][p];
+        rank += (k2 > key[r] || (k2 == key[r] && sel_c[b][p] < c)) ? 1 : 0;
+      }
+      for (int tt = 0; tt < tiers.n_tiers; ++tt) {
+        if (rank < tiers.top[tt]) { wgt = (uint32_t)tiers.weight[tt]; break; }
+      }
+    }
+    lut_bytes[(((int64_t)unit * NSUB + b) * 256 + c) * 4 + g] = (uint8_t)wgt;
+  }
+}
+
+// ===========================================================================
+// collide: tier-weighted collision votes (Slides Eq. (15), Sec. 4.2.2;
+// README "2. Decode") and per-tile score histograms.
+//
+// Workgroup = (unit, tile of `tile` keys).  The unit's LUT (16 x 256 u32, byte
+// g = weight for query head g) sits in LDS; a key's 16 code bytes index it
+// and the 16 words are summed: four 8-bit lanes of at most 64 never carry, so
+// one u32 add serves all query heads of the KV head.  S is stored packed.
+// Histogram bins 1..64 are kept per (head, bin, lane) with one byte per wave
+// (counts <= keys per lane <= 255).  The last workgroup of a unit (atomic
+// ticket) turns the tile histograms into the unit's threshold and per-tile
+// prefix counts for the selection.
+// ===========================================================================
+__global__ void __launch_bounds__(256)
+collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut,
+               uint32_t* __restrict__ scores, uint32_t* __restrict__ tile_hist,
+               SelParams* __restrict__ params, int2* __restrict__ tile_base,
+               uint32_t* __restrict__ tickets, int64_t n, int64_t n_cap, int tiles,
+               int max_tiles, int tile, int group, int n_candidates) {
+  __shared__ uint32_t s_lut[NSUB * 256];
+  __shared__ uint32_t s_hist[MAXG * NBIN * 64];
+
+  const int unit = blockIdx.x / tiles, tl = blockIdx.x - unit * tiles;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(lut + (int64_t)unit * NSUB * 256);
+    uint4* dst = reinterpret_cast<uint4*>(s_lut);
+    for (int i = tid; i < NSUB * 256 / 4; i += 256) dst[i] = src[i];
+    uint4* h4 = reinterpret_cast<uint4*>(s_hist);
+    for (int i = tid; i < group * NBIN * 64 / 4; i += 256) h4[i] = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+
+  const int64_t k0 = (int64_t)tl * tile;
+  const int64_t k1 = (k0 + tile < n) ? k0 + tile : n;
+  const uint4* crow = codes + (int64_t)unit * n_cap;
+  uint32_t* srow = scores + (int64_t)unit * n_cap;
+  const uint32_t incr = 1u << (8 * wave);
+  const uint32_t hbase = (uint32_t)lane * 4u - 256u;     // bin s lives at s*256 - 256 + lane*4
+
+  for (int64_t i = k0 + tid; i < k1; i += 256) {
+    const uint4 c = crow[i];
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    uint32_t acc = 0;
+#pragma unroll
+    for (int bb = 0; bb < NSUB; ++bb) acc += s_lut[bb * 256 + ((cw[bb >> 2] >> (8 * (bb & 3))) & 0xFFu)];
+    srow[i] = acc;
+    for (int g = 0; g < group; ++g) {
+      const uint32_t s = (acc >> (8 * g)) & 0xFFu;
+      if (s) atomicAdd(&s_hist[(g * NBIN * 64 * 4 + s * 256 + hbase) >> 2], incr);
+    }
+  }
+  __syncthreads();
+
+  // reduce to tile histograms [unit][tile][g][bin-1]
+  uint32_t* th = tile_hist + ((int64_t)unit * max_tiles + tl) * MAXG * NBIN;
+  if (tid < group * NBIN) {
+    const int g = tid / NBIN, bin = tid % NBIN;
+    const uint32_t* row = s_hist + (g * NBIN + bin) * 64;
+    uint32_t lo = 0, hi = 0;
+    for (int i = 0; i < 64; ++i) {
+      const uint32_t v = row[(i + tid) & 63];
+      lo += v & 0x00FF00FFu;
+      hi += (v >> 8) & 0x00FF00FFu;
+    }
+    th[g * NBIN + bin] = (lo & 0xFFFFu) + (lo >> 16) + (hi & 0xFFFFu) + (hi >> 16);
+  }
+  __threadfence();
+  __syncthreads();
+  // the LUT is no longer needed: its first word carries the "last tile" flag
+  if (tid == 0) {
+    __threadfence();
+    const uint32_t prev = atomicAdd(&tickets[unit], 1u);
+    s_lut[0] = (prev == (uint32_t)(tiles - 1)) ? 1u : 0u;
+    __threadfence();
+  }
+  __syncthreads();
+  if (!s_lut[0]) return;
+  __threadfence();
+
+  // ---- last workgroup of this unit: threshold and per-tile prefixes -------
+  const uint32_t* uh = tile_hist + (int64_t)unit * max_tiles * MAXG * NBIN;
+  if (wave < group) {
+    const int g = wave;
+    // lane = bin - 1: total count per bin
+    uint32_t tot = 0;
+    for (int t2 = 0; t2 < tiles; ++t2) tot += uh[((int64_t)t2 * MAXG + g) * NBIN + lane];
+    // suffix sums over bins (lane l holds #{S >= l+1})
+    uint32_t suf = tot;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += o;
+    }
+    const uint64_t ge = __ballot(suf >= (uint32_t)n_candidates);
+    int theta;
+    uint32_t n_gt;
+    if (ge) {
+      const int top = 63 - __builtin_clzll(ge);       // highest bin with suffix >= C
+      theta = top + 1;
+      n_gt = __shfl(suf, (top + 1) & 63, 64);
+      if (top == 63) n_gt = 0;
+    } else {
+      theta = 0;
+      n_gt = __shfl(suf, 0, 64);                      // all keys with S >= 1
+    }
+    const uint32_t eq_tot = (theta > 0) ? __shfl(tot, theta - 1, 64) : (uint32_t)(n - n_gt);
+    const uint32_t want = (uint32_t)n_candidates - n_gt;
+    const uint32_t need_eq = want < eq_tot ? want : eq_tot;
+    if (lane == 0) params[unit * MAXG + g] = SelParams{theta, (int)need_eq, (int)n_gt, (int)(n_gt + need_eq)};
+    // per-tile exclusive prefixes of (#gt, #eq), tiles in chunks of 64 lanes
+    int run_gt = 0, run_eq = 0;
+    for (int base = 0; base < tiles; base += 64) {
+      const int t2 = base + lane;
+      int gt = 0, eq = 0;
+      if (t2 < tiles) {
+        const uint32_t* hrow = uh + ((int64_t)t2 * MAXG + g) * NBIN;
+        int64_t len = n - (int64_t)t2 * tile;
+        if (len > tile) len = tile;
+        int nz = 0;
+        for (int s = 1; s <= NBIN; ++s) {
+          const int c = (int)hrow[s - 1];
+          nz += c;
+          if (s > theta) gt += c;
+          else if (s == theta) eq = c;
+        }
+        if (theta == 0) eq = (int)len - nz;
+      }
+      int pg = gt, pe = eq;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int og = __shfl_up(pg, off, 64), oe = __shfl_up(pe, off, 64);
+        if (lane >= off) { pg += og; pe += oe; }
+      }
+      if (t2 < tiles) tile_base[((int64_t)unit * max_tiles + t2) * MAXG + g] = make_int2(run_gt + pg - gt, run_eq + pe - eq);
+      run_gt += __shfl(pg, 63, 64);
+      run_eq += __shfl(pe, 63, 64);
+    }
+  }
+  if (tid == 0) tickets[unit] = 0;                    // ready for the next call
+}
+
+// ===========================================================================
+// select + rerank (Slides Sec. 4.2.2 candidate selection; Eqs. (7)-(10) and
+// README "2. Decode" fused 4-bit rerank).
+//
+// Workgroup = (unit, tile), same tiling as collide.  A key is a candidate of
+// head g iff S > theta, or S == theta and fewer than need_eq keys with
+// S == theta precede it; its slot is (#gt before) + min(#eq before, need_eq),
+// which lists candidates in ascending key order.  Selected (key, head) pairs
+// queue in LDS; one lane per pair gathers the 128-byte record and evaluates
+//   est = sum_b w_b * d_b,  d_b = sum_j T_g[8b+j][nib_j]   (sequential in j, b)
+// with T_g[j][nib] = fl(v(nib) * Rq_g[j]), v(nib) = (nib & 8 ? +1 : -1) L[nib & 7].
+// ===========================================================================
+__global__ void __launch_bounds__(256)
+select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restrict__ records,
+                     const float* __restrict__ rot_q, const SelParams* __restrict__ params,
+                     const int2* __restrict__ tile_base, int32_t* __restrict__ cand_idx,
+                     float* __restrict__ cand_est, int64_t n, int64_t n_cap, int tiles,
+                     int max_tiles, int tile, int group, int n_q_heads, int n_kv_heads,
+                     int n_candidates, Tables tb) {
+  __shared__ float s_T[MAXG * D * 16];
+  constexpr int QCAP = 256 + 256 * MAXG;   // < 256 queued + one chunk's pairs
+  __shared__ int s_widx[QCAP];
+  __shared__ int s_wpos[QCAP];
+  __shared__ int s_wcnt[4][2 * MAXG + 1];
+  __shared__ int s_nwork;
+
+  const int unit = blockIdx.x / tiles, tl = blockIdx.x - unit * tiles;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int seq = unit / n_kv_heads, kvh = unit - seq * n_kv_heads;
+  const int qhead0 = seq * n_q_heads + kvh * group;
+
+  for (int e = tid; e < group * D * 16; e += 256) {
+    const int g = e / (D * 16), j = (e / 16) % D, nb = e & 15;
+    const float lv = tb.levels[nb & 7];
+    const float v = (nb & 8) ? lv : -lv;
+    s_T[e] = v * rot_q[(int64_t)(qhead0 + g) * D + j];
+  }
+  int theta[MAXG], need[MAXG], bgt[MAXG], beq[MAXG];
+#pragma unroll
+  for (int g = 0; g < MAXG; ++g) {
+    if (g < group) {
+      const SelParams p = params[unit * MAXG + g];
+      const int2 tb2 = tile_base[((int64_t)unit * max_tiles + tl) * MAXG + g];
+      theta[g] = p.theta; need[g] = p.need_eq; bgt[g] = tb2.x; beq[g] = tb2.y;
+    } else {
+      theta[g] = 1 << 30; need[g] = 0; bgt[g] = 0; beq[g] = 0;
+    }
+  }
+  if (tid == 0) s_nwork = 0;
+  __syncthreads();
+
+  const int64_t k0 = (int64_t)tl * tile;
+  const int64_t k1 = (k0 + tile < n) ? k0 + tile : n;
+  const uint32_t* srow = scores + (int64_t)unit * n_cap;
+  const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
+
+  auto process = [&](int count) {
+    for (int w = tid; w < count; w += 256) {
+      const int i = s_widx[w], pp = s_wpos[w];
+      const int g = pp >> 24, pos = pp & 0xFFFFFF;
+      const uint4* rec = reinterpret_cast<const uint4*>(rbase + (int64_t)i * 128);
+      uint4 r4[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) r4[q] = rec[q];
+      const uint32_t* rw = reinterpret_cast<const uint32_t*>(r4);
+      const float* Tg = s_T + g * D * 16;
+      float est = 0.0f;
+#pragma unroll
+      for (int bb = 0; bb < NSUB; ++bb) {
+        const uint32_t word = rw[bb];
+        float d = Tg[(bb * SUBD) * 16 + (word & 15u)];
+#pragma unroll
+        for (int j = 1; j < SUBD; ++j) d = d + Tg[(bb * SUBD + j) * 16 + ((word >> (4 * j)) & 15u)];
+        const float tprod = __uint_as_float(rw[16 + bb]) * d;
+        est = (bb == 0) ? tprod : est + tprod;
+      }
+      if (pos < n_candidates) {             // always true when the parameters match S
+        const int64_t o = (int64_t)(qhead0 + g) * n_candidates + pos;
+        cand_idx[o] = i;
+        cand_est[o] = est;
+      }
+    }
+  };
+
+  int run_gt[MAXG] = {0, 0, 0, 0}, run_eq[MAXG] = {0, 0, 0, 0};
+  for (int64_t c0 = k0; c0 < k1; c0 += 256) {
+    const int64_t i = c0 + tid;
+    const bool valid = i < k1;
+    const uint32_t sp = valid ? srow[i] : 0u;
+    uint64_t gtm[MAXG], eqm[MAXG];
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) {
+      const int s = (int)((sp >> (8 * g)) & 0xFFu);
+      gtm[g] = __ballot(valid && g < group && s > theta[g]);
+      eqm[g] = __ballot(valid && g < group && s == theta[g]);
+      if ((tid & 63) == 0) {
+        s_wcnt[wave][2 * g] = __popcll(gtm[g]);
+        s_wcnt[wave][2 * g + 1] = __popcll(eqm[g]);
+      }
+    }
+    __syncthreads();
+    bool selg[MAXG];
+    int posg[MAXG];
+    int nsel = 0;
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) {
+      int wg = 0, we = 0, tg = 0, te = 0;
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const int a = s_wcnt[w2][2 * g], e2 = s_wcnt[w2][2 * g + 1];
+        if (w2 < wave) { wg += a; we += e2; }
+        tg += a; te += e2;
+      }
+      const bool isgt = (gtm[g] >> (tid & 63)) & 1ull;
+      const bool iseq = (eqm[g] >> (tid & 63)) & 1ull;
+      const int gt_before = bgt[g] + run_gt[g] + wg + (int)mbcnt(gtm[g]);
+      const int eq_before = beq[g] + run_eq[g] + we + (int)mbcnt(eqm[g]);
+      selg[g] = isgt || (iseq && eq_before < need[g]);
+      posg[g] = gt_before + (eq_before < need[g] ? eq_before : need[g]);
+      nsel += selg[g] ? 1 : 0;
+      run_gt[g] += tg;
+      run_eq[g] += te;
+    }
+    __syncthreads();
+    // append (key, head) pairs to the work queue
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) {
+      if (selg[g]) {
+        const int slot = atomicAdd(&s_nwork, 1);
+        s_widx[slot] = (int)i;
+        s_wpos[slot] = (g << 24) | posg[g];
+      }
+    }
+    __syncthreads();
+    const int cnt = s_nwork;
+    if (cnt >= 256) {
+      process(cnt);
+      __syncthreads();
+      if (tid == 0) s_nwork = 0;
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  process(s_nwork);
+}
+
+// ===========================================================================
+// top-k of the candidates by (estimate desc, key index asc)
+// (Slides Sec. 4.2.3: reranking returns the Top-100 indices).
+//
+// One workgroup per query head.  Radix select over order-preserving estimate
+// keys (four 8-bit passes with LDS histograms) finds the k-th largest key;
+// keys above it are taken, and of the keys equal to it the lowest candidate
+// slots (= lowest key indices, the list being in ascending key order).  The
+// k winners are bitonic-sorted in LDS.
+// ===========================================================================
+constexpr int TOPK_MAXR = 64;   // candidates per thread (C <= 16384)
+
+__global__ void __launch_bounds__(256)
+topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_sel,
+            int n_candidates, int k, int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint64_t s_sort[PK_SORT_N];
+  __shared__ int s_misc[4];
+  __shared__ int s_wcnt[4];
+
+  const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* ci = cand_idx + (int64_t)head * n_candidates;
+  float* ce = cand_est + (int64_t)head * n_candidates;
+  const int R = (n_sel + 255) / 256;
+  const int keff = k < n_sel ? k : n_sel;
+
+  uint32_t key[TOPK_MAXR];
+#pragma unroll
+  for (int r = 0; r < TOPK_MAXR; ++r) {
+    const int p = r * 256 + tid;
+    key[r] = (r < R && p < n_sel) ? orderable(ce[p]) : 0u;
+  }
+  // invalid tail slots of the candidate list (n < C)
+  for (int p = n_sel + tid; p < n_candidates; p += 256) {
+    ci[p] = -1;
+    ce[p] = -__builtin_inff();
+  }
+
+  uint32_t prefix = 0, pmask = 0;
+  int krem = keff;
+  int eq_count = 0;
+  for (int pass = 0; pass < 4 && keff > 0; ++pass) {
+    const int shift = 24 - 8 * pass;
+    s_hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < TOPK_MAXR; ++r) {
+      const int p = r * 256 + tid;
+      if (r < R && p < n_sel && (key[r] & pmask) == prefix) atomicAdd(&s_hist[(key[r] >> shift) & 0xFFu], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds bins 4l..4l+3; suffix counts from the top digit
+      uint32_t h[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { h[q] = s_hist[4 * lane + q]; sum += h[q]; }
+      uint32_t suf = sum;
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_down(suf, off, 64);
+        if (lane + off < 64) suf += o;
+      }
+      // suffix count above this lane's 4 bins
+      const uint32_t above = suf - sum;
+      uint32_t run = above;
+      int dsel = -1;
+      uint32_t above_sel = 0, cnt_sel = 0;
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        if (dsel < 0 && run + h[q] >= (uint32_t)krem) { dsel = 4 * lane + q; above_sel = run; cnt_sel = h[q]; }
+        run += h[q];
+      }
+      // the selected digit is the highest one whose suffix count reaches krem
+      const uint64_t has = __ballot(dsel >= 0 && above < (uint32_t)krem);
+      const int src = 63 - __builtin_clzll(has);
+      const int d = __shfl(dsel, src, 64);
+      const uint32_t ab = __shfl(above_sel, src, 64);
+      const uint32_t cn = __shfl(cnt_sel, src, 64);
+      if (lane == 0) { s_misc[0] = d; s_misc[1] = (int)ab; s_misc[2] = (int)cn; }
+    }
+    __syncthreads();
+    const int d = s_misc[0];
+    krem -= s_misc[1];
+    eq_count = s_misc[2];
+    prefix |= (uint32_t)d << shift;
+    pmask |= 0xFFu << shift;
+    __syncthreads();
+  }
+  const uint32_t thr = prefix;
+  const int need_eq = krem;              // keys equal to thr that are taken
+
+  if (tid == 0) s_misc[3] = 0;
+  __syncthreads();
+  if (keff > 0) {
+    int eq_run = 0;
+#pragma unroll
+    for (int r = 0; r < TOPK_MAXR; ++r) {
+      if (r < R) {                               // R is uniform: barriers below are safe
+        const int p = r * 256 + tid;
+        const bool valid = p < n_sel;
+        const bool gt = valid && key[r] > thr;
+        const bool eq = valid && key[r] == thr;
+        bool take = gt;
+        if (eq_count == need_eq) {
+          take = take || eq;
+        } else {
+          const uint64_t em = __ballot(eq);
+          if (lane == 0) s_wcnt[wave] = __popcll(em);
+          __syncthreads();
+          int before = eq_run + (int)mbcnt(em), tot = 0;
+          for (int w2 = 0; w2 < 4; ++w2) {
+            if (w2 < wave) before += s_wcnt[w2];
+            tot += s_wcnt[w2];
+          }
+          take = take || (eq && before < need_eq);
+          eq_run += tot;
+          __syncthreads();
+        }
+        if (take) {
+          const int slot = atomicAdd(&s_misc[3], 1);
+          if (slot < PK_SORT_N) s_sort[slot] = ((uint64_t)key[r] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)p);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int p = keff + tid; p < PK_SORT_N; p += 256) s_sort[p] = 0;
+  __syncthreads();
+  // bitonic sort, descending
+  for (int size = 2; size <= PK_SORT_N; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t2 = tid; t2 < PK_SORT_N / 2; t2 += 256) {
+        const int lo = 2 * t2 - (t2 & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = ((lo & size) == 0);
+        const uint64_t a = s_sort[lo], c = s_sort[hi];
+        if ((a < c) == desc) { s_sort[lo] = c; s_sort[hi] = a; }
+      }
+      __syncthreads();
+    }
+  }
+  for (int r = tid; r < k; r += 256) {
+    int32_t oi = -1;
+    float oe = -__builtin_inff();
+    if (r < keff) {
+      const uint64_t v = s_sort[r];
+      const int p = (int)(0xFFFFFFFFu - (uint32_t)v);
+      oi = ci[p];
+      oe = from_orderable((uint32_t)(v >> 32));
+    }
+    out_idx[(int64_t)head * k + r] = oi;
+    if (out_est) out_est[(int64_t)head * k + r] = oe;
+  }
+}
+
+// ===========================================================================
+// sparse attention over the retrieved rows (Slides Sec. 3, Eqs. (1)-(3);
+// README "3. Attention"; UVA fetch of host-resident rows, Slides Sec. 4.2.3).
+//
+// One workgroup (4 waves) per query head; wave w takes rows w, w+4, ...; lane
+// l holds dims 2l, 2l+1.  All K and V row loads of a wave are issued before
+// any use, so host-memory latency overlaps.  fp32 scores and softmax.
+// ===========================================================================
+template <typename KT, typename QT, typename OT, int MAXR>
+__global__ void __launch_bounds__(256)
+attend_kernel(const QT* __restrict__ q, const KT* __restrict__ kmat, const KT* __restrict__ vmat,
+              int64_t sb, int64_t sh, int64_t st, const int32_t* __restrict__ idx, int k,
+              int n_q_heads, int n_kv_heads, int group, float scale, OT* __restrict__ out) {
+  __shared__ float s_score[PK_MAX_TOPK_ATT];
+  __shared__ float s_acc[4][D];
+  __shared__ float s_red[2];
+
+  const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seq = head / n_q_heads, qh = head - seq * n_q_heads, kvh = qh / group;
+  float q0, q1;
+  if constexpr (sizeof(QT) == 2) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(q)[((int64_t)head * D >> 1) + lane];
+    q0 = bf16_lo(w); q1 = bf16_hi(w);
+  } else {
+    const float2 w = reinterpret_cast<const float2*>(q)[((int64_t)head * D >> 1) + lane];
+    q0 = w.x; q1 = w.y;
+  }
+  const int32_t* hidx = idx + (int64_t)head * k;
+  const KT* kb = kmat + seq * sb + kvh * sh;
+  const KT* vb = vmat + seq * sb + kvh * sh;
+
+  float k0v[MAXR], k1v[MAXR], v0v[MAXR], v1v[MAXR];
+  int rows[MAXR];
+#pragma unroll
+  for (int t = 0; t < MAXR; ++t) {
+    const int r = wave + 4 * t;
+    const int ix = (r < k) ? hidx[r] : -1;
+    rows[t] = ix;
+    k0v[t] = k1v[t] = v0v[t] = v1v[t] = 0.0f;
+    if (ix >= 0) {
+      if constexpr (sizeof(KT) == 2) {
+        const uint32_t kw = reinterpret_cast<const uint32_t*>(kb + (int64_t)ix * st)[lane];
+        const uint32_t vw = reinterpret_cast<const uint32_t*>(vb + (int64_t)ix * st)[lane];
+        k0v[t] = bf16_lo(kw); k1v[t] = bf16_hi(kw); v0v[t] = bf16_lo(vw); v1v[t] = bf16_hi(vw);
+      } else {
+        const float2 kw = reinterpret_cast<const float2*>(kb + (int64_t)ix * st)[lane];
+        const float2 vw = reinterpret_cast<const float2*>(vb + (int64_t)ix * st)[lane];
+        k0v[t] = kw.x; k1v[t] = kw.y; v0v[t] = vw.x; v1v[t] = vw.y;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MAXR; ++t) {
+    const int r = wave + 4 * t;
+    float p = __builtin_fmaf(q0, k0v[t], q1 * k1v[t]);
+    for (int off = 32; off >= 1; off >>= 1) p += __shfl_xor(p, off, 64);
+    if (lane == 0 && r < PK_MAX_TOPK_ATT) s_score[r] = (rows[t] >= 0) ? p * scale : -__builtin_inff();
+  }
+  __syncthreads();
+  float m = -__builtin_inff();
+  for (int r = lane; r < k; r += 64) m = fmaxf(m, s_score[r]);
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  float ssum = 0.0f;
+  for (int r = lane; r < k; r += 64) ssum += (s_score[r] == -__builtin_inff()) ? 0.0f : __expf(s_score[r] - m);
+  for (int off = 32; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, 64);
+
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int t = 0; t < MAXR; ++t) {
+    const int r = wave + 4 * t;
+    if (r < k && rows[t] >= 0) {
+      const float pr = __expf(s_score[r] - m);
+      a0 = __builtin_fmaf(pr, v0v[t], a0);
+      a1 = __builtin_fmaf(pr, v1v[t], a1);
+    }
+  }
+  s_acc[wave][2 * lane] = a0;
+  s_acc[wave][2 * lane + 1] = a1;
+  __syncthreads();
+  if (tid < D) {
+    const float acc = s_acc[0][tid] + s_acc[1][tid] + s_acc[2][tid] + s_acc[3][tid];
+    const float o = (ssum > 0.0f) ? acc / ssum : 0.0f;
+    if constexpr (sizeof(OT) == 2) {
+      reinterpret_cast<uint16_t*>(out)[(int64_t)head * D + tid] = (uint16_t)f32_to_bf16_rne(o);
+    } else {
+      out[(int64_t)head * D + tid] = o;
+    }
+  }
+}
+
+// fill top-k outputs for an empty key set
+__global__ void fill_empty_kernel(int32_t* __restrict__ idx, float* __restrict__ est, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) {
+    idx[i] = -1;
+    if (est) est[i] = -__builtin_inff();
+  }
+}
+
+}  // namespace pk
