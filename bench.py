@@ -1,0 +1,293 @@
+"""Decode-step benchmark of the ParisKV retrieval + sparse-attention path on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched128k]
+                    [--layers L] [--no-cpu] [--copy-calibration]
+
+A step is one pass of the whole hot path for one layer: pk_retrieve (query
+rotation, collision votes, candidate selection + 4-bit rerank, Top-k) and
+pk_sparse_attend for every (sequence, query head) of the workload, plus
+pk_append_keys of one key per KV head on the drift workload.  Inputs are seeded
+synthetic Llama-3.1-8B-shaped tensors already resident in HBM (or, for the
+1M-token workload, K/V in pinned host memory read through mapped pointers).
+Consecutive steps rotate over `--layers` distinct summary buffers and a pool
+of queries, so the codes are not served from the 256 MB last-level cache.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "retrieval+sparse-attn decode steps/s per layer at 128K/1M ctx; % HBM peak"
+HBM_PEAK_GBS = 8000.0
+CODE_BYTES = 16
+RECORD_BYTES = 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="batched128k")
+    ap.add_argument("--layers", type=int, default=0, help="distinct summary buffers rotated (0 = auto)")
+    ap.add_argument("--queries", type=int, default=8, help="query sets in the pool")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+def algorithmic_bytes(w, n: int) -> dict:
+    """Bytes the method itself must move per step (summaries read, K/V rows)."""
+    kv_row = 128 * (2 if w.kv_dtype == "bf16" else 4)
+    n_sel = min(n, w.n_candidates)
+    keff = min(w.top_k, n_sel)
+    return {
+        "collide": CODE_BYTES * n * w.units,
+        "select_rerank": RECORD_BYTES * n_sel * w.batch * w.n_q_heads,
+        "attend": 2 * kv_row * keff * w.batch * w.n_q_heads,
+        "encode": (kv_row + CODE_BYTES + RECORD_BYTES + 4) * w.units if w.append_steps else 0,
+    }
+
+
+def cpu_baseline(w, K, V, Q_pool, seconds: float) -> dict:
+    """The oracle's decode step on the host, on a bounded sample of the workload."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import pariskv_oracle as O
+    from workloads import synthetic as S
+    signs = O.srht_signs(w.srht_seed)
+    L32, T32 = O.magnitude_tables_f32()
+    units = [0] if w.units == 1 else [0, w.units - 1]
+    encs = {}
+    for u in units:                                   # prefill summaries: not timed
+        b, h = divmod(u, w.n_kv_heads)
+        kf = S.as_f32(K[b, h])
+        encs[u] = (kf, S.as_f32(V[b, h]),
+                   {k: np.concatenate([O.encode_f32(kf[i:i + 65536], signs, L32, T32)[k]
+                                       for i in range(0, kf.shape[0], 65536)])
+                    for k in ("codes", "nibbles", "weights", "norms")})
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            for u in units:
+                b, h = divmod(u, w.n_kv_heads)
+                kf, vf, enc = encs[u]
+                q = Q_pool[done % len(Q_pool)]
+                qs = S.as_f32(q[b, h * w.group:(h + 1) * w.group])
+                O.decode_unit(qs, kf, vf, enc, signs, L32, w.tier_top, w.tier_weight, w.n_candidates,
+                              w.top_k, w.softmax_scale)
+                done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    el = time.perf_counter() - t0
+    per_unit = el / done
+    return {"value": 1.0 / (per_unit * w.units), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} unit-steps (units {units}, {w.group} query heads each, full n={w.n}) "
+                      f"in {el:.1f} s; one step = {w.units} units"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this path has no multi-GPU mode; "
+              "units shard across GPUs with no exchange, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from kv_cache_top_amd import pariskv as P
+    from workloads import synthetic as S
+
+    def to_torch(a: np.ndarray):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    w = S.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    t0 = time.time()
+    log(f"[bench] generating {w.name}: units={w.units} n={w.n} C={w.n_candidates}")
+    K = S.all_keys(w)
+    V = S.all_values(w)
+    Q_pool = [S.all_queries(w, K, step=s) for s in range(args.queries)]
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
+
+    cap = w.n_capacity
+    cfg = P.make_config(w.batch, w.n_kv_heads, w.n_q_heads, cap, w.n_candidates, w.top_k, w.softmax_scale,
+                        w.srht_seed, w.tier_top, w.tier_weight)
+    ctx = P.Context(cfg)
+    kv_dt = P.PK_BF16 if w.kv_dtype == "bf16" else P.PK_F32
+    host_bufs = []
+    if w.kv_home == "host":
+        def mapped(A):
+            shape = (w.batch, w.n_kv_heads, cap, 128)
+            nbytes = int(np.prod(shape)) * A.itemsize
+            h, d = P.pk_host_alloc_mapped(nbytes)
+            host_bufs.append(h)
+            view = np.ctypeslib.as_array((ctypes.c_uint8 * nbytes).from_address(h)).view(A.dtype).reshape(shape)
+            view[:, :, :A.shape[2]] = A
+            return d
+        kptr, vptr = mapped(K), mapped(V)
+        kv_strides = (w.n_kv_heads * cap * 128, cap * 128, 128)
+        Kt = Vt = None
+    else:
+        def dev_full(A):
+            t = torch.empty((w.batch, w.n_kv_heads, cap, 128),
+                            dtype=torch.bfloat16 if A.dtype == np.uint16 else torch.float32, device=dev)
+            t[:, :, :A.shape[2]] = to_torch(A)
+            return t
+        Kt, Vt = dev_full(K), dev_full(V)
+        kptr, vptr = Kt.data_ptr(), Vt.data_ptr()
+        kv_strides = (Kt.stride(0), Kt.stride(1), Kt.stride(2))
+
+    sums0 = P.Summaries(cfg)
+    st3 = (ctypes.c_int64 * 3)(*kv_strides)
+    P._check(P._lib.pk_encode_keys(ctx.h, ctypes.c_void_p(kptr), kv_dt, st3, w.n, ctypes.byref(sums0.s),
+                                   P._stream(None)), ctx.h)
+    torch.cuda.synchronize()
+    # distinct summary buffers per layer so a step's codes are not LLC-resident
+    step_bytes = algorithmic_bytes(w, w.n)
+    touched = step_bytes["collide"] + step_bytes["select_rerank"]
+    layers = args.layers or max(1, min(8, int(np.ceil(1.0 * 2 ** 30 / max(touched, 1)))))
+    sums = [sums0] + [sums0.clone(cfg) for _ in range(layers - 1)]
+    Qd = [to_torch(q) for q in Q_pool]
+    H = w.batch * w.n_q_heads
+    idx = torch.empty((w.batch, w.n_q_heads, w.top_k), dtype=torch.int32, device=dev)
+    est = torch.empty((w.batch, w.n_q_heads, w.top_k), dtype=torch.float32, device=dev)
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.bfloat16 if kv_dt == P.PK_BF16 else torch.float32,
+                      device=dev)
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    # drift stream: appended keys per step (rows n0 + t of K/V)
+    app = None
+    if w.append_steps:
+        total = args.warmup + 2 * args.steps
+        if total > w.append_steps:
+            raise SystemExit(f"drift workload holds {w.append_steps} appended steps; warmup + 2*steps = {total}")
+        ak = np.stack([np.stack([np.stack([S.appended_key(w, b, h, t) for t in range(w.append_steps)])
+                                 for h in range(w.n_kv_heads)]) for b in range(w.batch)])
+        av = np.stack([np.stack([np.stack([S.appended_value(w, b, h, t) for t in range(w.append_steps)])
+                                 for h in range(w.n_kv_heads)]) for b in range(w.batch)])
+        if Kt is not None:
+            Kt[:, :, w.n:] = to_torch(ak)
+            Vt[:, :, w.n:] = to_torch(av)
+        app = True
+        layers = 1
+        sums = [sums0]
+
+    def step(i):
+        s = sums[i % layers]
+        if app:
+            t = s.s.n - w.n
+            off = (w.n + t) * kv_strides[2] * (2 if kv_dt == P.PK_BF16 else 4)
+            P._check(P._lib.pk_append_keys(ctx.h, ctypes.c_void_p(kptr + off), kv_dt, st3, 1, ctypes.byref(s.s),
+                                           sptr), ctx.h)
+        q = Qd[i % len(Qd)]
+        P._check(P._lib.pk_retrieve(ctx.h, ctypes.c_void_p(q.data_ptr()), kv_dt, ctypes.byref(s.s),
+                                    ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(est.data_ptr()), None, sptr),
+                 ctx.h)
+        P._check(P._lib.pk_sparse_attend(ctx.h, ctypes.c_void_p(q.data_ptr()), kv_dt, ctypes.c_void_p(kptr),
+                                         ctypes.c_void_p(vptr), kv_dt, st3, ctypes.c_int64(cap),
+                                         ctypes.c_void_p(idx.data_ptr()),
+                                         ctypes.c_void_p(out.data_ptr()), kv_dt, sptr), ctx.h)
+
+    log(f"[bench] warmup {args.warmup} steps, {layers} rotated layer buffers")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region 1: the step rate (no per-kernel events)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t1
+    ms = 1e3 * el / args.steps
+    log(f"[bench] {args.steps} steps in {el * 1e3:.1f} ms: {ms * 1e3:.1f} us/step")
+
+    # timed region 2: the same steps with HIP events around every kernel launch
+    P.pk_timing_begin(ctx.h, args.steps)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i if app else i)
+    torch.cuda.synchronize()
+    el2 = time.perf_counter() - t2
+    tim = P.pk_timing_end(ctx.h)
+    kern = {k: {"launches": c, "avg_us": (1e3 * t / c if c else None)} for k, (c, t) in tim.items()}
+    nb = algorithmic_bytes(w, w.n)
+    for k in kern:
+        if kern[k]["avg_us"] and nb.get(k):
+            kern[k]["alg_GBps"] = round(nb[k] / (kern[k]["avg_us"] * 1e-6) / 1e9, 1)
+    timed = {k: v for k, v in kern.items() if v["avg_us"]}
+    dom = max(timed, key=lambda k: timed[k]["avg_us"])
+    achieved = nb.get(dom, 0) / (kern[dom]["avg_us"] * 1e-6) / 1e9
+    log("[bench] per-kernel: " + json.dumps(kern))
+
+    if args.copy_calibration:
+        a = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+        b2 = torch.empty_like(a)
+        for _ in range(3):
+            b2.copy_(a)
+        torch.cuda.synchronize()
+        del a, b2
+
+    step_alg = nb["collide"] + nb["select_rerank"] + nb["attend"] + nb["encode"]
+    res = {
+        "metric": METRIC,
+        "value": round(1e3 / ms, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads, "n_q_heads": w.n_q_heads,
+                   "n": w.n, "n_candidates": w.n_candidates, "top_k": w.top_k, "kv_dtype": w.kv_dtype,
+                   "kv_home": w.kv_home, "layers_rotated": layers, "query_pool": len(Qd),
+                   "append_per_step": 1 if app else 0},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": nb.get(dom, 0)},
+        "step": {"alg_bytes": step_alg, "alg_GBps": round(step_alg / (ms * 1e-3) / 1e9, 1),
+                 "frac_of_peak": round(step_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "ms_per_step_with_kernel_events": round(1e3 * el2 / args.steps, 4)},
+        "kernels": kern,
+    }
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(w, K, V, Q_pool, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    ctx.close()
+    for h in host_bufs:
+        P.pk_host_free(h)
+
+
+if __name__ == "__main__":
+    main()

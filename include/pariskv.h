@@ -141,7 +141,8 @@ typedef enum {
   PK_KERNEL_SELECT_RERANK = 3,
   PK_KERNEL_TOPK = 4,
   PK_KERNEL_ATTEND = 5,
-  PK_N_KERNELS = 6
+  PK_KERNEL_THRESHOLD = 6,
+  PK_N_KERNELS = 7
 } pk_kernel_id;
 
 typedef struct {
@@ -209,13 +210,16 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype,
  * k, v       [batch][n_kv_heads][n][128] with element strides kv_strides =
  *            {batch, head, token} shared by K and V, last dim contiguous, rows
  *            16-byte aligned; device pointers or mapped host pointers;
- * topk_idx   device i32 [batch][n_q_heads][top_k], entries < 0 are skipped;
+ * n_rows     rows present per (sequence, KV head) in K and V;
+ * topk_idx   device i32 [batch][n_q_heads][top_k]; entries < 0 or >= n_rows
+ *            are skipped (never dereferenced);
  * out        device [batch][n_q_heads][128] in out_dtype; a head with no
  *            valid index gets zeros. */
 pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype,
                            const void* k, const void* v, pk_dtype kv_dtype,
-                           const int64_t kv_strides[3], const int32_t* topk_idx,
-                           void* out, pk_dtype out_dtype, void* hip_stream);
+                           const int64_t kv_strides[3], int64_t n_rows,
+                           const int32_t* topk_idx, void* out, pk_dtype out_dtype,
+                           void* hip_stream);
 
 /* ---- host-resident KV tier (README "Key Insight": UVA fetch) -------------- */
 

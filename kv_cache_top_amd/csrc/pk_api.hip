@@ -23,15 +23,15 @@ struct pk_context {
   int device = 0;
   pk::Tables tb;
   pk::TierSpec tiers;
-  int64_t max_tiles = 0;
+  int64_t max_tiles = 0;          // collide / select workgroups per unit at most
+  int64_t max_subs = 0;           // 4 sub-tiles (one per wave) per tile
   // scratch (device)
   uint32_t* lut = nullptr;        // [units][16][256]
   float* rq = nullptr;            // [qheads][128]
   uint32_t* scores = nullptr;     // [units][n_cap]
-  uint32_t* tile_hist = nullptr;  // [units][max_tiles][4][64]
+  uint32_t* tile_hist = nullptr;  // [units][max_subs][4][64]
   SelParams* params = nullptr;    // [units][4]
-  int2* tile_base = nullptr;      // [units][max_tiles][4]
-  uint32_t* tickets = nullptr;    // [units]
+  int2* sub_base = nullptr;       // [units][max_subs][4]
   int32_t* cand_idx = nullptr;    // [qheads][C]
   float* cand_est = nullptr;      // [qheads][C]
   std::string err;
@@ -65,12 +65,22 @@ pk_status fail(pk_context* ctx, pk_status st, const char* fmt, ...) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Keys per collide / select workgroup: about 1024 workgroups over all units,
-// 256 threads each doing 1..32 keys.
+// Keys per collide / select workgroup: about kTargetWG workgroups over all
+// units, 256 threads each doing 1..kMaxKPL keys.
+constexpr int64_t kTargetWG = 1024, kMaxKPL = 32;
 int tile_size(int units, int64_t n) {
-  const int64_t want = ((int64_t)units * n + 1024 * 256 - 1) / (1024 * 256);
-  int64_t kpl = want < 1 ? 1 : (want > 32 ? 32 : want);
+  const int64_t want = ((int64_t)units * n + kTargetWG * 256 - 1) / (kTargetWG * 256);
+  const int64_t kpl = want < 1 ? 1 : (want > kMaxKPL ? kMaxKPL : want);
   return (int)(256 * kpl);
+}
+// Upper bound of ceil(n / tile_size(units, n)) over 0 < n <= n_cap: the tile
+// holds >= 256 keys, >= units * n / kTargetWG keys, or is at its maximum.
+int64_t max_tiles_for(int units, int64_t n_cap) {
+  const int64_t by_min = (n_cap + 255) / 256;
+  const int64_t by_target = (kTargetWG + units - 1) / units;
+  const int64_t by_max = (n_cap + 256 * kMaxKPL - 1) / (256 * kMaxKPL);
+  const int64_t m = by_target > by_max ? by_target : by_max;
+  return (by_min < m ? by_min : m) + 2;
 }
 
 struct Launch {
@@ -96,8 +106,7 @@ pk_status check_launch(pk_context* ctx, const char* what) {
 }
 
 void free_scratch(pk_context* c) {
-  void* ptrs[] = {c->lut, c->rq, c->scores, c->tile_hist, c->params, c->tile_base, c->tickets,
-                  c->cand_idx, c->cand_est};
+  void* ptrs[] = {c->lut, c->rq, c->scores, c->tile_hist, c->params, c->sub_base, c->cand_idx, c->cand_est};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (int k = 0; k < PK_N_KERNELS; ++k) {
@@ -229,7 +238,8 @@ pk_status pk_create(const pk_config* cfg, pk_context** out) {
     c->tiers.top[t] = t < cfg->n_tiers ? cfg->tier_top[t] : 0;
     c->tiers.weight[t] = t < cfg->n_tiers ? cfg->tier_weight[t] : 0;
   }
-  c->max_tiles = (cfg->n_capacity + 255) / 256;
+  c->max_tiles = max_tiles_for(c->units, cfg->n_capacity);
+  c->max_subs = 4 * c->max_tiles;
 
   hipError_t e = hipGetDevice(&c->device);
   if (e != hipSuccess) {
@@ -237,15 +247,14 @@ pk_status pk_create(const pk_config* cfg, pk_context** out) {
     return fail(nullptr, PK_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
   }
   struct Alloc { void** p; size_t bytes; };
-  const size_t U = c->units, Q = c->qheads, C = cfg->n_candidates, N = cfg->n_capacity, MT = c->max_tiles;
+  const size_t U = c->units, Q = c->qheads, C = cfg->n_candidates, N = cfg->n_capacity, MS = c->max_subs;
   Alloc allocs[] = {
       {(void**)&c->lut, U * 16 * 256 * 4},
       {(void**)&c->rq, Q * 128 * 4},
       {(void**)&c->scores, U * N * 4},
-      {(void**)&c->tile_hist, U * MT * pk::MAXG * pk::NBIN * 4},
+      {(void**)&c->tile_hist, U * MS * pk::MAXG * pk::NBIN * 4},
       {(void**)&c->params, U * pk::MAXG * sizeof(SelParams)},
-      {(void**)&c->tile_base, U * MT * pk::MAXG * sizeof(int2)},
-      {(void**)&c->tickets, U * 4},
+      {(void**)&c->sub_base, U * MS * pk::MAXG * sizeof(int2)},
       {(void**)&c->cand_idx, Q * C * 4},
       {(void**)&c->cand_est, Q * C * 4},
   };
@@ -259,9 +268,8 @@ pk_status pk_create(const pk_config* cfg, pk_context** out) {
                   "hipMalloc(%zu) failed: %s", a.bytes, hipGetErrorString(e));
     }
   }
-  // LUT bytes of absent query heads stay zero; tickets start at zero
-  if (hipMemset(c->lut, 0, U * 16 * 256 * 4) != hipSuccess || hipMemset(c->tickets, 0, U * 4) != hipSuccess ||
-      hipDeviceSynchronize() != hipSuccess) {
+  // LUT bytes of absent query heads stay zero
+  if (hipMemset(c->lut, 0, U * 16 * 256 * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     free_scratch(c);
     delete c;
     return fail(nullptr, PK_ERR_HIP, "scratch initialisation failed");
@@ -366,6 +374,8 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
   }
   const int tile = tile_size(ctx->units, n);
   const int tiles = (int)((n + tile - 1) / tile);
+  if (tiles > ctx->max_tiles)
+    return fail(ctx, PK_ERR_CAPACITY, "internal tiling bound exceeded (%d > %lld)", tiles, (long long)ctx->max_tiles);
   const unsigned grid = (unsigned)((int64_t)ctx->units * tiles);
   const int n_sel = (int)(n < C ? n : C);
 
@@ -382,15 +392,21 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
   {
     Launch L(ctx, PK_KERNEL_COLLIDE, stream);
     hipLaunchKernelGGL(pk::collide_kernel, dim3(grid), dim3(256), 0, stream, (const uint4*)s->codes, ctx->lut,
-                       ctx->scores, ctx->tile_hist, ctx->params, ctx->tile_base, ctx->tickets, n, s->n_capacity,
-                       tiles, (int)ctx->max_tiles, tile, ctx->group, C);
+                       ctx->scores, ctx->tile_hist, n, s->n_capacity, tiles, (int)ctx->max_subs, tile,
+                       ctx->group);
   }
   if ((st = check_launch(ctx, "collide")) != PK_OK) return st;
   {
+    Launch L(ctx, PK_KERNEL_THRESHOLD, stream);
+    hipLaunchKernelGGL(pk::threshold_kernel, dim3(ctx->units), dim3(64 * ctx->group), 0, stream, ctx->tile_hist,
+                       ctx->params, ctx->sub_base, n, 4 * tiles, (int)ctx->max_subs, tile / 4, ctx->group, C);
+  }
+  if ((st = check_launch(ctx, "threshold")) != PK_OK) return st;
+  {
     Launch L(ctx, PK_KERNEL_SELECT_RERANK, stream);
     hipLaunchKernelGGL(pk::select_rerank_kernel, dim3(grid), dim3(256), 0, stream, ctx->scores, s->records, ctx->rq,
-                       ctx->params, ctx->tile_base, ctx->cand_idx, ctx->cand_est, n, s->n_capacity, tiles,
-                       (int)ctx->max_tiles, tile, ctx->group, cfg.n_q_heads, cfg.n_kv_heads, C, ctx->tb);
+                       ctx->params, ctx->sub_base, ctx->cand_idx, ctx->cand_est, n, s->n_capacity, tiles,
+                       (int)ctx->max_subs, tile, ctx->group, cfg.n_q_heads, cfg.n_kv_heads, C, ctx->tb);
   }
   if ((st = check_launch(ctx, "select_rerank")) != PK_OK) return st;
   {
@@ -416,8 +432,8 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
 }
 
 pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, const void* k, const void* v,
-                           pk_dtype kv_dtype, const int64_t kv_strides[3], const int32_t* topk_idx, void* out,
-                           pk_dtype out_dtype, void* hip_stream) {
+                           pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows,
+                           const int32_t* topk_idx, void* out, pk_dtype out_dtype, void* hip_stream) {
   if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
   if (!q || !topk_idx || !out) return fail(ctx, PK_ERR_INVALID_ARG, "q, topk_idx and out must be non-NULL");
   for (pk_dtype d : {q_dtype, kv_dtype, out_dtype})
@@ -425,6 +441,7 @@ pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, con
   pk_status st = check_strides(ctx, k, kv_dtype, kv_strides, "k");
   if (st != PK_OK) return st;
   if ((st = check_strides(ctx, v, kv_dtype, kv_strides, "v")) != PK_OK) return st;
+  if (n_rows < 0) return fail(ctx, PK_ERR_INVALID_ARG, "n_rows < 0");
   if (!aligned(q, 8) || !aligned(out, 4) || !aligned(topk_idx, 4))
     return fail(ctx, PK_ERR_INVALID_ARG, "misaligned q / out / topk_idx");
   hipStream_t stream = (hipStream_t)hip_stream;
@@ -433,7 +450,7 @@ pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, con
   Launch L(ctx, PK_KERNEL_ATTEND, stream);
 #define PK_ATT(KT, QT, OT, R)                                                                                   \
   hipLaunchKernelGGL((pk::attend_kernel<KT, QT, OT, R>), dim3(ctx->qheads), dim3(256), 0, stream, (const QT*)q, \
-                     (const KT*)k, (const KT*)v, kv_strides[0], kv_strides[1], kv_strides[2], topk_idx, kk,    \
+                     (const KT*)k, (const KT*)v, kv_strides[0], kv_strides[1], kv_strides[2], n_rows, topk_idx, kk, \
                      c.n_q_heads, c.n_kv_heads, ctx->group, c.softmax_scale, (OT*)out)
 #define PK_ATT_R(KT, QT, OT) \
   do {                       \

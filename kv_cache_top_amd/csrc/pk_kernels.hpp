@@ -319,23 +319,35 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
 // g = weight for query head g) sits in LDS; a key's 16 code bytes index it
 // and the 16 words are summed: four 8-bit lanes of at most 64 never carry, so
 // one u32 add serves all query heads of the KV head.  S is stored packed.
-// Histogram bins 1..64 are kept per (head, bin, lane) with one byte per wave
-// (counts <= keys per lane <= 255).  The last workgroup of a unit (atomic
-// ticket) turns the tile histograms into the unit's threshold and per-tile
-// prefix counts for the selection.
+// Wave w scores the w-th quarter ("sub-tile") of the tile.  Histogram bins
+// 1..64 are kept per (head, bin, lane) with one byte per wave (counts <= keys
+// per lane <= 255), giving one histogram per sub-tile; bin 0 is implied by the
+// sub-tile length.  Each lane keeps COLLIDE_UNROLL code loads in flight.
 // ===========================================================================
+constexpr int COLLIDE_UNROLL = 8;
+
 __global__ void __launch_bounds__(256)
 collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut,
                uint32_t* __restrict__ scores, uint32_t* __restrict__ tile_hist,
-               SelParams* __restrict__ params, int2* __restrict__ tile_base,
-               uint32_t* __restrict__ tickets, int64_t n, int64_t n_cap, int tiles,
-               int max_tiles, int tile, int group, int n_candidates) {
+               int64_t n, int64_t n_cap, int tiles, int max_subs, int tile, int group) {
   __shared__ uint32_t s_lut[NSUB * 256];
   __shared__ uint32_t s_hist[MAXG * NBIN * 64];
 
   const int unit = blockIdx.x / tiles, tl = blockIdx.x - unit * tiles;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wkeys = tile >> 2;                     // keys of this wave's sub-tile (multiple of 64)
+  const int64_t w0 = (int64_t)tl * tile + (int64_t)wave * wkeys;
+  const int64_t w1 = (w0 + wkeys < n) ? w0 + wkeys : n;
+  const uint4* crow = codes + (int64_t)unit * n_cap;
+  uint32_t* srow = scores + (int64_t)unit * n_cap;
 
+  // first batch of codes in flight while the tables are staged
+  uint4 c[COLLIDE_UNROLL];
+#pragma unroll
+  for (int u = 0; u < COLLIDE_UNROLL; ++u) {
+    const int64_t i = w0 + (int64_t)u * 64 + lane;
+    c[u] = (i < w1) ? crow[i] : make_uint4(0, 0, 0, 0);
+  }
   {
     const uint4* src = reinterpret_cast<const uint4*>(lut + (int64_t)unit * NSUB * 256);
     uint4* dst = reinterpret_cast<uint4*>(s_lut);
@@ -345,177 +357,208 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
   }
   __syncthreads();
 
-  const int64_t k0 = (int64_t)tl * tile;
-  const int64_t k1 = (k0 + tile < n) ? k0 + tile : n;
-  const uint4* crow = codes + (int64_t)unit * n_cap;
-  uint32_t* srow = scores + (int64_t)unit * n_cap;
   const uint32_t incr = 1u << (8 * wave);
   const uint32_t hbase = (uint32_t)lane * 4u - 256u;     // bin s lives at s*256 - 256 + lane*4
-
-  for (int64_t i = k0 + tid; i < k1; i += 256) {
-    const uint4 c = crow[i];
-    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-    uint32_t acc = 0;
+  for (int64_t base = w0; base < w1; base += 64 * COLLIDE_UNROLL) {
+    uint4 nx[COLLIDE_UNROLL];
+    const int64_t nb = base + 64 * COLLIDE_UNROLL;
 #pragma unroll
-    for (int bb = 0; bb < NSUB; ++bb) acc += s_lut[bb * 256 + ((cw[bb >> 2] >> (8 * (bb & 3))) & 0xFFu)];
-    srow[i] = acc;
-    for (int g = 0; g < group; ++g) {
-      const uint32_t s = (acc >> (8 * g)) & 0xFFu;
-      if (s) atomicAdd(&s_hist[(g * NBIN * 64 * 4 + s * 256 + hbase) >> 2], incr);
+    for (int u = 0; u < COLLIDE_UNROLL; ++u) {
+      const int64_t i = nb + (int64_t)u * 64 + lane;
+      nx[u] = (i < w1) ? crow[i] : make_uint4(0, 0, 0, 0);
     }
+#pragma unroll
+    for (int u = 0; u < COLLIDE_UNROLL; ++u) {
+      const int64_t i = base + (int64_t)u * 64 + lane;
+      if (i < w1) {
+        const uint32_t cw[4] = {c[u].x, c[u].y, c[u].z, c[u].w};
+        uint32_t acc = 0;
+#pragma unroll
+        for (int bb = 0; bb < NSUB; ++bb) acc += s_lut[bb * 256 + ((cw[bb >> 2] >> (8 * (bb & 3))) & 0xFFu)];
+        srow[i] = acc;
+        for (int g = 0; g < group; ++g) {
+          const uint32_t sc = (acc >> (8 * g)) & 0xFFu;
+          if (sc) atomicAdd(&s_hist[(g * NBIN * 64 * 4 + sc * 256 + hbase) >> 2], incr);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < COLLIDE_UNROLL; ++u) c[u] = nx[u];
   }
   __syncthreads();
 
-  // reduce to tile histograms [unit][tile][g][bin-1]
-  uint32_t* th = tile_hist + ((int64_t)unit * max_tiles + tl) * MAXG * NBIN;
+  // reduce to sub-tile histograms [unit][4 * tile + wave][g][bin - 1]; byte w of
+  // a counter word belongs to wave w
   if (tid < group * NBIN) {
     const int g = tid / NBIN, bin = tid % NBIN;
     const uint32_t* row = s_hist + (g * NBIN + bin) * 64;
     uint32_t lo = 0, hi = 0;
     for (int i = 0; i < 64; ++i) {
       const uint32_t v = row[(i + tid) & 63];
-      lo += v & 0x00FF00FFu;
-      hi += (v >> 8) & 0x00FF00FFu;
+      lo += v & 0x00FF00FFu;          // waves 0 and 2
+      hi += (v >> 8) & 0x00FF00FFu;   // waves 1 and 3
     }
-    th[g * NBIN + bin] = (lo & 0xFFFFu) + (lo >> 16) + (hi & 0xFFFFu) + (hi >> 16);
+    const uint32_t cnt[4] = {lo & 0xFFFFu, hi & 0xFFFFu, lo >> 16, hi >> 16};
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2)
+      tile_hist[(((int64_t)unit * max_subs + 4 * tl + w2) * MAXG + g) * NBIN + bin] = cnt[w2];
   }
-  __threadfence();
-  __syncthreads();
-  // the LUT is no longer needed: its first word carries the "last tile" flag
-  if (tid == 0) {
-    __threadfence();
-    const uint32_t prev = atomicAdd(&tickets[unit], 1u);
-    s_lut[0] = (prev == (uint32_t)(tiles - 1)) ? 1u : 0u;
-    __threadfence();
-  }
-  __syncthreads();
-  if (!s_lut[0]) return;
-  __threadfence();
+}
 
-  // ---- last workgroup of this unit: threshold and per-tile prefixes -------
-  const uint32_t* uh = tile_hist + (int64_t)unit * max_tiles * MAXG * NBIN;
-  if (wave < group) {
-    const int g = wave;
-    // lane = bin - 1: total count per bin
-    uint32_t tot = 0;
-    for (int t2 = 0; t2 < tiles; ++t2) tot += uh[((int64_t)t2 * MAXG + g) * NBIN + lane];
-    // suffix sums over bins (lane l holds #{S >= l+1})
-    uint32_t suf = tot;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_down(suf, off, 64);
-      if (lane + off < 64) suf += o;
-    }
-    const uint64_t ge = __ballot(suf >= (uint32_t)n_candidates);
-    int theta;
-    uint32_t n_gt;
-    if (ge) {
-      const int top = 63 - __builtin_clzll(ge);       // highest bin with suffix >= C
-      theta = top + 1;
-      n_gt = __shfl(suf, (top + 1) & 63, 64);
-      if (top == 63) n_gt = 0;
-    } else {
-      theta = 0;
-      n_gt = __shfl(suf, 0, 64);                      // all keys with S >= 1
-    }
-    const uint32_t eq_tot = (theta > 0) ? __shfl(tot, theta - 1, 64) : (uint32_t)(n - n_gt);
-    const uint32_t want = (uint32_t)n_candidates - n_gt;
-    const uint32_t need_eq = want < eq_tot ? want : eq_tot;
-    if (lane == 0) params[unit * MAXG + g] = SelParams{theta, (int)need_eq, (int)n_gt, (int)(n_gt + need_eq)};
-    // per-tile exclusive prefixes of (#gt, #eq), tiles in chunks of 64 lanes
-    int run_gt = 0, run_eq = 0;
-    for (int base = 0; base < tiles; base += 64) {
-      const int t2 = base + lane;
-      int gt = 0, eq = 0;
-      if (t2 < tiles) {
-        const uint32_t* hrow = uh + ((int64_t)t2 * MAXG + g) * NBIN;
-        int64_t len = n - (int64_t)t2 * tile;
-        if (len > tile) len = tile;
-        int nz = 0;
-        for (int s = 1; s <= NBIN; ++s) {
-          const int c = (int)hrow[s - 1];
-          nz += c;
-          if (s > theta) gt += c;
-          else if (s == theta) eq = c;
-        }
-        if (theta == 0) eq = (int)len - nz;
-      }
-      int pg = gt, pe = eq;
-      for (int off = 1; off < 64; off <<= 1) {
-        const int og = __shfl_up(pg, off, 64), oe = __shfl_up(pe, off, 64);
-        if (lane >= off) { pg += og; pe += oe; }
-      }
-      if (t2 < tiles) tile_base[((int64_t)unit * max_tiles + t2) * MAXG + g] = make_int2(run_gt + pg - gt, run_eq + pe - eq);
-      run_gt += __shfl(pg, 63, 64);
-      run_eq += __shfl(pe, 63, 64);
-    }
+// ===========================================================================
+// threshold: per (unit, head) the score theta of the C-th best key, how many
+// keys with S == theta are taken (the lowest indices, Slides Sec. 4.2.2
+// histogram + prefix-scan selection), and per sub-tile the exclusive prefix
+// counts of keys above / at theta.  One wave per query head of the unit.
+// ===========================================================================
+__global__ void __launch_bounds__(256)
+threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__ params,
+                 int2* __restrict__ sub_base, int64_t n, int subs, int max_subs, int sub_len, int group,
+                 int n_candidates) {
+  const int unit = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave >= group) return;
+  const int g = wave;
+  const uint32_t* uh = tile_hist + (int64_t)unit * max_subs * MAXG * NBIN;
+  // lane = bin - 1: total count per bin
+  uint32_t tot = 0;
+  for (int t2 = 0; t2 < subs; ++t2) tot += uh[((int64_t)t2 * MAXG + g) * NBIN + lane];
+  // suffix sums over bins (lane l holds #{S >= l+1})
+  uint32_t suf = tot;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_down(suf, off, 64);
+    if (lane + off < 64) suf += o;
   }
-  if (tid == 0) tickets[unit] = 0;                    // ready for the next call
+  const uint64_t ge = __ballot(suf >= (uint32_t)n_candidates);
+  int theta;
+  uint32_t n_gt;
+  if (ge) {
+    const int top = 63 - __builtin_clzll(ge);       // highest bin with suffix >= C
+    theta = top + 1;
+    n_gt = __shfl(suf, (top + 1) & 63, 64);
+    if (top == 63) n_gt = 0;
+  } else {
+    theta = 0;
+    n_gt = __shfl(suf, 0, 64);                      // every key with S >= 1
+  }
+  const uint32_t eq_tot = (theta > 0) ? __shfl(tot, theta - 1, 64) : (uint32_t)(n - n_gt);
+  const uint32_t want = (uint32_t)n_candidates - n_gt;
+  const uint32_t need_eq = want < eq_tot ? want : eq_tot;
+  if (lane == 0) params[unit * MAXG + g] = SelParams{theta, (int)need_eq, (int)n_gt, (int)(n_gt + need_eq)};
+  // per-sub-tile exclusive prefixes of (#gt, #eq), 64 sub-tiles at a time
+  int run_gt = 0, run_eq = 0;
+  for (int base = 0; base < subs; base += 64) {
+    const int t2 = base + lane;
+    int gt = 0, eq = 0;
+    if (t2 < subs) {
+      const uint32_t* hrow = uh + ((int64_t)t2 * MAXG + g) * NBIN;
+      int64_t len = n - (int64_t)t2 * sub_len;
+      len = len < 0 ? 0 : (len > sub_len ? sub_len : len);
+      int nz = 0;
+#pragma unroll 16
+      for (int s = 1; s <= NBIN; ++s) {
+        const int cnt = (int)hrow[s - 1];
+        nz += cnt;
+        gt += (s > theta) ? cnt : 0;
+        eq = (s == theta) ? cnt : eq;
+      }
+      if (theta == 0) eq = (int)len - nz;
+    }
+    int pg = gt, pe = eq;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int og = __shfl_up(pg, off, 64), oe = __shfl_up(pe, off, 64);
+      if (lane >= off) { pg += og; pe += oe; }
+    }
+    if (t2 < subs) sub_base[((int64_t)unit * max_subs + t2) * MAXG + g] = make_int2(run_gt + pg - gt, run_eq + pe - eq);
+    run_gt += __shfl(pg, 63, 64);
+    run_eq += __shfl(pe, 63, 64);
+  }
 }
 
 // ===========================================================================
 // select + rerank (Slides Sec. 4.2.2 candidate selection; Eqs. (7)-(10) and
 // README "2. Decode" fused 4-bit rerank).
 //
-// Workgroup = (unit, tile), same tiling as collide.  A key is a candidate of
-// head g iff S > theta, or S == theta and fewer than need_eq keys with
-// S == theta precede it; its slot is (#gt before) + min(#eq before, need_eq),
-// which lists candidates in ascending key order.  Selected (key, head) pairs
-// queue in LDS; one lane per pair gathers the 128-byte record and evaluates
+// Workgroup = (unit, tile), same tiling as collide; wave w owns the w-th
+// quarter of the tile.  A key is a candidate of head g iff S > theta, or
+// S == theta and fewer than need_eq keys with S == theta precede it; its slot
+// is (#gt before) + min(#eq before, need_eq), which lists candidates in
+// ascending key order.  The threshold kernel supplies each sub-tile's counts
+// of earlier keys above / at theta, so the waves run independently after the
+// shared tables are built: each walks its keys 64 at a time with ballots,
+// queues the selected (key, head) pairs in a private LDS queue, and evaluates
+// them one lane per pair:
 //   est = sum_b w_b * d_b,  d_b = sum_j T_g[8b+j][nib_j]   (sequential in j, b)
 // with T_g[j][nib] = fl(v(nib) * Rq_g[j]), v(nib) = (nib & 8 ? +1 : -1) L[nib & 7].
 // ===========================================================================
+constexpr int SEL_MAXKPL = 32;   // keys per lane (tile <= 8192)
+constexpr int SEL_QW = 512;      // per-wave queue: < 256 queued + 64 keys * MAXG heads
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 __global__ void __launch_bounds__(256)
 select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restrict__ records,
                      const float* __restrict__ rot_q, const SelParams* __restrict__ params,
-                     const int2* __restrict__ tile_base, int32_t* __restrict__ cand_idx,
+                     const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx,
                      float* __restrict__ cand_est, int64_t n, int64_t n_cap, int tiles,
-                     int max_tiles, int tile, int group, int n_q_heads, int n_kv_heads,
+                     int max_subs, int tile, int group, int n_q_heads, int n_kv_heads,
                      int n_candidates, Tables tb) {
   __shared__ float s_T[MAXG * D * 16];
-  constexpr int QCAP = 256 + 256 * MAXG;   // < 256 queued + one chunk's pairs
-  __shared__ int s_widx[QCAP];
-  __shared__ int s_wpos[QCAP];
-  __shared__ int s_wcnt[4][2 * MAXG + 1];
-  __shared__ int s_nwork;
+  __shared__ int2 s_q[4][SEL_QW];                 // (key, head << 24 | slot)
+  __shared__ float s_rq[MAXG * D];
 
   const int unit = blockIdx.x / tiles, tl = blockIdx.x - unit * tiles;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int seq = unit / n_kv_heads, kvh = unit - seq * n_kv_heads;
   const int qhead0 = seq * n_q_heads + kvh * group;
+  const int64_t k0 = (int64_t)tl * tile;
+  const int64_t k1 = (k0 + tile < n) ? k0 + tile : n;
+  const int wkeys = tile >> 2;                    // multiple of 64
+  const int64_t w0 = k0 + (int64_t)wave * wkeys;
+  const uint32_t* srow = scores + (int64_t)unit * n_cap;
+  const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
 
-  for (int e = tid; e < group * D * 16; e += 256) {
-    const int g = e / (D * 16), j = (e / 16) % D, nb = e & 15;
-    const float lv = tb.levels[nb & 7];
-    const float v = (nb & 8) ? lv : -lv;
-    s_T[e] = v * rot_q[(int64_t)(qhead0 + g) * D + j];
+  // this lane's packed scores: keys w0 + r*64 + lane, all loads in flight together
+  uint32_t sp[SEL_MAXKPL];
+#pragma unroll
+  for (int r = 0; r < SEL_MAXKPL; ++r) {
+    const int64_t i = w0 + (int64_t)r * 64 + lane;
+    sp[r] = (r * 64 < wkeys && i < k1) ? srow[i] : 0u;
   }
-  int theta[MAXG], need[MAXG], bgt[MAXG], beq[MAXG];
+  for (int e = tid; e < group * D; e += 256) s_rq[e] = rot_q[(int64_t)qhead0 * D + e];
+
+  int theta[MAXG], need[MAXG], run_gt[MAXG], run_eq[MAXG];
 #pragma unroll
   for (int g = 0; g < MAXG; ++g) {
     if (g < group) {
       const SelParams p = params[unit * MAXG + g];
-      const int2 tb2 = tile_base[((int64_t)unit * max_tiles + tl) * MAXG + g];
-      theta[g] = p.theta; need[g] = p.need_eq; bgt[g] = tb2.x; beq[g] = tb2.y;
+      const int2 sb2 = sub_base[((int64_t)unit * max_subs + 4 * tl + wave) * MAXG + g];
+      theta[g] = p.theta; need[g] = p.need_eq; run_gt[g] = sb2.x; run_eq[g] = sb2.y;
     } else {
-      theta[g] = 1 << 30; need[g] = 0; bgt[g] = 0; beq[g] = 0;
+      theta[g] = 1 << 30; need[g] = 0; run_gt[g] = 0; run_eq[g] = 0;
     }
   }
-  if (tid == 0) s_nwork = 0;
-  __syncthreads();
+  __syncthreads();                                // s_rq complete
+  for (int e = tid; e < group * D * 16; e += 256) {
+    const int g = e / (D * 16), j = (e / 16) % D, nb = e & 15;
+    const float lv = tb.levels[nb & 7];
+    const float v = (nb & 8) ? lv : -lv;
+    s_T[e] = v * s_rq[g * D + j];
+  }
+  __syncthreads();                                // T complete
 
-  const int64_t k0 = (int64_t)tl * tile;
-  const int64_t k1 = (k0 + tile < n) ? k0 + tile : n;
-  const uint32_t* srow = scores + (int64_t)unit * n_cap;
-  const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
-
+  int2* q = s_q[wave];
   auto process = [&](int count) {
-    for (int w = tid; w < count; w += 256) {
-      const int i = s_widx[w], pp = s_wpos[w];
-      const int g = pp >> 24, pos = pp & 0xFFFFFF;
+    for (int w = lane; w < count; w += 64) {
+      const int2 it = q[w];
+      const int i = it.x, g = it.y >> 24, pos = it.y & 0xFFFFFF;
       const uint4* rec = reinterpret_cast<const uint4*>(rbase + (int64_t)i * 128);
       uint4 r4[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) r4[q] = rec[q];
+      for (int k = 0; k < 8; ++k) r4[k] = rec[k];
       const uint32_t* rw = reinterpret_cast<const uint32_t*>(r4);
       const float* Tg = s_T + g * D * 16;
       float est = 0.0f;
@@ -536,65 +579,37 @@ select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restr
     }
   };
 
-  int run_gt[MAXG] = {0, 0, 0, 0}, run_eq[MAXG] = {0, 0, 0, 0};
-  for (int64_t c0 = k0; c0 < k1; c0 += 256) {
-    const int64_t i = c0 + tid;
+  int queued = 0;
+#pragma unroll
+  for (int r = 0; r < SEL_MAXKPL; ++r) {
+    const int64_t c0 = w0 + (int64_t)r * 64;
+    if (r * 64 >= wkeys || c0 >= k1) break;       // uniform across the wave
+    const int64_t i = c0 + lane;
     const bool valid = i < k1;
-    const uint32_t sp = valid ? srow[i] : 0u;
-    uint64_t gtm[MAXG], eqm[MAXG];
 #pragma unroll
     for (int g = 0; g < MAXG; ++g) {
-      const int s = (int)((sp >> (8 * g)) & 0xFFu);
-      gtm[g] = __ballot(valid && g < group && s > theta[g]);
-      eqm[g] = __ballot(valid && g < group && s == theta[g]);
-      if ((tid & 63) == 0) {
-        s_wcnt[wave][2 * g] = __popcll(gtm[g]);
-        s_wcnt[wave][2 * g + 1] = __popcll(eqm[g]);
-      }
+      const int sc = (int)((sp[r] >> (8 * g)) & 0xFFu);
+      const uint64_t gtm = __ballot(valid && sc > theta[g]);
+      const uint64_t eqm = __ballot(valid && sc == theta[g]);
+      const int gt_before = run_gt[g] + (int)mbcnt(gtm);
+      const int eq_before = run_eq[g] + (int)mbcnt(eqm);
+      const bool isgt = (gtm >> lane) & 1ull, iseq = (eqm >> lane) & 1ull;
+      const bool sel = isgt || (iseq && eq_before < need[g]);
+      const uint64_t sm = __ballot(sel);
+      if (sel) q[queued + (int)mbcnt(sm)] = make_int2((int)i, (g << 24) | (gt_before + min(eq_before, need[g])));
+      queued += __popcll(sm);
+      run_gt[g] += __popcll(gtm);
+      run_eq[g] += __popcll(eqm);
     }
-    __syncthreads();
-    bool selg[MAXG];
-    int posg[MAXG];
-    int nsel = 0;
-#pragma unroll
-    for (int g = 0; g < MAXG; ++g) {
-      int wg = 0, we = 0, tg = 0, te = 0;
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const int a = s_wcnt[w2][2 * g], e2 = s_wcnt[w2][2 * g + 1];
-        if (w2 < wave) { wg += a; we += e2; }
-        tg += a; te += e2;
-      }
-      const bool isgt = (gtm[g] >> (tid & 63)) & 1ull;
-      const bool iseq = (eqm[g] >> (tid & 63)) & 1ull;
-      const int gt_before = bgt[g] + run_gt[g] + wg + (int)mbcnt(gtm[g]);
-      const int eq_before = beq[g] + run_eq[g] + we + (int)mbcnt(eqm[g]);
-      selg[g] = isgt || (iseq && eq_before < need[g]);
-      posg[g] = gt_before + (eq_before < need[g] ? eq_before : need[g]);
-      nsel += selg[g] ? 1 : 0;
-      run_gt[g] += tg;
-      run_eq[g] += te;
-    }
-    __syncthreads();
-    // append (key, head) pairs to the work queue
-#pragma unroll
-    for (int g = 0; g < MAXG; ++g) {
-      if (selg[g]) {
-        const int slot = atomicAdd(&s_nwork, 1);
-        s_widx[slot] = (int)i;
-        s_wpos[slot] = (g << 24) | posg[g];
-      }
-    }
-    __syncthreads();
-    const int cnt = s_nwork;
-    if (cnt >= 256) {
-      process(cnt);
-      __syncthreads();
-      if (tid == 0) s_nwork = 0;
-      __syncthreads();
+    if (queued >= 256) {
+      wave_lds_sync();
+      process(queued);
+      wave_lds_sync();
+      queued = 0;
     }
   }
-  __syncthreads();
-  process(s_nwork);
+  wave_lds_sync();
+  process(queued);
 }
 
 // ===========================================================================
@@ -762,7 +777,7 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
 template <typename KT, typename QT, typename OT, int MAXR>
 __global__ void __launch_bounds__(256)
 attend_kernel(const QT* __restrict__ q, const KT* __restrict__ kmat, const KT* __restrict__ vmat,
-              int64_t sb, int64_t sh, int64_t st, const int32_t* __restrict__ idx, int k,
+              int64_t sb, int64_t sh, int64_t st, int64_t n_rows, const int32_t* __restrict__ idx, int k,
               int n_q_heads, int n_kv_heads, int group, float scale, OT* __restrict__ out) {
   __shared__ float s_score[PK_MAX_TOPK_ATT];
   __shared__ float s_acc[4][D];
@@ -787,7 +802,8 @@ attend_kernel(const QT* __restrict__ q, const KT* __restrict__ kmat, const KT* _
 #pragma unroll
   for (int t = 0; t < MAXR; ++t) {
     const int r = wave + 4 * t;
-    const int ix = (r < k) ? hidx[r] : -1;
+    int ix = (r < k) ? hidx[r] : -1;
+    if ((int64_t)ix >= n_rows) ix = -1;       // out-of-range indices are padding
     rows[t] = ix;
     k0v[t] = k1v[t] = v0v[t] = v1v[t] = 0.0f;
     if (ix >= 0) {

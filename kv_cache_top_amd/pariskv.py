@@ -24,7 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 PK_OK, PK_ERR_INVALID_ARG, PK_ERR_UNSUPPORTED, PK_ERR_CAPACITY, PK_ERR_OUT_OF_MEMORY, PK_ERR_HIP = \
     0, -1, -2, -3, -4, -5
 PK_F32, PK_BF16 = 0, 1
-KERNELS = ["encode", "qprep", "collide", "select_rerank", "topk", "attend"]
+KERNELS = ["encode", "qprep", "collide", "select_rerank", "topk", "attend", "threshold"]
 PK_N_KERNELS = len(KERNELS)
 
 
@@ -68,7 +68,8 @@ _SIGS = {
                        ctypes.c_int),
     "pk_retrieve": ([_P, _P, ctypes.c_int, ctypes.POINTER(pk_summaries), _P, _P, ctypes.POINTER(pk_debug), _P],
                     ctypes.c_int),
-    "pk_sparse_attend": ([_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _I64x3, _P, _P, ctypes.c_int, _P],
+    "pk_sparse_attend": ([_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _I64x3, ctypes.c_int64, _P, _P,
+                          ctypes.c_int, _P],
                          ctypes.c_int),
     "pk_host_alloc_mapped": ([ctypes.c_size_t, ctypes.POINTER(_P), ctypes.POINTER(_P)], ctypes.c_int),
     "pk_host_free": ([_P], ctypes.c_int),
@@ -196,13 +197,14 @@ def pk_sparse_attend(ctx, q, k, v, topk_idx, out, stream=None):
     if not q.is_contiguous() or not out.is_contiguous():
         raise ValueError("q and out must be contiguous")
     _check(_lib.pk_sparse_attend(ctx, _ptr(q), _dtype(q), _ptr(k), _ptr(v), _dtype(k), _strides4(k),
-                                 _ptr(topk_idx), _ptr(out), _dtype(out), _stream(stream)), ctx)
+                                 k.shape[2], _ptr(topk_idx), _ptr(out), _dtype(out), _stream(stream)), ctx)
 
 
-def pk_sparse_attend_raw(ctx, q, k_ptr: int, v_ptr: int, kv_dtype: int, kv_strides, topk_idx, out, stream=None):
+def pk_sparse_attend_raw(ctx, q, k_ptr: int, v_ptr: int, kv_dtype: int, kv_strides, n_rows: int, topk_idx, out,
+                         stream=None):
     """Variant for K/V that are not torch tensors (e.g. mapped host memory)."""
     _check(_lib.pk_sparse_attend(ctx, _ptr(q), _dtype(q), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
-                                 kv_dtype, _I64x3(*kv_strides), _ptr(topk_idx), _ptr(out), _dtype(out),
+                                 kv_dtype, _I64x3(*kv_strides), n_rows, _ptr(topk_idx), _ptr(out), _dtype(out),
                                  _stream(stream)), ctx)
 
 

@@ -82,10 +82,13 @@ class GpuRun:
             At = to_torch(append)
             P.pk_append_keys(self.ctx.h, At, self.sums.s)
         torch.cuda.synchronize()
-        self.n = self.sums.n
         self.Q = Q
         self.Qt = to_torch(Q)
         self.debug = debug
+
+    @property
+    def n(self) -> int:
+        return self.sums.n
 
     def _mapped(self, A: np.ndarray):
         P = self.P
@@ -125,7 +128,7 @@ class GpuRun:
         self.out = torch.zeros((w.batch, w.n_q_heads, 128), dtype=odt, device="cuda")
         if self.kv_host:
             P.pk_sparse_attend_raw(self.ctx.h, self.Qt, self.kptr, self.vptr, self.kv_dtype, self.kv_strides,
-                                   self.topk_idx, self.out)
+                                   self.Kd.shape[2], self.topk_idx, self.out)
         else:
             P.pk_sparse_attend(self.ctx.h, self.Qt, self.Kt, self.Vt, self.topk_idx, self.out)
         torch.cuda.synchronize()

@@ -111,9 +111,11 @@ def test_append_equals_full_encode():
     say("case append")
     K, V, Q = _inputs(w)
     full = GpuRun(w, K, V, Q)
-    part = GpuRun(w, K[:, :, :2000], V[:, :, :2000], Q, append=K[:, :, 2000:2990], capacity=3000)
+    # encode the first 2000 rows; attention later reads all 3000 rows of K / V
+    part = GpuRun(w, K, V, Q, n=2000, capacity=3000)
     from kv_cache_top_amd import pariskv as P
     from tests.parity_util import to_torch
+    P.pk_append_keys(part.ctx.h, to_torch(K[:, :, 2000:2990]), part.sums.s)
     for t in range(2990, 3000, 4):          # several small appends, ragged last one
         P.pk_append_keys(part.ctx.h, to_torch(K[:, :, t:min(t + 4, 3000)]), part.sums.s)
     import torch
@@ -141,7 +143,13 @@ def test_capacity_and_argument_errors():
     assert ei.value.status == P.PK_ERR_CAPACITY
     assert run.n == 64
     import torch
-    bad = torch.zeros((1, 1, 8), dtype=torch.int32, device="cuda")
+    out = torch.zeros((1, 1, 8), dtype=torch.int32, device="cuda")
+    strided_q = torch.zeros((1, 1, 256), dtype=torch.bfloat16, device="cuda")[:, :, ::2]
     with pytest.raises(ValueError):
-        P.pk_retrieve(run.ctx.h, run.Qt.transpose(0, 1), run.sums.s, bad)
+        P.pk_retrieve(run.ctx.h, strided_q, run.sums.s, out)
+    # a NULL output is rejected by the library before anything is enqueued
+    import ctypes
+    st = P._lib.pk_retrieve(run.ctx.h, ctypes.c_void_p(run.Qt.data_ptr()), P.PK_BF16, ctypes.byref(run.sums.s),
+                            None, None, None, None)
+    assert st == P.PK_ERR_INVALID_ARG
     run.close()
