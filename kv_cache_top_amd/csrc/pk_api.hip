@@ -411,8 +411,16 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
   if ((st = check_launch(ctx, "select_rerank")) != PK_OK) return st;
   {
     Launch L(ctx, PK_KERNEL_TOPK, stream);
-    hipLaunchKernelGGL(pk::topk_kernel, dim3(ctx->qheads), dim3(256), 0, stream, ctx->cand_idx, ctx->cand_est,
-                       n_sel, C, k, topk_idx, topk_est);
+    const int R = (n_sel + 255) / 256;
+#define PK_TOPK(RR)                                                                                      \
+  hipLaunchKernelGGL(pk::topk_kernel<RR>, dim3(ctx->qheads), dim3(256), 0, stream, ctx->cand_idx, ctx->cand_est, \
+                     n_sel, C, k, topk_idx, topk_est)
+    if (R <= 4) PK_TOPK(4);
+    else if (R <= 8) PK_TOPK(8);
+    else if (R <= 16) PK_TOPK(16);
+    else if (R <= 32) PK_TOPK(32);
+    else PK_TOPK(64);
+#undef PK_TOPK
   }
   if ((st = check_launch(ctx, "topk")) != PK_OK) return st;
 

@@ -204,12 +204,14 @@ encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
 // qprep: query rotation and centroid activation (README "2. Decode";
 // Slides Eqs. (5)-(6), Eq. (15) tiers).
 //
-// One workgroup of 16 waves per query head; wave b owns subspace b.  Centroid
-// c's score is sum_j (bit_j(c) ? +y_j : -y_j) in fp32, sequential in j.  The
-// centroids ranking r < tier_top[last] by (score desc, c asc) are found with a
-// bitwise threshold search over the order-preserving score keys, then ranked
-// among themselves; each gets its tier weight, every other centroid 0.  The
-// weight is written as byte g (query head g of the unit) of the unit's LUT.
+// One workgroup of 16 waves per query head; wave 0 rotates the query (s-flip,
+// then a 128-point fast Walsh-Hadamard transform with butterfly stages
+// h = 1, 2, ..., 64), then wave b owns subspace b.  Centroid c's score is
+// sum_j (bit_j(c) ? +y_j : -y_j) in fp32, sequential in j.  The centroids
+// ranking r < tier_top[last] by (score desc, c asc) are found with a bitwise
+// threshold search over the order-preserving score keys, then ranked among
+// themselves; each gets its tier weight, every other centroid 0.  The weight is
+// written as byte g (query head g of the unit) of the unit's LUT.
 // ===========================================================================
 template <typename QT>
 __global__ void __launch_bounds__(1024)
@@ -217,37 +219,45 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
              float* __restrict__ rot_q, uint8_t* __restrict__ lut_bytes, Tables tb,
              TierSpec tiers) {
   __shared__ float y[D];
-  __shared__ uint32_t sel_key[NSUB][256];
-  __shared__ uint32_t sel_c[NSUB][256];
+  __shared__ uint2 sel[NSUB][256];          // (score key, centroid) of the selected centroids
+  __shared__ uint8_t lw[NSUB][256];         // tier weight per centroid
 
   const int head = blockIdx.x;              // sequence * n_q_heads + query head
   const int seq = head / n_q_heads, qh = head - seq * n_q_heads;
   const int unit = seq * n_kv_heads + qh / group, g = qh % group;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, b = tid >> 6, lane = tid & 63;
 
-  if (tid < D) {
-    float v;
+  if (b == 0) {
+    // wave 0: lane l holds coordinates l and l + 64; butterflies h = 1..32
+    // pair lanes l and l ^ h, h = 64 pairs the two registers
+    float v0, v1;
     if constexpr (sizeof(QT) == 2) {
-      v = __uint_as_float(((uint32_t)reinterpret_cast<const uint16_t*>(q)[(int64_t)head * D + tid]) << 16);
+      const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q) + (int64_t)head * D;
+      v0 = __uint_as_float((uint32_t)q16[lane] << 16);
+      v1 = __uint_as_float((uint32_t)q16[lane + 64] << 16);
     } else {
-      v = q[(int64_t)head * D + tid];
+      v0 = q[(int64_t)head * D + lane];
+      v1 = q[(int64_t)head * D + lane + 64];
     }
-    const uint32_t negb = (tb.neg_bits[tid >> 5] >> (tid & 31)) & 1u;
-    y[tid] = __uint_as_float(__float_as_uint(v) ^ (negb << 31));
+    v0 = __uint_as_float(__float_as_uint(v0) ^ (((tb.neg_bits[lane >> 5] >> (lane & 31)) & 1u) << 31));
+    v1 = __uint_as_float(__float_as_uint(v1) ^ (((tb.neg_bits[2 + (lane >> 5)] >> (lane & 31)) & 1u) << 31));
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) {
+      const bool upper = (lane & h) != 0;
+      const float p0 = __shfl_xor(v0, h, 64), p1 = __shfl_xor(v1, h, 64);
+      v0 = upper ? (p0 - v0) : (v0 + p0);
+      v1 = upper ? (p1 - v1) : (v1 + p1);
+    }
+    const float a0 = v0, a1 = v1;
+    v0 = a0 + a1;
+    v1 = a0 - a1;
+    y[lane] = v0;
+    y[lane + 64] = v1;
+    rot_q[(int64_t)head * D + lane] = v0 * tb.inv_sqrt_d;
+    rot_q[(int64_t)head * D + lane + 64] = v1 * tb.inv_sqrt_d;
   }
   __syncthreads();
-  for (int h = 1; h < D; h <<= 1) {
-    if (tid < D / 2) {
-      const int lo = (tid / h) * 2 * h + (tid % h), hi = lo + h;
-      const float a = y[lo], c = y[hi];
-      y[lo] = a + c;
-      y[hi] = a - c;
-    }
-    __syncthreads();
-  }
-  if (tid < D) rot_q[(int64_t)head * D + tid] = y[tid] * tb.inv_sqrt_d;
 
-  const int b = tid >> 6, lane = tid & 63;
   float yb[SUBD];
 #pragma unroll
   for (int j = 0; j < SUBD; ++j) yb[j] = y[b * SUBD + j];
@@ -255,10 +265,11 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint32_t c = lane + 64 * r;
-    float s = (c & 1u) ? yb[0] : -yb[0];
+    float sc = (c & 1u) ? yb[0] : -yb[0];
 #pragma unroll
-    for (int j = 1; j < SUBD; ++j) s = s + (((c >> j) & 1u) ? yb[j] : -yb[j]);
-    key[r] = orderable(s);
+    for (int j = 1; j < SUBD; ++j) sc = sc + (((c >> j) & 1u) ? yb[j] : -yb[j]);
+    key[r] = orderable(sc);
+    lw[b][c] = 0;
   }
 
   const int T = tiers.top[tiers.n_tiers - 1];
@@ -275,39 +286,40 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
 #pragma unroll
   for (int r = 0; r < 4; ++r) n_gt += __popcll(__ballot(key[r] > thr));
   const int need_eq = T - n_gt;
-  // selected centroids, compacted in ascending centroid order
+  // compact the T selected centroids (ties at thr: lowest centroid index first)
   int eq_before = 0, sel_before = 0;
-  bool sel[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint64_t eqm = __ballot(key[r] == thr);
     const int eqrank = eq_before + (int)mbcnt(eqm);
-    sel[r] = key[r] > thr || (key[r] == thr && eqrank < need_eq);
-    const uint64_t sm = __ballot(sel[r]);
-    if (sel[r]) {
-      const int p = sel_before + (int)mbcnt(sm);
-      sel_key[b][p] = key[r];
-      sel_c[b][p] = lane + 64 * r;
-    }
+    const bool sl = key[r] > thr || (key[r] == thr && eqrank < need_eq);
+    const uint64_t sm = __ballot(sl);
+    if (sl) sel[b][sel_before + (int)mbcnt(sm)] = make_uint2(key[r], lane + 64 * r);
     eq_before += __popcll(eqm);
     sel_before += __popcll(sm);
   }
-  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // rank of each selected centroid by (score desc, centroid asc); tier weight
+  for (int j = lane; j < T; j += 64) {
+    const uint2 e = sel[b][j];
+    int rank = 0;
+    for (int j2 = 0; j2 < T; ++j2) {
+      const uint2 o = sel[b][j2];
+      rank += (o.x > e.x || (o.x == e.x && o.y < e.y)) ? 1 : 0;
+    }
+    uint32_t wgt = 0;
+    for (int tt = 0; tt < tiers.n_tiers; ++tt) {
+      if (rank < tiers.top[tt]) { wgt = (uint32_t)tiers.weight[tt]; break; }
+    }
+    lw[b][e.y] = (uint8_t)wgt;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint32_t c = lane + 64 * r;
-    uint32_t wgt = 0;
-    if (sel[r]) {
-      int rank = 0;
-      for (int p = 0; p < sel_before; ++p) {
-        const uint32_t k2 = sel_key[b][p];
-        rank += (k2 > key[r] || (k2 == key[r] && sel_c[b][p] < c)) ? 1 : 0;
-      }
-      for (int tt = 0; tt < tiers.n_tiers; ++tt) {
-        if (rank < tiers.top[tt]) { wgt = (uint32_t)tiers.weight[tt]; break; }
-      }
-    }
-    lut_bytes[(((int64_t)unit * NSUB + b) * 256 + c) * 4 + g] = (uint8_t)wgt;
+    lut_bytes[(((int64_t)unit * NSUB + b) * 256 + c) * 4 + g] = lw[b][c];
   }
 }
 
@@ -341,12 +353,16 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
   const uint4* crow = codes + (int64_t)unit * n_cap;
   uint32_t* srow = scores + (int64_t)unit * n_cap;
 
+  // Loads are issued unconditionally from a clamped index (lanes past the end
+  // re-read the last key and discard it): conditional loads compile to
+  // exec-masked blocks that serialise on the memory counter.
+  const int64_t last = (w1 > w0) ? w1 - 1 : 0;
   // first batch of codes in flight while the tables are staged
   uint4 c[COLLIDE_UNROLL];
 #pragma unroll
   for (int u = 0; u < COLLIDE_UNROLL; ++u) {
     const int64_t i = w0 + (int64_t)u * 64 + lane;
-    c[u] = (i < w1) ? crow[i] : make_uint4(0, 0, 0, 0);
+    c[u] = crow[i < last ? i : last];
   }
   {
     const uint4* src = reinterpret_cast<const uint4*>(lut + (int64_t)unit * NSUB * 256);
@@ -365,7 +381,7 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
 #pragma unroll
     for (int u = 0; u < COLLIDE_UNROLL; ++u) {
       const int64_t i = nb + (int64_t)u * 64 + lane;
-      nx[u] = (i < w1) ? crow[i] : make_uint4(0, 0, 0, 0);
+      nx[u] = crow[i < last ? i : last];
     }
 #pragma unroll
     for (int u = 0; u < COLLIDE_UNROLL; ++u) {
@@ -422,6 +438,7 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
   const uint32_t* uh = tile_hist + (int64_t)unit * max_subs * MAXG * NBIN;
   // lane = bin - 1: total count per bin
   uint32_t tot = 0;
+#pragma unroll 8
   for (int t2 = 0; t2 < subs; ++t2) tot += uh[((int64_t)t2 * MAXG + g) * NBIN + lane];
   // suffix sums over bins (lane l holds #{S >= l+1})
   uint32_t suf = tot;
@@ -454,13 +471,20 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
       const uint32_t* hrow = uh + ((int64_t)t2 * MAXG + g) * NBIN;
       int64_t len = n - (int64_t)t2 * sub_len;
       len = len < 0 ? 0 : (len > sub_len ? sub_len : len);
+      uint4 h4[NBIN / 4];
+#pragma unroll
+      for (int q4 = 0; q4 < NBIN / 4; ++q4) h4[q4] = reinterpret_cast<const uint4*>(hrow)[q4];
       int nz = 0;
-#pragma unroll 16
-      for (int s = 1; s <= NBIN; ++s) {
-        const int cnt = (int)hrow[s - 1];
-        nz += cnt;
-        gt += (s > theta) ? cnt : 0;
-        eq = (s == theta) ? cnt : eq;
+#pragma unroll
+      for (int q4 = 0; q4 < NBIN / 4; ++q4) {
+        const int c4[4] = {(int)h4[q4].x, (int)h4[q4].y, (int)h4[q4].z, (int)h4[q4].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int sbin = 4 * q4 + e + 1;
+          nz += c4[e];
+          gt += (sbin > theta) ? c4[e] : 0;
+          eq = (sbin == theta) ? c4[e] : eq;
+        }
       }
       if (theta == 0) eq = (int)len - nz;
     }
@@ -522,11 +546,13 @@ select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restr
   const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
 
   // this lane's packed scores: keys w0 + r*64 + lane, all loads in flight together
+  const int64_t w1 = (w0 + wkeys < k1) ? w0 + wkeys : k1;
+  const int64_t last = (w1 > w0) ? w1 - 1 : 0;   // clamped, unconditional loads
   uint32_t sp[SEL_MAXKPL];
 #pragma unroll
   for (int r = 0; r < SEL_MAXKPL; ++r) {
     const int64_t i = w0 + (int64_t)r * 64 + lane;
-    sp[r] = (r * 64 < wkeys && i < k1) ? srow[i] : 0u;
+    sp[r] = srow[i < last ? i : last];
   }
   for (int e = tid; e < group * D; e += 256) s_rq[e] = rot_q[(int64_t)qhead0 * D + e];
 
@@ -583,9 +609,8 @@ select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restr
 #pragma unroll
   for (int r = 0; r < SEL_MAXKPL; ++r) {
     const int64_t c0 = w0 + (int64_t)r * 64;
-    if (r * 64 >= wkeys || c0 >= k1) break;       // uniform across the wave
     const int64_t i = c0 + lane;
-    const bool valid = i < k1;
+    const bool valid = i < w1;                    // false for the whole wave past its keys
 #pragma unroll
     for (int g = 0; g < MAXG; ++g) {
       const int sc = (int)((sp[r] >> (8 * g)) & 0xFFu);
@@ -616,153 +641,199 @@ select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restr
 // top-k of the candidates by (estimate desc, key index asc)
 // (Slides Sec. 4.2.3: reranking returns the Top-100 indices).
 //
-// One workgroup per query head.  Radix select over order-preserving estimate
-// keys (four 8-bit passes with LDS histograms) finds the k-th largest key;
-// keys above it are taken, and of the keys equal to it the lowest candidate
-// slots (= lowest key indices, the list being in ascending key order).  The
-// k winners are bitonic-sorted in LDS.
+// One workgroup per query head; candidate slot p is held by thread p % 256.
+// Estimates map to order-preserving u32 keys; since the candidate list is in
+// ascending key order, a lower slot breaks ties.  A histogram of the top 12
+// key bits locates the bin b* holding the k-th largest key: keys in higher bins
+// are taken, and the need = k - (#above) best keys of bin b* are found by
+// ranking that bin's keys against each other.  When bin b* is large (many
+// equal or near-equal estimates) a four-pass 8-bit radix select over the full
+// keys finds the exact k-th key instead.  The k winners are finally placed by
+// rank (count of winners ahead of each).
 // ===========================================================================
-constexpr int TOPK_MAXR = 64;   // candidates per thread (C <= 16384)
+constexpr int TOPK_BINS = 4096;        // top 12 bits of the key
+constexpr int TOPK_MAXB = 512;         // boundary-bin size handled by ranking
 
+__device__ __forceinline__ uint64_t topk_item(uint32_t key, int p) {
+  return ((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)p);   // larger = better
+}
+
+template <int R>
 __global__ void __launch_bounds__(256)
 topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_sel,
             int n_candidates, int k, int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
-  __shared__ uint32_t s_hist[256];
-  __shared__ uint64_t s_sort[PK_SORT_N];
-  __shared__ int s_misc[4];
-  __shared__ int s_wcnt[4];
+  __shared__ uint32_t s_h[TOPK_BINS];
+  __shared__ uint64_t s_b[TOPK_MAXB];
+  __shared__ uint64_t s_f[PK_SORT_N];
+  __shared__ int s_misc[8];
+  __shared__ uint32_t s_wsum[4];
 
   const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* ci = cand_idx + (int64_t)head * n_candidates;
   float* ce = cand_est + (int64_t)head * n_candidates;
-  const int R = (n_sel + 255) / 256;
   const int keff = k < n_sel ? k : n_sel;
 
-  uint32_t key[TOPK_MAXR];
+  // candidate estimates: clamped unconditional loads, all in flight together
+  float ev[R];
+  const int plast = n_sel > 0 ? n_sel - 1 : 0;
 #pragma unroll
-  for (int r = 0; r < TOPK_MAXR; ++r) {
+  for (int r = 0; r < R; ++r) {
     const int p = r * 256 + tid;
-    key[r] = (r < R && p < n_sel) ? orderable(ce[p]) : 0u;
+    ev[r] = ce[p < plast ? p : plast];
   }
+  for (int i = tid; i < TOPK_BINS; i += 256) s_h[i] = 0;
+  if (tid < 8) s_misc[tid] = 0;
   // invalid tail slots of the candidate list (n < C)
   for (int p = n_sel + tid; p < n_candidates; p += 256) {
     ci[p] = -1;
     ce[p] = -__builtin_inff();
   }
-
-  uint32_t prefix = 0, pmask = 0;
-  int krem = keff;
-  int eq_count = 0;
-  for (int pass = 0; pass < 4 && keff > 0; ++pass) {
-    const int shift = 24 - 8 * pass;
-    s_hist[tid] = 0;
-    __syncthreads();
+  uint32_t key[R];
 #pragma unroll
-    for (int r = 0; r < TOPK_MAXR; ++r) {
+  for (int r = 0; r < R; ++r) key[r] = orderable(ev[r]);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (r * 256 + tid < n_sel) atomicAdd(&s_h[key[r] >> 20], 1u);
+  __syncthreads();
+
+  // thread t owns bins [16t, 16t + 16); suffix counts from the top bin
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mine += s_h[16 * tid + i];
+  uint32_t suf = mine;                      // inclusive suffix within the wave
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_down(suf, off, 64);
+    if (lane + off < 64) suf += o;
+  }
+  if (lane == 0) s_wsum[wave] = suf;
+  __syncthreads();
+  uint32_t above = suf - mine;             // keys in bins above this thread's bins
+  for (int w2 = wave + 1; w2 < 4; ++w2) above += s_wsum[w2];
+  if (keff > 0 && above < (uint32_t)keff && above + mine >= (uint32_t)keff) {
+    uint32_t run = above;
+    for (int i = 15; i >= 0; --i) {
+      const uint32_t c = s_h[16 * tid + i];
+      if (run + c >= (uint32_t)keff) {
+        s_misc[0] = 16 * tid + i;          // boundary bin b*
+        s_misc[1] = (int)run;              // keys above it
+        s_misc[2] = (int)c;                // keys in it
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  const uint32_t bstar = (uint32_t)s_misc[0];
+  const int n_above = s_misc[1], m = s_misc[2];
+  const int need = keff - n_above;
+
+  if (keff > 0 && m <= TOPK_MAXB) {
+    // winners above b*, and the keys of b* for ranking
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
       const int p = r * 256 + tid;
-      if (r < R && p < n_sel && (key[r] & pmask) == prefix) atomicAdd(&s_hist[(key[r] >> shift) & 0xFFu], 1u);
+      if (p < n_sel) {
+        const uint32_t bin = key[r] >> 20;
+        if (bin > bstar) s_f[atomicAdd(&s_misc[3], 1)] = topk_item(key[r], p);
+        else if (bin == bstar) s_b[atomicAdd(&s_misc[4], 1)] = topk_item(key[r], p);
+      }
     }
     __syncthreads();
-    if (wave == 0) {
-      // lane l holds bins 4l..4l+3; suffix counts from the top digit
-      uint32_t h[4], sum = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { h[q] = s_hist[4 * lane + q]; sum += h[q]; }
-      uint32_t suf = sum;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_down(suf, off, 64);
-        if (lane + off < 64) suf += o;
-      }
-      // suffix count above this lane's 4 bins
-      const uint32_t above = suf - sum;
-      uint32_t run = above;
-      int dsel = -1;
-      uint32_t above_sel = 0, cnt_sel = 0;
-#pragma unroll
-      for (int q = 3; q >= 0; --q) {
-        if (dsel < 0 && run + h[q] >= (uint32_t)krem) { dsel = 4 * lane + q; above_sel = run; cnt_sel = h[q]; }
-        run += h[q];
-      }
-      // the selected digit is the highest one whose suffix count reaches krem
-      const uint64_t has = __ballot(dsel >= 0 && above < (uint32_t)krem);
-      const int src = 63 - __builtin_clzll(has);
-      const int d = __shfl(dsel, src, 64);
-      const uint32_t ab = __shfl(above_sel, src, 64);
-      const uint32_t cn = __shfl(cnt_sel, src, 64);
-      if (lane == 0) { s_misc[0] = d; s_misc[1] = (int)ab; s_misc[2] = (int)cn; }
+    for (int j = tid; j < m; j += 256) {
+      const uint64_t e = s_b[j];
+      int rank = 0;
+      for (int j2 = 0; j2 < m; ++j2) rank += (s_b[j2] > e) ? 1 : 0;
+      if (rank < need) s_f[n_above + rank] = e;
     }
-    __syncthreads();
-    const int d = s_misc[0];
-    krem -= s_misc[1];
-    eq_count = s_misc[2];
-    prefix |= (uint32_t)d << shift;
-    pmask |= 0xFFu << shift;
-    __syncthreads();
-  }
-  const uint32_t thr = prefix;
-  const int need_eq = krem;              // keys equal to thr that are taken
-
-  if (tid == 0) s_misc[3] = 0;
-  __syncthreads();
-  if (keff > 0) {
-    int eq_run = 0;
+  } else if (keff > 0) {
+    // radix select of the keff-th largest key over all candidates
+    uint32_t prefix = 0, pmask = 0;
+    int krem = keff, eq_count = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      __syncthreads();
+      s_h[tid] = 0;
+      __syncthreads();
 #pragma unroll
-    for (int r = 0; r < TOPK_MAXR; ++r) {
-      if (r < R) {                               // R is uniform: barriers below are safe
+      for (int r = 0; r < R; ++r) {
         const int p = r * 256 + tid;
-        const bool valid = p < n_sel;
-        const bool gt = valid && key[r] > thr;
-        const bool eq = valid && key[r] == thr;
-        bool take = gt;
-        if (eq_count == need_eq) {
-          take = take || eq;
-        } else {
-          const uint64_t em = __ballot(eq);
-          if (lane == 0) s_wcnt[wave] = __popcll(em);
-          __syncthreads();
-          int before = eq_run + (int)mbcnt(em), tot = 0;
-          for (int w2 = 0; w2 < 4; ++w2) {
-            if (w2 < wave) before += s_wcnt[w2];
-            tot += s_wcnt[w2];
-          }
-          take = take || (eq && before < need_eq);
-          eq_run += tot;
-          __syncthreads();
-        }
-        if (take) {
-          const int slot = atomicAdd(&s_misc[3], 1);
-          if (slot < PK_SORT_N) s_sort[slot] = ((uint64_t)key[r] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)p);
-        }
-      }
-    }
-  }
-  __syncthreads();
-  for (int p = keff + tid; p < PK_SORT_N; p += 256) s_sort[p] = 0;
-  __syncthreads();
-  // bitonic sort, descending
-  for (int size = 2; size <= PK_SORT_N; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t2 = tid; t2 < PK_SORT_N / 2; t2 += 256) {
-        const int lo = 2 * t2 - (t2 & (stride - 1));
-        const int hi = lo + stride;
-        const bool desc = ((lo & size) == 0);
-        const uint64_t a = s_sort[lo], c = s_sort[hi];
-        if ((a < c) == desc) { s_sort[lo] = c; s_sort[hi] = a; }
+        if (p < n_sel && (key[r] & pmask) == prefix) atomicAdd(&s_h[(key[r] >> shift) & 0xFFu], 1u);
       }
       __syncthreads();
+      if (wave == 0) {
+        uint32_t h[4], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { h[q] = s_h[4 * lane + q]; sum += h[q]; }
+        uint32_t sf = sum;
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t o = __shfl_down(sf, off, 64);
+          if (lane + off < 64) sf += o;
+        }
+        const uint32_t abv = sf - sum;
+        uint32_t run = abv, above_sel = 0, cnt_sel = 0;
+        int dsel = -1;
+#pragma unroll
+        for (int q = 3; q >= 0; --q) {
+          if (dsel < 0 && run + h[q] >= (uint32_t)krem) { dsel = 4 * lane + q; above_sel = run; cnt_sel = h[q]; }
+          run += h[q];
+        }
+        const uint64_t has = __ballot(dsel >= 0 && abv < (uint32_t)krem);
+        const int src = has ? 63 - __builtin_clzll(has) : 0;
+        const int d = __shfl(dsel, src, 64);
+        const uint32_t ab = __shfl(above_sel, src, 64), cn = __shfl(cnt_sel, src, 64);
+        if (lane == 0) { s_misc[5] = d < 0 ? 0 : d; s_misc[6] = (int)ab; s_misc[7] = (int)cn; }
+      }
+      __syncthreads();
+      krem -= s_misc[6];
+      eq_count = s_misc[7];
+      prefix |= (uint32_t)s_misc[5] << shift;
+      pmask |= 0xFFu << shift;
+    }
+    const uint32_t thr = prefix;
+    const int need_eq = krem;              // keys equal to thr that are taken, lowest slots first
+    int eq_run = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int p = r * 256 + tid;
+      const bool valid = p < n_sel;
+      const bool gt = valid && key[r] > thr;
+      const bool eq = valid && key[r] == thr;
+      bool take = gt;
+      if (eq_count == need_eq) {
+        take = take || eq;
+      } else {
+        const uint64_t em = __ballot(eq);
+        __syncthreads();
+        if (lane == 0) s_wsum[wave] = (uint32_t)__popcll(em);
+        __syncthreads();
+        int before = eq_run + (int)mbcnt(em), tot = 0;
+        for (int w2 = 0; w2 < 4; ++w2) {
+          if (w2 < wave) before += (int)s_wsum[w2];
+          tot += (int)s_wsum[w2];
+        }
+        take = take || (eq && before < need_eq);
+        eq_run += tot;
+      }
+      if (take) {
+        const int slot = atomicAdd(&s_misc[3], 1);
+        if (slot < PK_SORT_N) s_f[slot] = topk_item(key[r], p);
+      }
     }
   }
-  for (int r = tid; r < k; r += 256) {
-    int32_t oi = -1;
-    float oe = -__builtin_inff();
-    if (r < keff) {
-      const uint64_t v = s_sort[r];
-      const int p = (int)(0xFFFFFFFFu - (uint32_t)v);
-      oi = ci[p];
-      oe = from_orderable((uint32_t)(v >> 32));
-    }
-    out_idx[(int64_t)head * k + r] = oi;
-    if (out_est) out_est[(int64_t)head * k + r] = oe;
+  __syncthreads();
+  // place the keff winners by rank
+  for (int j = tid; j < keff; j += 256) {
+    const uint64_t e = s_f[j];
+    int rank = 0;
+    for (int j2 = 0; j2 < keff; ++j2) rank += (s_f[j2] > e) ? 1 : 0;
+    const int p = (int)(0xFFFFFFFFu - (uint32_t)e);
+    out_idx[(int64_t)head * k + rank] = ci[p];
+    if (out_est) out_est[(int64_t)head * k + rank] = from_orderable((uint32_t)(e >> 32));
+  }
+  for (int r = keff + tid; r < k; r += 256) {
+    out_idx[(int64_t)head * k + r] = -1;
+    if (out_est) out_est[(int64_t)head * k + r] = -__builtin_inff();
   }
 }
 
@@ -793,29 +864,41 @@ attend_kernel(const QT* __restrict__ q, const KT* __restrict__ kmat, const KT* _
     const float2 w = reinterpret_cast<const float2*>(q)[((int64_t)head * D >> 1) + lane];
     q0 = w.x; q1 = w.y;
   }
+  if (n_rows <= 0) {                            // no rows: nothing may be read
+    if (tid < D) {
+      if constexpr (sizeof(OT) == 2) reinterpret_cast<uint16_t*>(out)[(int64_t)head * D + tid] = 0;
+      else out[(int64_t)head * D + tid] = 0.0f;
+    }
+    return;
+  }
   const int32_t* hidx = idx + (int64_t)head * k;
   const KT* kb = kmat + seq * sb + kvh * sh;
   const KT* vb = vmat + seq * sb + kvh * sh;
 
+  // lane t holds the index of this wave's row wave + 4t (-1: padding / out of range)
+  int myix = -1;
+  {
+    const int r = wave + 4 * lane;
+    const int v = hidx[r < k ? r : k - 1];
+    myix = (lane < MAXR && r < k && v >= 0 && (int64_t)v < n_rows) ? v : -1;
+  }
+  // every row load is issued unconditionally (invalid rows read row 0 and are
+  // masked below) so that all of them are in flight together
   float k0v[MAXR], k1v[MAXR], v0v[MAXR], v1v[MAXR];
-  int rows[MAXR];
+  uint64_t okmask = 0;
 #pragma unroll
   for (int t = 0; t < MAXR; ++t) {
-    const int r = wave + 4 * t;
-    int ix = (r < k) ? hidx[r] : -1;
-    if ((int64_t)ix >= n_rows) ix = -1;       // out-of-range indices are padding
-    rows[t] = ix;
-    k0v[t] = k1v[t] = v0v[t] = v1v[t] = 0.0f;
-    if (ix >= 0) {
-      if constexpr (sizeof(KT) == 2) {
-        const uint32_t kw = reinterpret_cast<const uint32_t*>(kb + (int64_t)ix * st)[lane];
-        const uint32_t vw = reinterpret_cast<const uint32_t*>(vb + (int64_t)ix * st)[lane];
-        k0v[t] = bf16_lo(kw); k1v[t] = bf16_hi(kw); v0v[t] = bf16_lo(vw); v1v[t] = bf16_hi(vw);
-      } else {
-        const float2 kw = reinterpret_cast<const float2*>(kb + (int64_t)ix * st)[lane];
-        const float2 vw = reinterpret_cast<const float2*>(vb + (int64_t)ix * st)[lane];
-        k0v[t] = kw.x; k1v[t] = kw.y; v0v[t] = vw.x; v1v[t] = vw.y;
-      }
+    const int ix = __shfl(myix, t, 64);
+    okmask |= (ix >= 0 ? 1ull : 0ull) << t;
+    const int64_t row = ix >= 0 ? ix : 0;
+    if constexpr (sizeof(KT) == 2) {
+      const uint32_t kw = reinterpret_cast<const uint32_t*>(kb + row * st)[lane];
+      const uint32_t vw = reinterpret_cast<const uint32_t*>(vb + row * st)[lane];
+      k0v[t] = bf16_lo(kw); k1v[t] = bf16_hi(kw); v0v[t] = bf16_lo(vw); v1v[t] = bf16_hi(vw);
+    } else {
+      const float2 kw = reinterpret_cast<const float2*>(kb + row * st)[lane];
+      const float2 vw = reinterpret_cast<const float2*>(vb + row * st)[lane];
+      k0v[t] = kw.x; k1v[t] = kw.y; v0v[t] = vw.x; v1v[t] = vw.y;
     }
   }
 #pragma unroll
@@ -823,7 +906,7 @@ attend_kernel(const QT* __restrict__ q, const KT* __restrict__ kmat, const KT* _
     const int r = wave + 4 * t;
     float p = __builtin_fmaf(q0, k0v[t], q1 * k1v[t]);
     for (int off = 32; off >= 1; off >>= 1) p += __shfl_xor(p, off, 64);
-    if (lane == 0 && r < PK_MAX_TOPK_ATT) s_score[r] = (rows[t] >= 0) ? p * scale : -__builtin_inff();
+    if (lane == 0 && r < k) s_score[r] = ((okmask >> t) & 1ull) ? p * scale : -__builtin_inff();
   }
   __syncthreads();
   float m = -__builtin_inff();
@@ -837,11 +920,9 @@ attend_kernel(const QT* __restrict__ q, const KT* __restrict__ kmat, const KT* _
 #pragma unroll
   for (int t = 0; t < MAXR; ++t) {
     const int r = wave + 4 * t;
-    if (r < k && rows[t] >= 0) {
-      const float pr = __expf(s_score[r] - m);
-      a0 = __builtin_fmaf(pr, v0v[t], a0);
-      a1 = __builtin_fmaf(pr, v1v[t], a1);
-    }
+    const float pr = ((okmask >> t) & 1ull) ? __expf(s_score[r < k ? r : 0] - m) : 0.0f;
+    a0 = __builtin_fmaf(pr, v0v[t], a0);
+    a1 = __builtin_fmaf(pr, v1v[t], a1);
   }
   s_acc[wave][2 * lane] = a0;
   s_acc[wave][2 * lane + 1] = a1;
