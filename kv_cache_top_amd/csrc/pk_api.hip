@@ -67,7 +67,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Keys per collide / select workgroup: about kTargetWG workgroups over all
 // units, 256 threads each doing 1..kMaxKPL keys.
-constexpr int64_t kTargetWG = 1024, kMaxKPL = 32;
+constexpr int64_t kTargetWG = 512, kMaxKPL = 64;
 int tile_size(int units, int64_t n) {
   const int64_t want = ((int64_t)units * n + kTargetWG * 256 - 1) / (kTargetWG * 256);
   const int64_t kpl = want < 1 ? 1 : (want > kMaxKPL ? kMaxKPL : want);
@@ -391,9 +391,16 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
   if ((st = check_launch(ctx, "qprep")) != PK_OK) return st;
   {
     Launch L(ctx, PK_KERNEL_COLLIDE, stream);
-    hipLaunchKernelGGL(pk::collide_kernel, dim3(grid), dim3(256), 0, stream, (const uint4*)s->codes, ctx->lut,
-                       ctx->scores, ctx->tile_hist, n, s->n_capacity, tiles, (int)ctx->max_subs, tile,
-                       ctx->group);
+#define PK_COLLIDE(GG)                                                                                      \
+  hipLaunchKernelGGL(pk::collide_kernel<GG>, dim3(grid), dim3(256), 0, stream, (const uint4*)s->codes, ctx->lut, \
+                     ctx->scores, ctx->tile_hist, n, s->n_capacity, tiles, (int)ctx->max_subs, tile)
+    switch (ctx->group) {
+      case 1: PK_COLLIDE(1); break;
+      case 2: PK_COLLIDE(2); break;
+      case 3: PK_COLLIDE(3); break;
+      default: PK_COLLIDE(4); break;
+    }
+#undef PK_COLLIDE
   }
   if ((st = check_launch(ctx, "collide")) != PK_OK) return st;
   {
@@ -404,9 +411,17 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
   if ((st = check_launch(ctx, "threshold")) != PK_OK) return st;
   {
     Launch L(ctx, PK_KERNEL_SELECT_RERANK, stream);
-    hipLaunchKernelGGL(pk::select_rerank_kernel, dim3(grid), dim3(256), 0, stream, ctx->scores, s->records, ctx->rq,
-                       ctx->params, ctx->sub_base, ctx->cand_idx, ctx->cand_est, n, s->n_capacity, tiles,
-                       (int)ctx->max_subs, tile, ctx->group, cfg.n_q_heads, cfg.n_kv_heads, C, ctx->tb);
+#define PK_SELECT(GG)                                                                                           \
+  hipLaunchKernelGGL(pk::select_rerank_kernel<GG>, dim3(grid), dim3(256), 0, stream, ctx->scores, s->records,       \
+                     ctx->rq, ctx->params, ctx->sub_base, ctx->cand_idx, ctx->cand_est, n, s->n_capacity, tiles,     \
+                     (int)ctx->max_subs, tile, cfg.n_q_heads, cfg.n_kv_heads, C, ctx->tb)
+    switch (ctx->group) {
+      case 1: PK_SELECT(1); break;
+      case 2: PK_SELECT(2); break;
+      case 3: PK_SELECT(3); break;
+      default: PK_SELECT(4); break;
+    }
+#undef PK_SELECT
   }
   if ((st = check_launch(ctx, "select_rerank")) != PK_OK) return st;
   {

@@ -336,12 +336,14 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
 // per lane <= 255), giving one histogram per sub-tile; bin 0 is implied by the
 // sub-tile length.  Each lane keeps COLLIDE_UNROLL code loads in flight.
 // ===========================================================================
-constexpr int COLLIDE_UNROLL = 8;
+constexpr int COLLIDE_UNROLL = 16;
 
+template <int G>
 __global__ void __launch_bounds__(256)
 collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut,
                uint32_t* __restrict__ scores, uint32_t* __restrict__ tile_hist,
-               int64_t n, int64_t n_cap, int tiles, int max_subs, int tile, int group) {
+               int64_t n, int64_t n_cap, int tiles, int max_subs, int tile) {
+  constexpr int group = G;
   __shared__ uint32_t s_lut[NSUB * 256];
   __shared__ uint32_t s_hist[MAXG * NBIN * 64];
 
@@ -392,7 +394,8 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
 #pragma unroll
         for (int bb = 0; bb < NSUB; ++bb) acc += s_lut[bb * 256 + ((cw[bb >> 2] >> (8 * (bb & 3))) & 0xFFu)];
         srow[i] = acc;
-        for (int g = 0; g < group; ++g) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
           const uint32_t sc = (acc >> (8 * g)) & 0xFFu;
           if (sc) atomicAdd(&s_hist[(g * NBIN * 64 * 4 + sc * 256 + hbase) >> 2], incr);
         }
@@ -431,15 +434,35 @@ __global__ void __launch_bounds__(256)
 threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__ params,
                  int2* __restrict__ sub_base, int64_t n, int subs, int max_subs, int sub_len, int group,
                  int n_candidates) {
+  __shared__ uint32_t s_h[MAXG][64][NBIN + 1];     // [head][sub-tile in chunk][bin], padded
   const int unit = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (wave >= group) return;
   const int g = wave;
   const uint32_t* uh = tile_hist + (int64_t)unit * max_subs * MAXG * NBIN;
-  // lane = bin - 1: total count per bin
-  uint32_t tot = 0;
-#pragma unroll 8
-  for (int t2 = 0; t2 < subs; ++t2) tot += uh[((int64_t)t2 * MAXG + g) * NBIN + lane];
+  uint32_t tot = 0;                                  // lane = bin - 1
+  // pass 1: per-bin totals; lane = sub-tile, its 64 bins fetched as 16 x 16 bytes
+  for (int base = 0; base < subs; base += 64) {
+    const int t2 = base + lane;
+    const int tl = t2 < subs ? t2 : subs - 1;
+    const uint4* hrow = reinterpret_cast<const uint4*>(uh + ((int64_t)tl * MAXG + g) * NBIN);
+    uint4 h4[NBIN / 4];
+#pragma unroll
+    for (int q4 = 0; q4 < NBIN / 4; ++q4) h4[q4] = hrow[q4];
+#pragma unroll
+    for (int q4 = 0; q4 < NBIN / 4; ++q4) {
+      const bool ok = t2 < subs;
+      s_h[g][lane][4 * q4 + 0] = ok ? h4[q4].x : 0u;
+      s_h[g][lane][4 * q4 + 1] = ok ? h4[q4].y : 0u;
+      s_h[g][lane][4 * q4 + 2] = ok ? h4[q4].z : 0u;
+      s_h[g][lane][4 * q4 + 3] = ok ? h4[q4].w : 0u;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    for (int t3 = 0; t3 < 64; ++t3) tot += s_h[g][t3][lane];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
   // suffix sums over bins (lane l holds #{S >= l+1})
   uint32_t suf = tot;
   for (int off = 1; off < 64; off <<= 1) {
@@ -462,32 +485,31 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
   const uint32_t want = (uint32_t)n_candidates - n_gt;
   const uint32_t need_eq = want < eq_tot ? want : eq_tot;
   if (lane == 0) params[unit * MAXG + g] = SelParams{theta, (int)need_eq, (int)n_gt, (int)(n_gt + need_eq)};
-  // per-sub-tile exclusive prefixes of (#gt, #eq), 64 sub-tiles at a time
+  // pass 2: per-sub-tile exclusive prefixes of (#gt, #eq), 64 sub-tiles at a time
   int run_gt = 0, run_eq = 0;
   for (int base = 0; base < subs; base += 64) {
     const int t2 = base + lane;
-    int gt = 0, eq = 0;
-    if (t2 < subs) {
-      const uint32_t* hrow = uh + ((int64_t)t2 * MAXG + g) * NBIN;
-      int64_t len = n - (int64_t)t2 * sub_len;
-      len = len < 0 ? 0 : (len > sub_len ? sub_len : len);
-      uint4 h4[NBIN / 4];
+    const int tl = t2 < subs ? t2 : subs - 1;
+    const uint4* hrow = reinterpret_cast<const uint4*>(uh + ((int64_t)tl * MAXG + g) * NBIN);
+    uint4 h4[NBIN / 4];
 #pragma unroll
-      for (int q4 = 0; q4 < NBIN / 4; ++q4) h4[q4] = reinterpret_cast<const uint4*>(hrow)[q4];
-      int nz = 0;
+    for (int q4 = 0; q4 < NBIN / 4; ++q4) h4[q4] = hrow[q4];
+    int gt = 0, eq = 0, nz = 0;
 #pragma unroll
-      for (int q4 = 0; q4 < NBIN / 4; ++q4) {
-        const int c4[4] = {(int)h4[q4].x, (int)h4[q4].y, (int)h4[q4].z, (int)h4[q4].w};
+    for (int q4 = 0; q4 < NBIN / 4; ++q4) {
+      const int c4[4] = {(int)h4[q4].x, (int)h4[q4].y, (int)h4[q4].z, (int)h4[q4].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int sbin = 4 * q4 + e + 1;
-          nz += c4[e];
-          gt += (sbin > theta) ? c4[e] : 0;
-          eq = (sbin == theta) ? c4[e] : eq;
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int sbin = 4 * q4 + e + 1;
+        nz += c4[e];
+        gt += (sbin > theta) ? c4[e] : 0;
+        eq = (sbin == theta) ? c4[e] : eq;
       }
-      if (theta == 0) eq = (int)len - nz;
     }
+    int64_t len = n - (int64_t)t2 * sub_len;
+    len = len < 0 ? 0 : (len > sub_len ? sub_len : len);
+    if (theta == 0) eq = (int)len - nz;
+    if (t2 >= subs) { gt = 0; eq = 0; }
     int pg = gt, pe = eq;
     for (int off = 1; off < 64; off <<= 1) {
       const int og = __shfl_up(pg, off, 64), oe = __shfl_up(pe, off, 64);
@@ -503,138 +525,213 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
 // select + rerank (Slides Sec. 4.2.2 candidate selection; Eqs. (7)-(10) and
 // README "2. Decode" fused 4-bit rerank).
 //
-// Workgroup = (unit, tile), same tiling as collide; wave w owns the w-th
-// quarter of the tile.  A key is a candidate of head g iff S > theta, or
-// S == theta and fewer than need_eq keys with S == theta precede it; its slot
-// is (#gt before) + min(#eq before, need_eq), which lists candidates in
-// ascending key order.  The threshold kernel supplies each sub-tile's counts
-// of earlier keys above / at theta, so the waves run independently after the
-// shared tables are built: each walks its keys 64 at a time with ballots,
-// queues the selected (key, head) pairs in a private LDS queue, and evaluates
-// them one lane per pair:
-//   est = sum_b w_b * d_b,  d_b = sum_j T_g[8b+j][nib_j]   (sequential in j, b)
-// with T_g[j][nib] = fl(v(nib) * Rq_g[j]), v(nib) = (nib & 8 ? +1 : -1) L[nib & 7].
+// Workgroup = (unit, tile), same tiling as collide; wave w owns sub-tile w and
+// starts from the counts of earlier keys above / at theta supplied by the
+// threshold kernel.  A key is a candidate of head g iff S > theta, or S ==
+// theta and fewer than need_eq keys with S == theta precede it; its slot is
+// (#gt before) + min(#eq before, need_eq), which lists candidates in ascending
+// key order.
+//   1. Byte-parallel compares of the packed scores against all heads' theta
+//      find the keys at or above some head's theta; only those are compacted
+//      (in key order) for the per-head ballot logic, since every other key
+//      leaves all counts unchanged.
+//   2. Selected (key, head) pairs queue in key order, so lanes evaluating the
+//      same key read the same record.
+//   3. One lane per pair gathers the 128-byte record (the next round's records
+//      are in flight meanwhile) and evaluates
+//        est = sum_b w_b * d_b,  d_b = sum_j T_g[8b+j][nib_j]  (sequential in j, b)
+//      with T_g[j][nib] = fl(v(nib) * Rq_g[j]), v(nib) = (nib & 8 ? +1 : -1) L[nib & 7].
 // ===========================================================================
-constexpr int SEL_MAXKPL = 32;   // keys per lane (tile <= 8192)
-constexpr int SEL_QW = 512;      // per-wave queue: < 256 queued + 64 keys * MAXG heads
+constexpr int SEL_MAXKPL = 64;          // keys per lane (tile <= 16384)
+constexpr int SEL_GRP = 16;             // score chunks loaded per group
+constexpr int SEL_QFLUSH = 192;         // evaluate queued pairs once this many are waiting
+constexpr int SEL_QW = 448;             // per-wave pair queue: < SEL_QFLUSH queued + 64 keys * MAXG heads
+constexpr int SEL_BSTRIDE = SUBD * 16;            // per-block table stride
+constexpr int SEL_TSTRIDE = NSUB * SEL_BSTRIDE + 8;  // per-head table stride
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
 
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+template <int G>
 __global__ void __launch_bounds__(256)
 select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restrict__ records,
                      const float* __restrict__ rot_q, const SelParams* __restrict__ params,
                      const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx,
                      float* __restrict__ cand_est, int64_t n, int64_t n_cap, int tiles,
-                     int max_subs, int tile, int group, int n_q_heads, int n_kv_heads,
-                     int n_candidates, Tables tb) {
-  __shared__ float s_T[MAXG * D * 16];
-  __shared__ int2 s_q[4][SEL_QW];                 // (key, head << 24 | slot)
-  __shared__ float s_rq[MAXG * D];
+                     int max_subs, int tile, int n_q_heads, int n_kv_heads, int n_candidates, Tables tb) {
+  __shared__ float s_T[G * SEL_TSTRIDE];
+  __shared__ float s_rq[G * D];
+  __shared__ uint2 s_ik[4][128];                  // compacted keys: (key, packed S)
+  __shared__ int2 s_q[4][SEL_QW];                 // pairs: (key, head << 24 | slot)
 
   const int unit = blockIdx.x / tiles, tl = blockIdx.x - unit * tiles;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int seq = unit / n_kv_heads, kvh = unit - seq * n_kv_heads;
-  const int qhead0 = seq * n_q_heads + kvh * group;
+  const int qhead0 = seq * n_q_heads + kvh * G;
   const int64_t k0 = (int64_t)tl * tile;
   const int64_t k1 = (k0 + tile < n) ? k0 + tile : n;
   const int wkeys = tile >> 2;                    // multiple of 64
   const int64_t w0 = k0 + (int64_t)wave * wkeys;
+  const int64_t w1 = (w0 + wkeys < k1) ? w0 + wkeys : k1;
   const uint32_t* srow = scores + (int64_t)unit * n_cap;
   const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
 
-  // this lane's packed scores: keys w0 + r*64 + lane, all loads in flight together
-  const int64_t w1 = (w0 + wkeys < k1) ? w0 + wkeys : k1;
-  const int64_t last = (w1 > w0) ? w1 - 1 : 0;   // clamped, unconditional loads
-  uint32_t sp[SEL_MAXKPL];
+  // this lane's packed scores, keys w0 + r*64 + lane, in groups of SEL_GRP chunks
+  // (clamped, unconditional loads; the next group is in flight while one is used)
+  const int64_t last = (w1 > w0) ? w1 - 1 : 0;
+  uint32_t sp[SEL_GRP];
 #pragma unroll
-  for (int r = 0; r < SEL_MAXKPL; ++r) {
+  for (int r = 0; r < SEL_GRP; ++r) {
     const int64_t i = w0 + (int64_t)r * 64 + lane;
     sp[r] = srow[i < last ? i : last];
   }
-  for (int e = tid; e < group * D; e += 256) s_rq[e] = rot_q[(int64_t)qhead0 * D + e];
+  for (int e = tid; e < G * D; e += 256) s_rq[e] = rot_q[(int64_t)qhead0 * D + e];
 
-  int theta[MAXG], need[MAXG], run_gt[MAXG], run_eq[MAXG];
+  int need[G], run_gt[G], run_eq[G];
+  uint32_t th4 = 0x7F7F7F7Fu;                     // absent heads: theta 127, never reached
 #pragma unroll
-  for (int g = 0; g < MAXG; ++g) {
-    if (g < group) {
-      const SelParams p = params[unit * MAXG + g];
-      const int2 sb2 = sub_base[((int64_t)unit * max_subs + 4 * tl + wave) * MAXG + g];
-      theta[g] = p.theta; need[g] = p.need_eq; run_gt[g] = sb2.x; run_eq[g] = sb2.y;
-    } else {
-      theta[g] = 1 << 30; need[g] = 0; run_gt[g] = 0; run_eq[g] = 0;
-    }
+  for (int g = 0; g < G; ++g) {
+    const SelParams p = params[unit * MAXG + g];
+    const int2 sb2 = sub_base[((int64_t)unit * max_subs + 4 * tl + wave) * MAXG + g];
+    need[g] = p.need_eq; run_gt[g] = sb2.x; run_eq[g] = sb2.y;
+    th4 = (th4 & ~(0xFFu << (8 * g))) | ((uint32_t)p.theta << (8 * g));
   }
+  const uint32_t thp4 = th4 + 0x01010101u;         // theta + 1 per byte (<= 128: no carry)
   __syncthreads();                                // s_rq complete
-  for (int e = tid; e < group * D * 16; e += 256) {
+  for (int e = tid; e < G * D * 16; e += 256) {
     const int g = e / (D * 16), j = (e / 16) % D, nb = e & 15;
     const float lv = tb.levels[nb & 7];
     const float v = (nb & 8) ? lv : -lv;
-    s_T[e] = v * s_rq[g * D + j];
+    s_T[g * SEL_TSTRIDE + (j >> 3) * SEL_BSTRIDE + (j & 7) * 16 + nb] = v * s_rq[g * D + j];
   }
   __syncthreads();                                // T complete
 
+  uint2* ik = s_ik[wave];
   int2* q = s_q[wave];
-  auto process = [&](int count) {
-    for (int w = lane; w < count; w += 64) {
-      const int2 it = q[w];
-      const int i = it.x, g = it.y >> 24, pos = it.y & 0xFFFFFF;
-      const uint4* rec = reinterpret_cast<const uint4*>(rbase + (int64_t)i * 128);
-      uint4 r4[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) r4[k] = rec[k];
-      const uint32_t* rw = reinterpret_cast<const uint32_t*>(r4);
-      const float* Tg = s_T + g * D * 16;
-      float est = 0.0f;
-#pragma unroll
-      for (int bb = 0; bb < NSUB; ++bb) {
-        const uint32_t word = rw[bb];
-        float d = Tg[(bb * SUBD) * 16 + (word & 15u)];
-#pragma unroll
-        for (int j = 1; j < SUBD; ++j) d = d + Tg[(bb * SUBD + j) * 16 + ((word >> (4 * j)) & 15u)];
-        const float tprod = __uint_as_float(rw[16 + bb]) * d;
-        est = (bb == 0) ? tprod : est + tprod;
-      }
-      if (pos < n_candidates) {             // always true when the parameters match S
-        const int64_t o = (int64_t)(qhead0 + g) * n_candidates + pos;
-        cand_idx[o] = i;
-        cand_est[o] = est;
-      }
-    }
-  };
+  int nk = 0, queued = 0;
 
-  int queued = 0;
+  // per-head selection of the first `cnt` compacted keys; pairs appended in key order
+  auto select_batch = [&](int cnt) {
+    const bool valid = lane < cnt;
+    const uint2 e = ik[valid ? lane : 0];
+    const uint32_t m = e.y | 0x80808080u;
+    const uint32_t gt4 = (m - thp4) & 0x80808080u;
+    const uint32_t eq4 = ((m - th4) & 0x80808080u) ^ gt4;
+    uint32_t selmask = 0;
+    int pos[G];
 #pragma unroll
-  for (int r = 0; r < SEL_MAXKPL; ++r) {
-    const int64_t c0 = w0 + (int64_t)r * 64;
-    const int64_t i = c0 + lane;
-    const bool valid = i < w1;                    // false for the whole wave past its keys
-#pragma unroll
-    for (int g = 0; g < MAXG; ++g) {
-      const int sc = (int)((sp[r] >> (8 * g)) & 0xFFu);
-      const uint64_t gtm = __ballot(valid && sc > theta[g]);
-      const uint64_t eqm = __ballot(valid && sc == theta[g]);
+    for (int g = 0; g < G; ++g) {
+      const bool isgt = valid && ((gt4 >> (8 * g + 7)) & 1u);
+      const bool iseq = valid && ((eq4 >> (8 * g + 7)) & 1u);
+      const uint64_t gtm = __ballot(isgt), eqm = __ballot(iseq);
       const int gt_before = run_gt[g] + (int)mbcnt(gtm);
       const int eq_before = run_eq[g] + (int)mbcnt(eqm);
-      const bool isgt = (gtm >> lane) & 1ull, iseq = (eqm >> lane) & 1ull;
       const bool sel = isgt || (iseq && eq_before < need[g]);
-      const uint64_t sm = __ballot(sel);
-      if (sel) q[queued + (int)mbcnt(sm)] = make_int2((int)i, (g << 24) | (gt_before + min(eq_before, need[g])));
-      queued += __popcll(sm);
+      pos[g] = gt_before + (eq_before < need[g] ? eq_before : need[g]);
+      selmask |= (sel ? 1u : 0u) << g;
       run_gt[g] += __popcll(gtm);
       run_eq[g] += __popcll(eqm);
     }
-    if (queued >= 256) {
-      wave_lds_sync();
-      process(queued);
-      wave_lds_sync();
-      queued = 0;
+    const int c = __popc(selmask);
+    const int incl = wave_incl_scan(c, lane);
+    int slot = queued + incl - c;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if ((selmask >> g) & 1u) q[slot++] = make_int2((int)e.x, (g << 24) | pos[g]);
+    queued += __shfl(incl, 63, 64);
+  };
+
+  // evaluate `count` queued pairs, one per lane, next round's records in flight
+  auto rerank = [&](int count) {
+    if (count == 0) return;
+    wave_lds_sync();
+    int2 it = q[lane < count ? lane : count - 1];
+    uint4 cur[8];
+    {
+      const uint4* rec = reinterpret_cast<const uint4*>(rbase + (int64_t)it.x * 128);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) cur[kk] = rec[kk];
     }
+    for (int base = 0; base < count; base += 64) {
+      const int nxt_i = base + 64 + lane;
+      const int2 itn = q[nxt_i < count ? nxt_i : count - 1];
+      uint4 nxt[8];
+      const uint4* recn = reinterpret_cast<const uint4*>(rbase + (int64_t)itn.x * 128);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) nxt[kk] = recn[kk];
+
+      const int g = it.y >> 24, pos = it.y & 0xFFFFFF;
+      const uint32_t* rw = reinterpret_cast<const uint32_t*>(cur);
+      const float* Tg = s_T + g * SEL_TSTRIDE;
+      float est = 0.0f;
+#pragma unroll
+      for (int bb = 0; bb < NSUB; ++bb) {
+        const float* Tb = Tg + bb * SEL_BSTRIDE;
+        const uint32_t word = rw[bb];
+        float d = Tb[word & 15u];
+#pragma unroll
+        for (int j = 1; j < SUBD; ++j) d = d + Tb[j * 16 + ((word >> (4 * j)) & 15u)];
+        const float tprod = __uint_as_float(rw[16 + bb]) * d;
+        est = (bb == 0) ? tprod : est + tprod;
+      }
+      if (base + lane < count && pos < n_candidates) {   // pos < C whenever the parameters match S
+        const int64_t o = (int64_t)(qhead0 + g) * n_candidates + pos;
+        cand_idx[o] = it.x;
+        cand_est[o] = est;
+      }
+      it = itn;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) cur[kk] = nxt[kk];
+    }
+    wave_lds_sync();
+  };
+
+  const int ngrp = (wkeys / 64 + SEL_GRP - 1) / SEL_GRP;
+  for (int grp = 0; grp < ngrp; ++grp) {
+    uint32_t spn[SEL_GRP];
+#pragma unroll
+    for (int r = 0; r < SEL_GRP; ++r) {
+      const int64_t i = w0 + (int64_t)((grp + 1) * SEL_GRP + r) * 64 + lane;
+      spn[r] = srow[i < last ? i : last];
+    }
+#pragma unroll
+    for (int r = 0; r < SEL_GRP; ++r) {
+      const int64_t i = w0 + (int64_t)(grp * SEL_GRP + r) * 64 + lane;
+      const bool valid = i < w1;                  // false for the whole wave past its keys
+      const uint32_t ge4 = ((sp[r] | 0x80808080u) - th4) & 0x80808080u;
+      const bool interesting = valid && ge4 != 0u;
+      const uint64_t im = __ballot(interesting);
+      if (interesting) ik[nk + (int)mbcnt(im)] = make_uint2((uint32_t)i, sp[r]);
+      nk += __popcll(im);
+      if (nk >= 64) {
+        wave_lds_sync();
+        select_batch(64);
+        wave_lds_sync();
+        if (lane < nk - 64) ik[lane] = ik[64 + lane];
+        nk -= 64;
+        if (queued >= SEL_QFLUSH) {
+          rerank(queued);
+          queued = 0;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < SEL_GRP; ++r) sp[r] = spn[r];
   }
   wave_lds_sync();
-  process(queued);
+  select_batch(nk);
+  rerank(queued);
 }
 
 // ===========================================================================
@@ -643,15 +740,15 @@ select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restr
 //
 // One workgroup per query head; candidate slot p is held by thread p % 256.
 // Estimates map to order-preserving u32 keys; since the candidate list is in
-// ascending key order, a lower slot breaks ties.  A histogram of the top 12
-// key bits locates the bin b* holding the k-th largest key: keys in higher bins
-// are taken, and the need = k - (#above) best keys of bin b* are found by
-// ranking that bin's keys against each other.  When bin b* is large (many
-// equal or near-equal estimates) a four-pass 8-bit radix select over the full
-// keys finds the exact k-th key instead.  The k winners are finally placed by
-// rank (count of winners ahead of each).
+// ascending key order, a lower slot breaks ties.  Leading bits shared by every
+// candidate key are skipped; histograms of successive 12-bit digits below them
+// narrow down the bin holding the k-th largest key until that bin holds at most
+// TOPK_MAXB keys (or all its keys are equal): keys in higher bins are taken,
+// and the remaining winners of the boundary bin are found by ranking its keys
+// against each other (or, when all of its keys are equal, by lowest slot).  The
+// k winners are finally placed by rank (count of winners ahead of each).
 // ===========================================================================
-constexpr int TOPK_BINS = 4096;        // top 12 bits of the key
+constexpr int TOPK_BINS = 4096;        // 12-bit digit
 constexpr int TOPK_MAXB = 512;         // boundary-bin size handled by ranking
 
 __device__ __forceinline__ uint64_t topk_item(uint32_t key, int p) {
@@ -681,7 +778,6 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
     const int p = r * 256 + tid;
     ev[r] = ce[p < plast ? p : plast];
   }
-  for (int i = tid; i < TOPK_BINS; i += 256) s_h[i] = 0;
   if (tid < 8) s_misc[tid] = 0;
   // invalid tail slots of the candidate list (n < C)
   for (int p = n_sel + tid; p < n_candidates; p += 256) {
@@ -691,120 +787,106 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
   uint32_t key[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) key[r] = orderable(ev[r]);
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-    if (r * 256 + tid < n_sel) atomicAdd(&s_h[key[r] >> 20], 1u);
-  __syncthreads();
 
-  // thread t owns bins [16t, 16t + 16); suffix counts from the top bin
-  uint32_t mine = 0;
+  // the common leading bits of all candidate keys need no histogram: digits
+  // start at the highest bit where the largest and smallest keys differ
+  uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) mine += s_h[16 * tid + i];
-  uint32_t suf = mine;                      // inclusive suffix within the wave
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_down(suf, off, 64);
-    if (lane + off < 64) suf += o;
+  for (int r = 0; r < R; ++r) {
+    const bool ok = r * 256 + tid < n_sel;
+    kmax = ok && key[r] > kmax ? key[r] : kmax;
+    kmin = ok && key[r] < kmin ? key[r] : kmin;
   }
-  if (lane == 0) s_wsum[wave] = suf;
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t a = __shfl_xor(kmax, off, 64), c = __shfl_xor(kmin, off, 64);
+    kmax = a > kmax ? a : kmax;
+    kmin = c < kmin ? c : kmin;
+  }
+  if (lane == 0) { s_wsum[wave] = kmax; s_h[wave] = kmin; }
   __syncthreads();
-  uint32_t above = suf - mine;             // keys in bins above this thread's bins
-  for (int w2 = wave + 1; w2 < 4; ++w2) above += s_wsum[w2];
-  if (keff > 0 && above < (uint32_t)keff && above + mine >= (uint32_t)keff) {
-    uint32_t run = above;
-    for (int i = 15; i >= 0; --i) {
-      const uint32_t c = s_h[16 * tid + i];
-      if (run + c >= (uint32_t)keff) {
-        s_misc[0] = 16 * tid + i;          // boundary bin b*
-        s_misc[1] = (int)run;              // keys above it
-        s_misc[2] = (int)c;                // keys in it
-        break;
-      }
-      run += c;
+  for (int w2 = 0; w2 < 4; ++w2) {
+    kmax = s_wsum[w2] > kmax ? s_wsum[w2] : kmax;
+    kmin = s_h[w2] < kmin ? s_h[w2] : kmin;
+  }
+  const uint32_t diff = kmax ^ kmin;
+  int top = diff ? 31 - __builtin_clz(diff) : -1;        // highest undecided bit
+  uint32_t pmask = top >= 0 ? ~((2u << top) - 1u) : 0xFFFFFFFFu;
+  if (top == 31) pmask = 0;
+  uint32_t prefix = kmax & pmask;
+  int n_above = 0, need = keff, m = n_sel;
+  while (keff > 0 && top >= 0 && m > TOPK_MAXB) {        // uniform
+    const int shift = top >= 11 ? top - 11 : 0;
+    const uint32_t dmask = (top - shift == 31) ? 0xFFFFFFFFu : ((2u << (top - shift)) - 1u);
+    const int per = 16;                                   // TOPK_BINS / 256 bins per thread
+    __syncthreads();
+    for (int i = tid; i < TOPK_BINS; i += 256) s_h[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r * 256 + tid < n_sel && (key[r] & pmask) == prefix) atomicAdd(&s_h[(key[r] >> shift) & dmask], 1u);
+    __syncthreads();
+    // thread t owns bins [per*t, per*t + per); suffix counts from the top bin
+    uint32_t mine = 0;
+    for (int i = 0; i < per; ++i) mine += s_h[per * tid + i];
+    uint32_t suf = mine;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += o;
     }
+    if (lane == 0) s_wsum[wave] = suf;
+    __syncthreads();
+    uint32_t above = suf - mine;
+    for (int w2 = wave + 1; w2 < 4; ++w2) above += s_wsum[w2];
+    if (above < (uint32_t)need && above + mine >= (uint32_t)need) {
+      uint32_t run = above;
+      for (int i = per - 1; i >= 0; --i) {
+        const uint32_t c = s_h[per * tid + i];
+        if (run + c >= (uint32_t)need) {
+          s_misc[0] = per * tid + i;       // boundary digit
+          s_misc[1] = (int)run;            // keys above it within the current range
+          s_misc[2] = (int)c;              // keys with this digit
+          break;
+        }
+        run += c;
+      }
+    }
+    __syncthreads();
+    n_above += s_misc[1];
+    need -= s_misc[1];
+    m = s_misc[2];
+    prefix |= (uint32_t)s_misc[0] << shift;
+    pmask |= dmask << shift;
+    top = shift - 1;
   }
   __syncthreads();
-  const uint32_t bstar = (uint32_t)s_misc[0];
-  const int n_above = s_misc[1], m = s_misc[2];
-  const int need = keff - n_above;
 
-  if (keff > 0 && m <= TOPK_MAXB) {
-    // winners above b*, and the keys of b* for ranking
+  if (keff > 0) {
+    // winners strictly above the boundary range, and the boundary range itself
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int p = r * 256 + tid;
       if (p < n_sel) {
-        const uint32_t bin = key[r] >> 20;
-        if (bin > bstar) s_f[atomicAdd(&s_misc[3], 1)] = topk_item(key[r], p);
-        else if (bin == bstar) s_b[atomicAdd(&s_misc[4], 1)] = topk_item(key[r], p);
+        const uint32_t mk = key[r] & pmask;
+        if (mk > prefix) s_f[atomicAdd(&s_misc[3], 1)] = topk_item(key[r], p);
+        else if (mk == prefix && m <= TOPK_MAXB) s_b[atomicAdd(&s_misc[4], 1)] = topk_item(key[r], p);
       }
     }
     __syncthreads();
-    for (int j = tid; j < m; j += 256) {
-      const uint64_t e = s_b[j];
-      int rank = 0;
-      for (int j2 = 0; j2 < m; ++j2) rank += (s_b[j2] > e) ? 1 : 0;
-      if (rank < need) s_f[n_above + rank] = e;
-    }
-  } else if (keff > 0) {
-    // radix select of the keff-th largest key over all candidates
-    uint32_t prefix = 0, pmask = 0;
-    int krem = keff, eq_count = 0;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      __syncthreads();
-      s_h[tid] = 0;
-      __syncthreads();
+    if (m <= TOPK_MAXB) {
+      for (int j = tid; j < m; j += 256) {
+        const uint64_t e = s_b[j];
+        int rank = 0;
+        for (int j2 = 0; j2 < m; ++j2) rank += (s_b[j2] > e) ? 1 : 0;
+        if (rank < need) s_f[n_above + rank] = e;
+      }
+    } else {
+      // every key of the boundary range is equal: the lowest slots win
+      int eq_run = 0;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int p = r * 256 + tid;
-        if (p < n_sel && (key[r] & pmask) == prefix) atomicAdd(&s_h[(key[r] >> shift) & 0xFFu], 1u);
-      }
-      __syncthreads();
-      if (wave == 0) {
-        uint32_t h[4], sum = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) { h[q] = s_h[4 * lane + q]; sum += h[q]; }
-        uint32_t sf = sum;
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t o = __shfl_down(sf, off, 64);
-          if (lane + off < 64) sf += o;
-        }
-        const uint32_t abv = sf - sum;
-        uint32_t run = abv, above_sel = 0, cnt_sel = 0;
-        int dsel = -1;
-#pragma unroll
-        for (int q = 3; q >= 0; --q) {
-          if (dsel < 0 && run + h[q] >= (uint32_t)krem) { dsel = 4 * lane + q; above_sel = run; cnt_sel = h[q]; }
-          run += h[q];
-        }
-        const uint64_t has = __ballot(dsel >= 0 && abv < (uint32_t)krem);
-        const int src = has ? 63 - __builtin_clzll(has) : 0;
-        const int d = __shfl(dsel, src, 64);
-        const uint32_t ab = __shfl(above_sel, src, 64), cn = __shfl(cnt_sel, src, 64);
-        if (lane == 0) { s_misc[5] = d < 0 ? 0 : d; s_misc[6] = (int)ab; s_misc[7] = (int)cn; }
-      }
-      __syncthreads();
-      krem -= s_misc[6];
-      eq_count = s_misc[7];
-      prefix |= (uint32_t)s_misc[5] << shift;
-      pmask |= 0xFFu << shift;
-    }
-    const uint32_t thr = prefix;
-    const int need_eq = krem;              // keys equal to thr that are taken, lowest slots first
-    int eq_run = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int p = r * 256 + tid;
-      const bool valid = p < n_sel;
-      const bool gt = valid && key[r] > thr;
-      const bool eq = valid && key[r] == thr;
-      bool take = gt;
-      if (eq_count == need_eq) {
-        take = take || eq;
-      } else {
+        const bool eq = p < n_sel && (key[r] & pmask) == prefix;
         const uint64_t em = __ballot(eq);
-        __syncthreads();
         if (lane == 0) s_wsum[wave] = (uint32_t)__popcll(em);
         __syncthreads();
         int before = eq_run + (int)mbcnt(em), tot = 0;
@@ -812,12 +894,9 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
           if (w2 < wave) before += (int)s_wsum[w2];
           tot += (int)s_wsum[w2];
         }
-        take = take || (eq && before < need_eq);
+        if (eq && before < need) s_f[n_above + before] = topk_item(key[r], p);
         eq_run += tot;
-      }
-      if (take) {
-        const int slot = atomicAdd(&s_misc[3], 1);
-        if (slot < PK_SORT_N) s_f[slot] = topk_item(key[r], p);
+        __syncthreads();
       }
     }
   }
