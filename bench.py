@@ -62,7 +62,7 @@ def algorithmic_bytes(w, n: int) -> dict:
     keff = min(w.top_k, n_sel)
     return {
         "collide": CODE_BYTES * n * w.units,
-        "select_rerank": RECORD_BYTES * n_sel * w.batch * w.n_q_heads,
+        "rerank": RECORD_BYTES * n_sel * w.batch * w.n_q_heads,
         "attend": 2 * kv_row * keff * w.batch * w.n_q_heads,
         "encode": (kv_row + CODE_BYTES + RECORD_BYTES + 4) * w.units if w.append_steps else 0,
     }
@@ -167,7 +167,7 @@ def main():
     torch.cuda.synchronize()
     # distinct summary buffers per layer so a step's codes are not LLC-resident
     step_bytes = algorithmic_bytes(w, w.n)
-    touched = step_bytes["collide"] + step_bytes["select_rerank"]
+    touched = step_bytes["collide"] + step_bytes["rerank"]
     layers = args.layers or max(1, min(8, int(np.ceil(1.0 * 2 ** 30 / max(touched, 1)))))
     sums = [sums0] + [sums0.clone(cfg) for _ in range(layers - 1)]
     Qd = [to_torch(q) for q in Q_pool]
@@ -254,7 +254,7 @@ def main():
         torch.cuda.synchronize()
         del a, b2
 
-    step_alg = nb["collide"] + nb["select_rerank"] + nb["attend"] + nb["encode"]
+    step_alg = nb["collide"] + nb["rerank"] + nb["attend"] + nb["encode"]
     res = {
         "metric": METRIC,
         "value": round(1e3 / ms, 2),

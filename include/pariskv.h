@@ -138,11 +138,12 @@ typedef enum {
   PK_KERNEL_ENCODE = 0,
   PK_KERNEL_QPREP = 1,
   PK_KERNEL_COLLIDE = 2,
-  PK_KERNEL_SELECT_RERANK = 3,
-  PK_KERNEL_TOPK = 4,
-  PK_KERNEL_ATTEND = 5,
-  PK_KERNEL_THRESHOLD = 6,
-  PK_N_KERNELS = 7
+  PK_KERNEL_THRESHOLD = 3,
+  PK_KERNEL_SELECT = 4,
+  PK_KERNEL_RERANK = 5,
+  PK_KERNEL_TOPK = 6,
+  PK_KERNEL_ATTEND = 7,
+  PK_N_KERNELS = 8
 } pk_kernel_id;
 
 typedef struct {

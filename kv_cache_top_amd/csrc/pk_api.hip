@@ -410,11 +410,11 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
   }
   if ((st = check_launch(ctx, "threshold")) != PK_OK) return st;
   {
-    Launch L(ctx, PK_KERNEL_SELECT_RERANK, stream);
-#define PK_SELECT(GG)                                                                                           \
-  hipLaunchKernelGGL(pk::select_rerank_kernel<GG>, dim3(grid), dim3(256), 0, stream, ctx->scores, s->records,       \
-                     ctx->rq, ctx->params, ctx->sub_base, ctx->cand_idx, ctx->cand_est, n, s->n_capacity, tiles,     \
-                     (int)ctx->max_subs, tile, cfg.n_q_heads, cfg.n_kv_heads, C, ctx->tb)
+    Launch L(ctx, PK_KERNEL_SELECT, stream);
+#define PK_SELECT(GG)                                                                                          \
+  hipLaunchKernelGGL(pk::select_kernel<GG>, dim3(grid), dim3(256), 0, stream, ctx->scores, ctx->params,          \
+                     ctx->sub_base, ctx->cand_idx, n, s->n_capacity, tiles, (int)ctx->max_subs, tile,              \
+                     cfg.n_q_heads, cfg.n_kv_heads, C)
     switch (ctx->group) {
       case 1: PK_SELECT(1); break;
       case 2: PK_SELECT(2); break;
@@ -423,7 +423,15 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
     }
 #undef PK_SELECT
   }
-  if ((st = check_launch(ctx, "select_rerank")) != PK_OK) return st;
+  if ((st = check_launch(ctx, "select")) != PK_OK) return st;
+  {
+    Launch L(ctx, PK_KERNEL_RERANK, stream);
+    const int chunks = (n_sel + pk::RR_PER_WG - 1) / pk::RR_PER_WG;
+    hipLaunchKernelGGL(pk::rerank_kernel, dim3((unsigned)((int64_t)ctx->qheads * chunks)), dim3(256), 0, stream,
+                       s->records, ctx->rq, ctx->cand_idx, ctx->cand_est, s->n_capacity, n_sel, C, chunks,
+                       cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->tb);
+  }
+  if ((st = check_launch(ctx, "rerank")) != PK_OK) return st;
   {
     Launch L(ctx, PK_KERNEL_TOPK, stream);
     const int R = (n_sel + 255) / 256;

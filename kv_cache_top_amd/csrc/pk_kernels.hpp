@@ -522,58 +522,33 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
 }
 
 // ===========================================================================
-// select + rerank (Slides Sec. 4.2.2 candidate selection; Eqs. (7)-(10) and
-// README "2. Decode" fused 4-bit rerank).
+// select: the candidate set of every query head (Slides Sec. 4.2.2: keep the
+// top-beta keys by S_i, chosen by histogram + prefix scan instead of a sort;
+// Sec. 4.3: C = ceil(beta n)).
 //
 // Workgroup = (unit, tile), same tiling as collide; wave w owns sub-tile w and
 // starts from the counts of earlier keys above / at theta supplied by the
 // threshold kernel.  A key is a candidate of head g iff S > theta, or S ==
 // theta and fewer than need_eq keys with S == theta precede it; its slot is
 // (#gt before) + min(#eq before, need_eq), which lists candidates in ascending
-// key order.
-//   1. Byte-parallel compares of the packed scores against all heads' theta
-//      find the keys at or above some head's theta; only those are compacted
-//      (in key order) for the per-head ballot logic, since every other key
-//      leaves all counts unchanged.
-//   2. Selected (key, head) pairs queue in key order, so lanes evaluating the
-//      same key read the same record.
-//   3. One lane per pair gathers the 128-byte record (the next round's records
-//      are in flight meanwhile) and evaluates
-//        est = sum_b w_b * d_b,  d_b = sum_j T_g[8b+j][nib_j]  (sequential in j, b)
-//      with T_g[j][nib] = fl(v(nib) * Rq_g[j]), v(nib) = (nib & 8 ? +1 : -1) L[nib & 7].
+// key order.  Byte-parallel compares of the packed scores against all heads'
+// theta find the keys at or above some head's theta; only those (about a
+// tenth of the keys) are compacted, in key order, for the per-head ballots,
+// since every other key leaves all counts unchanged.
 // ===========================================================================
-constexpr int SEL_MAXKPL = 64;          // keys per lane (tile <= 16384)
 constexpr int SEL_GRP = 16;             // score chunks loaded per group
-constexpr int SEL_QFLUSH = 192;         // evaluate queued pairs once this many are waiting
-constexpr int SEL_QW = 448;             // per-wave pair queue: < SEL_QFLUSH queued + 64 keys * MAXG heads
-constexpr int SEL_BSTRIDE = SUBD * 16;            // per-block table stride
-constexpr int SEL_TSTRIDE = NSUB * SEL_BSTRIDE + 8;  // per-head table stride
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
-  return v;
-}
-
 template <int G>
 __global__ void __launch_bounds__(256)
-select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restrict__ records,
-                     const float* __restrict__ rot_q, const SelParams* __restrict__ params,
-                     const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx,
-                     float* __restrict__ cand_est, int64_t n, int64_t n_cap, int tiles,
-                     int max_subs, int tile, int n_q_heads, int n_kv_heads, int n_candidates, Tables tb) {
-  __shared__ float s_T[G * SEL_TSTRIDE];
-  __shared__ float s_rq[G * D];
+select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__ params,
+              const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx, int64_t n, int64_t n_cap,
+              int tiles, int max_subs, int tile, int n_q_heads, int n_kv_heads, int n_candidates) {
   __shared__ uint2 s_ik[4][128];                  // compacted keys: (key, packed S)
-  __shared__ int2 s_q[4][SEL_QW];                 // pairs: (key, head << 24 | slot)
 
   const int unit = blockIdx.x / tiles, tl = blockIdx.x - unit * tiles;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -585,9 +560,8 @@ select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restr
   const int64_t w0 = k0 + (int64_t)wave * wkeys;
   const int64_t w1 = (w0 + wkeys < k1) ? w0 + wkeys : k1;
   const uint32_t* srow = scores + (int64_t)unit * n_cap;
-  const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
 
-  // this lane's packed scores, keys w0 + r*64 + lane, in groups of SEL_GRP chunks
+  // packed scores of keys w0 + r*64 + lane, in groups of SEL_GRP chunks
   // (clamped, unconditional loads; the next group is in flight while one is used)
   const int64_t last = (w1 > w0) ? w1 - 1 : 0;
   uint32_t sp[SEL_GRP];
@@ -596,8 +570,6 @@ select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restr
     const int64_t i = w0 + (int64_t)r * 64 + lane;
     sp[r] = srow[i < last ? i : last];
   }
-  for (int e = tid; e < G * D; e += 256) s_rq[e] = rot_q[(int64_t)qhead0 * D + e];
-
   int need[G], run_gt[G], run_eq[G];
   uint32_t th4 = 0x7F7F7F7Fu;                     // absent heads: theta 127, never reached
 #pragma unroll
@@ -608,28 +580,16 @@ select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restr
     th4 = (th4 & ~(0xFFu << (8 * g))) | ((uint32_t)p.theta << (8 * g));
   }
   const uint32_t thp4 = th4 + 0x01010101u;         // theta + 1 per byte (<= 128: no carry)
-  __syncthreads();                                // s_rq complete
-  for (int e = tid; e < G * D * 16; e += 256) {
-    const int g = e / (D * 16), j = (e / 16) % D, nb = e & 15;
-    const float lv = tb.levels[nb & 7];
-    const float v = (nb & 8) ? lv : -lv;
-    s_T[g * SEL_TSTRIDE + (j >> 3) * SEL_BSTRIDE + (j & 7) * 16 + nb] = v * s_rq[g * D + j];
-  }
-  __syncthreads();                                // T complete
-
   uint2* ik = s_ik[wave];
-  int2* q = s_q[wave];
-  int nk = 0, queued = 0;
+  int nk = 0;
 
-  // per-head selection of the first `cnt` compacted keys; pairs appended in key order
+  // per-head selection of the first `cnt` compacted keys
   auto select_batch = [&](int cnt) {
     const bool valid = lane < cnt;
     const uint2 e = ik[valid ? lane : 0];
     const uint32_t m = e.y | 0x80808080u;
     const uint32_t gt4 = (m - thp4) & 0x80808080u;
     const uint32_t eq4 = ((m - th4) & 0x80808080u) ^ gt4;
-    uint32_t selmask = 0;
-    int pos[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const bool isgt = valid && ((gt4 >> (8 * g + 7)) & 1u);
@@ -638,63 +598,12 @@ select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restr
       const int gt_before = run_gt[g] + (int)mbcnt(gtm);
       const int eq_before = run_eq[g] + (int)mbcnt(eqm);
       const bool sel = isgt || (iseq && eq_before < need[g]);
-      pos[g] = gt_before + (eq_before < need[g] ? eq_before : need[g]);
-      selmask |= (sel ? 1u : 0u) << g;
+      const int pos = gt_before + (eq_before < need[g] ? eq_before : need[g]);
+      if (sel && pos < n_candidates)              // pos < C whenever the parameters match S
+        cand_idx[(int64_t)(qhead0 + g) * n_candidates + pos] = (int)e.x;
       run_gt[g] += __popcll(gtm);
       run_eq[g] += __popcll(eqm);
     }
-    const int c = __popc(selmask);
-    const int incl = wave_incl_scan(c, lane);
-    int slot = queued + incl - c;
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      if ((selmask >> g) & 1u) q[slot++] = make_int2((int)e.x, (g << 24) | pos[g]);
-    queued += __shfl(incl, 63, 64);
-  };
-
-  // evaluate `count` queued pairs, one per lane, next round's records in flight
-  auto rerank = [&](int count) {
-    if (count == 0) return;
-    wave_lds_sync();
-    int2 it = q[lane < count ? lane : count - 1];
-    uint4 cur[8];
-    {
-      const uint4* rec = reinterpret_cast<const uint4*>(rbase + (int64_t)it.x * 128);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) cur[kk] = rec[kk];
-    }
-    for (int base = 0; base < count; base += 64) {
-      const int nxt_i = base + 64 + lane;
-      const int2 itn = q[nxt_i < count ? nxt_i : count - 1];
-      uint4 nxt[8];
-      const uint4* recn = reinterpret_cast<const uint4*>(rbase + (int64_t)itn.x * 128);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) nxt[kk] = recn[kk];
-
-      const int g = it.y >> 24, pos = it.y & 0xFFFFFF;
-      const uint32_t* rw = reinterpret_cast<const uint32_t*>(cur);
-      const float* Tg = s_T + g * SEL_TSTRIDE;
-      float est = 0.0f;
-#pragma unroll
-      for (int bb = 0; bb < NSUB; ++bb) {
-        const float* Tb = Tg + bb * SEL_BSTRIDE;
-        const uint32_t word = rw[bb];
-        float d = Tb[word & 15u];
-#pragma unroll
-        for (int j = 1; j < SUBD; ++j) d = d + Tb[j * 16 + ((word >> (4 * j)) & 15u)];
-        const float tprod = __uint_as_float(rw[16 + bb]) * d;
-        est = (bb == 0) ? tprod : est + tprod;
-      }
-      if (base + lane < count && pos < n_candidates) {   // pos < C whenever the parameters match S
-        const int64_t o = (int64_t)(qhead0 + g) * n_candidates + pos;
-        cand_idx[o] = it.x;
-        cand_est[o] = est;
-      }
-      it = itn;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) cur[kk] = nxt[kk];
-    }
-    wave_lds_sync();
   };
 
   const int ngrp = (wkeys / 64 + SEL_GRP - 1) / SEL_GRP;
@@ -720,10 +629,7 @@ select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restr
         wave_lds_sync();
         if (lane < nk - 64) ik[lane] = ik[64 + lane];
         nk -= 64;
-        if (queued >= SEL_QFLUSH) {
-          rerank(queued);
-          queued = 0;
-        }
+        wave_lds_sync();
       }
     }
 #pragma unroll
@@ -731,7 +637,86 @@ select_rerank_kernel(const uint32_t* __restrict__ scores, const uint8_t* __restr
   }
   wave_lds_sync();
   select_batch(nk);
-  rerank(queued);
+}
+
+// ===========================================================================
+// rerank: the 4-bit inner-product estimate of every candidate (Slides,
+// Eqs. (7)-(10); README "2. Decode", fused 4-bit reranking).
+//
+// Workgroup = (query head, RR_PER_WG consecutive candidate slots); one lane
+// per candidate gathers the key's 128-byte record (nibble words, then the 16
+// weights) and evaluates
+//   est = sum_b w_b * d_b,  d_b = sum_j T[8b+j][nib_j]   (sequential in j and b)
+// with T[j][nib] = fl(v(nib) * Rq[j]), v(nib) = (nib & 8 ? +1 : -1) L[nib & 7],
+// i.e. fl(v * Rq) of the estimator taken from an LDS table.  The kernel needs
+// few registers, so eight waves per SIMD hide the gathers' latency.
+// ===========================================================================
+constexpr int RR_ROUNDS = 4;                      // candidates per lane
+constexpr int RR_PER_WG = 256 * RR_ROUNDS;
+
+__global__ void __launch_bounds__(256)
+rerank_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot_q,
+              const int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int64_t n_cap,
+              int n_sel, int n_candidates, int chunks, int n_q_heads, int n_kv_heads, int group, Tables tb) {
+  __shared__ float s_T[D * 16];
+  const int head = blockIdx.x / chunks, ch = blockIdx.x - head * chunks;
+  const int tid = threadIdx.x;
+  const int seq = head / n_q_heads, qh = head - seq * n_q_heads;
+  const int unit = seq * n_kv_heads + qh / group;
+  const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
+  const int32_t* ci = cand_idx + (int64_t)head * n_candidates;
+  float* ce = cand_est + (int64_t)head * n_candidates;
+  const int p0 = ch * RR_PER_WG;
+  const int plast = n_sel - 1;
+
+  auto load = [&](int r, uint4 (&buf)[8]) {
+    const int p = p0 + r * 256 + tid;
+    const int key = ci[p < plast ? p : plast];
+    const uint4* rec = reinterpret_cast<const uint4*>(rbase + (int64_t)key * 128);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) buf[k] = rec[k];
+  };
+  uint4 ra[8];
+  load(0, ra);
+  for (int e = tid; e < D * 16; e += 256) {
+    const int j = e >> 4, nb = e & 15;
+    const float lv = tb.levels[nb & 7];
+    const float v = (nb & 8) ? lv : -lv;
+    s_T[e] = v * rot_q[(int64_t)head * D + j];
+  }
+  __syncthreads();
+
+  auto eval = [&](int r, const uint4 (&buf)[8]) {
+    const uint32_t* rw = reinterpret_cast<const uint32_t*>(buf);
+    float est = 0.0f;
+#pragma unroll
+    for (int bb = 0; bb < NSUB; ++bb) {
+      const uint32_t word = rw[bb];
+      // byte k of lo / hi = 4 * nibble (2k) / (2k + 1), a byte offset into the table row
+      uint32_t lo = (word << 2) & 0x3C3C3C3Cu, hi = (word >> 2) & 0x3C3C3C3Cu;
+      asm volatile("" : "+v"(lo), "+v"(hi));
+      const char* Tb = reinterpret_cast<const char*>(s_T) + bb * (SUBD * 16 * 4);
+      float v[SUBD];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = *reinterpret_cast<const float*>(Tb + (2 * k) * 64 + ((lo >> (8 * k)) & 0xFFu));
+        v[2 * k + 1] = *reinterpret_cast<const float*>(Tb + (2 * k + 1) * 64 + ((hi >> (8 * k)) & 0xFFu));
+      }
+      float d = v[0];
+#pragma unroll
+      for (int j = 1; j < SUBD; ++j) d = d + v[j];
+      const float tprod = __uint_as_float(rw[16 + bb]) * d;
+      est = (bb == 0) ? tprod : est + tprod;
+      asm volatile("" : "+v"(est));     // keep the sum here, not sunk into the store's branch
+    }
+    const int p = p0 + r * 256 + tid;
+    if (p < n_sel) ce[p] = est;
+  };
+#pragma unroll 1
+  for (int r = 0; r < RR_ROUNDS; ++r) {
+    if (r) load(r, ra);
+    eval(r, ra);
+  }
 }
 
 // ===========================================================================
