@@ -201,14 +201,13 @@ pk_status pk_summary_bytes(const pk_config* cfg, size_t* codes, size_t* records,
 pk_status pk_tables(uint64_t seed, int8_t signs[128], float levels[8], float thresholds[7]) {
   if (!signs || !levels || !thresholds) return fail(nullptr, PK_ERR_INVALID_ARG, "NULL table pointer");
   pk::srht_signs(seed, signs);
-  static float L[8], T[7];
-  static bool have = false;
-  if (!have) {      // the quantiser does not depend on the seed: compute once
-    pk::magnitude_tables(L, T);
-    have = true;
-  }
-  std::memcpy(levels, L, sizeof(L));
-  std::memcpy(thresholds, T, sizeof(T));
+  struct Quantiser {
+    float L[8], T[7];
+    Quantiser() { pk::magnitude_tables(L, T); }
+  };
+  static const Quantiser q;   // seed-independent; computed once, thread-safe initialisation
+  std::memcpy(levels, q.L, sizeof(q.L));
+  std::memcpy(thresholds, q.T, sizeof(q.T));
   return PK_OK;
 }
 
