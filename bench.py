@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+                    help="also run a plain 1 GiB device copy (HBM traffic counter calibration)")
     return ap.parse_args()
 
 
@@ -247,12 +247,20 @@ def main():
     log("[bench] per-kernel: " + json.dumps(kern))
 
     if args.copy_calibration:
-        a = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+        # 1 GiB each way through the library's 16-byte-per-lane copy: the counter
+        # runs divide by what FETCH_SIZE / WRITE_SIZE read for it
+        a = torch.ones(2 ** 30, dtype=torch.uint8, device=dev)
         b2 = torch.empty_like(a)
         for _ in range(3):
-            b2.copy_(a)
+            P.pk_calibration_copy(b2, a)
         torch.cuda.synchronize()
+        if not torch.equal(a, b2):
+            raise SystemExit("calibration copy mismatch")
         del a, b2
+
+    from kv_cache_top_amd.profiling import load_traffic
+    traffic_b = load_traffic(dom, w.name)
+    traffic = None if traffic_b is None else round(traffic_b / (kern[dom]["avg_us"] * 1e-6) / 1e9, 1)
 
     step_alg = nb["collide"] + nb["rerank"] + nb["attend"] + nb["encode"]
     res = {
@@ -273,8 +281,9 @@ def main():
                    "kv_home": w.kv_home, "layers_rotated": layers, "query_pool": len(Qd),
                    "append_per_step": 1 if app else 0},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "alg_bytes_per_launch": nb.get(dom, 0)},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "alg_bytes_per_launch": nb.get(dom, 0), "hbm_bytes_per_launch": traffic_b,
+                     "avg_launch_us": round(kern[dom]["avg_us"], 3)},
         "step": {"alg_bytes": step_alg, "alg_GBps": round(step_alg / (ms * 1e-3) / 1e9, 1),
                  "frac_of_peak": round(step_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "ms_per_step_with_kernel_events": round(1e3 * el2 / args.steps, 4)},

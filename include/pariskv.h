@@ -229,6 +229,16 @@ pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype,
 pk_status pk_host_alloc_mapped(size_t bytes, void** host_ptr, void** device_ptr);
 pk_status pk_host_free(void* host_ptr);
 
+/* ---- measurement aids ------------------------------------------------------ */
+
+/* Plain device-to-device copy of `bytes` (a multiple of 16; both pointers
+ * 16-byte aligned, non-overlapping) in which every lane moves 16 bytes per
+ * access, the access width of the collide and rerank kernels.  Used to
+ * calibrate the HBM traffic counters (bytes read / written per counted KiB)
+ * for that access pattern.  Asynchronous on `hip_stream`; PK_ERR_INVALID_ARG
+ * on a NULL pointer, a misaligned pointer or size. */
+pk_status pk_calibration_copy(void* dst, const void* src, size_t bytes, void* hip_stream);
+
 /* ---- timing --------------------------------------------------------------- */
 
 /* Start bracketing each launch of every kernel with HIP events on the stream

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -529,6 +530,19 @@ pk_status pk_host_alloc_mapped(size_t bytes, void** host_ptr, void** device_ptr)
   }
   *host_ptr = h;
   *device_ptr = d;
+  return PK_OK;
+}
+
+pk_status pk_calibration_copy(void* dst, const void* src, size_t bytes, void* hip_stream) {
+  if (!dst || !src || bytes % 16 != 0 || !aligned(dst, 16) || !aligned(src, 16))
+    return fail(nullptr, PK_ERR_INVALID_ARG, "calibration copy needs non-NULL 16-byte aligned pointers and size");
+  if (bytes == 0) return PK_OK;
+  const size_t n16 = bytes / 16;
+  const unsigned grid = (unsigned)std::min<size_t>((n16 + 255) / 256, 8192);
+  hipLaunchKernelGGL(pk::copy16_kernel, dim3(grid), dim3(256), 0, (hipStream_t)hip_stream,
+                     reinterpret_cast<uint4*>(dst), reinterpret_cast<const uint4*>(src), n16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(nullptr, PK_ERR_HIP, "copy launch failed: %s", hipGetErrorString(e));
   return PK_OK;
 }
 

@@ -522,6 +522,15 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
 }
 
 // ===========================================================================
+// streaming copy, 16 bytes per lane per access (traffic-counter calibration)
+// ===========================================================================
+__global__ void __launch_bounds__(256) copy16_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                                     size_t n16) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// ===========================================================================
 // select: the candidate set of every query head (Slides Sec. 4.2.2: keep the
 // top-beta keys by S_i, chosen by histogram + prefix scan instead of a sort;
 // Sec. 4.3: C = ceil(beta n)).

@@ -73,6 +73,7 @@ _SIGS = {
                          ctypes.c_int),
     "pk_host_alloc_mapped": ([ctypes.c_size_t, ctypes.POINTER(_P), ctypes.POINTER(_P)], ctypes.c_int),
     "pk_host_free": ([_P], ctypes.c_int),
+    "pk_calibration_copy": ([_P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "pk_timing_begin": ([_P, ctypes.c_int32], ctypes.c_int),
     "pk_timing_end": ([_P, ctypes.POINTER(pk_kernel_timing)], ctypes.c_int),
     "pk_status_str": ([ctypes.c_int], ctypes.c_char_p),
@@ -216,6 +217,14 @@ def pk_host_alloc_mapped(nbytes: int):
 
 def pk_host_free(host_ptr: int) -> None:
     _check(_lib.pk_host_free(ctypes.c_void_p(host_ptr)))
+
+
+def pk_calibration_copy(dst, src, stream=None) -> None:
+    """Copy the bytes of device tensor `src` into `dst` (same size) with 16-byte lane accesses."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("dst and src differ in size")
+    _check(_lib.pk_calibration_copy(_ptr(dst), _ptr(src), n, _stream(stream)))
 
 
 def pk_timing_begin(ctx, max_launches: int) -> None:
