@@ -258,6 +258,30 @@ def main():
             raise SystemExit("calibration copy mismatch")
         del a, b2
 
+    # retrieval quality of the final state: recall@k of every query head against
+    # the exact Top-k of <k_i, q> over all current keys (fp32 on the GPU, untimed)
+    s_last = sums[0]
+    n_now = s_last.s.n
+    qi = 0
+    P._check(P._lib.pk_retrieve(ctx.h, ctypes.c_void_p(Qd[qi].data_ptr()), kv_dt, ctypes.byref(s_last.s),
+                                ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(est.data_ptr()), None, sptr), ctx.h)
+    got = idx.cpu().numpy()
+    qf = Qd[qi].float()
+    hits = []
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            if Kt is not None:
+                kf = Kt[b, h, :n_now].float()
+            else:
+                kf = torch.from_numpy(S.as_f32(K[b, h, :n_now])).to(dev)
+            sc = kf @ qf[b, h * w.group:(h + 1) * w.group].T          # [n, G]
+            ex = torch.topk(sc, min(w.top_k, n_now), dim=0).indices.T.cpu().numpy()
+            for g in range(w.group):
+                hits.append(len(np.intersect1d(ex[g], got[b, h * w.group + g])) / ex.shape[1])
+            del kf, sc
+    recall = float(np.mean(hits))
+    log(f"[bench] recall@{w.top_k} over {len(hits)} query heads at n={n_now}: {recall:.3f}")
+
     from kv_cache_top_amd.profiling import load_traffic
     traffic_b = load_traffic(dom, w.name)
     traffic = None if traffic_b is None else round(traffic_b / (kern[dom]["avg_us"] * 1e-6) / 1e9, 1)
@@ -288,6 +312,8 @@ def main():
                  "frac_of_peak": round(step_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "ms_per_step_with_kernel_events": round(1e3 * el2 / args.steps, 4)},
         "kernels": kern,
+        "recall_at_k": {"value": round(recall, 4), "k": w.top_k, "n": int(n_now), "query_heads": len(hits),
+                        "reference": "exact Top-k of <k_i, q> in fp32 over all current keys"},
     }
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")

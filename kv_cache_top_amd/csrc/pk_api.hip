@@ -405,8 +405,9 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
   if ((st = check_launch(ctx, "collide")) != PK_OK) return st;
   {
     Launch L(ctx, PK_KERNEL_THRESHOLD, stream);
-    hipLaunchKernelGGL(pk::threshold_kernel, dim3(ctx->units), dim3(64 * ctx->group), 0, stream, ctx->tile_hist,
-                       ctx->params, ctx->sub_base, n, 4 * tiles, (int)ctx->max_subs, tile / 4, ctx->group, C);
+    hipLaunchKernelGGL(pk::threshold_kernel, dim3(ctx->units * ctx->group), dim3(pk::TH_THREADS), 0, stream,
+                       ctx->tile_hist, ctx->params, ctx->sub_base, n, 4 * tiles, (int)ctx->max_subs, tile / 4,
+                       ctx->group, C);
   }
   if ((st = check_launch(ctx, "threshold")) != PK_OK) return st;
   {

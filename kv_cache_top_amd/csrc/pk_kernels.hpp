@@ -332,11 +332,14 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
 // and the 16 words are summed: four 8-bit lanes of at most 64 never carry, so
 // one u32 add serves all query heads of the KV head.  S is stored packed.
 // Wave w scores the w-th quarter ("sub-tile") of the tile.  Histogram bins
-// 1..64 are kept per (head, bin, lane) with one byte per wave (counts <= keys
-// per lane <= 255), giving one histogram per sub-tile; bin 0 is implied by the
-// sub-tile length.  Each lane keeps COLLIDE_UNROLL code loads in flight.
+// 1..64 are counted in LDS words of HIST_LANES per (head, bin): lanes l and
+// l + 32 share a word, and byte w of it belongs to wave w (a byte counts at
+// most 2 * keys per lane <= 128), which gives one histogram per sub-tile; bin
+// 0 is implied by the sub-tile length.  Each lane keeps COLLIDE_UNROLL code
+// loads in flight.
 // ===========================================================================
-constexpr int COLLIDE_UNROLL = 16;
+constexpr int COLLIDE_UNROLL = 8;
+constexpr int HIST_LANES = 32;
 
 template <int G>
 __global__ void __launch_bounds__(256)
@@ -345,7 +348,7 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
                int64_t n, int64_t n_cap, int tiles, int max_subs, int tile) {
   constexpr int group = G;
   __shared__ uint32_t s_lut[NSUB * 256];
-  __shared__ uint32_t s_hist[MAXG * NBIN * 64];
+  __shared__ uint32_t s_hist[MAXG * NBIN * HIST_LANES];
 
   const int unit = blockIdx.x / tiles, tl = blockIdx.x - unit * tiles;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -371,12 +374,13 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
     uint4* dst = reinterpret_cast<uint4*>(s_lut);
     for (int i = tid; i < NSUB * 256 / 4; i += 256) dst[i] = src[i];
     uint4* h4 = reinterpret_cast<uint4*>(s_hist);
-    for (int i = tid; i < group * NBIN * 64 / 4; i += 256) h4[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < group * NBIN * HIST_LANES / 4; i += 256) h4[i] = make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 
   const uint32_t incr = 1u << (8 * wave);
-  const uint32_t hbase = (uint32_t)lane * 4u - 256u;     // bin s lives at s*256 - 256 + lane*4
+  // bin s of head g lives at word (g * NBIN + s - 1) * HIST_LANES + lane % HIST_LANES
+  const uint32_t hbase = (uint32_t)(lane & (HIST_LANES - 1)) * 4u - HIST_LANES * 4u;
   for (int64_t base = w0; base < w1; base += 64 * COLLIDE_UNROLL) {
     uint4 nx[COLLIDE_UNROLL];
     const int64_t nb = base + 64 * COLLIDE_UNROLL;
@@ -397,7 +401,7 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const uint32_t sc = (acc >> (8 * g)) & 0xFFu;
-          if (sc) atomicAdd(&s_hist[(g * NBIN * 64 * 4 + sc * 256 + hbase) >> 2], incr);
+          if (sc) atomicAdd(&s_hist[(g * NBIN * HIST_LANES * 4 + sc * HIST_LANES * 4 + hbase) >> 2], incr);
         }
       }
     }
@@ -410,10 +414,10 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
   // a counter word belongs to wave w
   if (tid < group * NBIN) {
     const int g = tid / NBIN, bin = tid % NBIN;
-    const uint32_t* row = s_hist + (g * NBIN + bin) * 64;
+    const uint32_t* row = s_hist + (g * NBIN + bin) * HIST_LANES;
     uint32_t lo = 0, hi = 0;
-    for (int i = 0; i < 64; ++i) {
-      const uint32_t v = row[(i + tid) & 63];
+    for (int i = 0; i < HIST_LANES; ++i) {
+      const uint32_t v = row[(i + tid) & (HIST_LANES - 1)];
       lo += v & 0x00FF00FFu;          // waves 0 and 2
       hi += (v >> 8) & 0x00FF00FFu;   // waves 1 and 3
     }
@@ -428,72 +432,97 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
 // threshold: per (unit, head) the score theta of the C-th best key, how many
 // keys with S == theta are taken (the lowest indices, Slides Sec. 4.2.2
 // histogram + prefix-scan selection), and per sub-tile the exclusive prefix
-// counts of keys above / at theta.  One wave per query head of the unit.
+// counts of keys above / at theta.
+//
+// Workgroup = (unit, query head); thread t holds the 64-bin histogram of
+// sub-tile t of each 256-sub-tile chunk in registers.  Bin totals come from an
+// LDS transpose, theta from a suffix scan over the bins, and the per-sub-tile
+// prefixes from a workgroup scan over the same registers, so a unit with at
+// most 256 sub-tiles reads its histograms once.
 // ===========================================================================
-__global__ void __launch_bounds__(256)
+constexpr int TH_THREADS = 256;
+
+__global__ void __launch_bounds__(TH_THREADS)
 threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__ params,
                  int2* __restrict__ sub_base, int64_t n, int subs, int max_subs, int sub_len, int group,
                  int n_candidates) {
-  __shared__ uint32_t s_h[MAXG][64][NBIN + 1];     // [head][sub-tile in chunk][bin], padded
-  const int unit = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wave >= group) return;
-  const int g = wave;
+  __shared__ uint32_t s_t[TH_THREADS][NBIN + 1];   // [sub-tile in chunk][bin], padded
+  __shared__ uint32_t s_q[4][NBIN];
+  __shared__ int s_par[2];
+  __shared__ int2 s_w[4];
+  const int unit = blockIdx.x / group, g = blockIdx.x - unit * group;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint32_t* uh = tile_hist + (int64_t)unit * max_subs * MAXG * NBIN;
-  uint32_t tot = 0;                                  // lane = bin - 1
-  // pass 1: per-bin totals; lane = sub-tile, its 64 bins fetched as 16 x 16 bytes
-  for (int base = 0; base < subs; base += 64) {
-    const int t2 = base + lane;
-    const int tl = t2 < subs ? t2 : subs - 1;
+
+  uint4 h4[NBIN / 4];
+  auto load_chunk = [&](int base) {
+    const int t = base + tid;
+    const int tl = t < subs ? t : subs - 1;
     const uint4* hrow = reinterpret_cast<const uint4*>(uh + ((int64_t)tl * MAXG + g) * NBIN);
-    uint4 h4[NBIN / 4];
 #pragma unroll
     for (int q4 = 0; q4 < NBIN / 4; ++q4) h4[q4] = hrow[q4];
+    if (t >= subs) {
+#pragma unroll
+      for (int q4 = 0; q4 < NBIN / 4; ++q4) h4[q4] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+
+  // pass 1: bin totals (thread tid < 64 holds bin tid + 1)
+  uint32_t tot = 0;
+  for (int base = 0; base < subs; base += TH_THREADS) {
+    load_chunk(base);
 #pragma unroll
     for (int q4 = 0; q4 < NBIN / 4; ++q4) {
-      const bool ok = t2 < subs;
-      s_h[g][lane][4 * q4 + 0] = ok ? h4[q4].x : 0u;
-      s_h[g][lane][4 * q4 + 1] = ok ? h4[q4].y : 0u;
-      s_h[g][lane][4 * q4 + 2] = ok ? h4[q4].z : 0u;
-      s_h[g][lane][4 * q4 + 3] = ok ? h4[q4].w : 0u;
+      s_t[tid][4 * q4 + 0] = h4[q4].x;
+      s_t[tid][4 * q4 + 1] = h4[q4].y;
+      s_t[tid][4 * q4 + 2] = h4[q4].z;
+      s_t[tid][4 * q4 + 3] = h4[q4].w;
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    for (int t3 = 0; t3 < 64; ++t3) tot += s_h[g][t3][lane];
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    __syncthreads();
+    uint32_t cs = 0;
+#pragma unroll 16
+    for (int r = 0; r < 64; ++r) cs += s_t[wave * 64 + r][lane];
+    s_q[wave][lane] = cs;
+    __syncthreads();
+    if (wave == 0) tot += s_q[0][lane] + s_q[1][lane] + s_q[2][lane] + s_q[3][lane];
+    __syncthreads();
   }
-  // suffix sums over bins (lane l holds #{S >= l+1})
-  uint32_t suf = tot;
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_down(suf, off, 64);
-    if (lane + off < 64) suf += o;
+
+  if (wave == 0) {
+    // suffix sums over bins (lane l holds #{S >= l+1})
+    uint32_t suf = tot;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += o;
+    }
+    const uint64_t ge = __ballot(suf >= (uint32_t)n_candidates);
+    int theta;
+    uint32_t n_gt;
+    if (ge) {
+      const int top = 63 - __builtin_clzll(ge);     // highest bin with suffix >= C
+      theta = top + 1;
+      n_gt = __shfl(suf, (top + 1) & 63, 64);
+      if (top == 63) n_gt = 0;
+    } else {
+      theta = 0;
+      n_gt = __shfl(suf, 0, 64);                    // every key with S >= 1
+    }
+    const uint32_t eq_tot = (theta > 0) ? __shfl(tot, theta - 1, 64) : (uint32_t)(n - n_gt);
+    const uint32_t want = (uint32_t)n_candidates - n_gt;
+    const uint32_t need_eq = want < eq_tot ? want : eq_tot;
+    if (lane == 0) {
+      params[unit * MAXG + g] = SelParams{theta, (int)need_eq, (int)n_gt, (int)(n_gt + need_eq)};
+      s_par[0] = theta;
+    }
   }
-  const uint64_t ge = __ballot(suf >= (uint32_t)n_candidates);
-  int theta;
-  uint32_t n_gt;
-  if (ge) {
-    const int top = 63 - __builtin_clzll(ge);       // highest bin with suffix >= C
-    theta = top + 1;
-    n_gt = __shfl(suf, (top + 1) & 63, 64);
-    if (top == 63) n_gt = 0;
-  } else {
-    theta = 0;
-    n_gt = __shfl(suf, 0, 64);                      // every key with S >= 1
-  }
-  const uint32_t eq_tot = (theta > 0) ? __shfl(tot, theta - 1, 64) : (uint32_t)(n - n_gt);
-  const uint32_t want = (uint32_t)n_candidates - n_gt;
-  const uint32_t need_eq = want < eq_tot ? want : eq_tot;
-  if (lane == 0) params[unit * MAXG + g] = SelParams{theta, (int)need_eq, (int)n_gt, (int)(n_gt + need_eq)};
-  // pass 2: per-sub-tile exclusive prefixes of (#gt, #eq), 64 sub-tiles at a time
+  __syncthreads();
+  const int theta = s_par[0];
+
+  // pass 2: per-sub-tile exclusive prefixes of (#gt, #eq)
   int run_gt = 0, run_eq = 0;
-  for (int base = 0; base < subs; base += 64) {
-    const int t2 = base + lane;
-    const int tl = t2 < subs ? t2 : subs - 1;
-    const uint4* hrow = reinterpret_cast<const uint4*>(uh + ((int64_t)tl * MAXG + g) * NBIN);
-    uint4 h4[NBIN / 4];
-#pragma unroll
-    for (int q4 = 0; q4 < NBIN / 4; ++q4) h4[q4] = hrow[q4];
+  for (int base = 0; base < subs; base += TH_THREADS) {
+    if (subs > TH_THREADS) load_chunk(base);      // else the registers still hold chunk 0
+    const int t = base + tid;
     int gt = 0, eq = 0, nz = 0;
 #pragma unroll
     for (int q4 = 0; q4 < NBIN / 4; ++q4) {
@@ -506,18 +535,30 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
         eq = (sbin == theta) ? c4[e] : eq;
       }
     }
-    int64_t len = n - (int64_t)t2 * sub_len;
+    int64_t len = n - (int64_t)t * sub_len;
     len = len < 0 ? 0 : (len > sub_len ? sub_len : len);
     if (theta == 0) eq = (int)len - nz;
-    if (t2 >= subs) { gt = 0; eq = 0; }
-    int pg = gt, pe = eq;
+    if (t >= subs) { gt = 0; eq = 0; }
+    int pg = gt, pe = eq;                          // inclusive scan within the wave
     for (int off = 1; off < 64; off <<= 1) {
       const int og = __shfl_up(pg, off, 64), oe = __shfl_up(pe, off, 64);
       if (lane >= off) { pg += og; pe += oe; }
     }
-    if (t2 < subs) sub_base[((int64_t)unit * max_subs + t2) * MAXG + g] = make_int2(run_gt + pg - gt, run_eq + pe - eq);
-    run_gt += __shfl(pg, 63, 64);
-    run_eq += __shfl(pe, 63, 64);
+    if (lane == 63) s_w[wave] = make_int2(pg, pe);
+    __syncthreads();
+    int wg = 0, we = 0, cg = 0, ce = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int2 x = s_w[v];
+      if (v < wave) { wg += x.x; we += x.y; }
+      cg += x.x; ce += x.y;
+    }
+    __syncthreads();                               // s_w is rewritten by the next chunk
+    if (t < subs)
+      sub_base[((int64_t)unit * max_subs + t) * MAXG + g] =
+          make_int2(run_gt + wg + pg - gt, run_eq + we + pe - eq);
+    run_gt += cg;
+    run_eq += ce;
   }
 }
 

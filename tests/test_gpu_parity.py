@@ -60,6 +60,17 @@ def test_group_sizes(group):
     run.close()
 
 
+def test_many_subtiles_single_unit():
+    """One KV head with a long ragged key range: the selection's per-sub-tile
+    prefix counts span several 256-sub-tile chunks."""
+    w = S.custom("llama32k", batch=1, n_kv_heads=1, n_q_heads=4, n=70001, n_candidates=1024, wid=250)
+    say("case single unit n=70001 C=1024")
+    K, V, Q = _inputs(w)
+    run = GpuRun(w, K, V, Q).retrieve().attend()
+    _check_all_units(run, K, V)
+    run.close()
+
+
 @pytest.mark.parametrize("n,C,k", [(200, 256, 100), (50, 256, 100), (1, 16, 8), (513, 512, 100), (100, 100, 100)])
 def test_small_n_edges(n, C, k):
     w = S.custom("llama32k", batch=1, n_kv_heads=2, n_q_heads=4, n=n, n_candidates=C, top_k=k, wid=300 + n)
