@@ -587,6 +587,7 @@ __global__ void __launch_bounds__(256) copy16_kernel(uint4* __restrict__ dst, co
 // since every other key leaves all counts unchanged.
 // ===========================================================================
 constexpr int SEL_GRP = 16;             // score chunks loaded per group
+constexpr int SEL_QCAP = SEL_GRP * 64 + 64;   // compaction queue per wave: a group + a remainder
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -598,7 +599,7 @@ __global__ void __launch_bounds__(256)
 select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__ params,
               const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx, int64_t n, int64_t n_cap,
               int tiles, int max_subs, int tile, int n_q_heads, int n_kv_heads, int n_candidates) {
-  __shared__ uint2 s_ik[4][128];                  // compacted keys: (key, packed S)
+  __shared__ uint2 s_ik[4][SEL_QCAP];             // compacted keys: (key, packed S)
 
   const int unit = blockIdx.x / tiles, tl = blockIdx.x - unit * tiles;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -633,10 +634,10 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
   uint2* ik = s_ik[wave];
   int nk = 0;
 
-  // per-head selection of the first `cnt` compacted keys
-  auto select_batch = [&](int cnt) {
+  // per-head selection of the compacted keys b0 .. b0 + cnt - 1 (cnt <= 64)
+  auto select_batch = [&](int b0, int cnt) {
     const bool valid = lane < cnt;
-    const uint2 e = ik[valid ? lane : 0];
+    const uint2 e = ik[b0 + (valid ? lane : 0)];
     const uint32_t m = e.y | 0x80808080u;
     const uint32_t gt4 = (m - thp4) & 0x80808080u;
     const uint32_t eq4 = ((m - th4) & 0x80808080u) ^ gt4;
@@ -656,6 +657,9 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
     }
   };
 
+  // Compact a group of chunks, then run the per-head ballots over whole
+  // batches of 64 compacted keys in a rolled loop (a short body per chunk keeps
+  // the unrolled code small); the remainder waits for the next group.
   const int ngrp = (wkeys / 64 + SEL_GRP - 1) / SEL_GRP;
   for (int grp = 0; grp < ngrp; ++grp) {
     uint32_t spn[SEL_GRP];
@@ -673,20 +677,23 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
       const uint64_t im = __ballot(interesting);
       if (interesting) ik[nk + (int)mbcnt(im)] = make_uint2((uint32_t)i, sp[r]);
       nk += __popcll(im);
-      if (nk >= 64) {
-        wave_lds_sync();
-        select_batch(64);
-        wave_lds_sync();
-        if (lane < nk - 64) ik[lane] = ik[64 + lane];
-        nk -= 64;
-        wave_lds_sync();
-      }
     }
+    wave_lds_sync();
+    int b0 = 0;
+    for (; b0 + 64 <= nk; b0 += 64) select_batch(b0, 64);
+    if (b0 > 0) {                                 // move the remainder (< 64) to the front
+      const int rem = nk - b0;
+      uint2 e = make_uint2(0u, 0u);
+      if (lane < rem) e = ik[b0 + lane];
+      wave_lds_sync();
+      if (lane < rem) ik[lane] = e;
+      nk = rem;
+    }
+    wave_lds_sync();
 #pragma unroll
     for (int r = 0; r < SEL_GRP; ++r) sp[r] = spn[r];
   }
-  wave_lds_sync();
-  select_batch(nk);
+  select_batch(0, nk);
 }
 
 // ===========================================================================
