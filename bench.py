@@ -63,6 +63,7 @@ def algorithmic_bytes(w, n: int) -> dict:
     return {
         "collide": CODE_BYTES * n * w.units,
         "rerank": RECORD_BYTES * n_sel * w.batch * w.n_q_heads,
+        "rerank_topk": RECORD_BYTES * n_sel * w.batch * w.n_q_heads,
         "attend": 2 * kv_row * keff * w.batch * w.n_q_heads,
         "encode": (kv_row + CODE_BYTES + RECORD_BYTES + 4) * w.units if w.append_steps else 0,
     }

@@ -140,10 +140,11 @@ typedef enum {
   PK_KERNEL_COLLIDE = 2,
   PK_KERNEL_THRESHOLD = 3,
   PK_KERNEL_SELECT = 4,
-  PK_KERNEL_RERANK = 5,
-  PK_KERNEL_TOPK = 6,
+  PK_KERNEL_RERANK = 5,        /* 4-bit rerank, several workgroups per head (few heads) */
+  PK_KERNEL_TOPK = 6,          /* final top-k after PK_KERNEL_RERANK */
   PK_KERNEL_ATTEND = 7,
-  PK_N_KERNELS = 8
+  PK_KERNEL_RERANK_TOPK = 8,   /* rerank and final top-k in one workgroup per head (many heads) */
+  PK_N_KERNELS = 9
 } pk_kernel_id;
 
 typedef struct {

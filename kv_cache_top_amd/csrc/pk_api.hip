@@ -69,6 +69,10 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Keys per collide / select workgroup: about kTargetWG workgroups over all
 // units, 256 threads each doing 1..kMaxKPL keys.
 constexpr int64_t kTargetWG = 512, kMaxKPL = 64;
+// rerank and top-k run as one workgroup per head when there are enough heads to
+// fill the chip, or few enough candidates per head (two per thread)
+constexpr int kFusedTopkHeads = 128;
+constexpr int kFusedTopkSlots = 2 * pk::RT_THREADS;
 int tile_size(int units, int64_t n) {
   const int64_t want = ((int64_t)units * n + kTargetWG * 256 - 1) / (kTargetWG * 256);
   const int64_t kpl = want < 1 ? 1 : (want > kMaxKPL ? kMaxKPL : want);
@@ -382,11 +386,13 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
   {
     Launch L(ctx, PK_KERNEL_QPREP, stream);
     if (q_dtype == PK_BF16)
-      hipLaunchKernelGGL(pk::qprep_kernel<uint16_t>, dim3(ctx->qheads), dim3(1024), 0, stream, (const uint16_t*)q,
-                         cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->rq, (uint8_t*)ctx->lut, ctx->tb, ctx->tiers);
+      hipLaunchKernelGGL(pk::qprep_kernel<uint16_t>, dim3(ctx->qheads * pk::QP_PARTS), dim3(64 * pk::QP_WAVES), 0,
+                         stream, (const uint16_t*)q, cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->rq,
+                         (uint8_t*)ctx->lut, ctx->tb, ctx->tiers);
     else
-      hipLaunchKernelGGL(pk::qprep_kernel<float>, dim3(ctx->qheads), dim3(1024), 0, stream, (const float*)q,
-                         cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->rq, (uint8_t*)ctx->lut, ctx->tb, ctx->tiers);
+      hipLaunchKernelGGL(pk::qprep_kernel<float>, dim3(ctx->qheads * pk::QP_PARTS), dim3(64 * pk::QP_WAVES), 0,
+                         stream, (const float*)q, cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->rq,
+                         (uint8_t*)ctx->lut, ctx->tb, ctx->tiers);
   }
   if ((st = check_launch(ctx, "qprep")) != PK_OK) return st;
   {
@@ -425,28 +431,47 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
 #undef PK_SELECT
   }
   if ((st = check_launch(ctx, "select")) != PK_OK) return st;
-  {
-    Launch L(ctx, PK_KERNEL_RERANK, stream);
-    const int chunks = (n_sel + pk::RR_PER_WG - 1) / pk::RR_PER_WG;
-    hipLaunchKernelGGL(pk::rerank_kernel, dim3((unsigned)((int64_t)ctx->qheads * chunks)), dim3(256), 0, stream,
-                       s->records, ctx->rq, ctx->cand_idx, ctx->cand_est, s->n_capacity, n_sel, C, chunks,
-                       cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->tb);
-  }
-  if ((st = check_launch(ctx, "rerank")) != PK_OK) return st;
-  {
-    Launch L(ctx, PK_KERNEL_TOPK, stream);
-    const int R = (n_sel + 255) / 256;
+  if (ctx->qheads >= kFusedTopkHeads || n_sel <= kFusedTopkSlots) {
+    // one workgroup per head: rerank and top-k together, estimates in LDS
+    Launch L(ctx, PK_KERNEL_RERANK_TOPK, stream);
+    const int R = (n_sel + pk::RT_THREADS - 1) / pk::RT_THREADS;
+    float* est_out = (dbg && dbg->cand_est) ? ctx->cand_est : nullptr;
+#define PK_RTK(RR)                                                                                             \
+  hipLaunchKernelGGL(pk::rerank_topk_kernel<RR>, dim3(ctx->qheads), dim3(pk::RT_THREADS), 0, stream, s->records, \
+                     ctx->rq, ctx->cand_idx, est_out, s->n_capacity, n_sel, C, cfg.n_q_heads, cfg.n_kv_heads,       \
+                     ctx->group, ctx->tb, k, topk_idx, topk_est)
+    if (R <= 1) PK_RTK(1);
+    else if (R <= 2) PK_RTK(2);
+    else if (R <= 4) PK_RTK(4);
+    else if (R <= 8) PK_RTK(8);
+    else PK_RTK(16);
+#undef PK_RTK
+    if ((st = check_launch(ctx, "rerank_topk")) != PK_OK) return st;
+  } else {
+    // few heads: spread the rerank over several workgroups per head, then select
+    {
+      Launch L(ctx, PK_KERNEL_RERANK, stream);
+      const int chunks = (n_sel + pk::RR_PER_WG - 1) / pk::RR_PER_WG;
+      hipLaunchKernelGGL(pk::rerank_kernel, dim3((unsigned)((int64_t)ctx->qheads * chunks)), dim3(256), 0, stream,
+                         s->records, ctx->rq, ctx->cand_idx, ctx->cand_est, s->n_capacity, n_sel, C, chunks,
+                         cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->tb);
+    }
+    if ((st = check_launch(ctx, "rerank")) != PK_OK) return st;
+    {
+      Launch L(ctx, PK_KERNEL_TOPK, stream);
+      const int R = (n_sel + 255) / 256;
 #define PK_TOPK(RR)                                                                                      \
   hipLaunchKernelGGL(pk::topk_kernel<RR>, dim3(ctx->qheads), dim3(256), 0, stream, ctx->cand_idx, ctx->cand_est, \
                      n_sel, C, k, topk_idx, topk_est)
-    if (R <= 4) PK_TOPK(4);
-    else if (R <= 8) PK_TOPK(8);
-    else if (R <= 16) PK_TOPK(16);
-    else if (R <= 32) PK_TOPK(32);
-    else PK_TOPK(64);
+      if (R <= 4) PK_TOPK(4);
+      else if (R <= 8) PK_TOPK(8);
+      else if (R <= 16) PK_TOPK(16);
+      else if (R <= 32) PK_TOPK(32);
+      else PK_TOPK(64);
 #undef PK_TOPK
+    }
+    if ((st = check_launch(ctx, "topk")) != PK_OK) return st;
   }
-  if ((st = check_launch(ctx, "topk")) != PK_OK) return st;
 
   if (dbg) {
     const size_t U = ctx->units, Q = ctx->qheads;

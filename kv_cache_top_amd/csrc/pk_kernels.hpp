@@ -204,30 +204,37 @@ encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
 // qprep: query rotation and centroid activation (README "2. Decode";
 // Slides Eqs. (5)-(6), Eq. (15) tiers).
 //
-// One workgroup of 16 waves per query head; wave 0 rotates the query (s-flip,
-// then a 128-point fast Walsh-Hadamard transform with butterfly stages
-// h = 1, 2, ..., 64), then wave b owns subspace b.  Centroid c's score is
+// QP_WAVES waves per workgroup and NSUB / QP_WAVES workgroups per query head:
+// wave 0 of each rotates the query (s-flip, then a 128-point fast
+// Walsh-Hadamard transform with butterfly stages h = 1, 2, ..., 64), then each
+// wave owns one subspace (one wave per SIMD, so the scalar ballot loops of the
+// subspaces run side by side instead of sharing an issue slot).  Centroid c's score is
 // sum_j (bit_j(c) ? +y_j : -y_j) in fp32, sequential in j.  The centroids
 // ranking r < tier_top[last] by (score desc, c asc) are found with a bitwise
 // threshold search over the order-preserving score keys, then ranked among
 // themselves; each gets its tier weight, every other centroid 0.  The weight is
 // written as byte g (query head g of the unit) of the unit's LUT.
 // ===========================================================================
+constexpr int QP_WAVES = 4;
+constexpr int QP_PARTS = NSUB / QP_WAVES;   // workgroups per query head
+
 template <typename QT>
-__global__ void __launch_bounds__(1024)
+__global__ void __launch_bounds__(64 * QP_WAVES)
 qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
              float* __restrict__ rot_q, uint8_t* __restrict__ lut_bytes, Tables tb,
              TierSpec tiers) {
   __shared__ float y[D];
-  __shared__ uint2 sel[NSUB][256];          // (score key, centroid) of the selected centroids
-  __shared__ uint8_t lw[NSUB][256];         // tier weight per centroid
+  __shared__ uint2 sel[QP_WAVES][256];      // (score key, centroid) of the selected centroids
+  __shared__ uint8_t lw[QP_WAVES][256];     // tier weight per centroid
 
-  const int head = blockIdx.x;              // sequence * n_q_heads + query head
+  const int head = blockIdx.x / QP_PARTS;   // sequence * n_q_heads + query head
+  const int part = blockIdx.x - head * QP_PARTS;
   const int seq = head / n_q_heads, qh = head - seq * n_q_heads;
   const int unit = seq * n_kv_heads + qh / group, g = qh % group;
-  const int tid = threadIdx.x, b = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int b = part * QP_WAVES + w;        // subspace of this wave
 
-  if (b == 0) {
+  if (w == 0) {
     // wave 0: lane l holds coordinates l and l + 64; butterflies h = 1..32
     // pair lanes l and l ^ h, h = 64 pairs the two registers
     float v0, v1;
@@ -253,8 +260,10 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
     v1 = a0 - a1;
     y[lane] = v0;
     y[lane + 64] = v1;
-    rot_q[(int64_t)head * D + lane] = v0 * tb.inv_sqrt_d;
-    rot_q[(int64_t)head * D + lane + 64] = v1 * tb.inv_sqrt_d;
+    if (part == 0) {
+      rot_q[(int64_t)head * D + lane] = v0 * tb.inv_sqrt_d;
+      rot_q[(int64_t)head * D + lane + 64] = v1 * tb.inv_sqrt_d;
+    }
   }
   __syncthreads();
 
@@ -269,7 +278,7 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
 #pragma unroll
     for (int j = 1; j < SUBD; ++j) sc = sc + (((c >> j) & 1u) ? yb[j] : -yb[j]);
     key[r] = orderable(sc);
-    lw[b][c] = 0;
+    lw[w][c] = 0;
   }
 
   const int T = tiers.top[tiers.n_tiers - 1];
@@ -294,7 +303,7 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
     const int eqrank = eq_before + (int)mbcnt(eqm);
     const bool sl = key[r] > thr || (key[r] == thr && eqrank < need_eq);
     const uint64_t sm = __ballot(sl);
-    if (sl) sel[b][sel_before + (int)mbcnt(sm)] = make_uint2(key[r], lane + 64 * r);
+    if (sl) sel[w][sel_before + (int)mbcnt(sm)] = make_uint2(key[r], lane + 64 * r);
     eq_before += __popcll(eqm);
     sel_before += __popcll(sm);
   }
@@ -302,24 +311,25 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
   __builtin_amdgcn_wave_barrier();
   // rank of each selected centroid by (score desc, centroid asc); tier weight
   for (int j = lane; j < T; j += 64) {
-    const uint2 e = sel[b][j];
+    const uint2 e = sel[w][j];
     int rank = 0;
+#pragma unroll 8
     for (int j2 = 0; j2 < T; ++j2) {
-      const uint2 o = sel[b][j2];
+      const uint2 o = sel[w][j2];
       rank += (o.x > e.x || (o.x == e.x && o.y < e.y)) ? 1 : 0;
     }
     uint32_t wgt = 0;
     for (int tt = 0; tt < tiers.n_tiers; ++tt) {
       if (rank < tiers.top[tt]) { wgt = (uint32_t)tiers.weight[tt]; break; }
     }
-    lw[b][e.y] = (uint8_t)wgt;
+    lw[w][e.y] = (uint8_t)wgt;
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint32_t c = lane + 64 * r;
-    lut_bytes[(((int64_t)unit * NSUB + b) * 256 + c) * 4 + g] = lw[b][c];
+    lut_bytes[(((int64_t)unit * NSUB + b) * 256 + c) * 4 + g] = lw[w][c];
   }
 }
 
@@ -697,98 +707,30 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
 }
 
 // ===========================================================================
-// rerank: the 4-bit inner-product estimate of every candidate (Slides,
-// Eqs. (7)-(10); README "2. Decode", fused 4-bit reranking).
+// rerank (Slides Eqs. (7)-(10); README "2. Decode", fused 4-bit reranking) and
+// top-k by (estimate desc, key index asc) (Slides Sec. 4.2.3: reranking
+// returns the Top-100 indices).
 //
-// Workgroup = (query head, RR_PER_WG consecutive candidate slots); one lane
-// per candidate gathers the key's 128-byte record (nibble words, then the 16
-// weights) and evaluates
+// Rerank: one lane per candidate gathers the key's 128-byte record (nibble
+// words, then the 16 weights) and evaluates
 //   est = sum_b w_b * d_b,  d_b = sum_j T[8b+j][nib_j]   (sequential in j and b)
 // with T[j][nib] = fl(v(nib) * Rq[j]), v(nib) = (nib & 8 ? +1 : -1) L[nib & 7],
-// i.e. fl(v * Rq) of the estimator taken from an LDS table.  The kernel needs
-// few registers, so eight waves per SIMD hide the gathers' latency.
-// ===========================================================================
-constexpr int RR_ROUNDS = 4;                      // candidates per lane
-constexpr int RR_PER_WG = 256 * RR_ROUNDS;
-
-__global__ void __launch_bounds__(256)
-rerank_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot_q,
-              const int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int64_t n_cap,
-              int n_sel, int n_candidates, int chunks, int n_q_heads, int n_kv_heads, int group, Tables tb) {
-  __shared__ float s_T[D * 16];
-  const int head = blockIdx.x / chunks, ch = blockIdx.x - head * chunks;
-  const int tid = threadIdx.x;
-  const int seq = head / n_q_heads, qh = head - seq * n_q_heads;
-  const int unit = seq * n_kv_heads + qh / group;
-  const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
-  const int32_t* ci = cand_idx + (int64_t)head * n_candidates;
-  float* ce = cand_est + (int64_t)head * n_candidates;
-  const int p0 = ch * RR_PER_WG;
-  const int plast = n_sel - 1;
-
-  auto load = [&](int r, uint4 (&buf)[8]) {
-    const int p = p0 + r * 256 + tid;
-    const int key = ci[p < plast ? p : plast];
-    const uint4* rec = reinterpret_cast<const uint4*>(rbase + (int64_t)key * 128);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) buf[k] = rec[k];
-  };
-  uint4 ra[8];
-  load(0, ra);
-  for (int e = tid; e < D * 16; e += 256) {
-    const int j = e >> 4, nb = e & 15;
-    const float lv = tb.levels[nb & 7];
-    const float v = (nb & 8) ? lv : -lv;
-    s_T[e] = v * rot_q[(int64_t)head * D + j];
-  }
-  __syncthreads();
-
-  auto eval = [&](int r, const uint4 (&buf)[8]) {
-    const uint32_t* rw = reinterpret_cast<const uint32_t*>(buf);
-    float est = 0.0f;
-#pragma unroll
-    for (int bb = 0; bb < NSUB; ++bb) {
-      const uint32_t word = rw[bb];
-      // byte k of lo / hi = 4 * nibble (2k) / (2k + 1), a byte offset into the table row
-      uint32_t lo = (word << 2) & 0x3C3C3C3Cu, hi = (word >> 2) & 0x3C3C3C3Cu;
-      asm volatile("" : "+v"(lo), "+v"(hi));
-      const char* Tb = reinterpret_cast<const char*>(s_T) + bb * (SUBD * 16 * 4);
-      float v[SUBD];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[2 * k] = *reinterpret_cast<const float*>(Tb + (2 * k) * 64 + ((lo >> (8 * k)) & 0xFFu));
-        v[2 * k + 1] = *reinterpret_cast<const float*>(Tb + (2 * k + 1) * 64 + ((hi >> (8 * k)) & 0xFFu));
-      }
-      float d = v[0];
-#pragma unroll
-      for (int j = 1; j < SUBD; ++j) d = d + v[j];
-      const float tprod = __uint_as_float(rw[16 + bb]) * d;
-      est = (bb == 0) ? tprod : est + tprod;
-      asm volatile("" : "+v"(est));     // keep the sum here, not sunk into the store's branch
-    }
-    const int p = p0 + r * 256 + tid;
-    if (p < n_sel) ce[p] = est;
-  };
-#pragma unroll 1
-  for (int r = 0; r < RR_ROUNDS; ++r) {
-    if (r) load(r, ra);
-    eval(r, ra);
-  }
-}
-
-// ===========================================================================
-// top-k of the candidates by (estimate desc, key index asc)
-// (Slides Sec. 4.2.3: reranking returns the Top-100 indices).
+// i.e. fl(v * Rq) of the estimator taken from an LDS table.
 //
-// One workgroup per query head; candidate slot p is held by thread p % 256.
-// Estimates map to order-preserving u32 keys; since the candidate list is in
-// ascending key order, a lower slot breaks ties.  Leading bits shared by every
-// candidate key are skipped; histograms of successive 12-bit digits below them
-// narrow down the bin holding the k-th largest key until that bin holds at most
-// TOPK_MAXB keys (or all its keys are equal): keys in higher bins are taken,
-// and the remaining winners of the boundary bin are found by ranking its keys
-// against each other (or, when all of its keys are equal, by lowest slot).  The
-// k winners are finally placed by rank (count of winners ahead of each).
+// Top-k: estimates map to order-preserving u32 keys; since the candidate list
+// is in ascending key order, a lower slot breaks ties.  Leading bits shared by
+// every candidate key are skipped; histograms of successive 12-bit digits
+// below them narrow down the bin holding the k-th largest key until that bin
+// holds at most TOPK_MAXB keys (or all its keys are equal): keys in higher bins
+// are taken, and the remaining winners of the boundary bin are found by
+// ranking its keys against each other (or, when all of its keys are equal, by
+// lowest slot).  The k winners are finally placed by rank (count of winners
+// ahead of each).
+//
+// With many query heads one workgroup of RT_THREADS does both for a head and
+// keeps the estimates in LDS (rerank_topk_kernel); with few heads the rerank
+// is spread over several workgroups per head (rerank_kernel) and a second
+// launch selects (topk_kernel), so that every compute unit takes part.
 // ===========================================================================
 constexpr int TOPK_BINS = 4096;        // 12-bit digit
 constexpr int TOPK_MAXB = 512;         // boundary-bin size handled by ranking
@@ -797,45 +739,72 @@ __device__ __forceinline__ uint64_t topk_item(uint32_t key, int p) {
   return ((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)p);   // larger = better
 }
 
-template <int R>
-__global__ void __launch_bounds__(256)
-topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_sel,
-            int n_candidates, int k, int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
-  __shared__ uint32_t s_h[TOPK_BINS];
-  __shared__ uint64_t s_b[TOPK_MAXB];
-  __shared__ uint64_t s_f[PK_SORT_N];
-  __shared__ int s_misc[8];
-  __shared__ uint32_t s_wsum[4];
+// LDS table T[j][nib] = fl(v(nib) * Rq[j]) of one query head
+template <int NT>
+__device__ __forceinline__ void rerank_table(float* s_T, const float* rq, const Tables& tb, int tid) {
+  for (int e = tid; e < D * 16; e += NT) {
+    const int j = e >> 4, nb = e & 15;
+    const float lv = tb.levels[nb & 7];
+    const float v = (nb & 8) ? lv : -lv;
+    s_T[e] = v * rq[j];
+  }
+}
 
-  const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int32_t* ci = cand_idx + (int64_t)head * n_candidates;
-  float* ce = cand_est + (int64_t)head * n_candidates;
+__device__ __forceinline__ void rerank_load(uint4 (&buf)[8], const uint8_t* rbase, int key) {
+  const uint4* rec = reinterpret_cast<const uint4*>(rbase + (int64_t)key * 128);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) buf[kk] = rec[kk];
+}
+
+__device__ __forceinline__ float rerank_eval(const uint4 (&buf)[8], const float* s_T) {
+  const uint32_t* rw = reinterpret_cast<const uint32_t*>(buf);
+  float est = 0.0f;
+#pragma unroll
+  for (int bb = 0; bb < NSUB; ++bb) {
+    const uint32_t word = rw[bb];
+    // byte k of lo / hi = 4 * nibble (2k) / (2k + 1), a byte offset into the table row
+    uint32_t lo = (word << 2) & 0x3C3C3C3Cu, hi = (word >> 2) & 0x3C3C3C3Cu;
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    const char* Tb = reinterpret_cast<const char*>(s_T) + bb * (SUBD * 16 * 4);
+    float v[SUBD];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      v[2 * kk] = *reinterpret_cast<const float*>(Tb + (2 * kk) * 64 + ((lo >> (8 * kk)) & 0xFFu));
+      v[2 * kk + 1] = *reinterpret_cast<const float*>(Tb + (2 * kk + 1) * 64 + ((hi >> (8 * kk)) & 0xFFu));
+    }
+    float d = v[0];
+#pragma unroll
+    for (int j = 1; j < SUBD; ++j) d = d + v[j];
+    const float tprod = __uint_as_float(rw[16 + bb]) * d;
+    est = (bb == 0) ? tprod : est + tprod;
+    asm volatile("" : "+v"(est));     // keep the sum here, not sunk into a store's branch
+  }
+  return est;
+}
+
+template <int NT>
+struct TopkShared {
+  uint32_t h[TOPK_BINS];
+  uint64_t b[TOPK_MAXB];
+  uint64_t f[PK_SORT_N];
+  int misc[8];
+  uint32_t wsum[NT / 64];
+};
+
+// Top-k of one head's n_sel candidates; thread tid holds slots r * NT + tid
+// as order-preserving keys key[r].  s.misc must be zero on entry.
+template <int R, int NT>
+__device__ void topk_block(const uint32_t (&key)[R], int n_sel, int k, const int32_t* ci, int32_t* out_idx,
+                           float* out_est, TopkShared<NT>& s, int tid) {
+  constexpr int NW = NT / 64;
+  const int lane = tid & 63, wave = tid >> 6;
   const int keff = k < n_sel ? k : n_sel;
-
-  // candidate estimates: clamped unconditional loads, all in flight together
-  float ev[R];
-  const int plast = n_sel > 0 ? n_sel - 1 : 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int p = r * 256 + tid;
-    ev[r] = ce[p < plast ? p : plast];
-  }
-  if (tid < 8) s_misc[tid] = 0;
-  // invalid tail slots of the candidate list (n < C)
-  for (int p = n_sel + tid; p < n_candidates; p += 256) {
-    ci[p] = -1;
-    ce[p] = -__builtin_inff();
-  }
-  uint32_t key[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) key[r] = orderable(ev[r]);
-
   // the common leading bits of all candidate keys need no histogram: digits
   // start at the highest bit where the largest and smallest keys differ
   uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const bool ok = r * 256 + tid < n_sel;
+    const bool ok = r * NT + tid < n_sel;
     kmax = ok && key[r] > kmax ? key[r] : kmax;
     kmin = ok && key[r] < kmin ? key[r] : kmin;
   }
@@ -844,11 +813,11 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
     kmax = a > kmax ? a : kmax;
     kmin = c < kmin ? c : kmin;
   }
-  if (lane == 0) { s_wsum[wave] = kmax; s_h[wave] = kmin; }
+  if (lane == 0) { s.wsum[wave] = kmax; s.h[wave] = kmin; }
   __syncthreads();
-  for (int w2 = 0; w2 < 4; ++w2) {
-    kmax = s_wsum[w2] > kmax ? s_wsum[w2] : kmax;
-    kmin = s_h[w2] < kmin ? s_h[w2] : kmin;
+  for (int w2 = 0; w2 < NW; ++w2) {
+    kmax = s.wsum[w2] > kmax ? s.wsum[w2] : kmax;
+    kmin = s.h[w2] < kmin ? s.h[w2] : kmin;
   }
   const uint32_t diff = kmax ^ kmin;
   int top = diff ? 31 - __builtin_clz(diff) : -1;        // highest undecided bit
@@ -856,47 +825,48 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
   if (top == 31) pmask = 0;
   uint32_t prefix = kmax & pmask;
   int n_above = 0, need = keff, m = n_sel;
+  constexpr int per = TOPK_BINS / NT;                   // bins per thread
   while (keff > 0 && top >= 0 && m > TOPK_MAXB) {        // uniform
     const int shift = top >= 11 ? top - 11 : 0;
     const uint32_t dmask = (top - shift == 31) ? 0xFFFFFFFFu : ((2u << (top - shift)) - 1u);
-    const int per = 16;                                   // TOPK_BINS / 256 bins per thread
     __syncthreads();
-    for (int i = tid; i < TOPK_BINS; i += 256) s_h[i] = 0;
+    for (int i = tid; i < TOPK_BINS; i += NT) s.h[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (r * 256 + tid < n_sel && (key[r] & pmask) == prefix) atomicAdd(&s_h[(key[r] >> shift) & dmask], 1u);
+      if (r * NT + tid < n_sel && (key[r] & pmask) == prefix) atomicAdd(&s.h[(key[r] >> shift) & dmask], 1u);
     __syncthreads();
     // thread t owns bins [per*t, per*t + per); suffix counts from the top bin
     uint32_t mine = 0;
-    for (int i = 0; i < per; ++i) mine += s_h[per * tid + i];
+#pragma unroll
+    for (int i = 0; i < per; ++i) mine += s.h[per * tid + i];
     uint32_t suf = mine;
     for (int off = 1; off < 64; off <<= 1) {
       const uint32_t o = __shfl_down(suf, off, 64);
       if (lane + off < 64) suf += o;
     }
-    if (lane == 0) s_wsum[wave] = suf;
+    if (lane == 0) s.wsum[wave] = suf;
     __syncthreads();
     uint32_t above = suf - mine;
-    for (int w2 = wave + 1; w2 < 4; ++w2) above += s_wsum[w2];
+    for (int w2 = wave + 1; w2 < NW; ++w2) above += s.wsum[w2];
     if (above < (uint32_t)need && above + mine >= (uint32_t)need) {
       uint32_t run = above;
       for (int i = per - 1; i >= 0; --i) {
-        const uint32_t c = s_h[per * tid + i];
+        const uint32_t c = s.h[per * tid + i];
         if (run + c >= (uint32_t)need) {
-          s_misc[0] = per * tid + i;       // boundary digit
-          s_misc[1] = (int)run;            // keys above it within the current range
-          s_misc[2] = (int)c;              // keys with this digit
+          s.misc[0] = per * tid + i;       // boundary digit
+          s.misc[1] = (int)run;            // keys above it within the current range
+          s.misc[2] = (int)c;              // keys with this digit
           break;
         }
         run += c;
       }
     }
     __syncthreads();
-    n_above += s_misc[1];
-    need -= s_misc[1];
-    m = s_misc[2];
-    prefix |= (uint32_t)s_misc[0] << shift;
+    n_above += s.misc[1];
+    need -= s.misc[1];
+    m = s.misc[2];
+    prefix |= (uint32_t)s.misc[0] << shift;
     pmask |= dmask << shift;
     top = shift - 1;
   }
@@ -906,37 +876,37 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
     // winners strictly above the boundary range, and the boundary range itself
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int p = r * 256 + tid;
+      const int p = r * NT + tid;
       if (p < n_sel) {
         const uint32_t mk = key[r] & pmask;
-        if (mk > prefix) s_f[atomicAdd(&s_misc[3], 1)] = topk_item(key[r], p);
-        else if (mk == prefix && m <= TOPK_MAXB) s_b[atomicAdd(&s_misc[4], 1)] = topk_item(key[r], p);
+        if (mk > prefix) s.f[atomicAdd(&s.misc[3], 1)] = topk_item(key[r], p);
+        else if (mk == prefix && m <= TOPK_MAXB) s.b[atomicAdd(&s.misc[4], 1)] = topk_item(key[r], p);
       }
     }
     __syncthreads();
     if (m <= TOPK_MAXB) {
-      for (int j = tid; j < m; j += 256) {
-        const uint64_t e = s_b[j];
+      for (int j = tid; j < m; j += NT) {
+        const uint64_t e = s.b[j];
         int rank = 0;
-        for (int j2 = 0; j2 < m; ++j2) rank += (s_b[j2] > e) ? 1 : 0;
-        if (rank < need) s_f[n_above + rank] = e;
+        for (int j2 = 0; j2 < m; ++j2) rank += (s.b[j2] > e) ? 1 : 0;
+        if (rank < need) s.f[n_above + rank] = e;
       }
     } else {
       // every key of the boundary range is equal: the lowest slots win
       int eq_run = 0;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int p = r * 256 + tid;
+        const int p = r * NT + tid;
         const bool eq = p < n_sel && (key[r] & pmask) == prefix;
         const uint64_t em = __ballot(eq);
-        if (lane == 0) s_wsum[wave] = (uint32_t)__popcll(em);
+        if (lane == 0) s.wsum[wave] = (uint32_t)__popcll(em);
         __syncthreads();
         int before = eq_run + (int)mbcnt(em), tot = 0;
-        for (int w2 = 0; w2 < 4; ++w2) {
-          if (w2 < wave) before += (int)s_wsum[w2];
-          tot += (int)s_wsum[w2];
+        for (int w2 = 0; w2 < NW; ++w2) {
+          if (w2 < wave) before += (int)s.wsum[w2];
+          tot += (int)s.wsum[w2];
         }
-        if (eq && before < need) s_f[n_above + before] = topk_item(key[r], p);
+        if (eq && before < need) s.f[n_above + before] = topk_item(key[r], p);
         eq_run += tot;
         __syncthreads();
       }
@@ -944,18 +914,128 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
   }
   __syncthreads();
   // place the keff winners by rank
-  for (int j = tid; j < keff; j += 256) {
-    const uint64_t e = s_f[j];
+  for (int j = tid; j < keff; j += NT) {
+    const uint64_t e = s.f[j];
     int rank = 0;
-    for (int j2 = 0; j2 < keff; ++j2) rank += (s_f[j2] > e) ? 1 : 0;
+    for (int j2 = 0; j2 < keff; ++j2) rank += (s.f[j2] > e) ? 1 : 0;
     const int p = (int)(0xFFFFFFFFu - (uint32_t)e);
-    out_idx[(int64_t)head * k + rank] = ci[p];
-    if (out_est) out_est[(int64_t)head * k + rank] = from_orderable((uint32_t)(e >> 32));
+    out_idx[rank] = ci[p];
+    if (out_est) out_est[rank] = from_orderable((uint32_t)(e >> 32));
   }
-  for (int r = keff + tid; r < k; r += 256) {
-    out_idx[(int64_t)head * k + r] = -1;
-    if (out_est) out_est[(int64_t)head * k + r] = -__builtin_inff();
+  for (int r = keff + tid; r < k; r += NT) {
+    out_idx[r] = -1;
+    if (out_est) out_est[r] = -__builtin_inff();
   }
+}
+
+// ---- many heads: rerank and top-k of one head in one workgroup -------------
+constexpr int RT_THREADS = 1024;
+
+template <int R>        // candidate slots per thread: n_sel <= R * RT_THREADS
+__global__ void __launch_bounds__(RT_THREADS)
+rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot_q,
+                   int32_t* __restrict__ cand_idx, float* __restrict__ cand_est_out, int64_t n_cap, int n_sel,
+                   int n_candidates, int n_q_heads, int n_kv_heads, int group, Tables tb, int k,
+                   int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
+  __shared__ float s_T[D * 16];
+  __shared__ float s_est[R * RT_THREADS];
+  __shared__ TopkShared<RT_THREADS> s_tk;
+
+  const int head = blockIdx.x, tid = threadIdx.x;
+  const int seq = head / n_q_heads, qh = head - seq * n_q_heads;
+  const int unit = seq * n_kv_heads + qh / group;
+  const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
+  int32_t* ci = cand_idx + (int64_t)head * n_candidates;
+  float* ce = cand_est_out ? cand_est_out + (int64_t)head * n_candidates : nullptr;
+  const int plast = n_sel > 0 ? n_sel - 1 : 0;
+  const int rounds = (n_sel + RT_THREADS - 1) / RT_THREADS;
+
+  uint4 ra[8];
+  if (n_sel > 0) rerank_load(ra, rbase, ci[tid < plast ? tid : plast]);
+  rerank_table<RT_THREADS>(s_T, rot_q + (int64_t)head * D, tb, tid);
+  if (tid < 8) s_tk.misc[tid] = 0;
+  for (int p = n_sel + tid; p < n_candidates; p += RT_THREADS) {   // invalid tail slots (n < C)
+    ci[p] = -1;
+    if (ce) ce[p] = -__builtin_inff();
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int r = 0; r < rounds; ++r) {
+    const int p = r * RT_THREADS + tid;
+    if (r) rerank_load(ra, rbase, ci[p < plast ? p : plast]);
+    const float est = rerank_eval(ra, s_T);
+    s_est[p] = est;
+    if (ce && p < n_sel) ce[p] = est;
+  }
+  __syncthreads();
+  uint32_t key[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int p = r * RT_THREADS + tid;
+    key[r] = orderable(s_est[p < plast ? p : plast]);
+  }
+  topk_block<R, RT_THREADS>(key, n_sel, k, ci, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
+                            s_tk, tid);
+}
+
+// ---- few heads: rerank spread over RR_PER_WG-candidate workgroups ----------
+constexpr int RR_ROUNDS = 4;                      // candidates per lane
+constexpr int RR_PER_WG = 256 * RR_ROUNDS;
+
+__global__ void __launch_bounds__(256)
+rerank_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot_q,
+              int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int64_t n_cap,
+              int n_sel, int n_candidates, int chunks, int n_q_heads, int n_kv_heads, int group, Tables tb) {
+  __shared__ float s_T[D * 16];
+  const int head = blockIdx.x / chunks, ch = blockIdx.x - head * chunks;
+  const int tid = threadIdx.x;
+  const int seq = head / n_q_heads, qh = head - seq * n_q_heads;
+  const int unit = seq * n_kv_heads + qh / group;
+  const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
+  int32_t* ci = cand_idx + (int64_t)head * n_candidates;
+  float* ce = cand_est + (int64_t)head * n_candidates;
+  const int p0 = ch * RR_PER_WG;
+  const int plast = n_sel - 1;
+
+  uint4 ra[8];
+  rerank_load(ra, rbase, ci[p0 + tid < plast ? p0 + tid : plast]);
+  rerank_table<256>(s_T, rot_q + (int64_t)head * D, tb, tid);
+  __syncthreads();
+#pragma unroll 1
+  for (int r = 0; r < RR_ROUNDS; ++r) {
+    const int p = p0 + r * 256 + tid;
+    if (r) rerank_load(ra, rbase, ci[p < plast ? p : plast]);
+    const float est = rerank_eval(ra, s_T);
+    if (p < n_sel) ce[p] = est;
+  }
+}
+
+template <int R>
+__global__ void __launch_bounds__(256)
+topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_sel,
+            int n_candidates, int k, int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
+  __shared__ TopkShared<256> s_tk;
+  const int head = blockIdx.x, tid = threadIdx.x;
+  int32_t* ci = cand_idx + (int64_t)head * n_candidates;
+  float* ce = cand_est + (int64_t)head * n_candidates;
+  // candidate estimates: clamped unconditional loads, all in flight together
+  float ev[R];
+  const int plast = n_sel > 0 ? n_sel - 1 : 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int p = r * 256 + tid;
+    ev[r] = ce[p < plast ? p : plast];
+  }
+  if (tid < 8) s_tk.misc[tid] = 0;
+  for (int p = n_sel + tid; p < n_candidates; p += 256) {   // invalid tail slots (n < C)
+    ci[p] = -1;
+    ce[p] = -__builtin_inff();
+  }
+  uint32_t key[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) key[r] = orderable(ev[r]);
+  topk_block<R, 256>(key, n_sel, k, ci, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
+                     s_tk, tid);
 }
 
 // ===========================================================================

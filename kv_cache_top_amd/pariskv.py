@@ -24,7 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 PK_OK, PK_ERR_INVALID_ARG, PK_ERR_UNSUPPORTED, PK_ERR_CAPACITY, PK_ERR_OUT_OF_MEMORY, PK_ERR_HIP = \
     0, -1, -2, -3, -4, -5
 PK_F32, PK_BF16 = 0, 1
-KERNELS = ["encode", "qprep", "collide", "threshold", "select", "rerank", "topk", "attend"]
+KERNELS = ["encode", "qprep", "collide", "threshold", "select", "rerank", "topk", "attend", "rerank_topk"]
 PK_N_KERNELS = len(KERNELS)
 
 

@@ -60,6 +60,17 @@ def test_group_sizes(group):
     run.close()
 
 
+@pytest.mark.parametrize("n,C", [(3001, 256), (2500, 1800)])
+def test_many_heads_one_workgroup_topk(n, C):
+    """128 query heads: rerank and top-k run in one workgroup per head."""
+    w = S.custom("llama32k", batch=4, n_kv_heads=8, n_q_heads=32, n=n, n_candidates=C, wid=260 + C)
+    say(f"case 128 heads n={n} C={C}")
+    K, V, Q = _inputs(w)
+    run = GpuRun(w, K, V, Q).retrieve().attend()
+    _check_all_units(run, K, V, units=[0, 13, 31])
+    run.close()
+
+
 def test_many_subtiles_single_unit():
     """One KV head with a long ragged key range: the selection's per-sub-tile
     prefix counts span several 256-sub-tile chunks."""
