@@ -350,8 +350,12 @@ pk_status pk_append_keys(pk_context* ctx, const void* keys, pk_dtype dt, const i
   return st;
 }
 
-pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s,
-                      int32_t* topk_idx, float* topk_est, const pk_debug* dbg, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+pk_status check_retrieve_args(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s,
+                              const int32_t* topk_idx, const float* topk_est) {
   if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
   pk_status st = check_summaries(ctx, s);
   if (st != PK_OK) return st;
@@ -359,7 +363,33 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
   if (q_dtype != PK_F32 && q_dtype != PK_BF16) return fail(ctx, PK_ERR_UNSUPPORTED, "q dtype %d", (int)q_dtype);
   if (!aligned(q, q_dtype == PK_BF16 ? 4 : 8) || !aligned(topk_idx, 4) || (topk_est && !aligned(topk_est, 4)))
     return fail(ctx, PK_ERR_INVALID_ARG, "misaligned q / output pointer");
-  hipStream_t stream = (hipStream_t)hip_stream;
+  return PK_OK;
+}
+
+pk_status check_attend_args(pk_context* ctx, const void* q, pk_dtype q_dtype, const void* k, const void* v,
+                            pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows, const int32_t* topk_idx,
+                            const void* out, pk_dtype out_dtype) {
+  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
+  if (!q || !topk_idx || !out) return fail(ctx, PK_ERR_INVALID_ARG, "q, topk_idx and out must be non-NULL");
+  for (pk_dtype d : {q_dtype, kv_dtype, out_dtype})
+    if (d != PK_F32 && d != PK_BF16) return fail(ctx, PK_ERR_UNSUPPORTED, "dtype %d", (int)d);
+  pk_status st = check_strides(ctx, k, kv_dtype, kv_strides, "k");
+  if (st != PK_OK) return st;
+  if ((st = check_strides(ctx, v, kv_dtype, kv_strides, "v")) != PK_OK) return st;
+  if (n_rows < 0) return fail(ctx, PK_ERR_INVALID_ARG, "n_rows < 0");
+  if (!aligned(q, 8) || !aligned(out, 4) || !aligned(topk_idx, 4))
+    return fail(ctx, PK_ERR_INVALID_ARG, "misaligned q / out / topk_idx");
+  return PK_OK;
+}
+
+// The retrieval chain.  With `att` (q, K/V and output of one dtype, the fused
+// rerank + top-k path taken) the last kernel also computes the attention and
+// *attended is set; otherwise the caller still has to attend.
+pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s,
+                        int32_t* topk_idx, float* topk_est, const pk_debug* dbg, hipStream_t stream,
+                        const pk::AttendArgs* att, bool* attended) {
+  pk_status st = PK_OK;
+  if (attended) *attended = false;
   const pk_config& cfg = ctx->cfg;
   const int64_t n = s->n;
   const int k = cfg.top_k, C = cfg.n_candidates;
@@ -436,16 +466,31 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
     Launch L(ctx, PK_KERNEL_RERANK_TOPK, stream);
     const int R = (n_sel + pk::RT_THREADS - 1) / pk::RT_THREADS;
     float* est_out = (dbg && dbg->cand_est) ? ctx->cand_est : nullptr;
-#define PK_RTK(RR)                                                                                             \
-  hipLaunchKernelGGL(pk::rerank_topk_kernel<RR>, dim3(ctx->qheads), dim3(pk::RT_THREADS), 0, stream, s->records, \
-                     ctx->rq, ctx->cand_idx, est_out, s->n_capacity, n_sel, C, cfg.n_q_heads, cfg.n_kv_heads,       \
-                     ctx->group, ctx->tb, k, topk_idx, topk_est)
-    if (R <= 1) PK_RTK(1);
-    else if (R <= 2) PK_RTK(2);
-    else if (R <= 4) PK_RTK(4);
-    else if (R <= 8) PK_RTK(8);
-    else PK_RTK(16);
-#undef PK_RTK
+    const pk::AttendArgs none{};
+#define PK_RTK_LAUNCH(RR, T, MR, A)                                                                               \
+  hipLaunchKernelGGL((pk::rerank_topk_kernel<RR, T, MR, A>), dim3(ctx->qheads), dim3(pk::RT_THREADS), 0, stream,   \
+                     s->records, ctx->rq, ctx->cand_idx, est_out, s->n_capacity, n_sel, C, cfg.n_q_heads,           \
+                     cfg.n_kv_heads, ctx->group, ctx->tb, k, topk_idx, topk_est, A ? *att : none)
+#define PK_RTK_R(T, MR, A)                         \
+  do {                                             \
+    if (R <= 1) PK_RTK_LAUNCH(1, T, MR, A);        \
+    else if (R <= 2) PK_RTK_LAUNCH(2, T, MR, A);   \
+    else if (R <= 4) PK_RTK_LAUNCH(4, T, MR, A);   \
+    else if (R <= 8) PK_RTK_LAUNCH(8, T, MR, A);   \
+    else PK_RTK_LAUNCH(16, T, MR, A);              \
+  } while (0)
+    if (att) {
+      const int mr = k <= 8 * (pk::RT_THREADS / 64) ? 8 : 16;   // rows per wave
+      if (q_dtype == PK_BF16 && mr == 8) PK_RTK_R(uint16_t, 8, true);
+      else if (q_dtype == PK_BF16) PK_RTK_R(uint16_t, 16, true);
+      else if (mr == 8) PK_RTK_R(float, 8, true);
+      else PK_RTK_R(float, 16, true);
+      if (attended) *attended = true;
+    } else {
+      PK_RTK_R(float, 1, false);
+    }
+#undef PK_RTK_R
+#undef PK_RTK_LAUNCH
     if ((st = check_launch(ctx, "rerank_topk")) != PK_OK) return st;
   } else {
     // few heads: spread the rerank over several workgroups per head, then select
@@ -488,27 +533,16 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk
   return PK_OK;
 }
 
-pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, const void* k, const void* v,
-                           pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows,
-                           const int32_t* topk_idx, void* out, pk_dtype out_dtype, void* hip_stream) {
-  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
-  if (!q || !topk_idx || !out) return fail(ctx, PK_ERR_INVALID_ARG, "q, topk_idx and out must be non-NULL");
-  for (pk_dtype d : {q_dtype, kv_dtype, out_dtype})
-    if (d != PK_F32 && d != PK_BF16) return fail(ctx, PK_ERR_UNSUPPORTED, "dtype %d", (int)d);
-  pk_status st = check_strides(ctx, k, kv_dtype, kv_strides, "k");
-  if (st != PK_OK) return st;
-  if ((st = check_strides(ctx, v, kv_dtype, kv_strides, "v")) != PK_OK) return st;
-  if (n_rows < 0) return fail(ctx, PK_ERR_INVALID_ARG, "n_rows < 0");
-  if (!aligned(q, 8) || !aligned(out, 4) || !aligned(topk_idx, 4))
-    return fail(ctx, PK_ERR_INVALID_ARG, "misaligned q / out / topk_idx");
-  hipStream_t stream = (hipStream_t)hip_stream;
+pk_status attend_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const void* k, const void* v,
+                      pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows, const int32_t* topk_idx,
+                      void* out, pk_dtype out_dtype, hipStream_t stream) {
   const pk_config& c = ctx->cfg;
   const int kk = c.top_k;
+  const pk::AttendArgs a{q, k, v, kv_strides[0], kv_strides[1], kv_strides[2], n_rows, c.softmax_scale, out};
   Launch L(ctx, PK_KERNEL_ATTEND, stream);
 #define PK_ATT(KT, QT, OT, R)                                                                                   \
-  hipLaunchKernelGGL((pk::attend_kernel<KT, QT, OT, R>), dim3(ctx->qheads), dim3(256), 0, stream, (const QT*)q, \
-                     (const KT*)k, (const KT*)v, kv_strides[0], kv_strides[1], kv_strides[2], n_rows, topk_idx, kk, \
-                     c.n_q_heads, c.n_kv_heads, ctx->group, c.softmax_scale, (OT*)out)
+  hipLaunchKernelGGL((pk::attend_kernel<KT, QT, OT, R>), dim3(ctx->qheads), dim3(256), 0, stream, a, topk_idx, kk, \
+                     c.n_q_heads, c.n_kv_heads, ctx->group)
 #define PK_ATT_R(KT, QT, OT) \
   do {                       \
     if (kk <= 128)           \
@@ -539,6 +573,43 @@ pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, con
 #undef PK_ATT_R
 #undef PK_ATT
   return check_launch(ctx, "attend");
+}
+
+}  // namespace
+
+extern "C" {
+
+pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s,
+                      int32_t* topk_idx, float* topk_est, const pk_debug* dbg, void* hip_stream) {
+  pk_status st = check_retrieve_args(ctx, q, q_dtype, s, topk_idx, topk_est);
+  if (st != PK_OK) return st;
+  return retrieve_impl(ctx, q, q_dtype, s, topk_idx, topk_est, dbg, (hipStream_t)hip_stream, nullptr, nullptr);
+}
+
+pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, const void* k, const void* v,
+                           pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows,
+                           const int32_t* topk_idx, void* out, pk_dtype out_dtype, void* hip_stream) {
+  pk_status st = check_attend_args(ctx, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype);
+  if (st != PK_OK) return st;
+  return attend_impl(ctx, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype,
+                     (hipStream_t)hip_stream);
+}
+
+pk_status pk_retrieve_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s,
+                             const void* k, const void* v, pk_dtype kv_dtype, const int64_t kv_strides[3],
+                             int64_t n_rows, int32_t* topk_idx, float* topk_est, void* out, pk_dtype out_dtype,
+                             const pk_debug* dbg, void* hip_stream) {
+  pk_status st = check_retrieve_args(ctx, q, q_dtype, s, topk_idx, topk_est);
+  if (st != PK_OK) return st;
+  st = check_attend_args(ctx, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype);
+  if (st != PK_OK) return st;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  const bool same_dtype = q_dtype == kv_dtype && kv_dtype == out_dtype;
+  const pk::AttendArgs a{q, k, v, kv_strides[0], kv_strides[1], kv_strides[2], n_rows, ctx->cfg.softmax_scale, out};
+  bool attended = false;
+  st = retrieve_impl(ctx, q, q_dtype, s, topk_idx, topk_est, dbg, stream, same_dtype ? &a : nullptr, &attended);
+  if (st != PK_OK || attended) return st;
+  return attend_impl(ctx, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype, stream);
 }
 
 pk_status pk_host_alloc_mapped(size_t bytes, void** host_ptr, void** device_ptr) {

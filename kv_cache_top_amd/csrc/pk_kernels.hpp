@@ -707,6 +707,129 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
 }
 
 // ===========================================================================
+// sparse attention over the retrieved rows (Slides Sec. 3, Eqs. (1)-(3);
+// README "3. Attention"; UVA fetch of host-resident rows, Slides Sec. 4.2.3).
+//
+// NW waves per query head; wave w takes rows w, w+NW, ...; lane l holds dims
+// 2l, 2l+1.  All K and V row loads of a wave are issued before any use, so
+// host-memory latency overlaps.  fp32 scores and softmax.
+// ===========================================================================
+template <int NW>
+struct AttShared {
+  float score[PK_MAX_TOPK_ATT];
+  float acc[NW][D];
+};
+
+template <typename KT, typename QT, typename OT, int MAXR, int NW>
+__device__ void attend_block(const QT* __restrict__ qh_ptr, const KT* __restrict__ kb, const KT* __restrict__ vb,
+                             int64_t st, int64_t n_rows, const int32_t* hidx, int k, float scale,
+                             OT* __restrict__ out_head, AttShared<NW>& s, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  float q0, q1;
+  if constexpr (sizeof(QT) == 2) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(qh_ptr)[lane];
+    q0 = bf16_lo(w); q1 = bf16_hi(w);
+  } else {
+    const float2 w = reinterpret_cast<const float2*>(qh_ptr)[lane];
+    q0 = w.x; q1 = w.y;
+  }
+  if (n_rows <= 0) {                            // no rows: nothing may be read
+    if (tid < D) {
+      if constexpr (sizeof(OT) == 2) reinterpret_cast<uint16_t*>(out_head)[tid] = 0;
+      else out_head[tid] = 0.0f;
+    }
+    return;
+  }
+  // lane t holds the index of this wave's row wave + NW t (-1: padding / out of range)
+  int myix = -1;
+  {
+    const int r = wave + NW * lane;
+    const int v = hidx[r < k ? r : k - 1];
+    myix = (lane < MAXR && r < k && v >= 0 && (int64_t)v < n_rows) ? v : -1;
+  }
+  // every row load is issued unconditionally (invalid rows read row 0 and are
+  // masked below) so that all of them are in flight together
+  float k0v[MAXR], k1v[MAXR], v0v[MAXR], v1v[MAXR];
+  uint64_t okmask = 0;
+#pragma unroll
+  for (int t = 0; t < MAXR; ++t) {
+    const int ix = __shfl(myix, t, 64);
+    okmask |= (ix >= 0 ? 1ull : 0ull) << t;
+    const int64_t row = ix >= 0 ? ix : 0;
+    if constexpr (sizeof(KT) == 2) {
+      const uint32_t kw = reinterpret_cast<const uint32_t*>(kb + row * st)[lane];
+      const uint32_t vw = reinterpret_cast<const uint32_t*>(vb + row * st)[lane];
+      k0v[t] = bf16_lo(kw); k1v[t] = bf16_hi(kw); v0v[t] = bf16_lo(vw); v1v[t] = bf16_hi(vw);
+    } else {
+      const float2 kw = reinterpret_cast<const float2*>(kb + row * st)[lane];
+      const float2 vw = reinterpret_cast<const float2*>(vb + row * st)[lane];
+      k0v[t] = kw.x; k1v[t] = kw.y; v0v[t] = vw.x; v1v[t] = vw.y;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MAXR; ++t) {
+    const int r = wave + NW * t;
+    float p = __builtin_fmaf(q0, k0v[t], q1 * k1v[t]);
+    for (int off = 32; off >= 1; off >>= 1) p += __shfl_xor(p, off, 64);
+    if (lane == 0 && r < k) s.score[r] = ((okmask >> t) & 1ull) ? p * scale : -__builtin_inff();
+  }
+  __syncthreads();
+  float m = -__builtin_inff();
+  for (int r = lane; r < k; r += 64) m = fmaxf(m, s.score[r]);
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  float ssum = 0.0f;
+  for (int r = lane; r < k; r += 64) ssum += (s.score[r] == -__builtin_inff()) ? 0.0f : __expf(s.score[r] - m);
+  for (int off = 32; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, 64);
+
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int t = 0; t < MAXR; ++t) {
+    const int r = wave + NW * t;
+    const float pr = ((okmask >> t) & 1ull) ? __expf(s.score[r < k ? r : 0] - m) : 0.0f;
+    a0 = __builtin_fmaf(pr, v0v[t], a0);
+    a1 = __builtin_fmaf(pr, v1v[t], a1);
+  }
+  s.acc[wave][2 * lane] = a0;
+  s.acc[wave][2 * lane + 1] = a1;
+  __syncthreads();
+  if (tid < D) {
+    float acc = s.acc[0][tid];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) acc += s.acc[w2][tid];
+    const float o = (ssum > 0.0f) ? acc / ssum : 0.0f;
+    if constexpr (sizeof(OT) == 2) {
+      reinterpret_cast<uint16_t*>(out_head)[tid] = (uint16_t)f32_to_bf16_rne(o);
+    } else {
+      out_head[tid] = o;
+    }
+  }
+}
+
+// K / V of one query head and where its output goes
+struct AttendArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t sb, sh, st;     // element strides: sequence, KV head, token
+  int64_t n_rows;
+  float scale;
+  void* out;
+};
+
+template <typename KT, typename QT, typename OT, int MAXR>
+__global__ void __launch_bounds__(256)
+attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k, int n_q_heads, int n_kv_heads, int group) {
+  __shared__ AttShared<4> s_att;
+  const int head = blockIdx.x;
+  const int seq = head / n_q_heads, qh = head - seq * n_q_heads, kvh = qh / group;
+  const KT* kb = reinterpret_cast<const KT*>(a.k) + seq * a.sb + kvh * a.sh;
+  const KT* vb = reinterpret_cast<const KT*>(a.v) + seq * a.sb + kvh * a.sh;
+  attend_block<KT, QT, OT, MAXR, 4>(reinterpret_cast<const QT*>(a.q) + (int64_t)head * D, kb, vb, a.st, a.n_rows,
+                                    idx + (int64_t)head * k, k, a.scale,
+                                    reinterpret_cast<OT*>(a.out) + (int64_t)head * D, s_att, threadIdx.x);
+}
+
+// ===========================================================================
 // rerank (Slides Eqs. (7)-(10); README "2. Decode", fused 4-bit reranking) and
 // top-k by (estimate desc, key index asc) (Slides Sec. 4.2.3: reranking
 // returns the Top-100 indices).
@@ -795,7 +918,7 @@ struct TopkShared {
 // as order-preserving keys key[r].  s.misc must be zero on entry.
 template <int R, int NT>
 __device__ void topk_block(const uint32_t (&key)[R], int n_sel, int k, const int32_t* ci, int32_t* out_idx,
-                           float* out_est, TopkShared<NT>& s, int tid) {
+                           float* out_est, TopkShared<NT>& s, int tid, int32_t* lds_idx = nullptr) {
   constexpr int NW = NT / 64;
   const int lane = tid & 63, wave = tid >> 6;
   const int keff = k < n_sel ? k : n_sel;
@@ -919,11 +1042,14 @@ __device__ void topk_block(const uint32_t (&key)[R], int n_sel, int k, const int
     int rank = 0;
     for (int j2 = 0; j2 < keff; ++j2) rank += (s.f[j2] > e) ? 1 : 0;
     const int p = (int)(0xFFFFFFFFu - (uint32_t)e);
-    out_idx[rank] = ci[p];
+    const int32_t key_index = ci[p];
+    out_idx[rank] = key_index;
+    if (lds_idx) lds_idx[rank] = key_index;
     if (out_est) out_est[rank] = from_orderable((uint32_t)(e >> 32));
   }
   for (int r = keff + tid; r < k; r += NT) {
     out_idx[r] = -1;
+    if (lds_idx) lds_idx[r] = -1;
     if (out_est) out_est[r] = -__builtin_inff();
   }
 }
@@ -931,15 +1057,19 @@ __device__ void topk_block(const uint32_t (&key)[R], int n_sel, int k, const int
 // ---- many heads: rerank and top-k of one head in one workgroup -------------
 constexpr int RT_THREADS = 1024;
 
-template <int R>        // candidate slots per thread: n_sel <= R * RT_THREADS
+// T, MAXR, ATT: with ATT the workgroup goes on to attend over its head's k
+// rows (q, K, V and the output all of type T; MAXR rows per wave).
+template <int R, typename T, int MAXR, bool ATT>   // candidate slots per thread: n_sel <= R * RT_THREADS
 __global__ void __launch_bounds__(RT_THREADS)
 rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot_q,
                    int32_t* __restrict__ cand_idx, float* __restrict__ cand_est_out, int64_t n_cap, int n_sel,
                    int n_candidates, int n_q_heads, int n_kv_heads, int group, Tables tb, int k,
-                   int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
+                   int32_t* __restrict__ out_idx, float* __restrict__ out_est, AttendArgs att) {
   __shared__ float s_T[D * 16];
   __shared__ float s_est[R * RT_THREADS];
   __shared__ TopkShared<RT_THREADS> s_tk;
+  __shared__ int32_t s_idx[ATT ? PK_MAX_TOPK_ATT : 1];
+  __shared__ AttShared<ATT ? RT_THREADS / 64 : 1> s_att;
 
   const int head = blockIdx.x, tid = threadIdx.x;
   const int seq = head / n_q_heads, qh = head - seq * n_q_heads;
@@ -975,7 +1105,16 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
     key[r] = orderable(s_est[p < plast ? p : plast]);
   }
   topk_block<R, RT_THREADS>(key, n_sel, k, ci, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
-                            s_tk, tid);
+                            s_tk, tid, ATT ? s_idx : nullptr);
+  if constexpr (ATT) {
+    __syncthreads();
+    const int kvh = qh / group;
+    const T* kb = reinterpret_cast<const T*>(att.k) + seq * att.sb + kvh * att.sh;
+    const T* vb = reinterpret_cast<const T*>(att.v) + seq * att.sb + kvh * att.sh;
+    attend_block<T, T, T, MAXR, RT_THREADS / 64>(reinterpret_cast<const T*>(att.q) + (int64_t)head * D, kb, vb, att.st,
+                                                 att.n_rows, s_idx, k, att.scale,
+                                                 reinterpret_cast<T*>(att.out) + (int64_t)head * D, s_att, tid);
+  }
 }
 
 // ---- few heads: rerank spread over RR_PER_WG-candidate workgroups ----------
@@ -1036,107 +1175,6 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
   for (int r = 0; r < R; ++r) key[r] = orderable(ev[r]);
   topk_block<R, 256>(key, n_sel, k, ci, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
                      s_tk, tid);
-}
-
-// ===========================================================================
-// sparse attention over the retrieved rows (Slides Sec. 3, Eqs. (1)-(3);
-// README "3. Attention"; UVA fetch of host-resident rows, Slides Sec. 4.2.3).
-//
-// One workgroup (4 waves) per query head; wave w takes rows w, w+4, ...; lane
-// l holds dims 2l, 2l+1.  All K and V row loads of a wave are issued before
-// any use, so host-memory latency overlaps.  fp32 scores and softmax.
-// ===========================================================================
-template <typename KT, typename QT, typename OT, int MAXR>
-__global__ void __launch_bounds__(256)
-attend_kernel(const QT* __restrict__ q, const KT* __restrict__ kmat, const KT* __restrict__ vmat,
-              int64_t sb, int64_t sh, int64_t st, int64_t n_rows, const int32_t* __restrict__ idx, int k,
-              int n_q_heads, int n_kv_heads, int group, float scale, OT* __restrict__ out) {
-  __shared__ float s_score[PK_MAX_TOPK_ATT];
-  __shared__ float s_acc[4][D];
-  __shared__ float s_red[2];
-
-  const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int seq = head / n_q_heads, qh = head - seq * n_q_heads, kvh = qh / group;
-  float q0, q1;
-  if constexpr (sizeof(QT) == 2) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(q)[((int64_t)head * D >> 1) + lane];
-    q0 = bf16_lo(w); q1 = bf16_hi(w);
-  } else {
-    const float2 w = reinterpret_cast<const float2*>(q)[((int64_t)head * D >> 1) + lane];
-    q0 = w.x; q1 = w.y;
-  }
-  if (n_rows <= 0) {                            // no rows: nothing may be read
-    if (tid < D) {
-      if constexpr (sizeof(OT) == 2) reinterpret_cast<uint16_t*>(out)[(int64_t)head * D + tid] = 0;
-      else out[(int64_t)head * D + tid] = 0.0f;
-    }
-    return;
-  }
-  const int32_t* hidx = idx + (int64_t)head * k;
-  const KT* kb = kmat + seq * sb + kvh * sh;
-  const KT* vb = vmat + seq * sb + kvh * sh;
-
-  // lane t holds the index of this wave's row wave + 4t (-1: padding / out of range)
-  int myix = -1;
-  {
-    const int r = wave + 4 * lane;
-    const int v = hidx[r < k ? r : k - 1];
-    myix = (lane < MAXR && r < k && v >= 0 && (int64_t)v < n_rows) ? v : -1;
-  }
-  // every row load is issued unconditionally (invalid rows read row 0 and are
-  // masked below) so that all of them are in flight together
-  float k0v[MAXR], k1v[MAXR], v0v[MAXR], v1v[MAXR];
-  uint64_t okmask = 0;
-#pragma unroll
-  for (int t = 0; t < MAXR; ++t) {
-    const int ix = __shfl(myix, t, 64);
-    okmask |= (ix >= 0 ? 1ull : 0ull) << t;
-    const int64_t row = ix >= 0 ? ix : 0;
-    if constexpr (sizeof(KT) == 2) {
-      const uint32_t kw = reinterpret_cast<const uint32_t*>(kb + row * st)[lane];
-      const uint32_t vw = reinterpret_cast<const uint32_t*>(vb + row * st)[lane];
-      k0v[t] = bf16_lo(kw); k1v[t] = bf16_hi(kw); v0v[t] = bf16_lo(vw); v1v[t] = bf16_hi(vw);
-    } else {
-      const float2 kw = reinterpret_cast<const float2*>(kb + row * st)[lane];
-      const float2 vw = reinterpret_cast<const float2*>(vb + row * st)[lane];
-      k0v[t] = kw.x; k1v[t] = kw.y; v0v[t] = vw.x; v1v[t] = vw.y;
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < MAXR; ++t) {
-    const int r = wave + 4 * t;
-    float p = __builtin_fmaf(q0, k0v[t], q1 * k1v[t]);
-    for (int off = 32; off >= 1; off >>= 1) p += __shfl_xor(p, off, 64);
-    if (lane == 0 && r < k) s_score[r] = ((okmask >> t) & 1ull) ? p * scale : -__builtin_inff();
-  }
-  __syncthreads();
-  float m = -__builtin_inff();
-  for (int r = lane; r < k; r += 64) m = fmaxf(m, s_score[r]);
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  float ssum = 0.0f;
-  for (int r = lane; r < k; r += 64) ssum += (s_score[r] == -__builtin_inff()) ? 0.0f : __expf(s_score[r] - m);
-  for (int off = 32; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, 64);
-
-  float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-  for (int t = 0; t < MAXR; ++t) {
-    const int r = wave + 4 * t;
-    const float pr = ((okmask >> t) & 1ull) ? __expf(s_score[r < k ? r : 0] - m) : 0.0f;
-    a0 = __builtin_fmaf(pr, v0v[t], a0);
-    a1 = __builtin_fmaf(pr, v1v[t], a1);
-  }
-  s_acc[wave][2 * lane] = a0;
-  s_acc[wave][2 * lane + 1] = a1;
-  __syncthreads();
-  if (tid < D) {
-    const float acc = s_acc[0][tid] + s_acc[1][tid] + s_acc[2][tid] + s_acc[3][tid];
-    const float o = (ssum > 0.0f) ? acc / ssum : 0.0f;
-    if constexpr (sizeof(OT) == 2) {
-      reinterpret_cast<uint16_t*>(out)[(int64_t)head * D + tid] = (uint16_t)f32_to_bf16_rne(o);
-    } else {
-      out[(int64_t)head * D + tid] = o;
-    }
-  }
 }
 
 // fill top-k outputs for an empty key set

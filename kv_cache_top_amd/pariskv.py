@@ -71,6 +71,8 @@ _SIGS = {
     "pk_sparse_attend": ([_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _I64x3, ctypes.c_int64, _P, _P,
                           ctypes.c_int, _P],
                          ctypes.c_int),
+    "pk_retrieve_attend": ([_P, _P, ctypes.c_int, ctypes.POINTER(pk_summaries), _P, _P, ctypes.c_int, _I64x3,
+                            ctypes.c_int64, _P, _P, _P, ctypes.c_int, ctypes.POINTER(pk_debug), _P], ctypes.c_int),
     "pk_host_alloc_mapped": ([ctypes.c_size_t, ctypes.POINTER(_P), ctypes.POINTER(_P)], ctypes.c_int),
     "pk_host_free": ([_P], ctypes.c_int),
     "pk_calibration_copy": ([_P, _P, ctypes.c_size_t, _P], ctypes.c_int),
@@ -207,6 +209,26 @@ def pk_sparse_attend_raw(ctx, q, k_ptr: int, v_ptr: int, kv_dtype: int, kv_strid
     _check(_lib.pk_sparse_attend(ctx, _ptr(q), _dtype(q), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
                                  kv_dtype, _I64x3(*kv_strides), n_rows, _ptr(topk_idx), _ptr(out), _dtype(out),
                                  _stream(stream)), ctx)
+
+
+def pk_retrieve_attend(ctx, q, sums: pk_summaries, k, v, topk_idx, out, topk_est=None,
+                       debug: pk_debug | None = None, stream=None):
+    if k.stride() != v.stride() or k.dtype != v.dtype:
+        raise ValueError("K and V must share dtype and strides")
+    if not q.is_contiguous() or not out.is_contiguous():
+        raise ValueError("q and out must be contiguous")
+    _check(_lib.pk_retrieve_attend(ctx, _ptr(q), _dtype(q), ctypes.byref(sums), _ptr(k), _ptr(v), _dtype(k),
+                                   _strides4(k), k.shape[2], _ptr(topk_idx), _ptr(topk_est), _ptr(out), _dtype(out),
+                                   ctypes.byref(debug) if debug is not None else None, _stream(stream)), ctx)
+
+
+def pk_retrieve_attend_raw(ctx, q, sums: pk_summaries, k_ptr: int, v_ptr: int, kv_dtype: int, kv_strides,
+                           n_rows: int, topk_idx, out, topk_est=None, debug: pk_debug | None = None, stream=None):
+    """Variant for K/V that are not torch tensors (e.g. mapped host memory)."""
+    _check(_lib.pk_retrieve_attend(ctx, _ptr(q), _dtype(q), ctypes.byref(sums), ctypes.c_void_p(k_ptr),
+                                   ctypes.c_void_p(v_ptr), kv_dtype, _I64x3(*kv_strides), n_rows, _ptr(topk_idx),
+                                   _ptr(topk_est), _ptr(out), _dtype(out),
+                                   ctypes.byref(debug) if debug is not None else None, _stream(stream)), ctx)
 
 
 def pk_host_alloc_mapped(nbytes: int):

@@ -99,11 +99,10 @@ class GpuRun:
         strides = (A.shape[1] * A.shape[2] * A.shape[3], A.shape[2] * A.shape[3], A.shape[3])
         return view, strides, d
 
-    def retrieve(self, Q: np.ndarray | None = None):
+    def _outputs(self, Q):
         import torch
         P = self.P
         w, cfg = self.w, self.cfg
-        Qt = self.Qt if Q is None else to_torch(Q)
         H = w.batch * w.n_q_heads
         self.topk_idx = torch.full((w.batch, w.n_q_heads, w.top_k), -7, dtype=torch.int32, device="cuda")
         self.topk_est = torch.zeros((w.batch, w.n_q_heads, w.top_k), dtype=torch.float32, device="cuda")
@@ -116,7 +115,29 @@ class GpuRun:
             self.cand_est = torch.zeros((H, cfg.n_candidates), dtype=torch.float32, device="cuda")
             dbg = P.pk_debug(self.rot_q.data_ptr(), self.lut.data_ptr(), self.scores.data_ptr(),
                              self.cand_idx.data_ptr(), self.cand_est.data_ptr())
-        P.pk_retrieve(self.ctx.h, Qt, self.sums.s, self.topk_idx, self.topk_est, dbg)
+        return (self.Qt if Q is None else to_torch(Q)), dbg
+
+    def retrieve(self, Q: np.ndarray | None = None):
+        import torch
+        Qt, dbg = self._outputs(Q)
+        self.P.pk_retrieve(self.ctx.h, Qt, self.sums.s, self.topk_idx, self.topk_est, dbg)
+        torch.cuda.synchronize()
+        return self
+
+    def retrieve_attend(self, out_dtype="match"):
+        """Retrieval and attention through the single fused call."""
+        import torch
+        P = self.P
+        w = self.w
+        Qt, dbg = self._outputs(None)
+        odt = torch.float32 if (self.kv_dtype == P.PK_F32 or out_dtype == "f32") else torch.bfloat16
+        self.out = torch.zeros((w.batch, w.n_q_heads, 128), dtype=odt, device="cuda")
+        if self.kv_host:
+            P.pk_retrieve_attend_raw(self.ctx.h, Qt, self.sums.s, self.kptr, self.vptr, self.kv_dtype,
+                                     self.kv_strides, self.Kd.shape[2], self.topk_idx, self.out, self.topk_est, dbg)
+        else:
+            P.pk_retrieve_attend(self.ctx.h, Qt, self.sums.s, self.Kt, self.Vt, self.topk_idx, self.out,
+                                 self.topk_est, dbg)
         torch.cuda.synchronize()
         return self
 

@@ -1,6 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times: the whole workload runs on the GPU; the oracle recomputes
-sampled units (every intermediate bit for bit, attention within 2e-2).
+benchmark times (one pk_retrieve_attend call per step): the whole workload
+runs on the GPU; the oracle recomputes sampled units (every intermediate bit
+for bit, attention within 2e-2).
 
   llama32k     1 x 8 KV / 32 q heads, n = 32768, C = 2048
   batched128k  8 x 8 KV / 32 q heads, n = 131072, C = 4096
@@ -26,7 +27,7 @@ def _run_full(name, units, kv_host=False):
     V = S.all_values(w)
     Q = S.all_queries(w, K)
     say(f"case {name}: GPU run")
-    run = GpuRun(w, K, V, Q, kv_host=kv_host).retrieve().attend()
+    run = GpuRun(w, K, V, Q, kv_host=kv_host).retrieve_attend()
     stats = {}
     for u in units:
         b, h = divmod(u, w.n_kv_heads)
@@ -90,7 +91,7 @@ def test_full_drift_stream():
         run.Q = Qt
         run.Qt = to_torch(Qt)
         run.debug = t in check_steps
-        run.retrieve().attend()
+        run.retrieve_attend()
         if t in check_steps:
             say(f"case drift128k: step {t}, oracle unit {unit}")
             enc = {k: v[:n_t] for k, v in enc_all.items()}

@@ -1,0 +1,70 @@
+"""GPU parity of the single retrieve + attend call (pk_retrieve_attend) against
+the oracle, on the paths it can take: the fused rerank + top-k + attention
+workgroup (many heads, or few candidates; one dtype throughout), the split
+rerank / top-k kernels followed by the attention kernel, mixed dtypes, mapped
+host K/V and the empty key set."""
+import numpy as np
+import pytest
+
+from workloads import synthetic as S
+from tests.parity_util import GpuRun, check_encode_unit, check_retrieve_unit, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, units, kv_host=False, out_dtype="match", n=None):
+    K = S.all_keys(w)
+    V = S.all_values(w)
+    Q = S.all_queries(w, K)
+    run = GpuRun(w, K, V, Q, kv_host=kv_host, n=n).retrieve_attend(out_dtype=out_dtype)
+    for u in units:
+        b, h = divmod(u, w.n_kv_heads)
+        kf = S.as_f32(K[b, h, :run.n])
+        vf = S.as_f32(V[b, h, :run.n])
+        enc = check_encode_unit(run, u, kf)
+        check_retrieve_unit(run, b, h, kf, vf, enc)
+    return run
+
+
+def test_fused_tiny_fp32():
+    say("case fused tiny4k fp32")
+    _run(S.WORKLOADS["tiny4k"], [0]).close()
+
+
+@pytest.mark.parametrize("n,C,k", [(3001, 256, 100), (2500, 1800, 100), (2500, 1800, 200)])
+def test_fused_many_heads(n, C, k):
+    w = S.custom("llama32k", batch=4, n_kv_heads=8, n_q_heads=32, n=n, n_candidates=C, top_k=k, wid=500 + C + k)
+    say(f"case fused 128 heads n={n} C={C} k={k}")
+    _run(w, [0, 17, 31]).close()
+
+
+def test_split_path_then_attention():
+    """Few heads and many candidates: split rerank / top-k, then the attention kernel."""
+    w = S.custom("llama32k", batch=1, n_kv_heads=2, n_q_heads=8, n=9000, n_candidates=4096, wid=520)
+    say("case split path n=9000 C=4096")
+    _run(w, [0, 1]).close()
+
+
+def test_mixed_dtype_output():
+    """bf16 K/V with an fp32 output: retrieval fused, attention as its own kernel."""
+    w = S.custom("llama32k", batch=4, n_kv_heads=8, n_q_heads=32, n=1500, n_candidates=300, wid=530)
+    say("case fused retrieval, fp32 output")
+    _run(w, [5], out_dtype="f32").close()
+
+
+def test_fused_mapped_host_kv():
+    w = S.custom("llama32k", batch=4, n_kv_heads=8, n_q_heads=32, n=2000, n_candidates=512, wid=540)
+    say("case fused, K/V in mapped host memory")
+    _run(w, [0, 30], kv_host=True).close()
+
+
+def test_fused_empty():
+    w = S.custom("llama32k", batch=4, n_kv_heads=8, n_q_heads=32, n=16, n_candidates=64, top_k=10, wid=550)
+    say("case fused, empty key set")
+    K = S.all_keys(w)
+    V = S.all_values(w)
+    Q = S.all_queries(w, K)
+    run = GpuRun(w, K, V, Q, n=0).retrieve_attend()
+    assert (run.topk_idx.cpu().numpy() == -1).all()
+    assert (run.out.float().cpu().numpy() == 0).all()
+    run.close()
