@@ -70,9 +70,9 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // units, 256 threads each doing 1..kMaxKPL keys.
 constexpr int64_t kTargetWG = 512, kMaxKPL = 64;
 // rerank and top-k run as one workgroup per head when there are enough heads to
-// fill the chip, or few enough candidates per head (two per thread)
+// fill the chip, or few enough candidates per head (four per thread)
 constexpr int kFusedTopkHeads = 128;
-constexpr int kFusedTopkSlots = 2 * pk::RT_THREADS;
+constexpr int kFusedTopkSlots = 4 * pk::RT_THREADS;
 int tile_size(int units, int64_t n) {
   const int64_t want = ((int64_t)units * n + kTargetWG * 256 - 1) / (kTargetWG * 256);
   const int64_t kpl = want < 1 ? 1 : (want > kMaxKPL ? kMaxKPL : want);
