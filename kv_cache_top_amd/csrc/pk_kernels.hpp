@@ -11,6 +11,8 @@
 // -ffp-contract=off); division and square root are correctly rounded.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 #define PK_SORT_N 256          // top-k sort slots (k <= 256)
@@ -596,8 +598,9 @@ __global__ void __launch_bounds__(256) copy16_kernel(uint4* __restrict__ dst, co
 // tenth of the keys) are compacted, in key order, for the per-head ballots,
 // since every other key leaves all counts unchanged.
 // ===========================================================================
-constexpr int SEL_GRP = 16;             // score chunks loaded per group
-constexpr int SEL_QCAP = SEL_GRP * 64 + 64;   // compaction queue per wave: a group + a remainder
+constexpr int SEL_GRP = 16;             // score chunks per group
+constexpr int SEL_MAXGRP = 4;           // groups of the largest sub-tile (64 chunks of 64 keys)
+constexpr int SEL_QCAP = 2 * SEL_GRP * 64;    // compaction queue per wave (2 groups)
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -667,31 +670,35 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
     }
   };
 
-  // Compact a group of chunks, then run the per-head ballots over whole
-  // batches of 64 compacted keys in a rolled loop (a short body per chunk keeps
-  // the unrolled code small); the remainder waits for the next group.
-  const int ngrp = (wkeys / 64 + SEL_GRP - 1) / SEL_GRP;
-  for (int grp = 0; grp < ngrp; ++grp) {
-    uint32_t spn[SEL_GRP];
+  // Every group of the sub-tile is loaded before the first is compacted, and
+  // no global store is issued until all of them have been compacted (a store
+  // inside a loop would make the wave wait for every load in flight).  The
+  // per-head ballots then run over the queued keys in batches of 64; a queue
+  // that could overflow is drained between groups.
+  auto load_group = [&](int grp, uint32_t (&dst)[SEL_GRP]) {
 #pragma unroll
     for (int r = 0; r < SEL_GRP; ++r) {
-      const int64_t i = w0 + (int64_t)((grp + 1) * SEL_GRP + r) * 64 + lane;
-      spn[r] = srow[i < last ? i : last];
+      const int64_t i = w0 + (int64_t)(grp * SEL_GRP + r) * 64 + lane;
+      dst[r] = srow[i < last ? i : last];
     }
+  };
+  auto compact_group = [&](int grp, const uint32_t (&src)[SEL_GRP]) {
 #pragma unroll
     for (int r = 0; r < SEL_GRP; ++r) {
       const int64_t i = w0 + (int64_t)(grp * SEL_GRP + r) * 64 + lane;
       const bool valid = i < w1;                  // false for the whole wave past its keys
-      const uint32_t ge4 = ((sp[r] | 0x80808080u) - th4) & 0x80808080u;
+      const uint32_t ge4 = ((src[r] | 0x80808080u) - th4) & 0x80808080u;
       const bool interesting = valid && ge4 != 0u;
       const uint64_t im = __ballot(interesting);
-      if (interesting) ik[nk + (int)mbcnt(im)] = make_uint2((uint32_t)i, sp[r]);
+      if (interesting) ik[nk + (int)mbcnt(im)] = make_uint2((uint32_t)i, src[r]);
       nk += __popcll(im);
     }
+  };
+  auto drain = [&]() {                            // whole batches; the remainder (< 64) moves to the front
     wave_lds_sync();
     int b0 = 0;
     for (; b0 + 64 <= nk; b0 += 64) select_batch(b0, 64);
-    if (b0 > 0) {                                 // move the remainder (< 64) to the front
+    if (b0 > 0) {
       const int rem = nk - b0;
       uint2 e = make_uint2(0u, 0u);
       if (lane < rem) e = ik[b0 + lane];
@@ -700,9 +707,25 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
       nk = rem;
     }
     wave_lds_sync();
+  };
+  // NG groups are loaded unconditionally (clamped addresses; groups past the
+  // sub-tile hold no valid key), which keeps the loads ahead of their use
+  auto run = [&](auto ng_tag) {
+    constexpr int NG = decltype(ng_tag)::value;
+    uint32_t sg[NG > 1 ? NG - 1 : 1][SEL_GRP];
 #pragma unroll
-    for (int r = 0; r < SEL_GRP; ++r) sp[r] = spn[r];
-  }
+    for (int g = 1; g < NG; ++g) load_group(g, sg[g - 1]);
+    compact_group(0, sp);
+#pragma unroll
+    for (int g = 1; g < NG; ++g) {
+      if (nk > SEL_QCAP - SEL_GRP * 64) drain();
+      compact_group(g, sg[g - 1]);
+    }
+    drain();
+  };
+  const int ngrp = (wkeys / 64 + SEL_GRP - 1) / SEL_GRP;
+  if (ngrp <= 1) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, SEL_MAXGRP>{});
   select_batch(0, nk);
 }
 
