@@ -48,6 +48,19 @@ Readings taken where the pages are silent (all also listed in the design doc):
       w_b * d_b, est = sum_b t_b sequentially (no fused multiply-add).
   R11 Final Top-k by (estimate desc, key index asc).
   R12 Attention softmax over the retrieved rows only, scores scale * <k_i, q>.
+  R13 Percentile tiers (Slides, frame "Stage I uses multi-tier collision
+      votes to prune keys", Sec. 4.2.2, Eq. (15)): in block b every key is
+      scored by its centroid, so the key order within a block is the centroid
+      order of R7 with a centroid's keys side by side.  A centroid whose first
+      key sits at position P (the number of keys in better-ranked centroids)
+      is kept iff P < M = ceil(rho n), and lies in tier floor(6 P / M) of the
+      six equal percentile slices of the kept positions; tiers 0..5 add the
+      bonuses 6..1.  A centroid that straddles a slice boundary takes the tier
+      of its first key.
+  R14 Ratios are fractions of the retrieval zone rounded up: C = ceil(beta n),
+      M = ceil(rho n), with beta and rho from the README's zone-length table
+      when they adapt; they are kept as per-mille integers so that the count is
+      exact.
 """
 from __future__ import annotations
 
@@ -331,6 +344,52 @@ def collision_scores(codes: np.ndarray, weights: np.ndarray) -> np.ndarray:
     return weights[np.arange(N_SUB)[None, :], codes].sum(axis=1)
 
 
+# -----------------------------------------------------------------------------
+# Percentile tiers and adaptive ratios
+# -----------------------------------------------------------------------------
+PERCENTILE_BONUSES = (6, 5, 4, 3, 2, 1)
+# README "Parameters": (zone length below, candidate ratio, collision ratio), per mille
+ADAPTIVE_RATIOS_PERMILLE = ((5000, 500, 500), (10000, 250, 300), (30000, 200, 250), (None, 100, 200))
+
+
+def adaptive_ratios_permille(zone_len: int):
+    """(beta, rho) in 1/1000 for a retrieval zone of zone_len keys (R14)."""
+    for limit, beta, rho in ADAPTIVE_RATIOS_PERMILLE:
+        if limit is None or zone_len < limit:
+            return beta, rho
+    raise AssertionError("unreachable")
+
+
+def ratio_count(permille: int, n: int) -> int:
+    """ceil(permille / 1000 * n), exact (R14)."""
+    return (permille * n + 999) // 1000
+
+
+def centroid_occupancy(codes: np.ndarray) -> np.ndarray:
+    """Keys per (block, centroid): int64 [16, 256]."""
+    codes = np.asarray(codes, dtype=np.int64).reshape(-1, N_SUB)
+    counts = np.zeros((N_SUB, N_CENTROIDS), dtype=np.int64)
+    for b in range(N_SUB):
+        counts[b] = np.bincount(codes[:, b], minlength=N_CENTROIDS)
+    return counts
+
+
+def percentile_tier_weights(ranks: np.ndarray, counts: np.ndarray, M: int,
+                            bonuses=PERCENTILE_BONUSES) -> np.ndarray:
+    """Per-(block, centroid) bonus of the six percentile tiers of the top M
+    keys of each block (R13; Slides Sec. 4.2.2, Eq. (15))."""
+    nt = len(bonuses)
+    w = np.zeros(ranks.shape, dtype=np.int64)
+    for b in range(ranks.shape[0]):
+        first = 0                                   # keys in better-ranked centroids
+        for c in np.argsort(ranks[b], kind="stable"):
+            if first >= M:
+                break
+            w[b, c] = bonuses[(nt * first) // M]
+            first += int(counts[b, c])
+    return w
+
+
 def select_candidates(S: np.ndarray, C: int) -> np.ndarray:
     """Indices of the C largest S, ties by ascending index, returned ascending (R9).
 
@@ -447,21 +506,27 @@ def exact_topk(K: np.ndarray, q: np.ndarray, k: int) -> np.ndarray:
 # One decode step for one (sequence, KV head) unit
 # =============================================================================
 def decode_unit(qs, keys_f32, values, enc, signs, L32, tier_top, tier_weight,
-                C: int, k: int, scale: float, n: int | None = None):
+                C: int, k: int, scale: float, n: int | None = None, percentile_M: int | None = None):
     """Retrieve and attend for the G query heads of one unit.
 
     qs: float32 [G, 128]; keys_f32 / values: [>= n, 128]; enc: encode_f32 output
     (or the same fields from elsewhere) covering >= n keys.
     Returns a list (one per head) of dicts with Rq, scores, weights, S, cand,
-    est32, est64, scale64, top_idx, top_est, out."""
+    est32, est64, scale64, top_idx, top_est, out.
+    With percentile_M the votes use the percentile tiers of the top
+    percentile_M keys per block (R13) instead of the rank tiers."""
     n = enc["codes"].shape[0] if n is None else n
     codes = enc["codes"][:n]
+    counts = centroid_occupancy(codes) if percentile_M is not None else None
     nib = enc["nibbles"][:n]
     w = enc["weights"][:n]
     out = []
     for q in np.asarray(qs, dtype=F32):
         Rq, _, sc = qprep_f32(q, signs)
-        wt = tier_weights(centroid_ranks(sc), tier_top, tier_weight)
+        if percentile_M is None:
+            wt = tier_weights(centroid_ranks(sc), tier_top, tier_weight)
+        else:
+            wt = percentile_tier_weights(centroid_ranks(sc), counts, percentile_M)
         S = collision_scores(codes, wt)
         cand = select_candidates(S, C)
         est32 = rerank_f32(nib[cand], w[cand], Rq, L32)
