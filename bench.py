@@ -56,10 +56,24 @@ def parse():
 
 
 # ---------------------------------------------------------------------------
+def zone_ratios_permille(n: int):
+    """README "Parameters" table: (candidate, collision) ratio per mille by zone length."""
+    for limit, beta, rho in ((5000, 500, 500), (10000, 250, 300), (30000, 200, 250)):
+        if n < limit:
+            return beta, rho
+    return 100, 200
+
+
+def candidates_per_call(w, n: int) -> int:
+    if w.adaptive:
+        return (zone_ratios_permille(n)[0] * n + 999) // 1000
+    return w.n_candidates
+
+
 def algorithmic_bytes(w, n: int) -> dict:
     """Bytes the method itself must move per step (summaries read, K/V rows)."""
     kv_row = 128 * (2 if w.kv_dtype == "bf16" else 4)
-    n_sel = min(n, w.n_candidates)
+    n_sel = min(n, candidates_per_call(w, n))
     keff = min(w.top_k, n_sel)
     return {
         "collide": CODE_BYTES * n * w.units,
@@ -96,8 +110,12 @@ def cpu_baseline(w, K, V, Q_pool, seconds: float) -> dict:
                 kf, vf, enc = encs[u]
                 q = Q_pool[done % len(Q_pool)]
                 qs = S.as_f32(q[b, h * w.group:(h + 1) * w.group])
-                O.decode_unit(qs, kf, vf, enc, signs, L32, w.tier_top, w.tier_weight, w.n_candidates,
-                              w.top_k, w.softmax_scale)
+                M = None
+                if w.tier_mode == "percentile":
+                    rho = O.adaptive_ratios_permille(w.n)[1] if w.adaptive else w.collision_permille
+                    M = O.ratio_count(rho, w.n)
+                O.decode_unit(qs, kf, vf, enc, signs, L32, w.tier_top, w.tier_weight, candidates_per_call(w, w.n),
+                              w.top_k, w.softmax_scale, percentile_M=M)
                 done += 1
             if time.perf_counter() - t0 >= seconds:
                 break
@@ -136,7 +154,9 @@ def main():
 
     cap = w.n_capacity
     cfg = P.make_config(w.batch, w.n_kv_heads, w.n_q_heads, cap, w.n_candidates, w.top_k, w.softmax_scale,
-                        w.srht_seed, w.tier_top, w.tier_weight)
+                        w.srht_seed, w.tier_top, w.tier_weight,
+                        P.PK_TIERS_PERCENTILE if w.tier_mode == "percentile" else P.PK_TIERS_RANK,
+                        w.collision_permille, w.adaptive)
     ctx = P.Context(cfg)
     kv_dt = P.PK_BF16 if w.kv_dtype == "bf16" else P.PK_F32
     host_bufs = []
@@ -307,7 +327,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads, "n_q_heads": w.n_q_heads,
-                   "n": w.n, "n_candidates": w.n_candidates, "top_k": w.top_k, "kv_dtype": w.kv_dtype,
+                   "n": w.n, "n_candidates": candidates_per_call(w, w.n), "top_k": w.top_k, "kv_dtype": w.kv_dtype,
+                   "tiers": w.tier_mode, "adaptive_ratios": w.adaptive,
                    "kv_home": w.kv_home, "layers_rotated": layers, "query_pool": len(Qd),
                    "append_per_step": 1 if app else 0},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

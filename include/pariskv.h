@@ -14,7 +14,8 @@
  *   1. SRHT normalise-rotate of the query and sign-pattern centroid scoring in
  *      each 8-dim subspace (Slides Eqs. (5)-(6); README "2. Decode");
  *   2. tier-weighted collision votes S_i over every key's 16 centroid IDs
- *      (Slides Eq. (15), Sec. 4.2.2);
+ *      (Slides Eq. (15), Sec. 4.2.2), with centroid-rank tiers or the paper's
+ *      six percentile tiers, and optionally the README's adaptive ratios;
  *   3. the C keys with the largest S_i, ties to the lower key index, found by
  *      histogram + prefix scan instead of a sort (Slides Sec. 4.2.2);
  *   4. the 4-bit inner-product estimate of each candidate (Slides Eqs. (7)-(10));
@@ -90,7 +91,26 @@ typedef struct {
                                 head h / (n_q_heads / n_kv_heads); the ratio
                                 must be an integer in 1..PK_MAX_GROUP          */
   int64_t n_capacity;        /* max keys per unit, 1..2^31-1                   */
+  int32_t tier_mode;         /* PK_TIERS_RANK: the tier_top / tier_weight votes
+                                above.  PK_TIERS_PERCENTILE (Slides Sec. 4.2.2,
+                                Eq. (15)): in each block the keys are ordered by
+                                their centroid's score for the query and the
+                                first M = ceil(rho n) positions are split into
+                                six equal percentile tiers with bonuses 6..1; a
+                                centroid takes the tier of its first key's
+                                position (needs pk_summaries.counts)          */
+  int32_t collision_permille;/* percentile tiers: rho in 1/1000, 1..1000; unused
+                                with adaptive_ratios                          */
+  int32_t adaptive_ratios;   /* 1: the candidate ratio beta and the collision
+                                ratio rho follow the retrieval-zone length n
+                                (README "Parameters" table: n < 5K 0.5/0.5,
+                                < 10K 0.25/0.3, < 30K 0.2/0.25, else 0.1/0.2);
+                                C = ceil(beta n) must not exceed n_candidates,
+                                which then only sizes the scratch            */
 } pk_config;
+
+#define PK_TIERS_RANK 0
+#define PK_TIERS_PERCENTILE 1
 
 typedef struct pk_context pk_context;   /* opaque */
 
@@ -105,12 +125,18 @@ typedef struct pk_context pk_context;   /* opaque */
  *                                         per-subspace weights w_b (Slides
  *                                         Eq. (9))
  *   norms   f32 [units][n_capacity]       ||k|| of each key
+ *   counts  u32 [units][16][256]          keys per (subspace, centroid) among
+ *                                         the n valid keys; kept up to date by
+ *                                         pk_encode_keys / pk_append_keys when
+ *                                         non-NULL; needed by percentile tiers
+ *                                         (NULL allowed with rank tiers)
  * codes rows must be 16-byte aligned and records 128-byte aligned (true for
  * hipMalloc'd bases).  `n` is the number of valid keys per unit. */
 typedef struct {
   uint8_t* codes;
   uint8_t* records;
   float* norms;
+  uint32_t* counts;
   int64_t n;
   int64_t n_capacity;
 } pk_summaries;
@@ -157,9 +183,11 @@ typedef struct {
 /* Check every field of `cfg`; PK_OK or PK_ERR_INVALID_ARG / _UNSUPPORTED. */
 pk_status pk_validate_config(const pk_config* cfg);
 
-/* Bytes of each summary array for `cfg` (units * n_capacity rows). */
+/* Bytes of each summary array for `cfg` (units * n_capacity rows; counts:
+ * units * 16 * 256 words).  Any output may be NULL. */
 pk_status pk_summary_bytes(const pk_config* cfg, size_t* codes_bytes,
-                           size_t* records_bytes, size_t* norms_bytes);
+                           size_t* records_bytes, size_t* norms_bytes,
+                           size_t* counts_bytes);
 
 /* The constant tables a context uses, computed on the host:
  * signs[128]  +-1, sign j = +1 iff the top bit of the j-th 64-bit output of
@@ -181,7 +209,8 @@ void pk_destroy(pk_context* ctx);
 
 /* Encode keys [batch][n_kv_heads][n][128] (element strides `key_strides` =
  * {batch, head, token}; the last dimension is contiguous) into rows [0, n) of
- * every unit and set inout->n = n.  keys: device pointer, PK_F32 or PK_BF16. */
+ * every unit and set inout->n = n.  keys: device pointer, PK_F32 or PK_BF16.
+ * When inout->counts is non-NULL it is recounted over the n keys. */
 pk_status pk_encode_keys(pk_context* ctx, const void* keys, pk_dtype key_dtype,
                          const int64_t key_strides[3], int64_t n,
                          pk_summaries* inout, void* hip_stream);
@@ -189,7 +218,8 @@ pk_status pk_encode_keys(pk_context* ctx, const void* keys, pk_dtype key_dtype,
 /* Encode t new keys per unit ([batch][n_kv_heads][t][128], strides as above)
  * into rows [inout->n, inout->n + t) and advance inout->n by t.  New keys use
  * the same fixed analytic codebook, no retraining (Slides, frame "The codebook
- * is data-independent"). PK_ERR_CAPACITY if n + t > n_capacity. */
+ * is data-independent"); inout->counts (when non-NULL) gains their codes.
+ * PK_ERR_CAPACITY if n + t > n_capacity. */
 pk_status pk_append_keys(pk_context* ctx, const void* new_keys, pk_dtype key_dtype,
                          const int64_t key_strides[3], int64_t t,
                          pk_summaries* inout, void* hip_stream);

@@ -73,6 +73,17 @@ constexpr int64_t kTargetWG = 512, kMaxKPL = 64;
 // fill the chip, or few enough candidates per head (four per thread)
 constexpr int kFusedTopkHeads = 128;
 constexpr int kFusedTopkSlots = 4 * pk::RT_THREADS;
+// README "Parameters": candidate / collision ratio (per mille) by retrieval-zone length
+void adaptive_permille(int64_t zone, int* beta, int* rho) {
+  if (zone < 5000) { *beta = 500; *rho = 500; }
+  else if (zone < 10000) { *beta = 250; *rho = 300; }
+  else if (zone < 30000) { *beta = 200; *rho = 250; }
+  else { *beta = 100; *rho = 200; }
+}
+
+// ceil(permille / 1000 * n), exact
+int64_t ceil_permille(int permille, int64_t n) { return ((int64_t)permille * n + 999) / 1000; }
+
 int tile_size(int units, int64_t n) {
   const int64_t want = ((int64_t)units * n + kTargetWG * 256 - 1) / (kTargetWG * 256);
   const int64_t kpl = want < 1 ? 1 : (want > kMaxKPL ? kMaxKPL : want);
@@ -159,19 +170,25 @@ pk_status pk_validate_config(const pk_config* c) {
   if (c->head_dim != PK_HEAD_DIM || c->n_sub != PK_N_SUB || c->sub_dim != PK_SUB_DIM)
     return fail(nullptr, PK_ERR_UNSUPPORTED, "geometry must be head_dim 128, n_sub 16, sub_dim 8 (got %d, %d, %d)",
                 c->head_dim, c->n_sub, c->sub_dim);
-  if (c->n_tiers < 1 || c->n_tiers > 4)
-    return fail(nullptr, PK_ERR_INVALID_ARG, "n_tiers must be 1..4 (got %d)", c->n_tiers);
-  int maxw = 0;
-  for (int t = 0; t < c->n_tiers; ++t) {
-    const int top = c->tier_top[t], prev = t ? c->tier_top[t - 1] : 0;
-    if (top <= prev || top > 256)
-      return fail(nullptr, PK_ERR_INVALID_ARG, "tier_top must increase strictly within 1..256 (tier %d: %d)", t, top);
-    if (c->tier_weight[t] < 0 || c->tier_weight[t] > 255)
-      return fail(nullptr, PK_ERR_INVALID_ARG, "tier_weight[%d] = %d out of range", t, c->tier_weight[t]);
-    if (c->tier_weight[t] > maxw) maxw = c->tier_weight[t];
+  if (c->tier_mode != PK_TIERS_RANK && c->tier_mode != PK_TIERS_PERCENTILE)
+    return fail(nullptr, PK_ERR_INVALID_ARG, "tier_mode must be PK_TIERS_RANK or PK_TIERS_PERCENTILE (got %d)",
+                c->tier_mode);
+  if (c->tier_mode == PK_TIERS_RANK) {
+    if (c->n_tiers < 1 || c->n_tiers > 4)
+      return fail(nullptr, PK_ERR_INVALID_ARG, "n_tiers must be 1..4 (got %d)", c->n_tiers);
+    int maxw = 0;
+    for (int t = 0; t < c->n_tiers; ++t) {
+      const int top = c->tier_top[t], prev = t ? c->tier_top[t - 1] : 0;
+      if (top <= prev || top > 256)
+        return fail(nullptr, PK_ERR_INVALID_ARG, "tier_top must increase strictly within 1..256 (tier %d: %d)", t,
+                    top);
+      if (c->tier_weight[t] < 0 || c->tier_weight[t] > 255)
+        return fail(nullptr, PK_ERR_INVALID_ARG, "tier_weight[%d] = %d out of range", t, c->tier_weight[t]);
+      if (c->tier_weight[t] > maxw) maxw = c->tier_weight[t];
+    }
+    if (maxw * PK_N_SUB > 64)
+      return fail(nullptr, PK_ERR_UNSUPPORTED, "n_sub * max tier weight must be <= 64 (got %d)", maxw * PK_N_SUB);
   }
-  if (maxw * PK_N_SUB > 64)
-    return fail(nullptr, PK_ERR_UNSUPPORTED, "n_sub * max tier weight must be <= 64 (got %d)", maxw * PK_N_SUB);
   if (c->n_candidates < 1 || c->n_candidates > PK_MAX_CANDIDATES)
     return fail(nullptr, PK_ERR_INVALID_ARG, "n_candidates must be 1..%d (got %d)", PK_MAX_CANDIDATES, c->n_candidates);
   if (c->top_k < 1 || c->top_k > PK_MAX_TOPK || c->top_k > c->n_candidates)
@@ -190,16 +207,23 @@ pk_status pk_validate_config(const pk_config* c) {
     return fail(nullptr, PK_ERR_INVALID_ARG, "n_capacity must be 1..2^31-1 (got %lld)", (long long)c->n_capacity);
   if ((int64_t)c->batch * c->n_q_heads > 0x7FFFFFFFll / 2)
     return fail(nullptr, PK_ERR_INVALID_ARG, "too many heads");
+  if (c->adaptive_ratios != 0 && c->adaptive_ratios != 1)
+    return fail(nullptr, PK_ERR_INVALID_ARG, "adaptive_ratios must be 0 or 1 (got %d)", c->adaptive_ratios);
+  if (c->tier_mode == PK_TIERS_PERCENTILE && !c->adaptive_ratios &&
+      (c->collision_permille < 1 || c->collision_permille > 1000))
+    return fail(nullptr, PK_ERR_INVALID_ARG, "collision_permille must be 1..1000 (got %d)", c->collision_permille);
   return PK_OK;
 }
 
-pk_status pk_summary_bytes(const pk_config* cfg, size_t* codes, size_t* records, size_t* norms) {
+pk_status pk_summary_bytes(const pk_config* cfg, size_t* codes, size_t* records, size_t* norms, size_t* counts) {
   pk_status st = pk_validate_config(cfg);
   if (st != PK_OK) return st;
-  const size_t rows = (size_t)cfg->batch * cfg->n_kv_heads * (size_t)cfg->n_capacity;
+  const size_t units = (size_t)cfg->batch * cfg->n_kv_heads;
+  const size_t rows = units * (size_t)cfg->n_capacity;
   if (codes) *codes = rows * 16;
   if (records) *records = rows * PK_RECORD_BYTES;
   if (norms) *norms = rows * sizeof(float);
+  if (counts) *counts = units * 16 * 256 * sizeof(uint32_t);
   return PK_OK;
 }
 
@@ -256,7 +280,7 @@ pk_status pk_create(const pk_config* cfg, pk_context** out) {
       {(void**)&c->lut, U * 16 * 256 * 4},
       {(void**)&c->rq, Q * 128 * 4},
       {(void**)&c->scores, U * N * 4},
-      {(void**)&c->tile_hist, U * MS * pk::MAXG * pk::NBIN * 4},
+      {(void**)&c->tile_hist, U * MS * pk::MAXG * pk::NBIN_MAX * 4},
       {(void**)&c->params, U * pk::MAXG * sizeof(SelParams)},
       {(void**)&c->sub_base, U * MS * pk::MAXG * sizeof(int2)},
       {(void**)&c->cand_idx, Q * C * 4},
@@ -298,12 +322,19 @@ static pk_status encode_rows(pk_context* ctx, const void* keys, pk_dtype dt, con
   if (dt == PK_BF16)
     hipLaunchKernelGGL(pk::encode_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const uint16_t*)keys, st[0], st[1], st[2], ctx->cfg.n_kv_heads, t, total, row0,
-                       s->n_capacity, s->codes, s->records, s->norms, ctx->tb);
+                       s->n_capacity, s->codes, s->records, s->norms, s->counts, ctx->tb);
   else
     hipLaunchKernelGGL(pk::encode_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const float*)keys, st[0], st[1], st[2], ctx->cfg.n_kv_heads, t, total, row0,
-                       s->n_capacity, s->codes, s->records, s->norms, ctx->tb);
+                       s->n_capacity, s->codes, s->records, s->norms, s->counts, ctx->tb);
   return check_launch(ctx, "encode");
+}
+
+static pk_status fill_words(pk_context* ctx, uint32_t* p, uint32_t value, int64_t count, hipStream_t stream) {
+  if (count <= 0) return PK_OK;
+  hipLaunchKernelGGL(pk::fill_u32_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream, p, value,
+                     count);
+  return check_launch(ctx, "fill");
 }
 
 static pk_status check_summaries(pk_context* ctx, const pk_summaries* s) {
@@ -316,6 +347,9 @@ static pk_status check_summaries(pk_context* ctx, const pk_summaries* s) {
                 (long long)s->n_capacity, (long long)ctx->cfg.n_capacity);
   if (s->n < 0 || s->n > s->n_capacity)
     return fail(ctx, PK_ERR_INVALID_ARG, "summaries n (%lld) outside 0..n_capacity", (long long)s->n);
+  if (s->counts && !aligned(s->counts, 4)) return fail(ctx, PK_ERR_INVALID_ARG, "counts must be 4-byte aligned");
+  if (ctx->cfg.tier_mode == PK_TIERS_PERCENTILE && !s->counts)
+    return fail(ctx, PK_ERR_INVALID_ARG, "percentile tiers need the summaries' centroid counts");
   return PK_OK;
 }
 
@@ -329,6 +363,9 @@ pk_status pk_encode_keys(pk_context* ctx, const void* keys, pk_dtype dt, const i
   if (n > inout->n_capacity)
     return fail(ctx, PK_ERR_CAPACITY, "n (%lld) exceeds n_capacity (%lld)", (long long)n, (long long)inout->n_capacity);
   if (n > 0 && (st = check_strides(ctx, keys, dt, key_strides, "keys")) != PK_OK) return st;
+  if (inout->counts &&
+      (st = fill_words(ctx, inout->counts, 0u, (int64_t)ctx->units * 16 * 256, (hipStream_t)hip_stream)) != PK_OK)
+    return st;
   st = encode_rows(ctx, keys, dt, key_strides, n, 0, inout, (hipStream_t)hip_stream);
   if (st == PK_OK) inout->n = n;
   return st;
@@ -392,20 +429,36 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
   if (attended) *attended = false;
   const pk_config& cfg = ctx->cfg;
   const int64_t n = s->n;
-  const int k = cfg.top_k, C = cfg.n_candidates;
+  const int k = cfg.top_k, C_cap = cfg.n_candidates;
   if (n == 0) {
     const int64_t cnt = (int64_t)ctx->qheads * k;
     hipLaunchKernelGGL(pk::fill_empty_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream, topk_idx,
                        topk_est, cnt);
     if ((st = check_launch(ctx, "fill")) != PK_OK) return st;
     if (dbg && dbg->cand_idx) {
-      const int64_t cc = (int64_t)ctx->qheads * C;
+      const int64_t cc = (int64_t)ctx->qheads * C_cap;
       hipLaunchKernelGGL(pk::fill_empty_kernel, dim3((unsigned)((cc + 255) / 256)), dim3(256), 0, stream,
                          dbg->cand_idx, dbg->cand_est, cc);
       if ((st = check_launch(ctx, "fill")) != PK_OK) return st;
     }
     return PK_OK;
   }
+  // candidates C and, with percentile tiers, the kept positions M of this call
+  // (Slides Sec. 4.2.2: C = ceil(beta n); README "Parameters": adaptive ratios)
+  int64_t C64 = C_cap;
+  uint32_t keep_m = 0;
+  if (cfg.adaptive_ratios) {
+    int beta = 0, rho = 0;
+    adaptive_permille(n, &beta, &rho);
+    C64 = ceil_permille(beta, n);
+    if (cfg.tier_mode == PK_TIERS_PERCENTILE) keep_m = (uint32_t)ceil_permille(rho, n);
+  } else if (cfg.tier_mode == PK_TIERS_PERCENTILE) {
+    keep_m = (uint32_t)ceil_permille(cfg.collision_permille, n);
+  }
+  if (C64 > C_cap)
+    return fail(ctx, PK_ERR_CAPACITY, "adaptive candidate count %lld exceeds n_candidates %d", (long long)C64, C_cap);
+  const int C = (int)C64;
+  const bool pct = cfg.tier_mode == PK_TIERS_PERCENTILE;
   const int tile = tile_size(ctx->units, n);
   const int tiles = (int)((n + tile - 1) / tile);
   if (tiles > ctx->max_tiles)
@@ -418,32 +471,44 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
     if (q_dtype == PK_BF16)
       hipLaunchKernelGGL(pk::qprep_kernel<uint16_t>, dim3(ctx->qheads * pk::QP_PARTS), dim3(64 * pk::QP_WAVES), 0,
                          stream, (const uint16_t*)q, cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->rq,
-                         (uint8_t*)ctx->lut, ctx->tb, ctx->tiers);
+                         (uint8_t*)ctx->lut, ctx->tb, ctx->tiers, s->counts, keep_m);
     else
       hipLaunchKernelGGL(pk::qprep_kernel<float>, dim3(ctx->qheads * pk::QP_PARTS), dim3(64 * pk::QP_WAVES), 0,
                          stream, (const float*)q, cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->rq,
-                         (uint8_t*)ctx->lut, ctx->tb, ctx->tiers);
+                         (uint8_t*)ctx->lut, ctx->tb, ctx->tiers, s->counts, keep_m);
   }
   if ((st = check_launch(ctx, "qprep")) != PK_OK) return st;
   {
     Launch L(ctx, PK_KERNEL_COLLIDE, stream);
-#define PK_COLLIDE(GG)                                                                                      \
-  hipLaunchKernelGGL(pk::collide_kernel<GG>, dim3(grid), dim3(256), 0, stream, (const uint4*)s->codes, ctx->lut, \
-                     ctx->scores, ctx->tile_hist, n, s->n_capacity, tiles, (int)ctx->max_subs, tile)
-    switch (ctx->group) {
-      case 1: PK_COLLIDE(1); break;
-      case 2: PK_COLLIDE(2); break;
-      case 3: PK_COLLIDE(3); break;
-      default: PK_COLLIDE(4); break;
+#define PK_COLLIDE(GG, NB)                                                                                    \
+  hipLaunchKernelGGL((pk::collide_kernel<GG, NB>), dim3(grid), dim3(256), 0, stream, (const uint4*)s->codes,      \
+                     ctx->lut, ctx->scores, ctx->tile_hist, n, s->n_capacity, tiles, (int)ctx->max_subs, tile)
+#define PK_COLLIDE_G(NB)                   \
+  switch (ctx->group) {                    \
+    case 1: PK_COLLIDE(1, NB); break;      \
+    case 2: PK_COLLIDE(2, NB); break;      \
+    case 3: PK_COLLIDE(3, NB); break;      \
+    default: PK_COLLIDE(4, NB); break;     \
+  }
+    if (pct) {
+      PK_COLLIDE_G(pk::NBIN_MAX);
+    } else {
+      PK_COLLIDE_G(pk::NBIN);
     }
+#undef PK_COLLIDE_G
 #undef PK_COLLIDE
   }
   if ((st = check_launch(ctx, "collide")) != PK_OK) return st;
   {
     Launch L(ctx, PK_KERNEL_THRESHOLD, stream);
-    hipLaunchKernelGGL(pk::threshold_kernel, dim3(ctx->units * ctx->group), dim3(pk::TH_THREADS), 0, stream,
-                       ctx->tile_hist, ctx->params, ctx->sub_base, n, 4 * tiles, (int)ctx->max_subs, tile / 4,
-                       ctx->group, C);
+    if (pct)
+      hipLaunchKernelGGL(pk::threshold_kernel<pk::NBIN_MAX>, dim3(ctx->units * ctx->group), dim3(pk::TH_THREADS), 0,
+                         stream, ctx->tile_hist, ctx->params, ctx->sub_base, n, 4 * tiles, (int)ctx->max_subs,
+                         tile / 4, ctx->group, C);
+    else
+      hipLaunchKernelGGL(pk::threshold_kernel<pk::NBIN>, dim3(ctx->units * ctx->group), dim3(pk::TH_THREADS), 0,
+                         stream, ctx->tile_hist, ctx->params, ctx->sub_base, n, 4 * tiles, (int)ctx->max_subs,
+                         tile / 4, ctx->group, C);
   }
   if ((st = check_launch(ctx, "threshold")) != PK_OK) return st;
   {
@@ -525,10 +590,24 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
     if (dbg->scores)
       PK_HIP(ctx, hipMemcpy2DAsync(dbg->scores, (size_t)n * 4, ctx->scores, (size_t)s->n_capacity * 4, (size_t)n * 4,
                                    U, hipMemcpyDeviceToDevice, stream));
+    // candidate lists are [heads][C] inside, [heads][n_candidates] in the debug copies
+    if (C < C_cap && (dbg->cand_idx || dbg->cand_est)) {
+      const int64_t cc = (int64_t)Q * C_cap;
+      if (dbg->cand_idx) {
+        hipLaunchKernelGGL(pk::fill_empty_kernel, dim3((unsigned)((cc + 255) / 256)), dim3(256), 0, stream,
+                           dbg->cand_idx, dbg->cand_est, cc);
+      } else {
+        hipLaunchKernelGGL(pk::fill_empty_kernel, dim3((unsigned)((cc + 255) / 256)), dim3(256), 0, stream,
+                           (int32_t*)nullptr, dbg->cand_est, cc);
+      }
+      if ((st = check_launch(ctx, "fill")) != PK_OK) return st;
+    }
     if (dbg->cand_idx)
-      PK_HIP(ctx, hipMemcpyAsync(dbg->cand_idx, ctx->cand_idx, Q * C * 4, hipMemcpyDeviceToDevice, stream));
+      PK_HIP(ctx, hipMemcpy2DAsync(dbg->cand_idx, (size_t)C_cap * 4, ctx->cand_idx, (size_t)C * 4, (size_t)C * 4, Q,
+                                   hipMemcpyDeviceToDevice, stream));
     if (dbg->cand_est)
-      PK_HIP(ctx, hipMemcpyAsync(dbg->cand_est, ctx->cand_est, Q * C * 4, hipMemcpyDeviceToDevice, stream));
+      PK_HIP(ctx, hipMemcpy2DAsync(dbg->cand_est, (size_t)C_cap * 4, ctx->cand_est, (size_t)C * 4, (size_t)C * 4, Q,
+                                   hipMemcpyDeviceToDevice, stream));
   }
   return PK_OK;
 }

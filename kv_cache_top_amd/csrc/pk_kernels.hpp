@@ -24,7 +24,8 @@ constexpr int D = 128;       // head dimension
 constexpr int NSUB = 16;     // subspaces
 constexpr int SUBD = 8;      // coordinates per subspace
 constexpr int NLEV = 8;      // magnitude levels
-constexpr int NBIN = 64;     // collision-score bins 1..64 (0 is derived)
+constexpr int NBIN = 64;     // collision-score bins 1..64 with rank tiers (0 is derived)
+constexpr int NBIN_MAX = 128; // bins with percentile tiers (S <= 16 * 6 = 96)
 constexpr int MAXG = 4;      // query heads per KV head
 
 // Constant tables passed by value to every kernel that needs them.
@@ -106,7 +107,7 @@ __global__ void __launch_bounds__(256)
 encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
               int n_kv_heads, int64_t t, int64_t total, int64_t row0, int64_t n_cap,
               uint8_t* __restrict__ codes, uint8_t* __restrict__ records,
-              float* __restrict__ norms, Tables tb) {
+              float* __restrict__ norms, uint32_t* __restrict__ counts, Tables tb) {
   const int64_t key = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int b = threadIdx.x & 15;
   if (key >= total) return;                 // whole 16-lane groups leave together
@@ -193,6 +194,7 @@ encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
 
   const int64_t row = unit * n_cap + row0 + r;
   codes[row * 16 + b] = (uint8_t)code;
+  if (counts) atomicAdd(&counts[(unit * NSUB + b) * 256 + code], 1u);   // keys per (subspace, centroid)
   uint32_t* rec = reinterpret_cast<uint32_t*>(records + row * 128);
   rec[b] = nib;
   reinterpret_cast<float*>(rec)[16 + b] = w;
@@ -217,6 +219,107 @@ encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
 // themselves; each gets its tier weight, every other centroid 0.  The weight is
 // written as byte g (query head g of the unit) of the unit's LUT.
 // ===========================================================================
+// Rank tiers of one subspace (one wave, centroid c = lane + 64 r holds score
+// key key[r]): the centroids ranked r < tiers.top[last] by (score desc, c asc)
+// are found with a bitwise threshold search over the score keys, then ranked
+// among themselves; each gets its tier weight in lw[c].
+__device__ __forceinline__ void rank_tiers(const uint32_t (&key)[4], const TierSpec& tiers, uint2* sel, uint8_t* lw,
+                                           int lane) {
+  const int T = tiers.top[tiers.n_tiers - 1];
+  // threshold key: the T-th largest score key among the 256 centroids
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cnt += __popcll(__ballot(key[r] >= cand));
+    if (cnt >= T) thr = cand;
+  }
+  int n_gt = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) n_gt += __popcll(__ballot(key[r] > thr));
+  const int need_eq = T - n_gt;
+  // compact the T selected centroids (ties at thr: lowest centroid index first)
+  int eq_before = 0, sel_before = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t eqm = __ballot(key[r] == thr);
+    const int eqrank = eq_before + (int)mbcnt(eqm);
+    const bool sl = key[r] > thr || (key[r] == thr && eqrank < need_eq);
+    const uint64_t sm = __ballot(sl);
+    if (sl) sel[sel_before + (int)mbcnt(sm)] = make_uint2(key[r], lane + 64 * r);
+    eq_before += __popcll(eqm);
+    sel_before += __popcll(sm);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // rank of each selected centroid by (score desc, centroid asc); tier weight
+  for (int j = lane; j < T; j += 64) {
+    const uint2 e = sel[j];
+    int rank = 0;
+#pragma unroll 8
+    for (int j2 = 0; j2 < T; ++j2) {
+      const uint2 o = sel[j2];
+      rank += (o.x > e.x || (o.x == e.x && o.y < e.y)) ? 1 : 0;
+    }
+    uint32_t wgt = 0;
+    for (int tt = 0; tt < tiers.n_tiers; ++tt) {
+      if (rank < tiers.top[tt]) { wgt = (uint32_t)tiers.weight[tt]; break; }
+    }
+    lw[e.y] = (uint8_t)wgt;
+  }
+}
+
+// Percentile tiers of one subspace (Slides Sec. 4.2.2, Eq. (15)): the 256
+// centroids are sorted by (score desc, c asc) with a bitonic network over the
+// wave (position x = 4 lane + r), their key counts are prefix-summed in that
+// order, and a centroid whose first key sits at position P < keep_m gets the
+// bonus 6 - floor(6 P / keep_m) (tiers 0..5 -> 6..1) in lw[c].
+__device__ __forceinline__ void percentile_tiers(const uint32_t (&key)[4], const uint32_t* __restrict__ cnt_row,
+                                                 uint32_t keep_m, uint8_t* lw, int lane) {
+  uint64_t v[4];                                  // (score key, 255 - c): larger = earlier
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = ((uint64_t)key[r] << 8) | (uint64_t)(255u - (uint32_t)(lane + 64 * r));
+#pragma unroll
+  for (int k = 2; k <= 256; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      uint64_t pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[r] = (j >= 4) ? __shfl_xor(v[r], j >> 2, 64) : v[r ^ (j & 3)];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int x = 4 * lane + r;
+        const bool desc_block = (x & k) == 0;     // blocks sorted descending keep the max low
+        const bool lower = (x & j) == 0;
+        const uint64_t hi = v[r] > pv[r] ? v[r] : pv[r];
+        const uint64_t lo = v[r] > pv[r] ? pv[r] : v[r];
+        v[r] = (lower == desc_block) ? hi : lo;
+      }
+    }
+  }
+  uint32_t c[4], nk[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    c[r] = 255u - (uint32_t)(v[r] & 0xFFu);
+    nk[r] = cnt_row[c[r]];
+  }
+  const uint32_t tot = nk[0] + nk[1] + nk[2] + nk[3];
+  uint32_t incl = tot;                            // keys in this and lower lanes
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  uint32_t first = incl - tot;                    // keys in better-ranked centroids
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (first < keep_m) lw[c[r]] = (uint8_t)(6u - (uint32_t)(((uint64_t)first * 6u) / keep_m));
+    first += nk[r];
+  }
+}
+
 constexpr int QP_WAVES = 4;
 constexpr int QP_PARTS = NSUB / QP_WAVES;   // workgroups per query head
 
@@ -224,7 +327,7 @@ template <typename QT>
 __global__ void __launch_bounds__(64 * QP_WAVES)
 qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
              float* __restrict__ rot_q, uint8_t* __restrict__ lut_bytes, Tables tb,
-             TierSpec tiers) {
+             TierSpec tiers, const uint32_t* __restrict__ counts, uint32_t keep_m) {
   __shared__ float y[D];
   __shared__ uint2 sel[QP_WAVES][256];      // (score key, centroid) of the selected centroids
   __shared__ uint8_t lw[QP_WAVES][256];     // tier weight per centroid
@@ -283,48 +386,10 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
     lw[w][c] = 0;
   }
 
-  const int T = tiers.top[tiers.n_tiers - 1];
-  // threshold key: the T-th largest score key among the 256 centroids
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) cnt += __popcll(__ballot(key[r] >= cand));
-    if (cnt >= T) thr = cand;
-  }
-  int n_gt = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) n_gt += __popcll(__ballot(key[r] > thr));
-  const int need_eq = T - n_gt;
-  // compact the T selected centroids (ties at thr: lowest centroid index first)
-  int eq_before = 0, sel_before = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint64_t eqm = __ballot(key[r] == thr);
-    const int eqrank = eq_before + (int)mbcnt(eqm);
-    const bool sl = key[r] > thr || (key[r] == thr && eqrank < need_eq);
-    const uint64_t sm = __ballot(sl);
-    if (sl) sel[w][sel_before + (int)mbcnt(sm)] = make_uint2(key[r], lane + 64 * r);
-    eq_before += __popcll(eqm);
-    sel_before += __popcll(sm);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  // rank of each selected centroid by (score desc, centroid asc); tier weight
-  for (int j = lane; j < T; j += 64) {
-    const uint2 e = sel[w][j];
-    int rank = 0;
-#pragma unroll 8
-    for (int j2 = 0; j2 < T; ++j2) {
-      const uint2 o = sel[w][j2];
-      rank += (o.x > e.x || (o.x == e.x && o.y < e.y)) ? 1 : 0;
-    }
-    uint32_t wgt = 0;
-    for (int tt = 0; tt < tiers.n_tiers; ++tt) {
-      if (rank < tiers.top[tt]) { wgt = (uint32_t)tiers.weight[tt]; break; }
-    }
-    lw[w][e.y] = (uint8_t)wgt;
+  if (keep_m > 0) {
+    percentile_tiers(key, counts + ((int64_t)unit * NSUB + b) * 256, keep_m, lw[w], lane);
+  } else {
+    rank_tiers(key, tiers, sel[w], lw[w], lane);
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -334,6 +399,7 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
     lut_bytes[(((int64_t)unit * NSUB + b) * 256 + c) * 4 + g] = lw[w][c];
   }
 }
+
 
 // ===========================================================================
 // collide: tier-weighted collision votes (Slides Eq. (15), Sec. 4.2.2;
@@ -353,14 +419,14 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
 constexpr int COLLIDE_UNROLL = 8;
 constexpr int HIST_LANES = 32;
 
-template <int G>
+template <int G, int NB>   // NB: histogram bins 1..NB
 __global__ void __launch_bounds__(256)
 collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut,
                uint32_t* __restrict__ scores, uint32_t* __restrict__ tile_hist,
                int64_t n, int64_t n_cap, int tiles, int max_subs, int tile) {
   constexpr int group = G;
   __shared__ uint32_t s_lut[NSUB * 256];
-  __shared__ uint32_t s_hist[MAXG * NBIN * HIST_LANES];
+  __shared__ uint32_t s_hist[MAXG * NB * HIST_LANES];
 
   const int unit = blockIdx.x / tiles, tl = blockIdx.x - unit * tiles;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -386,12 +452,12 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
     uint4* dst = reinterpret_cast<uint4*>(s_lut);
     for (int i = tid; i < NSUB * 256 / 4; i += 256) dst[i] = src[i];
     uint4* h4 = reinterpret_cast<uint4*>(s_hist);
-    for (int i = tid; i < group * NBIN * HIST_LANES / 4; i += 256) h4[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < group * NB * HIST_LANES / 4; i += 256) h4[i] = make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 
   const uint32_t incr = 1u << (8 * wave);
-  // bin s of head g lives at word (g * NBIN + s - 1) * HIST_LANES + lane % HIST_LANES
+  // bin s of head g lives at word (g * NB + s - 1) * HIST_LANES + lane % HIST_LANES
   const uint32_t hbase = (uint32_t)(lane & (HIST_LANES - 1)) * 4u - HIST_LANES * 4u;
   for (int64_t base = w0; base < w1; base += 64 * COLLIDE_UNROLL) {
     uint4 nx[COLLIDE_UNROLL];
@@ -413,7 +479,7 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const uint32_t sc = (acc >> (8 * g)) & 0xFFu;
-          if (sc) atomicAdd(&s_hist[(g * NBIN * HIST_LANES * 4 + sc * HIST_LANES * 4 + hbase) >> 2], incr);
+          if (sc) atomicAdd(&s_hist[(g * NB * HIST_LANES * 4 + sc * HIST_LANES * 4 + hbase) >> 2], incr);
         }
       }
     }
@@ -424,9 +490,9 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
 
   // reduce to sub-tile histograms [unit][4 * tile + wave][g][bin - 1]; byte w of
   // a counter word belongs to wave w
-  if (tid < group * NBIN) {
-    const int g = tid / NBIN, bin = tid % NBIN;
-    const uint32_t* row = s_hist + (g * NBIN + bin) * HIST_LANES;
+  for (int gb = tid; gb < group * NB; gb += 256) {
+    const int g = gb / NB, bin = gb % NB;
+    const uint32_t* row = s_hist + (g * NB + bin) * HIST_LANES;
     uint32_t lo = 0, hi = 0;
     for (int i = 0; i < HIST_LANES; ++i) {
       const uint32_t v = row[(i + tid) & (HIST_LANES - 1)];
@@ -436,7 +502,7 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
     const uint32_t cnt[4] = {lo & 0xFFFFu, hi & 0xFFFFu, lo >> 16, hi >> 16};
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2)
-      tile_hist[(((int64_t)unit * max_subs + 4 * tl + w2) * MAXG + g) * NBIN + bin] = cnt[w2];
+      tile_hist[(((int64_t)unit * max_subs + 4 * tl + w2) * MAXG + g) * NB + bin] = cnt[w2];
   }
 }
 
@@ -454,72 +520,95 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
 // ===========================================================================
 constexpr int TH_THREADS = 256;
 
+template <int NB>   // histogram bins 1..NB, a multiple of 64
 __global__ void __launch_bounds__(TH_THREADS)
 threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__ params,
                  int2* __restrict__ sub_base, int64_t n, int subs, int max_subs, int sub_len, int group,
                  int n_candidates) {
-  __shared__ uint32_t s_t[TH_THREADS][NBIN + 1];   // [sub-tile in chunk][bin], padded
-  __shared__ uint32_t s_q[4][NBIN];
+  constexpr int NH = NB / 64;                      // 64-bin slices
+  __shared__ uint32_t s_t[TH_THREADS][64 + 1];     // [sub-tile in chunk][bin of a slice], padded
+  __shared__ uint32_t s_q[4][64];
   __shared__ int s_par[2];
   __shared__ int2 s_w[4];
   const int unit = blockIdx.x / group, g = blockIdx.x - unit * group;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t* uh = tile_hist + (int64_t)unit * max_subs * MAXG * NBIN;
+  const uint32_t* uh = tile_hist + (int64_t)unit * max_subs * MAXG * NB;
 
-  uint4 h4[NBIN / 4];
+  uint4 h4[NB / 4];
   auto load_chunk = [&](int base) {
     const int t = base + tid;
     const int tl = t < subs ? t : subs - 1;
-    const uint4* hrow = reinterpret_cast<const uint4*>(uh + ((int64_t)tl * MAXG + g) * NBIN);
+    const uint4* hrow = reinterpret_cast<const uint4*>(uh + ((int64_t)tl * MAXG + g) * NB);
 #pragma unroll
-    for (int q4 = 0; q4 < NBIN / 4; ++q4) h4[q4] = hrow[q4];
+    for (int q4 = 0; q4 < NB / 4; ++q4) h4[q4] = hrow[q4];
     if (t >= subs) {
 #pragma unroll
-      for (int q4 = 0; q4 < NBIN / 4; ++q4) h4[q4] = make_uint4(0u, 0u, 0u, 0u);
+      for (int q4 = 0; q4 < NB / 4; ++q4) h4[q4] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
 
-  // pass 1: bin totals (thread tid < 64 holds bin tid + 1)
-  uint32_t tot = 0;
+  // pass 1: bin totals (wave 0, lane l holds bin 64 h + l + 1 in tot[h])
+  uint32_t tot[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) tot[h] = 0;
   for (int base = 0; base < subs; base += TH_THREADS) {
     load_chunk(base);
 #pragma unroll
-    for (int q4 = 0; q4 < NBIN / 4; ++q4) {
-      s_t[tid][4 * q4 + 0] = h4[q4].x;
-      s_t[tid][4 * q4 + 1] = h4[q4].y;
-      s_t[tid][4 * q4 + 2] = h4[q4].z;
-      s_t[tid][4 * q4 + 3] = h4[q4].w;
-    }
-    __syncthreads();
-    uint32_t cs = 0;
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+      for (int q4 = 0; q4 < 16; ++q4) {
+        const uint4 v = h4[16 * h + q4];
+        s_t[tid][4 * q4 + 0] = v.x;
+        s_t[tid][4 * q4 + 1] = v.y;
+        s_t[tid][4 * q4 + 2] = v.z;
+        s_t[tid][4 * q4 + 3] = v.w;
+      }
+      __syncthreads();
+      uint32_t cs = 0;
 #pragma unroll 16
-    for (int r = 0; r < 64; ++r) cs += s_t[wave * 64 + r][lane];
-    s_q[wave][lane] = cs;
-    __syncthreads();
-    if (wave == 0) tot += s_q[0][lane] + s_q[1][lane] + s_q[2][lane] + s_q[3][lane];
-    __syncthreads();
+      for (int r = 0; r < 64; ++r) cs += s_t[wave * 64 + r][lane];
+      s_q[wave][lane] = cs;
+      __syncthreads();
+      if (wave == 0) tot[h] += s_q[0][lane] + s_q[1][lane] + s_q[2][lane] + s_q[3][lane];
+      __syncthreads();
+    }
   }
 
   if (wave == 0) {
-    // suffix sums over bins (lane l holds #{S >= l+1})
-    uint32_t suf = tot;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_down(suf, off, 64);
-      if (lane + off < 64) suf += o;
+    // suffix sums over bins: suf[h] at lane l = #{S >= 64 h + l + 1}
+    uint32_t suf[NH];
+    uint32_t above = 0;                             // keys in higher slices
+#pragma unroll
+    for (int h = NH - 1; h >= 0; --h) {
+      uint32_t x = tot[h];
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_down(x, off, 64);
+        if (lane + off < 64) x += o;
+      }
+      suf[h] = x + above;
+      above = __shfl(suf[h], 0, 64);
     }
-    const uint64_t ge = __ballot(suf >= (uint32_t)n_candidates);
-    int theta;
-    uint32_t n_gt;
-    if (ge) {
-      const int top = 63 - __builtin_clzll(ge);     // highest bin with suffix >= C
-      theta = top + 1;
-      n_gt = __shfl(suf, (top + 1) & 63, 64);
-      if (top == 63) n_gt = 0;
-    } else {
-      theta = 0;
-      n_gt = __shfl(suf, 0, 64);                    // every key with S >= 1
+    int theta = 0;
+    uint32_t n_gt = above;                          // every key with S >= 1
+    bool found = false;
+#pragma unroll
+    for (int h = NH - 1; h >= 0; --h) {
+      const uint64_t ge = __ballot(suf[h] >= (uint32_t)n_candidates);
+      if (!found && ge) {
+        const int top = 63 - __builtin_clzll(ge);   // highest bin of the slice with suffix >= C
+        theta = 64 * h + top + 1;
+        const uint32_t next_in_slice = __shfl(suf[h], (top + 1) & 63, 64);
+        const uint32_t next_slice = (h + 1 < NH) ? __shfl(suf[(h + 1) % NH], 0, 64) : 0u;
+        n_gt = (top == 63) ? next_slice : next_in_slice;
+        found = true;
+      }
     }
-    const uint32_t eq_tot = (theta > 0) ? __shfl(tot, theta - 1, 64) : (uint32_t)(n - n_gt);
+    uint32_t eq_tot = (uint32_t)(n - n_gt);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const uint32_t v = __shfl(tot[h], (theta - 1) & 63, 64);
+      if (theta > 0 && (theta - 1) / 64 == h) eq_tot = v;
+    }
     const uint32_t want = (uint32_t)n_candidates - n_gt;
     const uint32_t need_eq = want < eq_tot ? want : eq_tot;
     if (lane == 0) {
@@ -537,7 +626,7 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
     const int t = base + tid;
     int gt = 0, eq = 0, nz = 0;
 #pragma unroll
-    for (int q4 = 0; q4 < NBIN / 4; ++q4) {
+    for (int q4 = 0; q4 < NB / 4; ++q4) {
       const int c4[4] = {(int)h4[q4].x, (int)h4[q4].y, (int)h4[q4].z, (int)h4[q4].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1200,11 +1289,17 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
                      s_tk, tid);
 }
 
+// set `count` words to `value`
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t value, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) p[i] = value;
+}
+
 // fill top-k outputs for an empty key set
 __global__ void fill_empty_kernel(int32_t* __restrict__ idx, float* __restrict__ est, int64_t count) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) {
-    idx[i] = -1;
+    if (idx) idx[i] = -1;
     if (est) est[i] = -__builtin_inff();
   }
 }

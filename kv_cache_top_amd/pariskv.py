@@ -24,6 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 PK_OK, PK_ERR_INVALID_ARG, PK_ERR_UNSUPPORTED, PK_ERR_CAPACITY, PK_ERR_OUT_OF_MEMORY, PK_ERR_HIP = \
     0, -1, -2, -3, -4, -5
 PK_F32, PK_BF16 = 0, 1
+PK_TIERS_RANK, PK_TIERS_PERCENTILE = 0, 1
 KERNELS = ["encode", "qprep", "collide", "threshold", "select", "rerank", "topk", "attend", "rerank_topk"]
 PK_N_KERNELS = len(KERNELS)
 
@@ -36,12 +37,13 @@ class pk_config(ctypes.Structure):
         ("n_candidates", ctypes.c_int32), ("top_k", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
         ("n_capacity", ctypes.c_int64),
+        ("tier_mode", ctypes.c_int32), ("collision_permille", ctypes.c_int32), ("adaptive_ratios", ctypes.c_int32),
     ]
 
 
 class pk_summaries(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("records", ctypes.c_void_p), ("norms", ctypes.c_void_p),
-                ("n", ctypes.c_int64), ("n_capacity", ctypes.c_int64)]
+                ("counts", ctypes.c_void_p), ("n", ctypes.c_int64), ("n_capacity", ctypes.c_int64)]
 
 
 class pk_debug(ctypes.Structure):
@@ -58,7 +60,8 @@ _I64x3 = ctypes.c_int64 * 3
 _SIGS = {
     "pk_validate_config": ([ctypes.POINTER(pk_config)], ctypes.c_int),
     "pk_summary_bytes": ([ctypes.POINTER(pk_config), ctypes.POINTER(ctypes.c_size_t),
-                          ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+                          ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t),
+                          ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "pk_tables": ([ctypes.c_uint64, _P, _P, _P], ctypes.c_int),
     "pk_create": ([ctypes.POINTER(pk_config), ctypes.POINTER(_P)], ctypes.c_int),
     "pk_destroy": ([_P], None),
@@ -131,7 +134,8 @@ def _strides4(t):
 
 
 def make_config(batch, n_kv_heads, n_q_heads, n_capacity, n_candidates, top_k=100, softmax_scale=None,
-                srht_seed=0, tier_top=(1, 4, 16), tier_weight=(4, 2, 1)) -> pk_config:
+                srht_seed=0, tier_top=(1, 4, 16), tier_weight=(4, 2, 1), tier_mode=PK_TIERS_RANK,
+                collision_permille=0, adaptive_ratios=False) -> pk_config:
     c = pk_config()
     c.head_dim, c.n_sub, c.sub_dim = 128, 16, 8
     c.srht_seed = srht_seed
@@ -141,6 +145,7 @@ def make_config(batch, n_kv_heads, n_q_heads, n_capacity, n_candidates, top_k=10
     c.n_candidates, c.top_k = n_candidates, top_k
     c.softmax_scale = (1.0 / 128 ** 0.5) if softmax_scale is None else softmax_scale
     c.batch, c.n_kv_heads, c.n_q_heads, c.n_capacity = batch, n_kv_heads, n_q_heads, n_capacity
+    c.tier_mode, c.collision_permille, c.adaptive_ratios = tier_mode, collision_permille, int(bool(adaptive_ratios))
     return c
 
 
@@ -152,9 +157,10 @@ def pk_validate_config(cfg: pk_config) -> int:
 
 
 def pk_summary_bytes(cfg: pk_config):
-    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
-    _check(_lib.pk_summary_bytes(ctypes.byref(cfg), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
-    return a.value, b.value, c.value
+    a, b, c, d = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib.pk_summary_bytes(ctypes.byref(cfg), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                 ctypes.byref(d)))
+    return a.value, b.value, c.value, d.value
 
 
 def pk_tables(seed: int):
@@ -275,14 +281,15 @@ class Summaries:
 
     def __init__(self, cfg: pk_config, device="cuda"):
         import torch
-        cb, rb, nb = pk_summary_bytes(cfg)
+        cb, rb, nb, kb = pk_summary_bytes(cfg)
         units = cfg.batch * cfg.n_kv_heads
         self.codes = torch.empty(cb, dtype=torch.uint8, device=device)
         self.records = torch.empty(rb, dtype=torch.uint8, device=device)
         self.norms = torch.empty(nb // 4, dtype=torch.float32, device=device)
+        self.counts = torch.zeros(kb // 4, dtype=torch.int32, device=device)
         self.units, self.n_capacity = units, cfg.n_capacity
-        self.s = pk_summaries(self.codes.data_ptr(), self.records.data_ptr(), self.norms.data_ptr(), 0,
-                              cfg.n_capacity)
+        self.s = pk_summaries(self.codes.data_ptr(), self.records.data_ptr(), self.norms.data_ptr(),
+                              self.counts.data_ptr(), 0, cfg.n_capacity)
 
     @property
     def n(self) -> int:
@@ -297,12 +304,16 @@ class Summaries:
     def norms_view(self):
         return self.norms.view(self.units, self.n_capacity)
 
+    def counts_view(self):
+        return self.counts.view(self.units, 16, 256)
+
     def clone(self, cfg: pk_config) -> "Summaries":
         other = Summaries.__new__(Summaries)
         other.codes, other.records, other.norms = self.codes.clone(), self.records.clone(), self.norms.clone()
+        other.counts = self.counts.clone()
         other.units, other.n_capacity = self.units, self.n_capacity
         other.s = pk_summaries(other.codes.data_ptr(), other.records.data_ptr(), other.norms.data_ptr(),
-                               self.s.n, self.s.n_capacity)
+                               other.counts.data_ptr(), self.s.n, self.s.n_capacity)
         return other
 
 

@@ -57,7 +57,9 @@ class GpuRun:
         n = K.shape[2] if n is None else n
         cap = n + (append.shape[2] if append is not None else 0) if capacity is None else capacity
         self.cfg = P.make_config(w.batch, w.n_kv_heads, w.n_q_heads, max(cap, 1), w.n_candidates, w.top_k,
-                                 w.softmax_scale, w.srht_seed, w.tier_top, w.tier_weight)
+                                 w.softmax_scale, w.srht_seed, w.tier_top, w.tier_weight,
+                                 P.PK_TIERS_PERCENTILE if w.tier_mode == "percentile" else P.PK_TIERS_RANK,
+                                 w.collision_permille, w.adaptive)
         self.ctx = P.Context(self.cfg)
         self.sums = P.Summaries(self.cfg)
         self.host_bufs = []
@@ -178,7 +180,21 @@ def check_encode_unit(run: GpuRun, u: int, keys_f32: np.ndarray, enc=None, rows=
     wg = np.ascontiguousarray(rec[sl, 64:]).view(np.float32)
     np.testing.assert_array_equal(wg, enc["weights"][sl], err_msg=f"weights unit {u}")
     np.testing.assert_allclose(norms[sl], enc["norms"][sl], rtol=1e-6, err_msg=f"norms unit {u}")
+    counts = run.sums.counts_view()[u].cpu().numpy()
+    np.testing.assert_array_equal(counts, O.centroid_occupancy(enc["codes"][:n]), err_msg=f"centroid counts unit {u}")
     return enc
+
+
+def call_sizes(w: S.Workload, n: int):
+    """(C, M) of a retrieval over n keys: candidates, and kept positions per block
+    with percentile tiers (None with rank tiers)."""
+    if w.adaptive:
+        beta, rho = O.adaptive_ratios_permille(n)
+        C = O.ratio_count(beta, n)
+    else:
+        C, rho = w.n_candidates, w.collision_permille
+    M = O.ratio_count(rho, n) if w.tier_mode == "percentile" else None
+    return C, M
 
 
 def attention_ok(o_gpu: np.ndarray, o_ref: np.ndarray, rel: float = 2e-2) -> bool:
@@ -196,11 +212,12 @@ def check_retrieve_unit(run: GpuRun, b: int, h: int, keys_f32, values_f32, enc, 
     u = b * w.n_kv_heads + h
     n = run.n
     qs = S.as_f32(run.Q[b, h * G:(h + 1) * G])
+    C, M = call_sizes(w, n)
     res = O.decode_unit(qs, keys_f32, values_f32, enc, signs, L32_, w.tier_top, w.tier_weight,
-                        w.n_candidates, w.top_k, w.softmax_scale, n=n)
+                        C, w.top_k, w.softmax_scale, n=n, percentile_M=M)
     lut = run.lut[u].cpu().numpy().view(np.uint32) if run.debug else None
     sc = run.scores[u, :n].cpu().numpy().view(np.uint32) if run.debug else None
-    n_sel = min(n, w.n_candidates)
+    n_sel = min(n, C)
     for g in (range(G) if heads is None else heads):
         qh = h * G + g
         hid = b * w.n_q_heads + qh

@@ -108,12 +108,29 @@ def test_validate_tiers():
 
 def test_summary_bytes():
     cfg = good_config(batch=3, n_kv_heads=2, n_q_heads=4, n_capacity=1000)
-    c, r, n = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
-    assert P._lib.pk_summary_bytes(ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(r), ctypes.byref(n)) == 0
+    c, r, n, k = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert P._lib.pk_summary_bytes(ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(r), ctypes.byref(n),
+                                   ctypes.byref(k)) == 0
     rows = 3 * 2 * 1000
-    assert (c.value, r.value, n.value) == (16 * rows, 128 * rows, 4 * rows)
+    assert (c.value, r.value, n.value, k.value) == (16 * rows, 128 * rows, 4 * rows, 6 * 16 * 256 * 4)
     cfg.head_dim = 64
-    assert P._lib.pk_summary_bytes(ctypes.byref(cfg), None, None, None) == P.PK_ERR_UNSUPPORTED
+    assert P._lib.pk_summary_bytes(ctypes.byref(cfg), None, None, None, None) == P.PK_ERR_UNSUPPORTED
+
+
+def test_validate_tier_modes():
+    cfg = good_config(tier_mode=P.PK_TIERS_PERCENTILE, collision_permille=200)
+    cfg.tier_weight[0] = 200                       # rank-tier fields are not used with percentile tiers
+    assert status(cfg) == P.PK_OK
+    cfg.collision_permille = 0
+    assert status(cfg) == P.PK_ERR_INVALID_ARG
+    cfg.adaptive_ratios = 1                        # the ratio then comes from the zone-length table
+    assert status(cfg) == P.PK_OK
+    cfg.adaptive_ratios = 2
+    assert status(cfg) == P.PK_ERR_INVALID_ARG
+    cfg = good_config(tier_mode=7)
+    assert status(cfg) == P.PK_ERR_INVALID_ARG
+    cfg = good_config(tier_mode=P.PK_TIERS_PERCENTILE, collision_permille=1001)
+    assert status(cfg) == P.PK_ERR_INVALID_ARG
 
 
 def test_create_rejects_before_touching_a_device():

@@ -9,6 +9,8 @@ for bit, attention within 2e-2).
                host memory read through mapped device pointers
   drift128k    n = 131072 prefill + 1024 decode steps appending one key per KV
                head with a drifting mean; sampled steps checked, recall reported
+  batched128k_pct  batched128k with the pages' percentile tiers and adaptive
+               ratios (C = 13108)
 """
 import numpy as np
 import pytest
@@ -54,6 +56,11 @@ def test_full_llama32k():
 
 def test_full_batched128k():
     _run_full("batched128k", units=[0, 37, 63])
+
+
+def test_full_batched128k_percentile_adaptive():
+    """The pages' Stage I at full size: percentile tiers, C = ceil(0.1 n) = 13108."""
+    _run_full("batched128k_pct", units=[0, 63])
 
 
 def test_full_offload1m_mapped_host_kv():

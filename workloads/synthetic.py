@@ -61,6 +61,13 @@ class Workload:
     srht_seed: int = 0
     tier_top: tuple = (1, 4, 16)
     tier_weight: tuple = (4, 2, 1)
+    # vote tiers: "rank" (the tiers above) or "percentile" (six percentile tiers
+    # of the top collision_permille / 1000 keys per block); with adaptive the
+    # candidate and collision ratios follow the retrieval-zone length and
+    # n_candidates is the largest candidate count the run may need
+    tier_mode: str = "rank"
+    collision_permille: int = 0
+    adaptive: bool = False
     extra: dict = field(default_factory=dict, compare=False)
 
     @property
@@ -88,6 +95,9 @@ WORKLOADS = {
         Workload("batched128k", 3, 8, 8, 32, 131072, "bf16", 4096),
         Workload("offload1m", 4, 1, 8, 32, 1048576, "bf16", 8192, kv_home="host"),
         Workload("drift128k", 5, 1, 8, 32, 131072, "bf16", 4096, append_steps=1024),
+        # the pages' own Stage I: percentile tiers with adaptive ratios
+        # (at n = 131072: beta = 0.1 -> C = 13108, rho = 0.2)
+        Workload("batched128k_pct", 6, 8, 8, 32, 131072, "bf16", 13108, tier_mode="percentile", adaptive=True),
     ]
 }
 
