@@ -495,6 +495,28 @@ def sparse_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarra
     return p @ v
 
 
+def layout_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
+                     K_dense: np.ndarray, V_dense: np.ndarray, scale: float) -> np.ndarray:
+    """One softmax over the retrieved rows K[idx] and every dense row.
+
+    README "3. Attention": attention runs over the sink tokens, the local
+    tokens and the retrieved tokens; Slides, frame "The memory layout
+    amortizes updates and fetches Top-k" (Fig. 5, Sec. 4.2.1-4.2.3): sink and
+    recent local tokens (with the update buffer) stay on the GPU for dense
+    attention.  K_dense / V_dense hold those rows; fp64, padding indices < 0
+    skipped, zero output when nothing is attended."""
+    idx = np.asarray(idx)
+    idx = idx[idx >= 0]
+    k = np.concatenate([np.asarray(K, dtype=np.float64)[idx], np.asarray(K_dense, dtype=np.float64).reshape(-1, D)])
+    v = np.concatenate([np.asarray(V, dtype=np.float64)[idx], np.asarray(V_dense, dtype=np.float64).reshape(-1, D)])
+    if k.shape[0] == 0:
+        return np.zeros(D, dtype=np.float64)
+    s = scale * (k @ np.asarray(q, dtype=np.float64))
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    return p @ v
+
+
 def exact_topk(K: np.ndarray, q: np.ndarray, k: int) -> np.ndarray:
     """Exact Top-k of <k_i, q> over all keys (fp64), ties by ascending index."""
     s = np.asarray(K, dtype=np.float64) @ np.asarray(q, dtype=np.float64)

@@ -208,3 +208,31 @@ def test_pipeline_recall_on_planted_query():
     assert recall > 0.5
     # the planted keys dominate the true scores and are retrieved
     assert np.all(np.abs(r["est32"] - r["est64"]) <= 1e-5 * r["abs_scale"])
+
+
+def test_layout_attention_special_cases():
+    """Dense + retrieved attention: no dense rows is the sparse attention; no
+    retrieved rows is plain softmax attention (torch's CPU routine); the dense
+    rows' order does not matter; one dominant row returns its value."""
+    import torch
+    rng = np.random.default_rng(11)
+    K = rng.standard_normal((300, O.D)).astype(np.float32)
+    V = rng.standard_normal((300, O.D)).astype(np.float32)
+    Kd = rng.standard_normal((70, O.D)).astype(np.float32)
+    Vd = rng.standard_normal((70, O.D)).astype(np.float32)
+    q = rng.standard_normal(O.D).astype(np.float32)
+    idx = np.array([5, 17, -1, 250, 3])
+    scale = 1 / np.sqrt(O.D)
+    np.testing.assert_allclose(O.layout_attention(q, K, V, idx, Kd[:0], Vd[:0], scale),
+                               O.sparse_attention(q, K, V, idx, scale), rtol=1e-12, atol=1e-12)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q[None, None, None].astype(np.float64)), torch.from_numpy(Kd[None, None].astype(np.float64)),
+        torch.from_numpy(Vd[None, None].astype(np.float64)), scale=scale)[0, 0, 0].numpy()
+    np.testing.assert_allclose(O.layout_attention(q, K, V, np.array([-1]), Kd, Vd, scale), ref, rtol=1e-10, atol=1e-12)
+    perm = rng.permutation(70)
+    np.testing.assert_allclose(O.layout_attention(q, K, V, idx, Kd, Vd, scale),
+                               O.layout_attention(q, K, V, idx, Kd[perm], Vd[perm], scale), rtol=1e-12, atol=1e-12)
+    Kd2 = Kd.copy()
+    Kd2[7] = 100.0 * q                                 # dominates every other score
+    np.testing.assert_allclose(O.layout_attention(q, K, V, idx, Kd2, Vd, scale), Vd[7], atol=1e-9)
+    assert not O.layout_attention(q, K, V, np.array([-1]), Kd[:0], Vd[:0], scale).any()
