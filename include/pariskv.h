@@ -70,6 +70,7 @@ typedef enum { PK_F32 = 0, PK_BF16 = 1 } pk_dtype;
 #define PK_MAX_GROUP 4       /* query heads per KV head                        */
 #define PK_MAX_TOPK 256
 #define PK_MAX_CANDIDATES 16384
+#define PK_MAX_DENSE 8192      /* dense rows per head in pk_sparse_dense_attend */
 
 typedef struct {
   int32_t head_dim;          /* must be 128                                    */
@@ -170,7 +171,8 @@ typedef enum {
   PK_KERNEL_TOPK = 6,          /* final top-k after PK_KERNEL_RERANK */
   PK_KERNEL_ATTEND = 7,
   PK_KERNEL_RERANK_TOPK = 8,   /* rerank and final top-k in one workgroup per head (many heads) */
-  PK_N_KERNELS = 9
+  PK_KERNEL_DENSE_ATTEND = 9,  /* pk_sparse_dense_attend */
+  PK_N_KERNELS = 10
 } pk_kernel_id;
 
 typedef struct {
@@ -267,6 +269,27 @@ pk_status pk_retrieve_attend(pk_context* ctx, const void* q, pk_dtype q_dtype,
                              pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows,
                              int32_t* topk_idx, float* topk_est, void* out, pk_dtype out_dtype,
                              const pk_debug* dbg, void* hip_stream);
+
+/* Attention over the retrieved rows and a set of dense rows in one softmax
+ * (README "3. Attention": sink, local and retrieved tokens; Slides Fig. 5,
+ * Sec. 4.2.1-4.2.3: sink tokens and the recent local window with the update
+ * buffer stay on the GPU for dense attention while the older retrieval zone
+ * is searched through its summaries and read row by row).
+ * q, k, v, kv_strides, n_rows, topk_idx as for pk_sparse_attend (k / v hold
+ * the retrieval zone; indices are zone rows);
+ * dense_k, dense_v  [batch][n_kv_heads][n_dense][128] in kv_dtype with
+ *            element strides dense_strides = {batch, head, token}, last dim
+ *            contiguous, rows 16-byte aligned: every row is attended (their
+ *            order does not matter, so a ring buffer works);
+ * n_dense    0..PK_MAX_DENSE;
+ * out        device [batch][n_q_heads][128] in out_dtype; zeros when nothing
+ *            is attended.  fp32 scores, softmax and sums. */
+pk_status pk_sparse_dense_attend(pk_context* ctx, const void* q, pk_dtype q_dtype,
+                                 const void* k, const void* v, pk_dtype kv_dtype,
+                                 const int64_t kv_strides[3], int64_t n_rows,
+                                 const int32_t* topk_idx, const void* dense_k, const void* dense_v,
+                                 const int64_t dense_strides[3], int64_t n_dense,
+                                 void* out, pk_dtype out_dtype, void* hip_stream);
 
 /* ---- host-resident KV tier (README "Key Insight": UVA fetch) -------------- */
 

@@ -674,6 +674,54 @@ pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, con
                      (hipStream_t)hip_stream);
 }
 
+pk_status pk_sparse_dense_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, const void* k, const void* v,
+                                 pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows,
+                                 const int32_t* topk_idx, const void* dense_k, const void* dense_v,
+                                 const int64_t dense_strides[3], int64_t n_dense, void* out, pk_dtype out_dtype,
+                                 void* hip_stream) {
+  pk_status st = check_attend_args(ctx, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype);
+  if (st != PK_OK) return st;
+  if (n_dense < 0 || n_dense > PK_MAX_DENSE)
+    return fail(ctx, PK_ERR_INVALID_ARG, "n_dense must be 0..%d (got %lld)", PK_MAX_DENSE, (long long)n_dense);
+  if (n_dense > 0) {
+    if ((st = check_strides(ctx, dense_k, kv_dtype, dense_strides, "dense_k")) != PK_OK) return st;
+    if ((st = check_strides(ctx, dense_v, kv_dtype, dense_strides, "dense_v")) != PK_OK) return st;
+  }
+  hipStream_t stream = (hipStream_t)hip_stream;
+  const pk_config& c = ctx->cfg;
+  const int kk = c.top_k;
+  const pk::AttendArgs a{q, k, v, kv_strides[0], kv_strides[1], kv_strides[2], n_rows, c.softmax_scale, out};
+  const int64_t ds[3] = {n_dense > 0 ? dense_strides[0] : 0, n_dense > 0 ? dense_strides[1] : 0,
+                         n_dense > 0 ? dense_strides[2] : 0};
+  Launch L(ctx, PK_KERNEL_DENSE_ATTEND, stream);
+#define PK_DA(KT, QT, OT)                                                                                      \
+  hipLaunchKernelGGL((pk::dense_sparse_attend_kernel<KT, QT, OT>), dim3(ctx->qheads), dim3(pk::DA_THREADS), 0,  \
+                     stream, a, topk_idx, kk, (const KT*)dense_k, (const KT*)dense_v, ds[0], ds[1], ds[2],          \
+                     (int)n_dense, c.n_q_heads, c.n_kv_heads, ctx->group)
+#define PK_DA_O(KT, QT)                 \
+  do {                                  \
+    if (out_dtype == PK_BF16)           \
+      PK_DA(KT, QT, uint16_t);          \
+    else                                \
+      PK_DA(KT, QT, float);             \
+  } while (0)
+#define PK_DA_Q(KT)                     \
+  do {                                  \
+    if (q_dtype == PK_BF16)             \
+      PK_DA_O(KT, uint16_t);            \
+    else                                \
+      PK_DA_O(KT, float);               \
+  } while (0)
+  if (kv_dtype == PK_BF16)
+    PK_DA_Q(uint16_t);
+  else
+    PK_DA_Q(float);
+#undef PK_DA_Q
+#undef PK_DA_O
+#undef PK_DA
+  return check_launch(ctx, "dense_attend");
+}
+
 pk_status pk_retrieve_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s,
                              const void* k, const void* v, pk_dtype kv_dtype, const int64_t kv_strides[3],
                              int64_t n_rows, int32_t* topk_idx, float* topk_est, void* out, pk_dtype out_dtype,

@@ -17,6 +17,7 @@
 
 #define PK_SORT_N 256          // top-k sort slots (k <= 256)
 #define PK_MAX_TOPK_ATT 256    // rows per attention head (k <= 256)
+#define PK_MAX_DENSE 8192      // dense rows per head in dense + retrieved attention
 
 namespace pk {
 
@@ -1287,6 +1288,150 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
   for (int r = 0; r < R; ++r) key[r] = orderable(ev[r]);
   topk_block<R, 256>(key, n_sel, k, ci, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
                      s_tk, tid);
+}
+
+// ===========================================================================
+// attention over the retrieved rows and the dense rows together (README
+// "3. Attention": sink, local and retrieved tokens; Slides Fig. 5,
+// Sec. 4.2.1-4.2.3: sink and recent local tokens, with the update buffer,
+// stay on the GPU for dense attention).
+//
+// One workgroup per query head.  Thread t scores rows t, t+256, ... of the
+// concatenation (k retrieved rows, then n_dense dense rows) against the query
+// in LDS; one max and one sum over all scores; then thread t accumulates
+// dimension t % 128 over half of the rows and the halves are added.  fp32.
+// ===========================================================================
+constexpr int DA_THREADS = 256;
+
+template <typename KT>
+__device__ __forceinline__ float dot_row(const KT* __restrict__ row, const float* s_q) {
+  float acc = 0.0f;
+  if constexpr (sizeof(KT) == 2) {
+    const uint4* r4 = reinterpret_cast<const uint4*>(row);
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      const uint4 v = r4[c];
+      const float* qq = s_q + 8 * c;
+      acc = __builtin_fmaf(bf16_lo(v.x), qq[0], acc);
+      acc = __builtin_fmaf(bf16_hi(v.x), qq[1], acc);
+      acc = __builtin_fmaf(bf16_lo(v.y), qq[2], acc);
+      acc = __builtin_fmaf(bf16_hi(v.y), qq[3], acc);
+      acc = __builtin_fmaf(bf16_lo(v.z), qq[4], acc);
+      acc = __builtin_fmaf(bf16_hi(v.z), qq[5], acc);
+      acc = __builtin_fmaf(bf16_lo(v.w), qq[6], acc);
+      acc = __builtin_fmaf(bf16_hi(v.w), qq[7], acc);
+    }
+  } else {
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) {
+      const float4 v = r4[c];
+      const float* qq = s_q + 4 * c;
+      acc = __builtin_fmaf(v.x, qq[0], acc);
+      acc = __builtin_fmaf(v.y, qq[1], acc);
+      acc = __builtin_fmaf(v.z, qq[2], acc);
+      acc = __builtin_fmaf(v.w, qq[3], acc);
+    }
+  }
+  return acc;
+}
+
+template <typename KT>
+__device__ __forceinline__ float elem(const KT* __restrict__ row, int d) {
+  if constexpr (sizeof(KT) == 2) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[d] << 16);
+  else return row[d];
+}
+
+template <typename KT, typename QT, typename OT>
+__global__ void __launch_bounds__(DA_THREADS)
+dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k, const KT* __restrict__ dk,
+                           const KT* __restrict__ dv, int64_t dsb, int64_t dsh, int64_t dst, int n_dense,
+                           int n_q_heads, int n_kv_heads, int group) {
+  __shared__ float s_q[D];
+  __shared__ float s_p[PK_MAX_TOPK_ATT + PK_MAX_DENSE];   // scores, then probabilities
+  __shared__ int32_t s_ix[PK_MAX_TOPK_ATT];                // retrieved rows (-1: skipped)
+  __shared__ float s_red[DA_THREADS / 64];
+  __shared__ float s_half[D];
+
+  const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seq = head / n_q_heads, qh = head - seq * n_q_heads, kvh = qh / group;
+  const KT* kb = reinterpret_cast<const KT*>(a.k) + seq * a.sb + kvh * a.sh;
+  const KT* vb = reinterpret_cast<const KT*>(a.v) + seq * a.sb + kvh * a.sh;
+  const KT* dkb = dk + seq * dsb + kvh * dsh;
+  const KT* dvb = dv + seq * dsb + kvh * dsh;
+  if (tid < D) {
+    if constexpr (sizeof(QT) == 2)
+      s_q[tid] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a.q)[(int64_t)head * D + tid] << 16);
+    else
+      s_q[tid] = reinterpret_cast<const float*>(a.q)[(int64_t)head * D + tid];
+  }
+  for (int r = tid; r < k; r += DA_THREADS) {
+    const int v = idx[(int64_t)head * k + r];
+    s_ix[r] = (v >= 0 && (int64_t)v < a.n_rows) ? v : -1;
+  }
+  __syncthreads();
+  const int total = k + n_dense;
+
+  // scores (invalid retrieved rows: -inf)
+  float m = -__builtin_inff();
+  for (int r = tid; r < total; r += DA_THREADS) {
+    float sc;
+    if (r < k) {
+      const int ix = s_ix[r];
+      sc = ix >= 0 ? dot_row(kb + (int64_t)ix * a.st, s_q) * a.scale : -__builtin_inff();
+    } else {
+      sc = dot_row(dkb + (int64_t)(r - k) * dst, s_q) * a.scale;
+    }
+    s_p[r] = sc;
+    m = fmaxf(m, sc);
+  }
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = s_red[0];
+#pragma unroll
+  for (int w2 = 1; w2 < DA_THREADS / 64; ++w2) m = fmaxf(m, s_red[w2]);
+  __syncthreads();
+  float ssum = 0.0f;
+  for (int r = tid; r < total; r += DA_THREADS) {
+    const float sc = s_p[r];
+    const float p = (sc == -__builtin_inff()) ? 0.0f : __expf(sc - m);
+    s_p[r] = p;
+    ssum += p;
+  }
+  for (int off = 32; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, 64);
+  if (lane == 0) s_red[wave] = ssum;
+  __syncthreads();
+  ssum = 0.0f;
+#pragma unroll
+  for (int w2 = 0; w2 < DA_THREADS / 64; ++w2) ssum += s_red[w2];
+
+  // weighted sum of the value rows: dimension tid % 128, rows of parity tid / 128
+  const int d = tid & (D - 1), half = tid >> 7;
+  float o = 0.0f;
+#pragma unroll 4
+  for (int r = half; r < total; r += 2) {
+    const float p = s_p[r];
+    const KT* vrow;
+    if (r < k) {
+      const int ix = s_ix[r];
+      vrow = vb + (int64_t)(ix >= 0 ? ix : 0) * a.st;
+    } else {
+      vrow = dvb + (int64_t)(r - k) * dst;
+    }
+    o = __builtin_fmaf(p, elem(vrow, d), o);
+  }
+  if (half == 1) s_half[d] = o;
+  __syncthreads();
+  if (half == 0) {
+    const float acc = o + s_half[d];
+    const float res = (ssum > 0.0f) ? acc / ssum : 0.0f;
+    if constexpr (sizeof(OT) == 2) {
+      reinterpret_cast<uint16_t*>(a.out)[(int64_t)head * D + d] = (uint16_t)f32_to_bf16_rne(res);
+    } else {
+      reinterpret_cast<float*>(a.out)[(int64_t)head * D + d] = res;
+    }
+  }
 }
 
 // set `count` words to `value`

@@ -10,6 +10,11 @@ from __future__ import annotations
 import ctypes
 import os
 
+# PyTorch first: its HIP runtime must be the one in the process before the
+# library's own dependency on libamdhip64 is resolved, or torch later finds
+# the device taken by a second runtime.
+import torch  # noqa: F401
+
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpariskv.so")
 
@@ -25,7 +30,8 @@ PK_OK, PK_ERR_INVALID_ARG, PK_ERR_UNSUPPORTED, PK_ERR_CAPACITY, PK_ERR_OUT_OF_ME
     0, -1, -2, -3, -4, -5
 PK_F32, PK_BF16 = 0, 1
 PK_TIERS_RANK, PK_TIERS_PERCENTILE = 0, 1
-KERNELS = ["encode", "qprep", "collide", "threshold", "select", "rerank", "topk", "attend", "rerank_topk"]
+KERNELS = ["encode", "qprep", "collide", "threshold", "select", "rerank", "topk", "attend", "rerank_topk",
+           "dense_attend"]
 PK_N_KERNELS = len(KERNELS)
 
 
@@ -76,6 +82,8 @@ _SIGS = {
                          ctypes.c_int),
     "pk_retrieve_attend": ([_P, _P, ctypes.c_int, ctypes.POINTER(pk_summaries), _P, _P, ctypes.c_int, _I64x3,
                             ctypes.c_int64, _P, _P, _P, ctypes.c_int, ctypes.POINTER(pk_debug), _P], ctypes.c_int),
+    "pk_sparse_dense_attend": ([_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _I64x3, ctypes.c_int64, _P, _P, _P,
+                                _I64x3, ctypes.c_int64, _P, ctypes.c_int, _P], ctypes.c_int),
     "pk_host_alloc_mapped": ([ctypes.c_size_t, ctypes.POINTER(_P), ctypes.POINTER(_P)], ctypes.c_int),
     "pk_host_free": ([_P], ctypes.c_int),
     "pk_calibration_copy": ([_P, _P, ctypes.c_size_t, _P], ctypes.c_int),
@@ -235,6 +243,20 @@ def pk_retrieve_attend_raw(ctx, q, sums: pk_summaries, k_ptr: int, v_ptr: int, k
                                    ctypes.c_void_p(v_ptr), kv_dtype, _I64x3(*kv_strides), n_rows, _ptr(topk_idx),
                                    _ptr(topk_est), _ptr(out), _dtype(out),
                                    ctypes.byref(debug) if debug is not None else None, _stream(stream)), ctx)
+
+
+def pk_sparse_dense_attend(ctx, q, k, v, topk_idx, dense_k, dense_v, out, stream=None):
+    """Attention over the retrieved rows of k / v and every row of dense_k / dense_v."""
+    if k.stride() != v.stride() or k.dtype != v.dtype or dense_k.stride() != dense_v.stride():
+        raise ValueError("K and V must share dtype and strides")
+    if dense_k.dtype != k.dtype or dense_v.dtype != k.dtype:
+        raise ValueError("dense rows must have the dtype of K / V")
+    if not q.is_contiguous() or not out.is_contiguous():
+        raise ValueError("q and out must be contiguous")
+    _check(_lib.pk_sparse_dense_attend(ctx, _ptr(q), _dtype(q), _ptr(k), _ptr(v), _dtype(k), _strides4(k),
+                                       k.shape[2], _ptr(topk_idx), _ptr(dense_k), _ptr(dense_v),
+                                       _strides4(dense_k), dense_k.shape[2], _ptr(out), _dtype(out),
+                                       _stream(stream)), ctx)
 
 
 def pk_host_alloc_mapped(nbytes: int):
