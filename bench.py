@@ -143,6 +143,8 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     w = S.WORKLOADS[args.workload]
+    if w.sink_tokens or w.local_tokens:
+        return run_layout(args, w)
     torch.cuda.set_device(0)
     dev = torch.device("cuda")
     t0 = time.time()
@@ -348,6 +350,126 @@ def main():
     ctx.close()
     for h in host_bufs:
         P.pk_host_free(h)
+
+
+def run_layout(args, w):
+    """Decode stream with the pages' memory layout (README "Parameters": sink,
+    local window, update interval; Slides Fig. 5): per step the new token joins
+    the dense window, the zone is retrieved from and one softmax covers the
+    retrieved rows and the dense rows; every update_tokens steps the oldest
+    update_tokens of the window are encoded into the zone."""
+    import torch
+
+    from kv_cache_top_amd import pariskv as P
+    from workloads import synthetic as S
+    dev = torch.device("cuda")
+    torch.cuda.set_device(0)
+
+    def to_torch(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    sink, local, upd = w.sink_tokens, w.local_tokens, w.update_tokens
+    total_steps = args.warmup + 2 * args.steps
+    if local + total_steps > w.append_steps:
+        raise SystemExit(f"{w.name} holds {w.append_steps} stream tokens; local + warmup + 2*steps = "
+                         f"{local + total_steps}")
+    log(f"[bench] generating {w.name}: prefill {w.n}, sink {sink}, local {local}, update {upd}")
+    K = S.all_keys(w)
+    V = S.all_values(w)
+    Q_pool = [S.all_queries(w, K, step=s_) for s_ in range(args.queries)]
+    ak = np.stack([np.stack([np.stack([S.appended_key(w, b, h, t) for t in range(w.append_steps)])
+                             for h in range(w.n_kv_heads)]) for b in range(w.batch)])
+    av = np.stack([np.stack([np.stack([S.appended_value(w, b, h, t) for t in range(w.append_steps)])
+                             for h in range(w.n_kv_heads)]) for b in range(w.batch)])
+    zone0 = w.n - sink
+    cap = zone0 + w.append_steps
+    # zone K/V: prefill rows [sink, n) then every stream token in order
+    Kz = torch.empty((w.batch, w.n_kv_heads, cap, 128), dtype=torch.bfloat16, device=dev)
+    Vz = torch.empty_like(Kz)
+    Kz[:, :, :zone0] = to_torch(K[:, :, sink:])
+    Vz[:, :, :zone0] = to_torch(V[:, :, sink:])
+    Kz[:, :, zone0:] = to_torch(ak)
+    Vz[:, :, zone0:] = to_torch(av)
+    # dense rows: the sink, then the window (oldest first)
+    nd_max = sink + local + upd
+    Kd = torch.empty((w.batch, w.n_kv_heads, nd_max, 128), dtype=torch.bfloat16, device=dev)
+    Vd = torch.empty_like(Kd)
+    Kd[:, :, :sink] = to_torch(K[:, :, :sink])
+    Vd[:, :, :sink] = to_torch(V[:, :, :sink])
+    Kd[:, :, sink:sink + local] = Kz[:, :, zone0:zone0 + local]
+    Vd[:, :, sink:sink + local] = Vz[:, :, zone0:zone0 + local]
+    cfg = P.make_config(w.batch, w.n_kv_heads, w.n_q_heads, cap, w.n_candidates, w.top_k, w.softmax_scale,
+                        w.srht_seed, w.tier_top, w.tier_weight)
+    ctx = P.Context(cfg)
+    sums = P.Summaries(cfg)
+    P.pk_encode_keys(ctx.h, Kz[:, :, :zone0], sums.s)
+    torch.cuda.synchronize()
+    Qd = [to_torch(q) for q in Q_pool]
+    idx = torch.empty((w.batch, w.n_q_heads, w.top_k), dtype=torch.int32, device=dev)
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    state = {"window": local, "next": local}          # tokens in the window; next stream token
+
+    def step(i):
+        s_ = state
+        j = s_["next"]
+        slot = sink + s_["window"]
+        Kd[:, :, slot] = Kz[:, :, zone0 + j]           # the new token joins the dense window
+        Vd[:, :, slot] = Vz[:, :, zone0 + j]
+        s_["window"] += 1
+        s_["next"] += 1
+        q = Qd[i % len(Qd)]
+        P.pk_retrieve(ctx.h, q, sums.s, idx, None, None, stream)
+        P.pk_sparse_dense_attend(ctx.h, q, Kz, Vz, idx, Kd[:, :, :sink + s_["window"]],
+                                 Vd[:, :, :sink + s_["window"]], out, stream)
+        if s_["window"] == local + upd:                # full update buffer: oldest upd tokens join the zone
+            P.pk_append_keys(ctx.h, Kz[:, :, sums.n:sums.n + upd], sums.s, stream)
+            Kd[:, :, sink:sink + local] = Kd[:, :, sink + upd:sink + upd + local].clone()
+            Vd[:, :, sink:sink + local] = Vd[:, :, sink + upd:sink + upd + local].clone()
+            s_["window"] = local
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t1
+    ms = 1e3 * el / args.steps
+    log(f"[bench] {args.steps} steps in {el * 1e3:.1f} ms: {ms * 1e3:.1f} us/step")
+    P.pk_timing_begin(ctx.h, args.steps)
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
+    torch.cuda.synchronize()
+    tim = P.pk_timing_end(ctx.h)
+    kern = {k: {"launches": c, "avg_us": (1e3 * t / c if c else None)} for k, (c, t) in tim.items()}
+    log("[bench] per-kernel: " + json.dumps(kern))
+    n_zone = sums.n
+    dense_rows = sink + local + upd // 2              # average over an update cycle
+    kv_row = 256
+    rec = RECORD_BYTES * min(n_zone, w.n_candidates) * w.batch * w.n_q_heads
+    nb = {"collide": CODE_BYTES * n_zone * w.units, "rerank": rec, "rerank_topk": rec,
+          "dense_attend": 2 * kv_row * (w.top_k + dense_rows) * w.batch * w.n_q_heads}
+    timed = {k: v for k, v in kern.items() if v["avg_us"]}
+    dom = max(timed, key=lambda k: timed[k]["avg_us"])
+    alg = nb.get(dom, 0)
+    achieved = alg / (kern[dom]["avg_us"] * 1e-6) / 1e9
+    res = {
+        "metric": METRIC, "value": round(1e3 / ms, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads, "n_q_heads": w.n_q_heads,
+                   "prefill": w.n, "zone_keys_end": int(n_zone), "sink": sink, "local": local, "update": upd,
+                   "n_candidates": w.n_candidates, "top_k": w.top_k, "kv_dtype": w.kv_dtype},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": alg, "avg_launch_us": round(kern[dom]["avg_us"], 3)},
+        "kernels": kern,
+    }
+    print(json.dumps(res), flush=True)
+    ctx.close()
 
 
 if __name__ == "__main__":

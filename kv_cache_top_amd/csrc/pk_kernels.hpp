@@ -1296,50 +1296,28 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
 // Sec. 4.2.1-4.2.3: sink and recent local tokens, with the update buffer,
 // stay on the GPU for dense attention).
 //
-// One workgroup per query head.  Thread t scores rows t, t+256, ... of the
-// concatenation (k retrieved rows, then n_dense dense rows) against the query
-// in LDS; one max and one sum over all scores; then thread t accumulates
-// dimension t % 128 over half of the rows and the halves are added.  fp32.
+// One workgroup per query head.  Sixteen threads share a row, each holding 8
+// of its 128 dimensions (one 16-byte load of bf16, two of fp32), so a
+// workgroup covers DA_THREADS / 16 rows per pass with coalesced loads.  Rows
+// are the k retrieved rows, then the n_dense dense rows.  Scores: partial dot
+// products reduced over the 16 threads; one max and one sum over all scores;
+// then each thread accumulates its 8 dimensions over its rows and the row
+// groups are added in LDS.  fp32.
 // ===========================================================================
-constexpr int DA_THREADS = 256;
+constexpr int DA_THREADS = 1024;
+constexpr int DA_GROUPS = DA_THREADS / 16;     // rows per pass
 
 template <typename KT>
-__device__ __forceinline__ float dot_row(const KT* __restrict__ row, const float* s_q) {
-  float acc = 0.0f;
+__device__ __forceinline__ void load8(const KT* __restrict__ row, int part, float (&x)[8]) {
   if constexpr (sizeof(KT) == 2) {
-    const uint4* r4 = reinterpret_cast<const uint4*>(row);
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      const uint4 v = r4[c];
-      const float* qq = s_q + 8 * c;
-      acc = __builtin_fmaf(bf16_lo(v.x), qq[0], acc);
-      acc = __builtin_fmaf(bf16_hi(v.x), qq[1], acc);
-      acc = __builtin_fmaf(bf16_lo(v.y), qq[2], acc);
-      acc = __builtin_fmaf(bf16_hi(v.y), qq[3], acc);
-      acc = __builtin_fmaf(bf16_lo(v.z), qq[4], acc);
-      acc = __builtin_fmaf(bf16_hi(v.z), qq[5], acc);
-      acc = __builtin_fmaf(bf16_lo(v.w), qq[6], acc);
-      acc = __builtin_fmaf(bf16_hi(v.w), qq[7], acc);
-    }
+    const uint4 v = reinterpret_cast<const uint4*>(row)[part];
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
   } else {
-    const float4* r4 = reinterpret_cast<const float4*>(row);
-#pragma unroll
-    for (int c = 0; c < D / 4; ++c) {
-      const float4 v = r4[c];
-      const float* qq = s_q + 4 * c;
-      acc = __builtin_fmaf(v.x, qq[0], acc);
-      acc = __builtin_fmaf(v.y, qq[1], acc);
-      acc = __builtin_fmaf(v.z, qq[2], acc);
-      acc = __builtin_fmaf(v.w, qq[3], acc);
-    }
+    const float4 a = reinterpret_cast<const float4*>(row)[2 * part];
+    const float4 b = reinterpret_cast<const float4*>(row)[2 * part + 1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
   }
-  return acc;
-}
-
-template <typename KT>
-__device__ __forceinline__ float elem(const KT* __restrict__ row, int d) {
-  if constexpr (sizeof(KT) == 2) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[d] << 16);
-  else return row[d];
 }
 
 template <typename KT, typename QT, typename OT>
@@ -1347,43 +1325,72 @@ __global__ void __launch_bounds__(DA_THREADS)
 dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k, const KT* __restrict__ dk,
                            const KT* __restrict__ dv, int64_t dsb, int64_t dsh, int64_t dst, int n_dense,
                            int n_q_heads, int n_kv_heads, int group) {
-  __shared__ float s_q[D];
   __shared__ float s_p[PK_MAX_TOPK_ATT + PK_MAX_DENSE];   // scores, then probabilities
   __shared__ int32_t s_ix[PK_MAX_TOPK_ATT];                // retrieved rows (-1: skipped)
   __shared__ float s_red[DA_THREADS / 64];
-  __shared__ float s_half[D];
+  __shared__ float s_acc[DA_GROUPS][D + 4];
 
   const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int part = tid & 15, rg = tid >> 4;           // dimensions 8 part .. 8 part + 7; row group
   const int seq = head / n_q_heads, qh = head - seq * n_q_heads, kvh = qh / group;
   const KT* kb = reinterpret_cast<const KT*>(a.k) + seq * a.sb + kvh * a.sh;
   const KT* vb = reinterpret_cast<const KT*>(a.v) + seq * a.sb + kvh * a.sh;
   const KT* dkb = dk + seq * dsb + kvh * dsh;
   const KT* dvb = dv + seq * dsb + kvh * dsh;
-  if (tid < D) {
-    if constexpr (sizeof(QT) == 2)
-      s_q[tid] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a.q)[(int64_t)head * D + tid] << 16);
-    else
-      s_q[tid] = reinterpret_cast<const float*>(a.q)[(int64_t)head * D + tid];
+  float qv[8];
+  if constexpr (sizeof(QT) == 2) {
+    const uint4 v = reinterpret_cast<const uint4*>(a.q)[(int64_t)head * (D / 8) + part];
+    qv[0] = bf16_lo(v.x); qv[1] = bf16_hi(v.x); qv[2] = bf16_lo(v.y); qv[3] = bf16_hi(v.y);
+    qv[4] = bf16_lo(v.z); qv[5] = bf16_hi(v.z); qv[6] = bf16_lo(v.w); qv[7] = bf16_hi(v.w);
+  } else {
+    const float4 x = reinterpret_cast<const float4*>(a.q)[(int64_t)head * (D / 4) + 2 * part];
+    const float4 y = reinterpret_cast<const float4*>(a.q)[(int64_t)head * (D / 4) + 2 * part + 1];
+    qv[0] = x.x; qv[1] = x.y; qv[2] = x.z; qv[3] = x.w; qv[4] = y.x; qv[5] = y.y; qv[6] = y.z; qv[7] = y.w;
   }
-  for (int r = tid; r < k; r += DA_THREADS) {
+  // with no zone rows the retrieved indices are all skipped and nothing of
+  // the zone is read
+  const int kz = a.n_rows > 0 ? k : 0;
+  for (int r = tid; r < kz; r += DA_THREADS) {
     const int v = idx[(int64_t)head * k + r];
     s_ix[r] = (v >= 0 && (int64_t)v < a.n_rows) ? v : -1;
   }
   __syncthreads();
-  const int total = k + n_dense;
-
-  // scores (invalid retrieved rows: -inf)
-  float m = -__builtin_inff();
-  for (int r = tid; r < total; r += DA_THREADS) {
-    float sc;
-    if (r < k) {
-      const int ix = s_ix[r];
-      sc = ix >= 0 ? dot_row(kb + (int64_t)ix * a.st, s_q) * a.scale : -__builtin_inff();
-    } else {
-      sc = dot_row(dkb + (int64_t)(r - k) * dst, s_q) * a.scale;
+  const int total = kz + n_dense;
+  if (total == 0) {
+    if (tid < D) {
+      if constexpr (sizeof(OT) == 2) reinterpret_cast<uint16_t*>(a.out)[(int64_t)head * D + tid] = 0;
+      else reinterpret_cast<float*>(a.out)[(int64_t)head * D + tid] = 0.0f;
     }
-    s_p[r] = sc;
-    m = fmaxf(m, sc);
+    return;
+  }
+
+  // scores (invalid retrieved rows: -inf); rows past the end re-read the last one
+  float m = -__builtin_inff();
+#pragma unroll 2
+  for (int r0 = 0; r0 < total; r0 += DA_GROUPS) {
+    const int r = r0 + rg;
+    const int rr = r < total ? r : total - 1;
+    bool ok = true;
+    const KT* row;
+    if (rr < kz) {
+      const int ix = s_ix[rr];
+      ok = ix >= 0;
+      row = kb + (int64_t)(ok ? ix : 0) * a.st;
+    } else {
+      row = dkb + (int64_t)(rr - kz) * dst;
+    }
+    float x[8];
+    load8(row, part, x);
+    float p = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p = __builtin_fmaf(qv[e], x[e], p);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) p += __shfl_xor(p, off, 16);
+    const float sc = ok ? p * a.scale : -__builtin_inff();
+    if (r < total) {
+      if (part == 0) s_p[r] = sc;
+      m = fmaxf(m, sc);
+    }
   }
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   if (lane == 0) s_red[wave] = m;
@@ -1406,30 +1413,38 @@ dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k,
 #pragma unroll
   for (int w2 = 0; w2 < DA_THREADS / 64; ++w2) ssum += s_red[w2];
 
-  // weighted sum of the value rows: dimension tid % 128, rows of parity tid / 128
-  const int d = tid & (D - 1), half = tid >> 7;
-  float o = 0.0f;
-#pragma unroll 4
-  for (int r = half; r < total; r += 2) {
-    const float p = s_p[r];
-    const KT* vrow;
-    if (r < k) {
-      const int ix = s_ix[r];
-      vrow = vb + (int64_t)(ix >= 0 ? ix : 0) * a.st;
+  // weighted sum of the value rows
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll 2
+  for (int r0 = 0; r0 < total; r0 += DA_GROUPS) {
+    const int r = r0 + rg;
+    const int rr = r < total ? r : total - 1;
+    const float p = r < total ? s_p[rr] : 0.0f;
+    const KT* row;
+    if (rr < kz) {
+      const int ix = s_ix[rr];
+      row = vb + (int64_t)(ix >= 0 ? ix : 0) * a.st;
     } else {
-      vrow = dvb + (int64_t)(r - k) * dst;
+      row = dvb + (int64_t)(rr - kz) * dst;
     }
-    o = __builtin_fmaf(p, elem(vrow, d), o);
+    float x[8];
+    load8(row, part, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(p, x[e], acc[e]);
   }
-  if (half == 1) s_half[d] = o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_acc[rg][8 * part + e] = acc[e];
   __syncthreads();
-  if (half == 0) {
-    const float acc = o + s_half[d];
-    const float res = (ssum > 0.0f) ? acc / ssum : 0.0f;
+  if (tid < D) {
+    float o = s_acc[0][tid];
+    for (int g2 = 1; g2 < DA_GROUPS; ++g2) o += s_acc[g2][tid];
+    const float res = (ssum > 0.0f) ? o / ssum : 0.0f;
     if constexpr (sizeof(OT) == 2) {
-      reinterpret_cast<uint16_t*>(a.out)[(int64_t)head * D + d] = (uint16_t)f32_to_bf16_rne(res);
+      reinterpret_cast<uint16_t*>(a.out)[(int64_t)head * D + tid] = (uint16_t)f32_to_bf16_rne(res);
     } else {
-      reinterpret_cast<float*>(a.out)[(int64_t)head * D + d] = res;
+      reinterpret_cast<float*>(a.out)[(int64_t)head * D + tid] = res;
     }
   }
 }

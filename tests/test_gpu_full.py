@@ -11,6 +11,7 @@ for bit, attention within 2e-2).
                head with a drifting mean; sampled steps checked, recall reported
   batched128k_pct  batched128k with the pages' percentile tiers and adaptive
                ratios (C = 13108)
+  drift128k_layout the sink / local / update-buffer layout over the drift stream
 """
 import numpy as np
 import pytest
@@ -109,3 +110,59 @@ def test_full_drift_stream():
     assert run.n == w.n + T
     run.close()
     say(f"case drift128k: recall@100 at checked steps {np.round(recalls, 3).tolist()}")
+
+
+def test_full_layout_stream():
+    """drift128k_layout as the benchmark runs it: 64 sink tokens and a window of
+    512 + up to 256 new tokens attended densely, the rest of the 128K prefill as
+    the retrieval zone; 300 steps with one update-buffer flush; the last step is
+    checked against the oracle on one unit."""
+    import torch
+    from kv_cache_top_amd import pariskv as P
+    w = S.WORKLOADS["drift128k_layout"]
+    sink, local, upd, steps = w.sink_tokens, w.local_tokens, w.update_tokens, 300
+    say("case drift128k_layout: generating")
+    K = S.all_keys(w)
+    V = S.all_values(w)
+    T = local + steps
+    ak = np.stack([np.stack([np.stack([S.appended_key(w, b, h, t) for t in range(T)])
+                             for h in range(w.n_kv_heads)]) for b in range(w.batch)])
+    av = np.stack([np.stack([np.stack([S.appended_value(w, b, h, t) for t in range(T)])
+                             for h in range(w.n_kv_heads)]) for b in range(w.batch)])
+    zone0 = w.n - sink
+    Kz = np.concatenate([K[:, :, sink:], ak], axis=2)
+    Vz = np.concatenate([V[:, :, sink:], av], axis=2)
+    Q = S.all_queries(w, K)
+    run = GpuRun(w, Kz, Vz, Q, n=zone0, capacity=Kz.shape[2])
+    window = local                                     # stream tokens 0..local-1 are in the window
+    for t in range(steps):
+        window += 1                                   # token local + t joins the window
+        if window == local + upd:
+            P.pk_append_keys(run.ctx.h, run.Kt[:, :, run.n:run.n + upd], run.sums.s)
+            window = local
+    torch.cuda.synchronize()
+    n_zone = run.n
+    assert n_zone == zone0 + upd
+    run.retrieve()
+    lo = n_zone                                        # first window row in the zone tensor
+    Kd = np.concatenate([K[:, :, :sink], Kz[:, :, lo:lo + window]], axis=2)
+    Vd = np.concatenate([V[:, :, :sink], Vz[:, :, lo:lo + window]], axis=2)
+    out = torch.zeros((w.batch, w.n_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    P.pk_sparse_dense_attend(run.ctx.h, run.Qt, run.Kt, run.Vt, run.topk_idx, to_torch(Kd), to_torch(Vd), out)
+    torch.cuda.synchronize()
+    u = 3
+    b, h = divmod(u, w.n_kv_heads)
+    kf = S.as_f32(Kz[b, h, :n_zone])
+    vf = S.as_f32(Vz[b, h, :n_zone])
+    enc = oracle_encode(kf)
+    check_encode_unit(run, u, kf, enc=enc, rows=slice(zone0 - 8, n_zone))
+    check_retrieve_unit(run, b, h, kf, vf, enc, check_attention=False)
+    ti = run.topk_idx.cpu().numpy()
+    from tests.parity_util import attention_ok
+    for g in range(w.group):
+        qh = h * w.group + g
+        ref = O.layout_attention(S.as_f32(Q[b, qh]), kf, vf, ti[b, qh], S.as_f32(Kd[b, h]), S.as_f32(Vd[b, h]),
+                                 w.softmax_scale)
+        o = out[b, qh].float().cpu().numpy()
+        assert attention_ok(o, ref), f"layout attention g={g}: {np.abs(o - ref).max()}"
+    run.close()

@@ -84,6 +84,37 @@ def test_dense_only_and_empty_dense():
     run.close()
 
 
+def test_zone_buffer_without_rows():
+    """A zone K/V tensor with no rows: only the dense rows are read."""
+    import torch
+    from kv_cache_top_amd import pariskv as P
+    w = S.custom("llama32k", batch=1, n_kv_heads=2, n_q_heads=8, n=300, n_candidates=64, top_k=20, wid=725)
+    say("case layout with a zero-row zone tensor")
+    K, V, Q = _split(w, 0, 300, 150)
+    Kd, Vd = np.ascontiguousarray(K[:, :, 300:]), np.ascontiguousarray(V[:, :, 300:])
+    run = GpuRun(w, np.ascontiguousarray(K[:, :, :300]), np.ascontiguousarray(V[:, :, :300]), Q).retrieve()
+    empty = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
+    Kdt, Vdt = to_torch(Kd), to_torch(Vd)
+    P._check(P._lib.pk_sparse_dense_attend(run.ctx.h, P._ptr(run.Qt), P.PK_BF16, ctypes_ptr(empty), ctypes_ptr(empty),
+                                           P.PK_BF16, P._I64x3(256, 128, 128), 0, P._ptr(run.topk_idx),
+                                           P._ptr(Kdt), P._ptr(Vdt), P._strides4(Kdt), 150,
+                                           P._ptr(out), P.PK_BF16, P._stream(None)), run.ctx.h)
+    torch.cuda.synchronize()
+    for qh in range(8):
+        h = qh // 4
+        ref = O.layout_attention(S.as_f32(Q[0, qh]), np.zeros((0, 128)), np.zeros((0, 128)), np.array([-1]),
+                                 S.as_f32(Kd[0, h]), S.as_f32(Vd[0, h]), w.softmax_scale)
+        assert attention_ok(out[0, qh].float().cpu().numpy(), ref)
+    run.close()
+
+
+def ctypes_ptr(t):
+    import ctypes
+    # a tensor with no elements may have a null data pointer: pass an aligned dummy address instead
+    return ctypes.c_void_p(t.data_ptr() or 256)
+
+
 def test_many_dense_rows_and_limit():
     from kv_cache_top_amd import pariskv as P
     w = S.custom("llama32k", batch=1, n_kv_heads=1, n_q_heads=4, n=1000, n_candidates=256, wid=730)

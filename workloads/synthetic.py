@@ -68,6 +68,13 @@ class Workload:
     tier_mode: str = "rank"
     collision_permille: int = 0
     adaptive: bool = False
+    # sink / local / update-buffer layout: the first sink_tokens prefill rows
+    # and a window of the newest tokens are attended densely; the window holds
+    # local_tokens plus up to update_tokens new ones, after which the oldest
+    # update_tokens of it move into the summarised retrieval zone
+    sink_tokens: int = 0
+    local_tokens: int = 0
+    update_tokens: int = 0
     extra: dict = field(default_factory=dict, compare=False)
 
     @property
@@ -98,6 +105,11 @@ WORKLOADS = {
         # the pages' own Stage I: percentile tiers with adaptive ratios
         # (at n = 131072: beta = 0.1 -> C = 13108, rho = 0.2)
         Workload("batched128k_pct", 6, 8, 8, 32, 131072, "bf16", 13108, tier_mode="percentile", adaptive=True),
+        # decode stream with the pages' memory layout: 64 sink tokens, a
+        # 512-token local window and a 256-token update buffer stay dense;
+        # the zone (the rest of the 128K prefill) is retrieved from
+        Workload("drift128k_layout", 7, 1, 8, 32, 131072, "bf16", 4096, append_steps=1024, sink_tokens=64,
+                 local_tokens=512, update_tokens=256),
     ]
 }
 
