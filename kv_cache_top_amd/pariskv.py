@@ -30,6 +30,7 @@ PK_OK, PK_ERR_INVALID_ARG, PK_ERR_UNSUPPORTED, PK_ERR_CAPACITY, PK_ERR_OUT_OF_ME
     0, -1, -2, -3, -4, -5
 PK_F32, PK_BF16 = 0, 1
 PK_TIERS_RANK, PK_TIERS_PERCENTILE = 0, 1
+PK_MAX_CANDIDATES, PK_MAX_TOPK, PK_MAX_DENSE = 16384, 256, 8192
 KERNELS = ["encode", "qprep", "collide", "threshold", "select", "rerank", "topk", "attend", "rerank_topk",
            "dense_attend"]
 PK_N_KERNELS = len(KERNELS)
