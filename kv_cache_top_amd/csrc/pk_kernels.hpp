@@ -971,8 +971,9 @@ attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k, int n_q_head
 constexpr int TOPK_BINS = 4096;        // 12-bit digit
 constexpr int TOPK_MAXB = 512;         // boundary-bin size handled by ranking
 
-__device__ __forceinline__ uint64_t topk_item(uint32_t key, int p) {
-  return ((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)p);   // larger = better
+// (estimate key, key index): larger = better, so equal estimates go to the lower index
+__device__ __forceinline__ uint64_t topk_item(uint32_t key, int32_t ix) {
+  return ((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)ix);
 }
 
 // LDS table T[j][nib] = fl(v(nib) * Rq[j]) of one query head
@@ -1028,9 +1029,11 @@ struct TopkShared {
 };
 
 // Top-k of one head's n_sel candidates; thread tid holds slots r * NT + tid
-// as order-preserving keys key[r].  s.misc must be zero on entry.
+// as order-preserving estimate keys key[r] and the slots' key indices kix[r].
+// Slots are in ascending key order, so slot order breaks ties as the key index
+// does.  s.misc must be zero on entry.
 template <int R, int NT>
-__device__ void topk_block(const uint32_t (&key)[R], int n_sel, int k, const int32_t* ci, int32_t* out_idx,
+__device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], int n_sel, int k, int32_t* out_idx,
                            float* out_est, TopkShared<NT>& s, int tid, int32_t* lds_idx = nullptr) {
   constexpr int NW = NT / 64;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1115,8 +1118,8 @@ __device__ void topk_block(const uint32_t (&key)[R], int n_sel, int k, const int
       const int p = r * NT + tid;
       if (p < n_sel) {
         const uint32_t mk = key[r] & pmask;
-        if (mk > prefix) s.f[atomicAdd(&s.misc[3], 1)] = topk_item(key[r], p);
-        else if (mk == prefix && m <= TOPK_MAXB) s.b[atomicAdd(&s.misc[4], 1)] = topk_item(key[r], p);
+        if (mk > prefix) s.f[atomicAdd(&s.misc[3], 1)] = topk_item(key[r], kix[r]);
+        else if (mk == prefix && m <= TOPK_MAXB) s.b[atomicAdd(&s.misc[4], 1)] = topk_item(key[r], kix[r]);
       }
     }
     __syncthreads();
@@ -1142,23 +1145,31 @@ __device__ void topk_block(const uint32_t (&key)[R], int n_sel, int k, const int
           if (w2 < wave) before += (int)s.wsum[w2];
           tot += (int)s.wsum[w2];
         }
-        if (eq && before < need) s.f[n_above + before] = topk_item(key[r], p);
+        if (eq && before < need) s.f[n_above + before] = topk_item(key[r], kix[r]);
         eq_run += tot;
         __syncthreads();
       }
     }
   }
   __syncthreads();
-  // place the keff winners by rank
-  for (int j = tid; j < keff; j += NT) {
-    const uint64_t e = s.f[j];
+  // place the keff winners by rank; PARTS neighbouring lanes count the
+  // winners above winner j, each over every PARTS-th entry
+  constexpr int PARTS = NT >= 4 * PK_SORT_N ? 4 : (NT >= 2 * PK_SORT_N ? 2 : 1);
+  for (int jb = 0; jb < keff; jb += NT / PARTS) {      // uniform
+    const int j = jb + tid / PARTS, part = tid % PARTS;
+    const bool act = j < keff;
+    const uint64_t e = s.f[act ? j : 0];
     int rank = 0;
-    for (int j2 = 0; j2 < keff; ++j2) rank += (s.f[j2] > e) ? 1 : 0;
-    const int p = (int)(0xFFFFFFFFu - (uint32_t)e);
-    const int32_t key_index = ci[p];
-    out_idx[rank] = key_index;
-    if (lds_idx) lds_idx[rank] = key_index;
-    if (out_est) out_est[rank] = from_orderable((uint32_t)(e >> 32));
+#pragma unroll 4
+    for (int j2 = part; j2 < keff; j2 += PARTS) rank += (s.f[j2] > e) ? 1 : 0;
+    if constexpr (PARTS >= 2) rank += __shfl_xor(rank, 1, 64);
+    if constexpr (PARTS >= 4) rank += __shfl_xor(rank, 2, 64);
+    if (act && part == 0) {
+      const int32_t key_index = (int32_t)(0xFFFFFFFFu - (uint32_t)e);
+      out_idx[rank] = key_index;
+      if (lds_idx) lds_idx[rank] = key_index;
+      if (out_est) out_est[rank] = from_orderable((uint32_t)(e >> 32));
+    }
   }
   for (int r = keff + tid; r < k; r += NT) {
     out_idx[r] = -1;
@@ -1210,6 +1221,12 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
     s_est[p] = est;
     if (ce && p < n_sel) ce[p] = est;
   }
+  int32_t kix[R];                   // the slots' key indices (L2), in flight during the first top-k steps
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int p = r * RT_THREADS + tid;
+    kix[r] = ci[p < plast ? p : plast];
+  }
   __syncthreads();
   uint32_t key[R];
 #pragma unroll
@@ -1217,7 +1234,7 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
     const int p = r * RT_THREADS + tid;
     key[r] = orderable(s_est[p < plast ? p : plast]);
   }
-  topk_block<R, RT_THREADS>(key, n_sel, k, ci, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
+  topk_block<R, RT_THREADS>(key, kix, n_sel, k, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
                             s_tk, tid, ATT ? s_idx : nullptr);
   if constexpr (ATT) {
     __syncthreads();
@@ -1272,11 +1289,13 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
   float* ce = cand_est + (int64_t)head * n_candidates;
   // candidate estimates: clamped unconditional loads, all in flight together
   float ev[R];
+  int32_t kix[R];
   const int plast = n_sel > 0 ? n_sel - 1 : 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int p = r * 256 + tid;
     ev[r] = ce[p < plast ? p : plast];
+    kix[r] = ci[p < plast ? p : plast];
   }
   if (tid < 8) s_tk.misc[tid] = 0;
   for (int p = n_sel + tid; p < n_candidates; p += 256) {   // invalid tail slots (n < C)
@@ -1286,7 +1305,7 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
   uint32_t key[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) key[r] = orderable(ev[r]);
-  topk_block<R, 256>(key, n_sel, k, ci, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
+  topk_block<R, 256>(key, kix, n_sel, k, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
                      s_tk, tid);
 }
 
