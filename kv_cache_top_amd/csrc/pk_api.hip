@@ -316,16 +316,16 @@ void pk_destroy(pk_context* ctx) {
 static pk_status encode_rows(pk_context* ctx, const void* keys, pk_dtype dt, const int64_t* st,
                              int64_t t, int64_t row0, pk_summaries* s, hipStream_t stream) {
   if (t == 0) return PK_OK;
-  const int64_t total = (int64_t)ctx->units * t;
-  const int64_t blocks = (total + 15) / 16;
+  const int64_t chunks = (t + pk::ENC_KEYS - 1) / pk::ENC_KEYS;   // t <= n_capacity < 2^31
+  const int64_t blocks = (int64_t)ctx->units * chunks;
   Launch L(ctx, PK_KERNEL_ENCODE, stream);
   if (dt == PK_BF16)
     hipLaunchKernelGGL(pk::encode_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint16_t*)keys, st[0], st[1], st[2], ctx->cfg.n_kv_heads, t, total, row0,
+                       (const uint16_t*)keys, st[0], st[1], st[2], ctx->cfg.n_kv_heads, t, (int)chunks, row0,
                        s->n_capacity, s->codes, s->records, s->norms, s->counts, ctx->tb);
   else
     hipLaunchKernelGGL(pk::encode_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const float*)keys, st[0], st[1], st[2], ctx->cfg.n_kv_heads, t, total, row0,
+                       (const float*)keys, st[0], st[1], st[2], ctx->cfg.n_kv_heads, t, (int)chunks, row0,
                        s->n_capacity, s->codes, s->records, s->norms, s->counts, ctx->tb);
   return check_launch(ctx, "encode");
 }

@@ -102,22 +102,17 @@ __device__ __forceinline__ uint32_t mbcnt(uint64_t mask) {
 //   y = H (s * k); rho_b = ||y_b||; bit j = [y_j > 0]; u = y / rho;
 //   idx_j = #{tau_l <= |u_j|}; alpha = sum_j |u_j| L[idx_j];
 //   w_b = rho_b fl(1/sqrt(128)) / alpha  (= ||k|| r_b / alpha_b, Eq. (9)).
+// A workgroup encodes up to ENC_KEYS consecutive rows of one unit, 16 keys
+// at a time, and counts its keys per (subspace, centroid) in LDS; the counts
+// are added to the unit's totals once at the end.  A short append (at most
+// ENC_DIRECT rows per unit) adds each key's counts directly instead.
 // ===========================================================================
-template <typename KT>
-__global__ void __launch_bounds__(256)
-encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
-              int n_kv_heads, int64_t t, int64_t total, int64_t row0, int64_t n_cap,
-              uint8_t* __restrict__ codes, uint8_t* __restrict__ records,
-              float* __restrict__ norms, uint32_t* __restrict__ counts, Tables tb) {
-  const int64_t key = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int b = threadIdx.x & 15;
-  if (key >= total) return;                 // whole 16-lane groups leave together
-  const int64_t unit = key / t;
-  const int64_t r = key - unit * t;
-  const int64_t seq = unit / n_kv_heads, head = unit - seq * n_kv_heads;
-  const KT* src = keys + seq * sb + head * sh + r * st + b * SUBD;
+constexpr int ENC_KEYS = 1024;
+constexpr int ENC_DIRECT = 64;
 
-  float x[SUBD];
+// lane b's 8 coordinates of one key, as fp32
+template <typename KT>
+__device__ __forceinline__ void load_key(const KT* __restrict__ src, float (&x)[SUBD]) {
   if constexpr (sizeof(KT) == 2) {
     const uint4 v = *reinterpret_cast<const uint4*>(src);
     x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
@@ -128,6 +123,11 @@ encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
     x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
     x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
   }
+}
+
+// code byte, nibbles, weight and partial squared norm of subspace b of one key
+__device__ __forceinline__ void encode_key(float (&x)[SUBD], int b, const Tables& tb, uint32_t& code_out,
+                                           uint32_t& nib_out, float& w_out, float& nsq_out) {
   float nsq = 0.0f;
 #pragma unroll
   for (int j = 0; j < SUBD; ++j) nsq += x[j] * x[j];
@@ -193,16 +193,62 @@ encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
     w = __fdiv_rn(rho * tb.inv_sqrt_d, alpha);
   }
 
-  const int64_t row = unit * n_cap + row0 + r;
-  codes[row * 16 + b] = (uint8_t)code;
-  if (counts) atomicAdd(&counts[(unit * NSUB + b) * 256 + code], 1u);   // keys per (subspace, centroid)
-  uint32_t* rec = reinterpret_cast<uint32_t*>(records + row * 128);
-  rec[b] = nib;
-  reinterpret_cast<float*>(rec)[16 + b] = w;
+  code_out = code;
+  nib_out = nib;
+  w_out = w;
+  nsq_out = nsq;
+}
 
+template <typename KT>
+__global__ void __launch_bounds__(256)
+encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
+              int n_kv_heads, int64_t t, int chunks, int64_t row0, int64_t n_cap,
+              uint8_t* __restrict__ codes, uint8_t* __restrict__ records,
+              float* __restrict__ norms, uint32_t* __restrict__ counts, Tables tb) {
+  __shared__ uint32_t s_cnt[NSUB * 256];
+  const int64_t unit = blockIdx.x / chunks;
+  const int64_t r0 = (int64_t)(blockIdx.x - unit * chunks) * ENC_KEYS;
+  const int64_t r1 = (r0 + ENC_KEYS < t) ? r0 + ENC_KEYS : t;
+  const int tid = threadIdx.x, b = tid & 15;
+  const int64_t seq = unit / n_kv_heads, head = unit - seq * n_kv_heads;
+  const KT* ubase = keys + seq * sb + head * sh + b * SUBD;
+  const bool direct = t <= ENC_DIRECT;
+  uint32_t* ucnt = counts ? counts + unit * NSUB * 256 : nullptr;
+  if (ucnt && !direct) {
+    for (int i = tid; i < NSUB * 256; i += 256) s_cnt[i] = 0;
+    __syncthreads();
+  }
+
+  // whole 16-lane groups; the next key's load is in flight while one is encoded
+  int64_t r = r0 + (tid >> 4);
+  float xa[SUBD];
+  if (r < r1) load_key<KT>(ubase + r * st, xa);
+  for (; r < r1; r += 16) {
+    float xb[SUBD];
+    if (r + 16 < r1) load_key<KT>(ubase + (r + 16) * st, xb);
+    uint32_t code, nib;
+    float w, nsq;
+    encode_key(xa, b, tb, code, nib, w, nsq);
 #pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) nsq += __shfl_xor(nsq, m, 16);
-  if (b == 0) norms[row] = sqrt_rn(nsq);
+    for (int j = 0; j < SUBD; ++j) xa[j] = xb[j];
+    const int64_t row = unit * n_cap + row0 + r;
+    codes[row * 16 + b] = (uint8_t)code;
+    if (ucnt) {
+      if (direct) atomicAdd(&ucnt[b * 256 + code], 1u);
+      else atomicAdd(&s_cnt[b * 256 + code], 1u);
+    }
+    uint32_t* rec = reinterpret_cast<uint32_t*>(records + row * 128);
+    rec[b] = nib;
+    reinterpret_cast<float*>(rec)[16 + b] = w;
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) nsq += __shfl_xor(nsq, m, 16);
+    if (b == 0) norms[row] = sqrt_rn(nsq);
+  }
+  if (ucnt && !direct) {                    // keys per (subspace, centroid)
+    __syncthreads();
+    for (int i = tid; i < NSUB * 256; i += 256)
+      if (s_cnt[i]) atomicAdd(&ucnt[i], s_cnt[i]);
+  }
 }
 
 // ===========================================================================

@@ -148,6 +148,9 @@ def test_append_equals_full_encode():
                                       full.sums.codes_view()[u, :3000].cpu().numpy())
         np.testing.assert_array_equal(part.sums.records_view()[u, :3000].cpu().numpy(),
                                       full.sums.records_view()[u, :3000].cpu().numpy())
+    # centroid counts: workgroup-aggregated (long encodes) and per-key (short appends) agree
+    np.testing.assert_array_equal(part.sums.counts_view().cpu().numpy(), full.sums.counts_view().cpu().numpy())
+    assert int(full.sums.counts_view()[0].sum()) == 16 * 3000
     part.retrieve().attend()
     _check_all_units(part, K, V)
     full.close()
