@@ -10,12 +10,16 @@ final two-stage result; Fig. 9, recall against the candidate ratio):
   keys with the largest collision score (Stage I alone), for the candidate set
   (how many of the exact Top-k it holds) and for the final Top-k.
 * ``ratio``: recall against the candidate ratio beta = C / n at several n.
+* ``union``: how many distinct keys the G query heads of one KV head select
+  together, i.e. the tighter Stage II byte count 128 B x |union of the G
+  candidate sets| per unit, against the per-head sum 128 B x G x C.
 
 The exact Top-k is <k_i, q> in fp32 over all current keys (torch on the GPU).
 Each result is printed as one JSON line, then a markdown table.
 
     python -m kv_cache_top_amd.studies drift [--every 64]
     python -m kv_cache_top_amd.studies ratio
+    python -m kv_cache_top_amd.studies union
 """
 from __future__ import annotations
 
@@ -159,6 +163,44 @@ def ratio(n_list, permilles, modes):
     return rows
 
 
+def union(names):
+    import torch
+
+    from kv_cache_top_amd import pariskv as P
+    from workloads import synthetic as S
+    dev = torch.device("cuda")
+    rows = []
+    for name in names:
+        w = S.WORKLOADS[name]
+        K = S.all_keys(w)
+        Kt = _torch(K, dev)
+        cfg = _config(P, w, w.n)
+        ctx = P.Context(cfg)
+        sums = P.Summaries(cfg)
+        P.pk_encode_keys(ctx.h, Kt, sums.s)
+        del Kt
+        sizes = []
+        C = w.n_candidates
+        for step in range(2):
+            Q = S.all_queries(w, K, step=step)
+            cand, _, _ = _retrieve(P, ctx, sums, _torch(Q, dev), w, C, dev)
+            cand = cand.reshape(w.batch, w.n_q_heads, -1)
+            for b in range(w.batch):
+                for h in range(w.n_kv_heads):
+                    ids = cand[b, h * w.group:(h + 1) * w.group].reshape(-1)
+                    sizes.append(int(np.unique(ids[ids >= 0]).size))
+        c_used = int((cand >= 0).sum(axis=-1).max())
+        u = float(np.mean(sizes))
+        row = {"study": "union", "workload": name, "G": w.group, "C": c_used, "mean_union": round(u, 1),
+               "union_over_GC": round(u / (w.group * c_used), 4),
+               "stage2_bytes_per_head_sum": 128 * w.group * c_used * w.units,
+               "stage2_bytes_union": int(round(128 * u * w.units))}
+        print(json.dumps(row), flush=True)
+        rows.append(row)
+        ctx.close()
+    return rows
+
+
 def table(rows):
     if not rows:
         return ""
@@ -170,13 +212,15 @@ def table(rows):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("study", choices=["drift", "ratio"])
+    ap.add_argument("study", choices=["drift", "ratio", "union"])
     ap.add_argument("--every", type=int, default=128)
     ap.add_argument("--modes", default="rank,percentile")
     args = ap.parse_args()
     modes = args.modes.split(",")
     if args.study == "drift":
         rows = drift(args.every, modes)
+    elif args.study == "union":
+        rows = union(("llama32k", "batched128k", "batched128k_pct"))
     else:
         rows = ratio((32768, 131072), (10, 20, 50, 100, 200, 400), modes)
     print(table(rows), flush=True)
