@@ -1200,7 +1200,7 @@ __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], in
   __syncthreads();
   // place the keff winners by rank; PARTS neighbouring lanes count the
   // winners above winner j, each over every PARTS-th entry
-  constexpr int PARTS = NT >= 4 * PK_SORT_N ? 4 : (NT >= 2 * PK_SORT_N ? 2 : 1);
+  constexpr int PARTS = NT >= 1024 ? 8 : (NT >= 512 ? 4 : 2);
   for (int jb = 0; jb < keff; jb += NT / PARTS) {      // uniform
     const int j = jb + tid / PARTS, part = tid % PARTS;
     const bool act = j < keff;
@@ -1210,6 +1210,7 @@ __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], in
     for (int j2 = part; j2 < keff; j2 += PARTS) rank += (s.f[j2] > e) ? 1 : 0;
     if constexpr (PARTS >= 2) rank += __shfl_xor(rank, 1, 64);
     if constexpr (PARTS >= 4) rank += __shfl_xor(rank, 2, 64);
+    if constexpr (PARTS >= 8) rank += __shfl_xor(rank, 4, 64);
     if (act && part == 0) {
       const int32_t key_index = (int32_t)(0xFFFFFFFFu - (uint32_t)e);
       out_idx[rank] = key_index;
