@@ -71,6 +71,22 @@ def test_many_heads_one_workgroup_topk(n, C):
     run.close()
 
 
+@pytest.mark.parametrize("batch,n_kv,n_q,n", [(1, 1, 4, 20000), (4, 8, 32, 17000)])
+def test_maximum_candidates_and_top_k(batch, n_kv, n_q, n):
+    """C = 16384 and k = 256, the largest the ABI takes: the split rerank /
+    top-k kernels (4 heads) and the one-workgroup-per-head path (128 heads,
+    sixteen candidate slots per thread)."""
+    from kv_cache_top_amd import pariskv as P
+    C, k = P.PK_MAX_CANDIDATES, P.PK_MAX_TOPK
+    w = S.custom("llama32k", batch=batch, n_kv_heads=n_kv, n_q_heads=n_q, n=n, n_candidates=C, top_k=k,
+                 wid=270 + n_q)
+    say(f"case maximum C={C} k={k} heads={batch * n_q} n={n}")
+    K, V, Q = _inputs(w)
+    run = GpuRun(w, K, V, Q).retrieve().attend()
+    _check_all_units(run, K, V, units=None if w.units == 1 else [0, 31])
+    run.close()
+
+
 def test_many_subtiles_single_unit():
     """One KV head with a long ragged key range: the selection's per-sub-tile
     prefix counts span several 256-sub-tile chunks."""
