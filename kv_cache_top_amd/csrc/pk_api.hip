@@ -499,7 +499,10 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
 #undef PK_COLLIDE
   }
   if ((st = check_launch(ctx, "collide")) != PK_OK) return st;
-  {
+  // at most 64 sub-tiles of 64-bin histograms per unit: each select workgroup
+  // derives theta and its prefix counts itself
+  const bool fused_params = !pct && 4 * tiles <= 64;
+  if (!fused_params) {
     Launch L(ctx, PK_KERNEL_THRESHOLD, stream);
     if (pct)
       hipLaunchKernelGGL(pk::threshold_kernel<pk::NBIN_MAX>, dim3(ctx->units * ctx->group), dim3(pk::TH_THREADS), 0,
@@ -513,16 +516,23 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
   if ((st = check_launch(ctx, "threshold")) != PK_OK) return st;
   {
     Launch L(ctx, PK_KERNEL_SELECT, stream);
-#define PK_SELECT(GG)                                                                                          \
-  hipLaunchKernelGGL(pk::select_kernel<GG>, dim3(grid), dim3(256), 0, stream, ctx->scores, ctx->params,          \
+#define PK_SELECT(GG, F)                                                                                        \
+  hipLaunchKernelGGL((pk::select_kernel<GG, F>), dim3(grid), dim3(256), 0, stream, ctx->scores, ctx->params,      \
                      ctx->sub_base, ctx->cand_idx, n, s->n_capacity, tiles, (int)ctx->max_subs, tile,              \
-                     cfg.n_q_heads, cfg.n_kv_heads, C)
-    switch (ctx->group) {
-      case 1: PK_SELECT(1); break;
-      case 2: PK_SELECT(2); break;
-      case 3: PK_SELECT(3); break;
-      default: PK_SELECT(4); break;
+                     cfg.n_q_heads, cfg.n_kv_heads, C, ctx->tile_hist)
+#define PK_SELECT_G(F)                     \
+  switch (ctx->group) {                    \
+    case 1: PK_SELECT(1, F); break;        \
+    case 2: PK_SELECT(2, F); break;        \
+    case 3: PK_SELECT(3, F); break;        \
+    default: PK_SELECT(4, F); break;       \
+  }
+    if (fused_params) {
+      PK_SELECT_G(true);
+    } else {
+      PK_SELECT_G(false);
     }
+#undef PK_SELECT_G
 #undef PK_SELECT
   }
   if ((st = check_launch(ctx, "select")) != PK_OK) return st;

@@ -743,43 +743,154 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int G>
+// Selection parameters of query head g from the unit's 64-bin sub-tile
+// histograms when the unit has at most 64 sub-tiles (one per lane): the same
+// theta / need_eq / prefix counts as the threshold kernel, for the sub-tiles
+// 4 tl .. 4 tl + 3 of one select workgroup.  Bin totals come from a register
+// reduce-scatter over the lanes (lane l ends with the total of bin l + 1).
+// h: this lane's sub-tile histogram (hist_row_load); results go to s_par[g]
+// = (theta, need_eq) and s_base[w][g] = (#gt, #eq) before sub-tile 4 tl + w.
+__device__ __forceinline__ void hist_row_load(const uint32_t* __restrict__ uh, int subs, int g, int lane,
+                                              uint32_t (&h)[64]) {
+  if (lane < subs) {
+    const uint4* row = reinterpret_cast<const uint4*>(uh + ((int64_t)lane * MAXG + g) * NBIN);
+#pragma unroll
+    for (int q4 = 0; q4 < 16; ++q4) {
+      const uint4 x = row[q4];
+      h[4 * q4] = x.x; h[4 * q4 + 1] = x.y; h[4 * q4 + 2] = x.z; h[4 * q4 + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) h[i] = 0;
+  }
+}
+
+__device__ __forceinline__ void select_params_wave(const uint32_t (&h)[64], int64_t n, int subs, int sub_len,
+                                                   int tl, int g, int n_candidates, int lane, int2* s_par,
+                                                   int2 (*s_base)[MAXG]) {
+  uint32_t v[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) v[i] = h[i];
+  // after the stage of width w, v[i] (i < w) of lane l is the sum, over the
+  // 64 / w lanes that share l's bits below w, of bin i + (l & (64 - w))
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const bool up = (lane & w) != 0;
+#pragma unroll
+    for (int i = 0; i < w; ++i) {
+      const uint32_t send = up ? v[i] : v[i + w];
+      const uint32_t keep = up ? v[i + w] : v[i];
+      v[i] = keep + (uint32_t)__shfl_xor((int)send, w, 64);
+    }
+  }
+  const uint32_t tot = v[0];
+  // suffix counts: suf at lane l = #{S >= l + 1}; theta = the highest bin
+  // whose suffix reaches C (0: every key is taken)
+  uint32_t suf = tot;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_down(suf, off, 64);
+    if (lane + off < 64) suf += o;
+  }
+  const uint64_t ge = __ballot(suf >= (uint32_t)n_candidates);
+  const int top = ge ? 63 - __builtin_clzll(ge) : -1;
+  const int theta = top + 1;
+  const uint32_t all_nz = __shfl(suf, 0, 64);
+  const uint32_t n_gt = (top < 0) ? all_nz : (top == 63 ? 0u : (uint32_t)__shfl(suf, (top + 1) & 63, 64));
+  const uint32_t eq_tot = (theta > 0) ? (uint32_t)__shfl(tot, (theta - 1) & 63, 64) : (uint32_t)(n - n_gt);
+  const uint32_t want = (uint32_t)n_candidates - n_gt;
+  const uint32_t need_eq = want < eq_tot ? want : eq_tot;
+  // this lane's sub-tile: keys above / at theta, then exclusive prefixes
+  int gt = 0, eq = 0, nz = 0;
+#pragma unroll
+  for (int b = 0; b < 64; ++b) {
+    const int c = (int)h[b];
+    nz += c;
+    gt += (b + 1 > theta) ? c : 0;
+    eq = (b + 1 == theta) ? c : eq;
+  }
+  int64_t len = n - (int64_t)lane * sub_len;
+  len = len < 0 ? 0 : (len > sub_len ? sub_len : len);
+  if (theta == 0) eq = (int)len - nz;
+  if (lane >= subs) { gt = 0; eq = 0; }
+  int pg = gt, pe = eq;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int og = __shfl_up(pg, off, 64), oe = __shfl_up(pe, off, 64);
+    if (lane >= off) { pg += og; pe += oe; }
+  }
+  const int w = lane - 4 * tl;
+  if (w >= 0 && w < 4) s_base[w][g] = make_int2(pg - gt, pe - eq);
+  if (lane == 0) s_par[g] = make_int2(theta, (int)need_eq);
+}
+
+// FUSED: the unit has at most 64 sub-tiles of 64-bin histograms, and each
+// workgroup derives the parameters itself (select_params_wave) instead of
+// reading the threshold kernel's.
+template <int G, bool FUSED>
 __global__ void __launch_bounds__(256)
 select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__ params,
               const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx, int64_t n, int64_t n_cap,
-              int tiles, int max_subs, int tile, int n_q_heads, int n_kv_heads, int n_candidates) {
+              int tiles, int max_subs, int tile, int n_q_heads, int n_kv_heads, int n_candidates,
+              const uint32_t* __restrict__ tile_hist) {
   __shared__ uint2 s_ik[4][SEL_QCAP];             // compacted keys: (key, packed S)
+  __shared__ int2 s_par[FUSED ? MAXG : 1];
+  __shared__ int2 s_base[FUSED ? 4 : 1][MAXG];
 
   const int unit = blockIdx.x / tiles, tl = blockIdx.x - unit * tiles;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int seq = unit / n_kv_heads, kvh = unit - seq * n_kv_heads;
   const int qhead0 = seq * n_q_heads + kvh * G;
-  const int64_t k0 = (int64_t)tl * tile;
-  const int64_t k1 = (k0 + tile < n) ? k0 + tile : n;
+  // key indices fit in 32 bits (n <= n_capacity < 2^31)
+  const int k0 = tl * tile;
+  const int k1 = ((int64_t)k0 + tile < n) ? k0 + tile : (int)n;
   const int wkeys = tile >> 2;                    // multiple of 64
-  const int64_t w0 = k0 + (int64_t)wave * wkeys;
-  const int64_t w1 = (w0 + wkeys < k1) ? w0 + wkeys : k1;
+  const int w0 = k0 + wave * wkeys;
+  const int w1 = (w0 + wkeys < k1) ? w0 + wkeys : k1;
   const uint32_t* srow = scores + (int64_t)unit * n_cap;
+
+  // fused parameters: the histogram rows are requested before the scores, so
+  // that waiting for them does not wait for the scores (the memory counter is
+  // in order)
+  uint32_t hrow[FUSED ? 64 : 1];
+  if constexpr (FUSED) {
+    if (wave < G) hist_row_load(tile_hist + (int64_t)unit * max_subs * MAXG * NBIN, 4 * tiles, wave, lane, hrow);
+  }
 
   // packed scores of keys w0 + r*64 + lane, in groups of SEL_GRP chunks
   // (clamped, unconditional loads; the next group is in flight while one is used)
-  const int64_t last = (w1 > w0) ? w1 - 1 : 0;
+  const int last = (w1 > w0) ? w1 - 1 : 0;
   uint32_t sp[SEL_GRP];
 #pragma unroll
   for (int r = 0; r < SEL_GRP; ++r) {
-    const int64_t i = w0 + (int64_t)r * 64 + lane;
+    const int i = w0 + r * 64 + lane;
     sp[r] = srow[i < last ? i : last];
   }
   int need[G], run_gt[G], run_eq[G];
   uint32_t th4 = 0x7F7F7F7Fu;                     // absent heads: theta 127, never reached
+  uint32_t thp4 = 0;
+  // per head: theta, need_eq, and the counts of keys above / at theta before
+  // this wave's sub-tile
+  auto setup = [&]() __attribute__((always_inline)) {
+    if constexpr (FUSED) {
+      if (wave < G) select_params_wave(hrow, n, 4 * tiles, tile >> 2, tl, wave, n_candidates, lane, s_par, s_base);
+      __syncthreads();
+    }
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const SelParams p = params[unit * MAXG + g];
-    const int2 sb2 = sub_base[((int64_t)unit * max_subs + 4 * tl + wave) * MAXG + g];
-    need[g] = p.need_eq; run_gt[g] = sb2.x; run_eq[g] = sb2.y;
-    th4 = (th4 & ~(0xFFu << (8 * g))) | ((uint32_t)p.theta << (8 * g));
-  }
-  const uint32_t thp4 = th4 + 0x01010101u;         // theta + 1 per byte (<= 128: no carry)
+    for (int g = 0; g < G; ++g) {
+      int theta, ne, bg, be;
+      if constexpr (FUSED) {
+        const int2 pr = s_par[g], sb2 = s_base[wave][g];
+        theta = pr.x; ne = pr.y; bg = sb2.x; be = sb2.y;
+      } else {
+        const SelParams p = params[unit * MAXG + g];
+        const int2 sb2 = sub_base[((int64_t)unit * max_subs + 4 * tl + wave) * MAXG + g];
+        theta = p.theta; ne = p.need_eq; bg = sb2.x; be = sb2.y;
+      }
+      need[g] = ne; run_gt[g] = bg; run_eq[g] = be;
+      th4 = (th4 & ~(0xFFu << (8 * g))) | ((uint32_t)theta << (8 * g));
+    }
+    thp4 = th4 + 0x01010101u;                     // theta + 1 per byte (<= 128: no carry)
+  };
+  if constexpr (!FUSED) setup();                  // parameter loads right behind the first group's
   uint2* ik = s_ik[wave];
   int nk = 0;
 
@@ -814,14 +925,14 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
   auto load_group = [&](int grp, uint32_t (&dst)[SEL_GRP]) {
 #pragma unroll
     for (int r = 0; r < SEL_GRP; ++r) {
-      const int64_t i = w0 + (int64_t)(grp * SEL_GRP + r) * 64 + lane;
+      const int i = w0 + (grp * SEL_GRP + r) * 64 + lane;
       dst[r] = srow[i < last ? i : last];
     }
   };
   auto compact_group = [&](int grp, const uint32_t (&src)[SEL_GRP]) {
 #pragma unroll
     for (int r = 0; r < SEL_GRP; ++r) {
-      const int64_t i = w0 + (int64_t)(grp * SEL_GRP + r) * 64 + lane;
+      const int i = w0 + (grp * SEL_GRP + r) * 64 + lane;
       const bool valid = i < w1;                  // false for the whole wave past its keys
       const uint32_t ge4 = ((src[r] | 0x80808080u) - th4) & 0x80808080u;
       const bool interesting = valid && ge4 != 0u;
@@ -851,6 +962,7 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
     uint32_t sg[NG > 1 ? NG - 1 : 1][SEL_GRP];
 #pragma unroll
     for (int g = 1; g < NG; ++g) load_group(g, sg[g - 1]);
+    if constexpr (FUSED) setup();                 // while the scores are in flight
     compact_group(0, sp);
 #pragma unroll
     for (int g = 1; g < NG; ++g) {
@@ -1085,31 +1197,48 @@ __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], in
   const int lane = tid & 63, wave = tid >> 6;
   const int keff = k < n_sel ? k : n_sel;
   // the common leading bits of all candidate keys need no histogram: digits
-  // start at the highest bit where the largest and smallest keys differ
-  uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
+  // start at the highest bit where the largest and smallest keys differ.
+  // When at least k estimates are >= 0 (keys with the top bit set), the
+  // negative ones cannot win and the range starts at the smallest such key.
+  constexpr uint32_t POS = 0x80000000u;
+  uint32_t kmax = 0, kmin = 0xFFFFFFFFu, kminp = 0xFFFFFFFFu, npos = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const bool ok = r * NT + tid < n_sel;
     kmax = ok && key[r] > kmax ? key[r] : kmax;
     kmin = ok && key[r] < kmin ? key[r] : kmin;
+    const bool pos = ok && key[r] >= POS;
+    kminp = pos && key[r] < kminp ? key[r] : kminp;
+    npos += pos ? 1u : 0u;
   }
   for (int off = 32; off >= 1; off >>= 1) {
     const uint32_t a = __shfl_xor(kmax, off, 64), c = __shfl_xor(kmin, off, 64);
+    const uint32_t cp = __shfl_xor(kminp, off, 64), np = __shfl_xor(npos, off, 64);
     kmax = a > kmax ? a : kmax;
     kmin = c < kmin ? c : kmin;
+    kminp = cp < kminp ? cp : kminp;
+    npos += np;
   }
-  if (lane == 0) { s.wsum[wave] = kmax; s.h[wave] = kmin; }
+  if (lane == 0) { s.wsum[wave] = kmax; s.h[wave] = kmin; s.h[NW + wave] = kminp; s.h[2 * NW + wave] = npos; }
   __syncthreads();
+  npos = 0;
   for (int w2 = 0; w2 < NW; ++w2) {
     kmax = s.wsum[w2] > kmax ? s.wsum[w2] : kmax;
     kmin = s.h[w2] < kmin ? s.h[w2] : kmin;
+    kminp = s.h[NW + w2] < kminp ? s.h[NW + w2] : kminp;
+    npos += s.h[2 * NW + w2];
+  }
+  int m = n_sel;
+  if (kmin < POS && npos >= (uint32_t)keff && keff > 0) {   // uniform
+    kmin = kminp;
+    m = (int)npos;
   }
   const uint32_t diff = kmax ^ kmin;
   int top = diff ? 31 - __builtin_clz(diff) : -1;        // highest undecided bit
   uint32_t pmask = top >= 0 ? ~((2u << top) - 1u) : 0xFFFFFFFFu;
   if (top == 31) pmask = 0;
-  uint32_t prefix = kmax & pmask;
-  int n_above = 0, need = keff, m = n_sel;
+  uint32_t prefix = kmax & pmask;                       // the keys in [kmin, kmax] share it
+  int n_above = 0, need = keff;
   constexpr int per = TOPK_BINS / NT;                   // bins per thread
   while (keff > 0 && top >= 0 && m > TOPK_MAXB) {        // uniform
     const int shift = top >= 11 ? top - 11 : 0;
