@@ -824,7 +824,9 @@ __device__ __forceinline__ void select_params_wave(const uint32_t (&h)[64], int6
 
 // FUSED: the unit has at most 64 sub-tiles of 64-bin histograms, and each
 // workgroup derives the parameters itself (select_params_wave) instead of
-// reading the threshold kernel's.
+// reading the threshold kernel's.  Workgroups are dealt to the 8 XCDs in
+// turn; when the units split evenly over them, the tiles of one unit get
+// workgroups on one XCD, so its histograms are fetched into that L2 once.
 template <int G, bool FUSED>
 __global__ void __launch_bounds__(256)
 select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__ params,
@@ -835,7 +837,18 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
   __shared__ int2 s_par[FUSED ? MAXG : 1];
   __shared__ int2 s_base[FUSED ? 4 : 1][MAXG];
 
-  const int unit = blockIdx.x / tiles, tl = blockIdx.x - unit * tiles;
+  int unit, tl;
+  {
+    const int i = blockIdx.x, units = gridDim.x / tiles;
+    if (FUSED && units % 8 == 0) {
+      const int slot = i / 8;
+      unit = i % 8 + 8 * (slot / tiles);
+      tl = slot % tiles;
+    } else {
+      unit = i / tiles;
+      tl = i - unit * tiles;
+    }
+  }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int seq = unit / n_kv_heads, kvh = unit - seq * n_kv_heads;
   const int qhead0 = seq * n_q_heads + kvh * G;
