@@ -466,6 +466,20 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
 constexpr int COLLIDE_UNROLL = 8;
 constexpr int HIST_LANES = 32;
 
+// (unit, tile) of workgroup i of a units x tiles grid.  Workgroups are dealt
+// to the 8 XCDs in turn; when the units split evenly over them, all tiles of
+// one unit run on one XCD (its LUT and histograms then share that L2).
+__device__ __forceinline__ void xcd_unit_tile(int i, int units, int tiles, int& unit, int& tl) {
+  if (units % 8 == 0) {
+    const int slot = i / 8;
+    unit = i % 8 + 8 * (slot / tiles);
+    tl = slot % tiles;
+  } else {
+    unit = i / tiles;
+    tl = i - unit * tiles;
+  }
+}
+
 template <int G, int NB>   // NB: histogram bins 1..NB
 __global__ void __launch_bounds__(256)
 collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut,
@@ -475,7 +489,8 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
   __shared__ uint32_t s_lut[NSUB * 256];
   __shared__ uint32_t s_hist[MAXG * NB * HIST_LANES];
 
-  const int unit = blockIdx.x / tiles, tl = blockIdx.x - unit * tiles;
+  int unit, tl;
+  xcd_unit_tile(blockIdx.x, gridDim.x / tiles, tiles, unit, tl);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wkeys = tile >> 2;                     // keys of this wave's sub-tile (multiple of 64)
   const int64_t w0 = (int64_t)tl * tile + (int64_t)wave * wkeys;
@@ -824,9 +839,9 @@ __device__ __forceinline__ void select_params_wave(const uint32_t (&h)[64], int6
 
 // FUSED: the unit has at most 64 sub-tiles of 64-bin histograms, and each
 // workgroup derives the parameters itself (select_params_wave) instead of
-// reading the threshold kernel's.  Workgroups are dealt to the 8 XCDs in
-// turn; when the units split evenly over them, the tiles of one unit get
-// workgroups on one XCD, so its histograms are fetched into that L2 once.
+// reading the threshold kernel's.  The tiles of one unit share an XCD where
+// they can (xcd_unit_tile), so the unit's histograms are fetched into its L2
+// once.
 template <int G, bool FUSED>
 __global__ void __launch_bounds__(256)
 select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__ params,
@@ -838,17 +853,7 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
   __shared__ int2 s_base[FUSED ? 4 : 1][MAXG];
 
   int unit, tl;
-  {
-    const int i = blockIdx.x, units = gridDim.x / tiles;
-    if (FUSED && units % 8 == 0) {
-      const int slot = i / 8;
-      unit = i % 8 + 8 * (slot / tiles);
-      tl = slot % tiles;
-    } else {
-      unit = i / tiles;
-      tl = i - unit * tiles;
-    }
-  }
+  xcd_unit_tile(blockIdx.x, gridDim.x / tiles, tiles, unit, tl);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int seq = unit / n_kv_heads, kvh = unit - seq * n_kv_heads;
   const int qhead0 = seq * n_q_heads + kvh * G;
