@@ -69,6 +69,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Keys per collide / select workgroup: about kTargetWG workgroups over all
 // units, 256 threads each doing 1..kMaxKPL keys.
 constexpr int64_t kTargetWG = 512, kMaxKPL = 64;
+constexpr int64_t kFuseTile = 4096;
 // rerank and top-k run as one workgroup per head when there are enough heads to
 // fill the chip, or few enough candidates per head (four per thread)
 constexpr int kFusedTopkHeads = 128;
@@ -459,7 +460,14 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
     return fail(ctx, PK_ERR_CAPACITY, "adaptive candidate count %lld exceeds n_candidates %d", (long long)C64, C_cap);
   const int C = (int)C64;
   const bool pct = cfg.tier_mode == PK_TIERS_PERCENTILE;
-  const int tile = tile_size(ctx->units, n);
+  // 64-bin histograms: with at most 16 tiles (64 sub-tiles) per unit the
+  // select workgroups derive theta themselves and no threshold launch is
+  // needed; worth a few larger tiles while a tile stays within kFuseTile keys
+  int tile = tile_size(ctx->units, n);
+  if (!pct) {
+    const int64_t want = ((n + 15) / 16 + 255) / 256 * 256;
+    if (want > tile && want <= kFuseTile) tile = (int)want;
+  }
   const int tiles = (int)((n + tile - 1) / tile);
   if (tiles > ctx->max_tiles)
     return fail(ctx, PK_ERR_CAPACITY, "internal tiling bound exceeded (%d > %lld)", tiles, (long long)ctx->max_tiles);
