@@ -1398,8 +1398,14 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
   const int plast = n_sel > 0 ? n_sel - 1 : 0;
   const int rounds = (n_sel + RT_THREADS - 1) / RT_THREADS;
 
+  // the key index of the next round is loaded one round ahead, so each
+  // round waits for one memory trip (its records), not two
   uint4 ra[8];
-  if (n_sel > 0) rerank_load(ra, rbase, ci[tid < plast ? tid : plast]);
+  int ixn = 0;
+  if (n_sel > 0) {
+    rerank_load(ra, rbase, ci[tid < plast ? tid : plast]);
+    ixn = ci[RT_THREADS + tid < plast ? RT_THREADS + tid : plast];
+  }
   rerank_table<RT_THREADS>(s_T, rot_q + (int64_t)head * D, tb, tid);
   if (tid < 8) s_tk.misc[tid] = 0;
   for (int p = n_sel + tid; p < n_candidates; p += RT_THREADS) {   // invalid tail slots (n < C)
@@ -1410,7 +1416,10 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
 #pragma unroll 1
   for (int r = 0; r < rounds; ++r) {
     const int p = r * RT_THREADS + tid;
-    if (r) rerank_load(ra, rbase, ci[p < plast ? p : plast]);
+    if (r) {
+      rerank_load(ra, rbase, ixn);
+      ixn = ci[p + RT_THREADS < plast ? p + RT_THREADS : plast];
+    }
     const float est = rerank_eval(ra, s_T);
     s_est[p] = est;
     if (ce && p < n_sel) ce[p] = est;
@@ -1462,12 +1471,16 @@ rerank_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot
 
   uint4 ra[8];
   rerank_load(ra, rbase, ci[p0 + tid < plast ? p0 + tid : plast]);
+  int ixn = ci[p0 + 256 + tid < plast ? p0 + 256 + tid : plast];   // next round's key index
   rerank_table<256>(s_T, rot_q + (int64_t)head * D, tb, tid);
   __syncthreads();
 #pragma unroll 1
   for (int r = 0; r < RR_ROUNDS; ++r) {
     const int p = p0 + r * 256 + tid;
-    if (r) rerank_load(ra, rbase, ci[p < plast ? p : plast]);
+    if (r) {
+      rerank_load(ra, rbase, ixn);
+      ixn = ci[p + 256 < plast ? p + 256 : plast];
+    }
     const float est = rerank_eval(ra, s_T);
     if (p < n_sel) ce[p] = est;
   }
