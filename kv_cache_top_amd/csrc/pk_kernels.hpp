@@ -529,15 +529,19 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
       const int64_t i = nb + (int64_t)u * 64 + lane;
       nx[u] = crow[i < last ? i : last];
     }
+    // Every lane stores: a lane past the end holds the last key's codes, so it
+    // rewrites that key's score with the same value.  Unconditional stores let
+    // the wait for the next batch's loads leave this batch's stores in flight.
 #pragma unroll
     for (int u = 0; u < COLLIDE_UNROLL; ++u) {
       const int64_t i = base + (int64_t)u * 64 + lane;
-      if (i < w1) {
-        const uint32_t cw[4] = {c[u].x, c[u].y, c[u].z, c[u].w};
-        uint32_t acc = 0;
+      const bool inb = i < w1;
+      const uint32_t cw[4] = {c[u].x, c[u].y, c[u].z, c[u].w};
+      uint32_t acc = 0;
 #pragma unroll
-        for (int bb = 0; bb < NSUB; ++bb) acc += s_lut[bb * 256 + ((cw[bb >> 2] >> (8 * (bb & 3))) & 0xFFu)];
-        srow[i] = acc;
+      for (int bb = 0; bb < NSUB; ++bb) acc += s_lut[bb * 256 + ((cw[bb >> 2] >> (8 * (bb & 3))) & 0xFFu)];
+      srow[inb ? i : last] = acc;
+      if (inb) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const uint32_t sc = (acc >> (8 * g)) & 0xFFu;
