@@ -1156,14 +1156,25 @@ __device__ __forceinline__ uint64_t topk_item(uint32_t key, int32_t ix) {
   return ((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)ix);
 }
 
-// LDS table T[j][nib] = fl(v(nib) * Rq[j]) of one query head
+// LDS table T[j][nib] = fl(v(nib) * Rq[j]) of one query head; thread tid
+// fills entries tid + k NT.  The Rq values are loaded first (rerank_rq_load),
+// ahead of the record loads, so that building the table does not wait for
+// the records.
 template <int NT>
-__device__ __forceinline__ void rerank_table(float* s_T, const float* rq, const Tables& tb, int tid) {
-  for (int e = tid; e < D * 16; e += NT) {
-    const int j = e >> 4, nb = e & 15;
+__device__ __forceinline__ void rerank_rq_load(const float* rq, int tid, float (&rqv)[D * 16 / NT]) {
+#pragma unroll
+  for (int k = 0; k < D * 16 / NT; ++k) rqv[k] = rq[(tid + k * NT) >> 4];
+}
+
+template <int NT>
+__device__ __forceinline__ void rerank_table(float* s_T, const float (&rqv)[D * 16 / NT], const Tables& tb,
+                                             int tid) {
+#pragma unroll
+  for (int k = 0; k < D * 16 / NT; ++k) {
+    const int e = tid + k * NT, nb = e & 15;
     const float lv = tb.levels[nb & 7];
     const float v = (nb & 8) ? lv : -lv;
-    s_T[e] = v * rq[j];
+    s_T[e] = v * rqv[k];
   }
 }
 
@@ -1404,13 +1415,15 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
 
   // the key index of the next round is loaded one round ahead, so each
   // round waits for one memory trip (its records), not two
+  float rqv[D * 16 / RT_THREADS];
+  rerank_rq_load<RT_THREADS>(rot_q + (int64_t)head * D, tid, rqv);
   uint4 ra[8];
   int ixn = 0;
   if (n_sel > 0) {
     rerank_load(ra, rbase, ci[tid < plast ? tid : plast]);
     ixn = ci[RT_THREADS + tid < plast ? RT_THREADS + tid : plast];
   }
-  rerank_table<RT_THREADS>(s_T, rot_q + (int64_t)head * D, tb, tid);
+  rerank_table<RT_THREADS>(s_T, rqv, tb, tid);
   if (tid < 8) s_tk.misc[tid] = 0;
   for (int p = n_sel + tid; p < n_candidates; p += RT_THREADS) {   // invalid tail slots (n < C)
     ci[p] = -1;
@@ -1473,10 +1486,12 @@ rerank_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot
   const int p0 = ch * RR_PER_WG;
   const int plast = n_sel - 1;
 
+  float rqv[D * 16 / 256];
+  rerank_rq_load<256>(rot_q + (int64_t)head * D, tid, rqv);
   uint4 ra[8];
   rerank_load(ra, rbase, ci[p0 + tid < plast ? p0 + tid : plast]);
   int ixn = ci[p0 + 256 + tid < plast ? p0 + 256 + tid : plast];   // next round's key index
-  rerank_table<256>(s_T, rot_q + (int64_t)head * D, tb, tid);
+  rerank_table<256>(s_T, rqv, tb, tid);
   __syncthreads();
 #pragma unroll 1
   for (int r = 0; r < RR_ROUNDS; ++r) {
