@@ -563,11 +563,11 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
     else PK_RTK_LAUNCH(16, T, MR, A);              \
   } while (0)
     if (att) {
-      const int mr = k <= 8 * (pk::RT_THREADS / 64) ? 8 : 16;   // rows per wave
-      if (q_dtype == PK_BF16 && mr == 8) PK_RTK_R(uint16_t, 8, true);
-      else if (q_dtype == PK_BF16) PK_RTK_R(uint16_t, 16, true);
-      else if (mr == 8) PK_RTK_R(float, 8, true);
-      else PK_RTK_R(float, 16, true);
+      const int np = k <= 2 * (pk::RT_THREADS / 16) ? 2 : 4;   // passes of 64 rows
+      if (q_dtype == PK_BF16 && np == 2) PK_RTK_R(uint16_t, 2, true);
+      else if (q_dtype == PK_BF16) PK_RTK_R(uint16_t, 4, true);
+      else if (np == 2) PK_RTK_R(float, 2, true);
+      else PK_RTK_R(float, 4, true);
       if (attended) *attended = true;
     } else {
       PK_RTK_R(float, 1, false);

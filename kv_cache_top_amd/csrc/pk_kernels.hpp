@@ -1387,12 +1387,117 @@ __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], in
   }
 }
 
+// lane part's 8 of a row's 128 coordinates, as fp32
+template <typename KT>
+__device__ __forceinline__ void load8(const KT* __restrict__ row, int part, float (&x)[8]) {
+  if constexpr (sizeof(KT) == 2) {
+    const uint4 v = reinterpret_cast<const uint4*>(row)[part];
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+  } else {
+    const float4 a = reinterpret_cast<const float4*>(row)[2 * part];
+    const float4 b = reinterpret_cast<const float4*>(row)[2 * part + 1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+}
+
 // ---- many heads: rerank and top-k of one head in one workgroup -------------
 constexpr int RT_THREADS = 1024;
 
+// Attention of one query head over its k <= 64 P retrieved rows with
+// RT_THREADS threads: sixteen threads share a row, each holding 8 of its 128
+// dimensions, so 64 rows are covered per pass; the K and V rows of all P
+// passes are loaded before any is used.  Scores: 16-lane partial dot
+// products; one max and one sum over the workgroup; the value rows are
+// weighted in registers, summed over the four rows of a wave by shuffles and
+// over the waves in LDS.  fp32; indices < 0 or >= n_rows are skipped.
+template <int NW>
+struct AttRowsShared {
+  float red[NW];
+  float acc[NW][D];
+};
+
+template <typename T, int P>
+__device__ void attend_rows16(const T* __restrict__ qh_ptr, const T* __restrict__ kb, const T* __restrict__ vb,
+                              int64_t st, int64_t n_rows, const int32_t* hidx, int k, float scale,
+                              T* __restrict__ out_head, AttRowsShared<RT_THREADS / 64>& s, int tid) {
+  constexpr int NW = RT_THREADS / 64, RG = RT_THREADS / 16;
+  const int lane = tid & 63, wave = tid >> 6, part = tid & 15, rg = tid >> 4;
+  if (n_rows <= 0) {                              // no rows: nothing may be read
+    if (tid < D) {
+      if constexpr (sizeof(T) == 2) reinterpret_cast<uint16_t*>(out_head)[tid] = 0;
+      else out_head[tid] = 0.0f;
+    }
+    return;
+  }
+  float qv[8];
+  load8(qh_ptr, part, qv);
+  float kx[P][8], vx[P][8];
+  bool ok[P];
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp) {
+    const int r = rg + RG * pp;
+    const int v = hidx[r < k ? r : k - 1];
+    ok[pp] = r < k && v >= 0 && (int64_t)v < n_rows;
+    const int64_t row = ok[pp] ? v : 0;          // skipped rows read row 0 and are masked
+    load8(kb + row * st, part, kx[pp]);
+    load8(vb + row * st, part, vx[pp]);
+  }
+  float sc[P];
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp) {
+    float d = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qv[e], kx[pp][e], d);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) d += __shfl_xor(d, off, 16);
+    sc[pp] = ok[pp] ? d * scale : -__builtin_inff();
+    m = fmaxf(m, sc[pp]);
+  }
+  for (int off = 32; off >= 16; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane == 0) s.red[wave] = m;
+  __syncthreads();
+  m = s.red[0];
+#pragma unroll
+  for (int w2 = 1; w2 < NW; ++w2) m = fmaxf(m, s.red[w2]);
+  __syncthreads();                               // s.red is reused for the sums
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  float ssum = 0.0f;
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp) {
+    const float pr = ok[pp] ? __expf(sc[pp] - m) : 0.0f;
+    ssum += pr;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(pr, vx[pp][e], acc[e]);
+  }
+  // the four row groups of the wave: every lane of a group holds the group's sum
+  for (int off = 16; off <= 32; off <<= 1) {
+    ssum += __shfl_xor(ssum, off, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+  }
+  if (lane == 0) s.red[wave] = ssum;
+  if (lane < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s.acc[wave][8 * part + e] = acc[e];
+  }
+  __syncthreads();
+  if (tid < D) {
+    float o = s.acc[0][tid], tot = s.red[0];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) { o += s.acc[w2][tid]; tot += s.red[w2]; }
+    const float res = (tot > 0.0f) ? o / tot : 0.0f;
+    if constexpr (sizeof(T) == 2) reinterpret_cast<uint16_t*>(out_head)[tid] = (uint16_t)f32_to_bf16_rne(res);
+    else out_head[tid] = res;
+  }
+}
+
 // T, MAXR, ATT: with ATT the workgroup goes on to attend over its head's k
 // rows (q, K, V and the output all of type T; MAXR rows per wave).
-template <int R, typename T, int MAXR, bool ATT>   // candidate slots per thread: n_sel <= R * RT_THREADS
+template <int R, typename T, int P, bool ATT>   // candidate slots per thread: n_sel <= R * RT_THREADS
 __global__ void __launch_bounds__(RT_THREADS)
 rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot_q,
                    int32_t* __restrict__ cand_idx, float* __restrict__ cand_est_out, int64_t n_cap, int n_sel,
@@ -1402,7 +1507,7 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
   __shared__ float s_est[R * RT_THREADS];
   __shared__ TopkShared<RT_THREADS> s_tk;
   __shared__ int32_t s_idx[ATT ? PK_MAX_TOPK_ATT : 1];
-  __shared__ AttShared<ATT ? RT_THREADS / 64 : 1> s_att;
+  __shared__ AttRowsShared<ATT ? RT_THREADS / 64 : 1> s_att;
 
   const int head = blockIdx.x, tid = threadIdx.x;
   const int seq = head / n_q_heads, qh = head - seq * n_q_heads;
@@ -1461,9 +1566,8 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
     const int kvh = qh / group;
     const T* kb = reinterpret_cast<const T*>(att.k) + seq * att.sb + kvh * att.sh;
     const T* vb = reinterpret_cast<const T*>(att.v) + seq * att.sb + kvh * att.sh;
-    attend_block<T, T, T, MAXR, RT_THREADS / 64>(reinterpret_cast<const T*>(att.q) + (int64_t)head * D, kb, vb, att.st,
-                                                 att.n_rows, s_idx, k, att.scale,
-                                                 reinterpret_cast<T*>(att.out) + (int64_t)head * D, s_att, tid);
+    attend_rows16<T, P>(reinterpret_cast<const T*>(att.q) + (int64_t)head * D, kb, vb, att.st, att.n_rows, s_idx,
+                        k, att.scale, reinterpret_cast<T*>(att.out) + (int64_t)head * D, s_att, tid);
   }
 }
 
@@ -1552,18 +1656,6 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
 constexpr int DA_THREADS = 1024;
 constexpr int DA_GROUPS = DA_THREADS / 16;     // rows per pass
 
-template <typename KT>
-__device__ __forceinline__ void load8(const KT* __restrict__ row, int part, float (&x)[8]) {
-  if constexpr (sizeof(KT) == 2) {
-    const uint4 v = reinterpret_cast<const uint4*>(row)[part];
-    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
-  } else {
-    const float4 a = reinterpret_cast<const float4*>(row)[2 * part];
-    const float4 b = reinterpret_cast<const float4*>(row)[2 * part + 1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  }
-}
 
 template <typename KT, typename QT, typename OT>
 __global__ void __launch_bounds__(DA_THREADS)
