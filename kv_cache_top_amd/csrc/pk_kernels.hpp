@@ -1648,13 +1648,14 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
 // One workgroup per query head.  Sixteen threads share a row, each holding 8
 // of its 128 dimensions (one 16-byte load of bf16, two of fp32), so a
 // workgroup covers DA_THREADS / 16 rows per pass with coalesced loads.  Rows
-// are the k retrieved rows, then the n_dense dense rows.  Scores: partial dot
-// products reduced over the 16 threads; one max and one sum over all scores;
-// then each thread accumulates its 8 dimensions over its rows and the row
-// groups are added in LDS.  fp32.
+// are the k retrieved rows, then the n_dense dense rows; a row's K and V are
+// loaded together.  Each row group keeps a running softmax over its rows
+// (max, sum, and its 8 dimensions of the weighted value sum); the groups are
+// rescaled to the workgroup max and added in LDS.  fp32.
 // ===========================================================================
 constexpr int DA_THREADS = 1024;
 constexpr int DA_GROUPS = DA_THREADS / 16;     // rows per pass
+constexpr int DA_UNROLL = 4;                   // passes whose rows are loaded together
 
 
 template <typename KT, typename QT, typename OT>
@@ -1662,7 +1663,6 @@ __global__ void __launch_bounds__(DA_THREADS)
 dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k, const KT* __restrict__ dk,
                            const KT* __restrict__ dv, int64_t dsb, int64_t dsh, int64_t dst, int n_dense,
                            int n_q_heads, int n_kv_heads, int group) {
-  __shared__ float s_p[PK_MAX_TOPK_ATT + PK_MAX_DENSE];   // scores, then probabilities
   __shared__ int32_t s_ix[PK_MAX_TOPK_ATT];                // retrieved rows (-1: skipped)
   __shared__ float s_red[DA_THREADS / 64];
   __shared__ float s_acc[DA_GROUPS][D + 4];
@@ -1701,48 +1701,66 @@ dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k,
     return;
   }
 
-  // scores (invalid retrieved rows: -inf); rows past the end re-read the last one
-  float m = -__builtin_inff();
-#pragma unroll 2
-  for (int r0 = 0; r0 < total; r0 += DA_GROUPS) {
-    const int r = r0 + rg;
-    const int rr = r < total ? r : total - 1;
-    bool ok = true;
-    const KT* row;
-    if (rr < kz) {
-      const int ix = s_ix[rr];
-      ok = ix >= 0;
-      row = kb + (int64_t)(ok ? ix : 0) * a.st;
-    } else {
-      row = dkb + (int64_t)(rr - kz) * dst;
+  // one pass over the rows: each row group keeps a running max, sum and
+  // weighted value sum of its rows (invalid retrieved rows and rows past the
+  // end are skipped; they re-read a valid row)
+  float m = -__builtin_inff(), l = 0.0f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int r0 = 0; r0 < total; r0 += DA_UNROLL * DA_GROUPS) {   // uniform
+    float x[DA_UNROLL][8], y[DA_UNROLL][8];
+    bool ok[DA_UNROLL];
+#pragma unroll
+    for (int u = 0; u < DA_UNROLL; ++u) {         // every row's K and V in flight first
+      const int r = r0 + u * DA_GROUPS + rg;
+      const int rr = r < total ? r : total - 1;
+      ok[u] = r < total;
+      const KT* krow;
+      const KT* vrow;
+      if (rr < kz) {
+        const int ix = s_ix[rr];
+        ok[u] = ok[u] && ix >= 0;
+        krow = kb + (int64_t)(ix >= 0 ? ix : 0) * a.st;
+        vrow = vb + (int64_t)(ix >= 0 ? ix : 0) * a.st;
+      } else {
+        krow = dkb + (int64_t)(rr - kz) * dst;
+        vrow = dvb + (int64_t)(rr - kz) * dst;
+      }
+      load8(krow, part, x[u]);
+      load8(vrow, part, y[u]);
     }
-    float x[8];
-    load8(row, part, x);
-    float p = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p = __builtin_fmaf(qv[e], x[e], p);
+    for (int u = 0; u < DA_UNROLL; ++u) {
+      float d = 0.0f;
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) p += __shfl_xor(p, off, 16);
-    const float sc = ok ? p * a.scale : -__builtin_inff();
-    if (r < total) {
-      if (part == 0) s_p[r] = sc;
-      m = fmaxf(m, sc);
+      for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qv[e], x[u][e], d);
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) d += __shfl_xor(d, off, 16);
+      if (ok[u]) {                                // uniform over the row group
+        const float sc = d * a.scale;
+        const float mn = fmaxf(m, sc);
+        const float f = __expf(m - mn);           // m = -inf: 0
+        const float pr = __expf(sc - mn);
+        l = l * f + pr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(pr, y[u][e], acc[e] * f);
+        m = mn;
+      }
     }
   }
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if (lane == 0) s_red[wave] = m;
+  // workgroup max of the group maxima, then rescale each group's sums to it
+  float mw = m;
+  for (int off = 32; off >= 16; off >>= 1) mw = fmaxf(mw, __shfl_xor(mw, off, 64));
+  if (lane == 0) s_red[wave] = mw;
   __syncthreads();
-  m = s_red[0];
+  float M = s_red[0];
 #pragma unroll
-  for (int w2 = 1; w2 < DA_THREADS / 64; ++w2) m = fmaxf(m, s_red[w2]);
-  __syncthreads();
-  float ssum = 0.0f;
-  for (int r = tid; r < total; r += DA_THREADS) {
-    const float sc = s_p[r];
-    const float p = (sc == -__builtin_inff()) ? 0.0f : __expf(sc - m);
-    s_p[r] = p;
-    ssum += p;
-  }
+  for (int w2 = 1; w2 < DA_THREADS / 64; ++w2) M = fmaxf(M, s_red[w2]);
+  __syncthreads();                                // s_red is reused for the sums
+  const float f = (m == -__builtin_inff()) ? 0.0f : __expf(m - M);
+  float ssum = (part == 0) ? l * f : 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] *= f;
   for (int off = 32; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, 64);
   if (lane == 0) s_red[wave] = ssum;
   __syncthreads();
@@ -1750,27 +1768,6 @@ dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k,
 #pragma unroll
   for (int w2 = 0; w2 < DA_THREADS / 64; ++w2) ssum += s_red[w2];
 
-  // weighted sum of the value rows
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-#pragma unroll 2
-  for (int r0 = 0; r0 < total; r0 += DA_GROUPS) {
-    const int r = r0 + rg;
-    const int rr = r < total ? r : total - 1;
-    const float p = r < total ? s_p[rr] : 0.0f;
-    const KT* row;
-    if (rr < kz) {
-      const int ix = s_ix[rr];
-      row = vb + (int64_t)(ix >= 0 ? ix : 0) * a.st;
-    } else {
-      row = dvb + (int64_t)(rr - kz) * dst;
-    }
-    float x[8];
-    load8(row, part, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(p, x[e], acc[e]);
-  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) s_acc[rg][8 * part + e] = acc[e];
   __syncthreads();
