@@ -587,15 +587,14 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
     if ((st = check_launch(ctx, "rerank")) != PK_OK) return st;
     {
       Launch L(ctx, PK_KERNEL_TOPK, stream);
-      const int R = (n_sel + 255) / 256;
+      const int R = (n_sel + pk::TK_THREADS - 1) / pk::TK_THREADS;
 #define PK_TOPK(RR)                                                                                      \
-  hipLaunchKernelGGL(pk::topk_kernel<RR>, dim3(ctx->qheads), dim3(256), 0, stream, ctx->cand_idx, ctx->cand_est, \
-                     n_sel, C, k, topk_idx, topk_est)
-      if (R <= 4) PK_TOPK(4);
+  hipLaunchKernelGGL(pk::topk_kernel<RR>, dim3(ctx->qheads), dim3(pk::TK_THREADS), 0, stream, ctx->cand_idx,     \
+                     ctx->cand_est, n_sel, C, k, topk_idx, topk_est)
+      if (R <= 2) PK_TOPK(2);
+      else if (R <= 4) PK_TOPK(4);
       else if (R <= 8) PK_TOPK(8);
-      else if (R <= 16) PK_TOPK(16);
-      else if (R <= 32) PK_TOPK(32);
-      else PK_TOPK(64);
+      else PK_TOPK(16);
 #undef PK_TOPK
     }
     if ((st = check_launch(ctx, "topk")) != PK_OK) return st;

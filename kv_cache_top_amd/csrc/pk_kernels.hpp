@@ -1609,11 +1609,13 @@ rerank_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot
   }
 }
 
+constexpr int TK_THREADS = 1024;     // top-k workgroup (few heads, many candidates)
+
 template <int R>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(TK_THREADS)
 topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_sel,
             int n_candidates, int k, int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
-  __shared__ TopkShared<256> s_tk;
+  __shared__ TopkShared<TK_THREADS> s_tk;
   const int head = blockIdx.x, tid = threadIdx.x;
   int32_t* ci = cand_idx + (int64_t)head * n_candidates;
   float* ce = cand_est + (int64_t)head * n_candidates;
@@ -1623,19 +1625,19 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
   const int plast = n_sel > 0 ? n_sel - 1 : 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int p = r * 256 + tid;
+    const int p = r * TK_THREADS + tid;
     ev[r] = ce[p < plast ? p : plast];
     kix[r] = ci[p < plast ? p : plast];
   }
   if (tid < 8) s_tk.misc[tid] = 0;
-  for (int p = n_sel + tid; p < n_candidates; p += 256) {   // invalid tail slots (n < C)
+  for (int p = n_sel + tid; p < n_candidates; p += TK_THREADS) {   // invalid tail slots (n < C)
     ci[p] = -1;
     ce[p] = -__builtin_inff();
   }
   uint32_t key[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) key[r] = orderable(ev[r]);
-  topk_block<R, 256>(key, kix, n_sel, k, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
+  topk_block<R, TK_THREADS>(key, kix, n_sel, k, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
                      s_tk, tid);
 }
 
