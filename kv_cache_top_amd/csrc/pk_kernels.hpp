@@ -463,7 +463,7 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
 // 0 is implied by the sub-tile length.  Each lane keeps COLLIDE_UNROLL code
 // loads in flight.
 // ===========================================================================
-constexpr int COLLIDE_UNROLL = 8;
+constexpr int COLLIDE_UNROLL = 4;
 constexpr int HIST_LANES = 32;
 
 // (unit, tile) of workgroup i of a units x tiles grid.  Workgroups are dealt
