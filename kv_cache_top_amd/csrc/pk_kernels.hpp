@@ -367,7 +367,7 @@ __device__ __forceinline__ void percentile_tiers(const uint32_t (&key)[4], const
   }
 }
 
-constexpr int QP_WAVES = 4;
+constexpr int QP_WAVES = 2;
 constexpr int QP_PARTS = NSUB / QP_WAVES;   // workgroups per query head
 
 template <typename QT>
