@@ -1219,11 +1219,44 @@ struct TopkShared {
   uint32_t wsum[NT / 64];
 };
 
+// Range statistics of a thread's estimate keys (largest, smallest, smallest
+// non-negative, count of non-negative), for topk_block.
+constexpr uint32_t TOPK_POS = 0x80000000u;      // keys of estimates >= 0 have the top bit set
+
+struct TopkStats {
+  uint32_t kmax = 0, kmin = 0xFFFFFFFFu, kminp = 0xFFFFFFFFu, npos = 0;
+  __device__ __forceinline__ void add(uint32_t key) {
+    kmax = key > kmax ? key : kmax;
+    kmin = key < kmin ? key : kmin;
+    if (key >= TOPK_POS) {
+      kminp = key < kminp ? key : kminp;
+      ++npos;
+    }
+  }
+};
+
+// reduces the statistics over the wave; lane 0 leaves them in s for
+// topk_block (a barrier must come between)
+template <int NT>
+__device__ __forceinline__ void topk_stats_wave(TopkStats st, TopkShared<NT>& s, int lane, int wave) {
+  constexpr int NW = NT / 64;
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t a = __shfl_xor(st.kmax, off, 64), c = __shfl_xor(st.kmin, off, 64);
+    const uint32_t cp = __shfl_xor(st.kminp, off, 64), np = __shfl_xor(st.npos, off, 64);
+    st.kmax = a > st.kmax ? a : st.kmax;
+    st.kmin = c < st.kmin ? c : st.kmin;
+    st.kminp = cp < st.kminp ? cp : st.kminp;
+    st.npos += np;
+  }
+  if (lane == 0) { s.wsum[wave] = st.kmax; s.h[wave] = st.kmin; s.h[NW + wave] = st.kminp; s.h[2 * NW + wave] = st.npos; }
+}
+
 // Top-k of one head's n_sel candidates; thread tid holds slots r * NT + tid
 // as order-preserving estimate keys key[r] and the slots' key indices kix[r].
 // Slots are in ascending key order, so slot order breaks ties as the key index
-// does.  s.misc must be zero on entry.
-template <int R, int NT>
+// does.  s.misc must be zero on entry.  With PRE the caller has already left
+// the waves' range statistics in s (topk_stats_wave, then a barrier).
+template <int R, int NT, bool PRE = false>
 __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], int n_sel, int k, int32_t* out_idx,
                            float* out_est, TopkShared<NT>& s, int tid, int32_t* lds_idx = nullptr) {
   constexpr int NW = NT / 64;
@@ -1233,28 +1266,15 @@ __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], in
   // start at the highest bit where the largest and smallest keys differ.
   // When at least k estimates are >= 0 (keys with the top bit set), the
   // negative ones cannot win and the range starts at the smallest such key.
-  constexpr uint32_t POS = 0x80000000u;
-  uint32_t kmax = 0, kmin = 0xFFFFFFFFu, kminp = 0xFFFFFFFFu, npos = 0;
+  if constexpr (!PRE) {
+    TopkStats st;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const bool ok = r * NT + tid < n_sel;
-    kmax = ok && key[r] > kmax ? key[r] : kmax;
-    kmin = ok && key[r] < kmin ? key[r] : kmin;
-    const bool pos = ok && key[r] >= POS;
-    kminp = pos && key[r] < kminp ? key[r] : kminp;
-    npos += pos ? 1u : 0u;
+    for (int r = 0; r < R; ++r)
+      if (r * NT + tid < n_sel) st.add(key[r]);
+    topk_stats_wave<NT>(st, s, lane, wave);
+    __syncthreads();
   }
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t a = __shfl_xor(kmax, off, 64), c = __shfl_xor(kmin, off, 64);
-    const uint32_t cp = __shfl_xor(kminp, off, 64), np = __shfl_xor(npos, off, 64);
-    kmax = a > kmax ? a : kmax;
-    kmin = c < kmin ? c : kmin;
-    kminp = cp < kminp ? cp : kminp;
-    npos += np;
-  }
-  if (lane == 0) { s.wsum[wave] = kmax; s.h[wave] = kmin; s.h[NW + wave] = kminp; s.h[2 * NW + wave] = npos; }
-  __syncthreads();
-  npos = 0;
+  uint32_t kmax = 0, kmin = 0xFFFFFFFFu, kminp = 0xFFFFFFFFu, npos = 0;
   for (int w2 = 0; w2 < NW; ++w2) {
     kmax = s.wsum[w2] > kmax ? s.wsum[w2] : kmax;
     kmin = s.h[w2] < kmin ? s.h[w2] : kmin;
@@ -1262,7 +1282,7 @@ __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], in
     npos += s.h[2 * NW + w2];
   }
   int m = n_sel;
-  if (kmin < POS && npos >= (uint32_t)keff && keff > 0) {   // uniform
+  if (kmin < TOPK_POS && npos >= (uint32_t)keff && keff > 0) {   // uniform
     kmin = kminp;
     m = (int)npos;
   }
@@ -1535,6 +1555,7 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
     if (ce) ce[p] = -__builtin_inff();
   }
   __syncthreads();
+  TopkStats st;
 #pragma unroll 1
   for (int r = 0; r < rounds; ++r) {
     const int p = r * RT_THREADS + tid;
@@ -1544,6 +1565,7 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
     }
     const float est = rerank_eval(ra, s_T);
     s_est[p] = est;
+    if (p < n_sel) st.add(orderable(est));
     if (ce && p < n_sel) ce[p] = est;
   }
   int32_t kix[R];                   // the slots' key indices (L2), in flight during the first top-k steps
@@ -1552,6 +1574,7 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
     const int p = r * RT_THREADS + tid;
     kix[r] = ci[p < plast ? p : plast];
   }
+  topk_stats_wave<RT_THREADS>(st, s_tk, tid & 63, tid >> 6);
   __syncthreads();
   uint32_t key[R];
 #pragma unroll
@@ -1559,7 +1582,7 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
     const int p = r * RT_THREADS + tid;
     key[r] = orderable(s_est[p < plast ? p : plast]);
   }
-  topk_block<R, RT_THREADS>(key, kix, n_sel, k, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
+  topk_block<R, RT_THREADS, true>(key, kix, n_sel, k, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
                             s_tk, tid, ATT ? s_idx : nullptr);
   if constexpr (ATT) {
     __syncthreads();
