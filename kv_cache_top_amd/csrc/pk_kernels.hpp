@@ -1217,7 +1217,16 @@ struct TopkShared {
   uint64_t f[PK_SORT_N];
   int misc[8];
   uint32_t wsum[NT / 64];
+  uint32_t stat[3][NT / 64];
 };
+
+// zeroes what topk_block expects zeroed on entry (a barrier must follow)
+template <int NT>
+__device__ __forceinline__ void topk_shared_init(TopkShared<NT>& s, int tid) {
+  uint4* h4 = reinterpret_cast<uint4*>(s.h);
+  for (int i = tid; i < TOPK_BINS / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < 8) s.misc[tid] = 0;
+}
 
 // Range statistics of a thread's estimate keys (largest, smallest, smallest
 // non-negative, count of non-negative), for topk_block.
@@ -1248,13 +1257,14 @@ __device__ __forceinline__ void topk_stats_wave(TopkStats st, TopkShared<NT>& s,
     st.kminp = cp < st.kminp ? cp : st.kminp;
     st.npos += np;
   }
-  if (lane == 0) { s.wsum[wave] = st.kmax; s.h[wave] = st.kmin; s.h[NW + wave] = st.kminp; s.h[2 * NW + wave] = st.npos; }
+  if (lane == 0) { s.wsum[wave] = st.kmax; s.stat[0][wave] = st.kmin; s.stat[1][wave] = st.kminp; s.stat[2][wave] = st.npos; }
 }
 
 // Top-k of one head's n_sel candidates; thread tid holds slots r * NT + tid
 // as order-preserving estimate keys key[r] and the slots' key indices kix[r].
 // Slots are in ascending key order, so slot order breaks ties as the key index
-// does.  s.misc must be zero on entry.  With PRE the caller has already left
+// does.  s.misc and s.h must be zero on entry (topk_shared_init).  With PRE
+// the caller has already left
 // the waves' range statistics in s (topk_stats_wave, then a barrier).
 template <int R, int NT, bool PRE = false>
 __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], int n_sel, int k, int32_t* out_idx,
@@ -1277,9 +1287,9 @@ __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], in
   uint32_t kmax = 0, kmin = 0xFFFFFFFFu, kminp = 0xFFFFFFFFu, npos = 0;
   for (int w2 = 0; w2 < NW; ++w2) {
     kmax = s.wsum[w2] > kmax ? s.wsum[w2] : kmax;
-    kmin = s.h[w2] < kmin ? s.h[w2] : kmin;
-    kminp = s.h[NW + w2] < kminp ? s.h[NW + w2] : kminp;
-    npos += s.h[2 * NW + w2];
+    kmin = s.stat[0][w2] < kmin ? s.stat[0][w2] : kmin;
+    kminp = s.stat[1][w2] < kminp ? s.stat[1][w2] : kminp;
+    npos += s.stat[2][w2];
   }
   int m = n_sel;
   if (kmin < TOPK_POS && npos >= (uint32_t)keff && keff > 0) {   // uniform
@@ -1296,9 +1306,6 @@ __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], in
   while (keff > 0 && top >= 0 && m > TOPK_MAXB) {        // uniform
     const int shift = top >= 11 ? top - 11 : 0;
     const uint32_t dmask = (top - shift == 31) ? 0xFFFFFFFFu : ((2u << (top - shift)) - 1u);
-    __syncthreads();
-    for (int i = tid; i < TOPK_BINS; i += NT) s.h[i] = 0;
-    __syncthreads();
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (r * NT + tid < n_sel && (key[r] & pmask) == prefix) atomicAdd(&s.h[(key[r] >> shift) & dmask], 1u);
@@ -1336,6 +1343,11 @@ __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], in
     prefix |= (uint32_t)s.misc[0] << shift;
     pmask |= dmask << shift;
     top = shift - 1;
+    if (keff > 0 && top >= 0 && m > TOPK_MAXB) {  // another pass: a zeroed histogram
+      uint4* h4 = reinterpret_cast<uint4*>(s.h);
+      for (int i = tid; i < TOPK_BINS / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+      __syncthreads();
+    }
   }
   __syncthreads();
 
@@ -1549,7 +1561,7 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
     ixn = ci[RT_THREADS + tid < plast ? RT_THREADS + tid : plast];
   }
   rerank_table<RT_THREADS>(s_T, rqv, tb, tid);
-  if (tid < 8) s_tk.misc[tid] = 0;
+  topk_shared_init<RT_THREADS>(s_tk, tid);
   for (int p = n_sel + tid; p < n_candidates; p += RT_THREADS) {   // invalid tail slots (n < C)
     ci[p] = -1;
     if (ce) ce[p] = -__builtin_inff();
@@ -1652,7 +1664,7 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
     ev[r] = ce[p < plast ? p : plast];
     kix[r] = ci[p < plast ? p : plast];
   }
-  if (tid < 8) s_tk.misc[tid] = 0;
+  topk_shared_init<TK_THREADS>(s_tk, tid);
   for (int p = n_sel + tid; p < n_candidates; p += TK_THREADS) {   // invalid tail slots (n < C)
     ci[p] = -1;
     ce[p] = -__builtin_inff();
