@@ -270,23 +270,40 @@ encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
 // key key[r]): the centroids ranked r < tiers.top[last] by (score desc, c asc)
 // are found with a bitwise threshold search over the score keys, then ranked
 // among themselves; each gets its tier weight in lw[c].
-__device__ __forceinline__ void rank_tiers(const uint32_t (&key)[4], const TierSpec& tiers, uint2* sel, uint8_t* lw,
-                                           int lane) {
+__device__ __forceinline__ void rank_tiers(const uint32_t (&key)[4], const TierSpec& tiers, uint64_t* sel,
+                                           uint8_t* lw, int lane) {
   const int T = tiers.top[tiers.n_tiers - 1];
-  // threshold key: the T-th largest score key among the 256 centroids
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
+  auto count_ge = [&](uint32_t x) {
     int cnt = 0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) cnt += __popcll(__ballot(key[r] >= cand));
-    if (cnt >= T) thr = cand;
+    for (int r = 0; r < 4; ++r) cnt += __popcll(__ballot(key[r] >= x));
+    return cnt;
+  };
+  // threshold key: the T-th largest score key among the 256 centroids, the
+  // largest x with at least T keys >= x, built from the top bit down.  When
+  // at least T keys share the sign and exponent bits of the largest key, the
+  // threshold shares them too and the search starts below them.
+  uint32_t kmax = key[0] > key[1] ? key[0] : key[1];
+  kmax = kmax > key[2] ? kmax : key[2];
+  kmax = kmax > key[3] ? kmax : key[3];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)kmax, off, 64);
+    kmax = kmax > o ? kmax : o;
+  }
+  const uint32_t top9 = kmax & 0xFF800000u;
+  const bool skip = count_ge(top9) >= T;
+  uint32_t thr = skip ? top9 : 0u;
+  for (int bit = skip ? 22 : 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    if (count_ge(cand) >= T) thr = cand;
   }
   int n_gt = 0;
 #pragma unroll
   for (int r = 0; r < 4; ++r) n_gt += __popcll(__ballot(key[r] > thr));
   const int need_eq = T - n_gt;
-  // compact the T selected centroids (ties at thr: lowest centroid index first)
+  // compact the T selected centroids (ties at thr: lowest centroid index
+  // first) as (score key << 32 | 255 - c): the larger value ranks first
   int eq_before = 0, sel_before = 0;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -294,26 +311,24 @@ __device__ __forceinline__ void rank_tiers(const uint32_t (&key)[4], const TierS
     const int eqrank = eq_before + (int)mbcnt(eqm);
     const bool sl = key[r] > thr || (key[r] == thr && eqrank < need_eq);
     const uint64_t sm = __ballot(sl);
-    if (sl) sel[sel_before + (int)mbcnt(sm)] = make_uint2(key[r], lane + 64 * r);
+    if (sl) sel[sel_before + (int)mbcnt(sm)] = ((uint64_t)key[r] << 32) | (uint64_t)(255 - (lane + 64 * r));
     eq_before += __popcll(eqm);
     sel_before += __popcll(sm);
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  // rank of each selected centroid by (score desc, centroid asc); tier weight
+  // rank of each selected centroid = how many selected ones rank before it
+  // (all packed values differ); tier weight by rank
   for (int j = lane; j < T; j += 64) {
-    const uint2 e = sel[j];
+    const uint64_t e = sel[j];
     int rank = 0;
-#pragma unroll 8
-    for (int j2 = 0; j2 < T; ++j2) {
-      const uint2 o = sel[j2];
-      rank += (o.x > e.x || (o.x == e.x && o.y < e.y)) ? 1 : 0;
-    }
+#pragma unroll 16
+    for (int j2 = 0; j2 < T; ++j2) rank += (sel[j2] > e) ? 1 : 0;
     uint32_t wgt = 0;
     for (int tt = 0; tt < tiers.n_tiers; ++tt) {
       if (rank < tiers.top[tt]) { wgt = (uint32_t)tiers.weight[tt]; break; }
     }
-    lw[e.y] = (uint8_t)wgt;
+    lw[255 - (int)(e & 0xFFu)] = (uint8_t)wgt;
   }
 }
 
@@ -376,7 +391,7 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
              float* __restrict__ rot_q, uint8_t* __restrict__ lut_bytes, Tables tb,
              TierSpec tiers, const uint32_t* __restrict__ counts, uint32_t keep_m) {
   __shared__ float y[D];
-  __shared__ uint2 sel[QP_WAVES][256];      // (score key, centroid) of the selected centroids
+  __shared__ uint64_t sel[QP_WAVES][256];   // (score key, 255 - centroid) of the selected centroids
   __shared__ uint8_t lw[QP_WAVES][256];     // tier weight per centroid
 
   const int head = blockIdx.x / QP_PARTS;   // sequence * n_q_heads + query head
