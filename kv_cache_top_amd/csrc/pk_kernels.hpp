@@ -291,10 +291,17 @@ __device__ __forceinline__ void rank_tiers(const uint32_t (&key)[4], const TierS
     const uint32_t o = (uint32_t)__shfl_xor((int)kmax, off, 64);
     kmax = kmax > o ? kmax : o;
   }
-  const uint32_t top9 = kmax & 0xFF800000u;
-  const bool skip = count_ge(top9) >= T;
-  uint32_t thr = skip ? top9 : 0u;
-  for (int bit = skip ? 22 : 31; bit >= 0; --bit) {
+  const uint32_t top9 = (uint32_t)__builtin_amdgcn_readfirstlane((int)kmax) & 0xFF800000u;   // wave-uniform
+  uint32_t thr = top9;
+  if (count_ge(top9) < T) {
+    thr = 0;
+    for (int bit = 31; bit >= 23; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      if (count_ge(cand) >= T) thr = cand;
+    }
+  }
+#pragma unroll
+  for (int bit = 22; bit >= 0; --bit) {
     const uint32_t cand = thr | (1u << bit);
     if (count_ge(cand) >= T) thr = cand;
   }
