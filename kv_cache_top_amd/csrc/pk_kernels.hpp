@@ -92,6 +92,44 @@ __device__ __forceinline__ uint32_t mbcnt(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// ---- cross-lane moves without LDS -------------------------------------------
+// swap32_sum(a, b): lanes 32..63 of a trade places with lanes 0..31 of b
+// (v_permlane32_swap), then the two are added, so lane l < 32 gets a + a of
+// lane l + 32 and lane l >= 32 gets b + b of lane l - 32.  swap16_sum does the
+// same between the odd 16-lane rows of a and the even rows of b (partner l ^ 16).
+__device__ __forceinline__ uint32_t swap32_sum(uint32_t a, uint32_t b) {
+  const auto t = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return t[0] + t[1];
+}
+__device__ __forceinline__ uint32_t swap16_sum(uint32_t a, uint32_t b) {
+  const auto t = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  return t[0] + t[1];
+}
+// x of lane l ^ W for W = 1, 2, 4, 8 (DPP: quad permutations, half-row mirror, row rotate)
+template <int W>
+__device__ __forceinline__ uint32_t dpp_xor(uint32_t x) {
+  if constexpr (W == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  else if constexpr (W == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  else if constexpr (W == 4) {
+    const int m = __builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);   // row_half_mirror: l -> 7 - l
+    return (uint32_t)__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false);      // quad_perm 3,2,1,0
+  } else {
+    static_assert(W == 8, "W is 1, 2, 4 or 8");
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);  // row_ror 8
+  }
+}
+// inclusive prefix sum over the 64 lanes (lane l: lanes 0..l): shifts by 1, 2,
+// 4, 8 inside each 16-lane row, then row totals carried upward
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr 1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr 2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr 4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr 8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast 15 -> rows 1, 3
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast 31 -> rows 2, 3
+  return x;
+}
+
 // ===========================================================================
 // encode: key summaries (Slides Eqs. (5)-(9); README "1. Prefill")
 //
@@ -806,6 +844,18 @@ __device__ __forceinline__ void hist_row_load(const uint32_t* __restrict__ uh, i
   }
 }
 
+// one stage of the reduce-scatter below, width W <= 8 (DPP partner lane ^ W)
+template <int W>
+__device__ __forceinline__ void reduce_scatter_stage(uint32_t (&v)[64], int lane) {
+  const bool up = (lane & W) != 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const uint32_t send = up ? v[i] : v[i + W];
+    const uint32_t keep = up ? v[i + W] : v[i];
+    v[i] = keep + dpp_xor<W>(send);
+  }
+}
+
 __device__ __forceinline__ void select_params_wave(const uint32_t (&h)[64], int64_t n, int subs, int sub_len,
                                                    int tl, int g, int n_candidates, int lane, int2* s_par,
                                                    int2 (*s_base)[MAXG]) {
@@ -813,31 +863,29 @@ __device__ __forceinline__ void select_params_wave(const uint32_t (&h)[64], int6
 #pragma unroll
   for (int i = 0; i < 64; ++i) v[i] = h[i];
   // after the stage of width w, v[i] (i < w) of lane l is the sum, over the
-  // 64 / w lanes that share l's bits below w, of bin i + (l & (64 - w))
+  // 64 / w lanes that share l's bits below w, of bin i + (l & (64 - w));
+  // widths 32 and 16 trade register halves between lane halves / rows
 #pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) {
-    const bool up = (lane & w) != 0;
+  for (int i = 0; i < 32; ++i) v[i] = swap32_sum(v[i], v[i + 32]);
 #pragma unroll
-    for (int i = 0; i < w; ++i) {
-      const uint32_t send = up ? v[i] : v[i + w];
-      const uint32_t keep = up ? v[i + w] : v[i];
-      v[i] = keep + (uint32_t)__shfl_xor((int)send, w, 64);
-    }
-  }
+  for (int i = 0; i < 16; ++i) v[i] = swap16_sum(v[i], v[i + 16]);
+  reduce_scatter_stage<8>(v, lane);
+  reduce_scatter_stage<4>(v, lane);
+  reduce_scatter_stage<2>(v, lane);
+  reduce_scatter_stage<1>(v, lane);
   const uint32_t tot = v[0];
   // suffix counts: suf at lane l = #{S >= l + 1}; theta = the highest bin
   // whose suffix reaches C (0: every key is taken)
-  uint32_t suf = tot;
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_down(suf, off, 64);
-    if (lane + off < 64) suf += o;
-  }
+  const uint32_t incl = wave_incl_scan(tot);
+  const uint32_t all_nz = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  const uint32_t suf = all_nz - incl + tot;
   const uint64_t ge = __ballot(suf >= (uint32_t)n_candidates);
   const int top = ge ? 63 - __builtin_clzll(ge) : -1;
   const int theta = top + 1;
-  const uint32_t all_nz = __shfl(suf, 0, 64);
-  const uint32_t n_gt = (top < 0) ? all_nz : (top == 63 ? 0u : (uint32_t)__shfl(suf, (top + 1) & 63, 64));
-  const uint32_t eq_tot = (theta > 0) ? (uint32_t)__shfl(tot, (theta - 1) & 63, 64) : (uint32_t)(n - n_gt);
+  const uint32_t n_gt = (top < 0) ? all_nz
+                        : (top == 63 ? 0u : (uint32_t)__builtin_amdgcn_readlane((int)suf, (top + 1) & 63));
+  const uint32_t eq_tot = (theta > 0) ? (uint32_t)__builtin_amdgcn_readlane((int)tot, (theta - 1) & 63)
+                                      : (uint32_t)(n - n_gt);
   const uint32_t want = (uint32_t)n_candidates - n_gt;
   const uint32_t need_eq = want < eq_tot ? want : eq_tot;
   // this lane's sub-tile: keys above / at theta, then exclusive prefixes
@@ -853,11 +901,7 @@ __device__ __forceinline__ void select_params_wave(const uint32_t (&h)[64], int6
   len = len < 0 ? 0 : (len > sub_len ? sub_len : len);
   if (theta == 0) eq = (int)len - nz;
   if (lane >= subs) { gt = 0; eq = 0; }
-  int pg = gt, pe = eq;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int og = __shfl_up(pg, off, 64), oe = __shfl_up(pe, off, 64);
-    if (lane >= off) { pg += og; pe += oe; }
-  }
+  const int pg = (int)wave_incl_scan((uint32_t)gt), pe = (int)wave_incl_scan((uint32_t)eq);
   const int w = lane - 4 * tl;
   if (w >= 0 && w < 4) s_base[w][g] = make_int2(pg - gt, pe - eq);
   if (lane == 0) s_par[g] = make_int2(theta, (int)need_eq);
