@@ -129,6 +129,55 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast 31 -> rows 2, 3
   return x;
 }
+// x of lane l ^ W for W = 1 .. 32: DPP inside a 16-lane row, the lane-half
+// swaps across rows (W = 16) and halves (W = 32).  Every lane must be active.
+template <int W>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
+  if constexpr (W <= 8) {
+    return dpp_xor<W>(x);
+  } else if constexpr (W == 16) {
+    const auto t = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? t[0] : t[1];
+  } else {
+    static_assert(W == 32, "W is a power of two up to 32");
+    const auto t = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? t[0] : t[1];
+  }
+}
+template <int W>
+__device__ __forceinline__ float lane_xor_f(float x, int lane) {
+  return __uint_as_float(lane_xor<W>(__float_as_uint(x), lane));
+}
+// x = op(x, x of lane l ^ w) for w = 32, 16, 8, 4, 2, 1 in turn (the whole
+// wave), or for w = 8, 4, 2, 1 (each 16-lane row); written out, since loops
+// around these convergent moves are not unrolled
+template <typename Op>
+__device__ __forceinline__ float xor_butterfly16(float x, int lane, Op op) {
+  x = op(x, lane_xor_f<8>(x, lane));
+  x = op(x, lane_xor_f<4>(x, lane));
+  x = op(x, lane_xor_f<2>(x, lane));
+  return op(x, lane_xor_f<1>(x, lane));
+}
+template <typename Op>
+__device__ __forceinline__ float xor_butterfly(float x, int lane, Op op) {
+  x = op(x, lane_xor_f<32>(x, lane));
+  x = op(x, lane_xor_f<16>(x, lane));
+  return xor_butterfly16(x, lane, op);
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t xor_butterfly_u(uint32_t x, int lane, Op op) {
+  x = op(x, lane_xor<32>(x, lane));
+  x = op(x, lane_xor<16>(x, lane));
+  x = op(x, lane_xor<8>(x, lane));
+  x = op(x, lane_xor<4>(x, lane));
+  x = op(x, lane_xor<2>(x, lane));
+  return op(x, lane_xor<1>(x, lane));
+}
+struct AddF { __device__ float operator()(float a, float b) const { return a + b; } };
+struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct MaxU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
+struct MinU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+struct AddU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
 
 // ===========================================================================
 // encode: key summaries (Slides Eqs. (5)-(9); README "1. Prefill")
@@ -324,11 +373,7 @@ __device__ __forceinline__ void rank_tiers(const uint32_t (&key)[4], const TierS
   uint32_t kmax = key[0] > key[1] ? key[0] : key[1];
   kmax = kmax > key[2] ? kmax : key[2];
   kmax = kmax > key[3] ? kmax : key[3];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t o = (uint32_t)__shfl_xor((int)kmax, off, 64);
-    kmax = kmax > o ? kmax : o;
-  }
+  kmax = xor_butterfly_u(kmax, lane, MaxU());
   const uint32_t top9 = (uint32_t)__builtin_amdgcn_readfirstlane((int)kmax) & 0xFF800000u;   // wave-uniform
   uint32_t thr = top9;
   if (count_ge(top9) < T) {
@@ -377,6 +422,43 @@ __device__ __forceinline__ void rank_tiers(const uint32_t (&key)[4], const TierS
   }
 }
 
+// Bitonic sort, descending, of 256 values over a wave: position x = 4 lane + r
+// holds v[r].  Stage (K, J) compare-exchanges positions x and x ^ J (in the
+// lane for J < 4, else with lane l ^ J / 4); blocks of K with (x & K) == 0
+// keep the larger value at the lower position.
+template <int K, int J>
+__device__ __forceinline__ void bitonic_step(uint64_t (&v)[4], int lane) {
+  uint64_t pv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (J >= 4) {
+      pv[r] = ((uint64_t)lane_xor<J / 4>((uint32_t)(v[r] >> 32), lane) << 32) |
+              (uint64_t)lane_xor<J / 4>((uint32_t)v[r], lane);
+    } else {
+      pv[r] = v[r ^ J];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int x = 4 * lane + r;
+    const bool desc_block = (x & K) == 0;
+    const bool lower = (x & J) == 0;
+    const uint64_t hi = v[r] > pv[r] ? v[r] : pv[r];
+    const uint64_t lo = v[r] > pv[r] ? pv[r] : v[r];
+    v[r] = (lower == desc_block) ? hi : lo;
+  }
+}
+template <int K, int J>
+__device__ __forceinline__ void bitonic_j(uint64_t (&v)[4], int lane) {
+  bitonic_step<K, J>(v, lane);
+  if constexpr (J > 1) bitonic_j<K, J / 2>(v, lane);
+}
+template <int K>
+__device__ __forceinline__ void bitonic_k(uint64_t (&v)[4], int lane) {
+  bitonic_j<K, K / 2>(v, lane);
+  if constexpr (K < 256) bitonic_k<K * 2>(v, lane);
+}
+
 // Percentile tiers of one subspace (Slides Sec. 4.2.2, Eq. (15)): the 256
 // centroids are sorted by (score desc, c asc) with a bitonic network over the
 // wave (position x = 4 lane + r), their key counts are prefix-summed in that
@@ -387,24 +469,7 @@ __device__ __forceinline__ void percentile_tiers(const uint32_t (&key)[4], const
   uint64_t v[4];                                  // (score key, 255 - c): larger = earlier
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = ((uint64_t)key[r] << 8) | (uint64_t)(255u - (uint32_t)(lane + 64 * r));
-#pragma unroll
-  for (int k = 2; k <= 256; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      uint64_t pv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pv[r] = (j >= 4) ? __shfl_xor(v[r], j >> 2, 64) : v[r ^ (j & 3)];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int x = 4 * lane + r;
-        const bool desc_block = (x & k) == 0;     // blocks sorted descending keep the max low
-        const bool lower = (x & j) == 0;
-        const uint64_t hi = v[r] > pv[r] ? v[r] : pv[r];
-        const uint64_t lo = v[r] > pv[r] ? pv[r] : v[r];
-        v[r] = (lower == desc_block) ? hi : lo;
-      }
-    }
-  }
+  bitonic_k<2>(v, lane);
   uint32_t c[4], nk[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -412,11 +477,7 @@ __device__ __forceinline__ void percentile_tiers(const uint32_t (&key)[4], const
     nk[r] = cnt_row[c[r]];
   }
   const uint32_t tot = nk[0] + nk[1] + nk[2] + nk[3];
-  uint32_t incl = tot;                            // keys in this and lower lanes
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
+  const uint32_t incl = wave_incl_scan(tot);     // keys in this and lower lanes
   uint32_t first = incl - tot;                    // keys in better-ranked centroids
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -425,6 +486,16 @@ __device__ __forceinline__ void percentile_tiers(const uint32_t (&key)[4], const
     if (first < keep_m) lw[c[r]] = (uint8_t)(6u - (uint32_t)(((uint64_t)first * 6u) / keep_m));
     first += nk[r];
   }
+}
+
+// one butterfly stage of the query's Walsh-Hadamard transform: lanes l and
+// l ^ H exchange; the lower one keeps the sum, the upper the difference
+template <int H>
+__device__ __forceinline__ void fwht_stage(float& v0, float& v1, int lane) {
+  const bool upper = (lane & H) != 0;
+  const float p0 = lane_xor_f<H>(v0, lane), p1 = lane_xor_f<H>(v1, lane);
+  v0 = upper ? (p0 - v0) : (v0 + p0);
+  v1 = upper ? (p1 - v1) : (v1 + p1);
 }
 
 constexpr int QP_WAVES = 2;
@@ -460,13 +531,12 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
     }
     v0 = __uint_as_float(__float_as_uint(v0) ^ (((tb.neg_bits[lane >> 5] >> (lane & 31)) & 1u) << 31));
     v1 = __uint_as_float(__float_as_uint(v1) ^ (((tb.neg_bits[2 + (lane >> 5)] >> (lane & 31)) & 1u) << 31));
-#pragma unroll
-    for (int h = 1; h < 64; h <<= 1) {
-      const bool upper = (lane & h) != 0;
-      const float p0 = __shfl_xor(v0, h, 64), p1 = __shfl_xor(v1, h, 64);
-      v0 = upper ? (p0 - v0) : (v0 + p0);
-      v1 = upper ? (p1 - v1) : (v1 + p1);
-    }
+    fwht_stage<1>(v0, v1, lane);
+    fwht_stage<2>(v0, v1, lane);
+    fwht_stage<4>(v0, v1, lane);
+    fwht_stage<8>(v0, v1, lane);
+    fwht_stage<16>(v0, v1, lane);
+    fwht_stage<32>(v0, v1, lane);
     const float a0 = v0, a1 = v1;
     v0 = a0 + a1;
     v1 = a0 - a1;
@@ -706,13 +776,10 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
     uint32_t above = 0;                             // keys in higher slices
 #pragma unroll
     for (int h = NH - 1; h >= 0; --h) {
-      uint32_t x = tot[h];
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_down(x, off, 64);
-        if (lane + off < 64) x += o;
-      }
+      const uint32_t incl = wave_incl_scan(tot[h]);
+      const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl + tot[h];   // lanes >= l
       suf[h] = x + above;
-      above = __shfl(suf[h], 0, 64);
+      above = (uint32_t)__builtin_amdgcn_readlane((int)suf[h], 0);
     }
     int theta = 0;
     uint32_t n_gt = above;                          // every key with S >= 1
@@ -723,8 +790,8 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
       if (!found && ge) {
         const int top = 63 - __builtin_clzll(ge);   // highest bin of the slice with suffix >= C
         theta = 64 * h + top + 1;
-        const uint32_t next_in_slice = __shfl(suf[h], (top + 1) & 63, 64);
-        const uint32_t next_slice = (h + 1 < NH) ? __shfl(suf[(h + 1) % NH], 0, 64) : 0u;
+        const uint32_t next_in_slice = (uint32_t)__builtin_amdgcn_readlane((int)suf[h], (top + 1) & 63);
+        const uint32_t next_slice = (h + 1 < NH) ? (uint32_t)__builtin_amdgcn_readlane((int)suf[(h + 1) % NH], 0) : 0u;
         n_gt = (top == 63) ? next_slice : next_in_slice;
         found = true;
       }
@@ -732,7 +799,7 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
     uint32_t eq_tot = (uint32_t)(n - n_gt);
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      const uint32_t v = __shfl(tot[h], (theta - 1) & 63, 64);
+      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)tot[h], (theta - 1) & 63);
       if (theta > 0 && (theta - 1) / 64 == h) eq_tot = v;
     }
     const uint32_t want = (uint32_t)n_candidates - n_gt;
@@ -766,11 +833,8 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
     len = len < 0 ? 0 : (len > sub_len ? sub_len : len);
     if (theta == 0) eq = (int)len - nz;
     if (t >= subs) { gt = 0; eq = 0; }
-    int pg = gt, pe = eq;                          // inclusive scan within the wave
-    for (int off = 1; off < 64; off <<= 1) {
-      const int og = __shfl_up(pg, off, 64), oe = __shfl_up(pe, off, 64);
-      if (lane >= off) { pg += og; pe += oe; }
-    }
+    const int pg = (int)wave_incl_scan((uint32_t)gt);   // inclusive scans within the wave
+    const int pe = (int)wave_incl_scan((uint32_t)eq);
     if (lane == 63) s_w[wave] = make_int2(pg, pe);
     __syncthreads();
     int wg = 0, we = 0, cg = 0, ce = 0;
@@ -1112,7 +1176,7 @@ __device__ void attend_block(const QT* __restrict__ qh_ptr, const KT* __restrict
   uint64_t okmask = 0;
 #pragma unroll
   for (int t = 0; t < MAXR; ++t) {
-    const int ix = __shfl(myix, t, 64);
+    const int ix = __builtin_amdgcn_readlane(myix, t);
     okmask |= (ix >= 0 ? 1ull : 0ull) << t;
     const int64_t row = ix >= 0 ? ix : 0;
     if constexpr (sizeof(KT) == 2) {
@@ -1129,16 +1193,16 @@ __device__ void attend_block(const QT* __restrict__ qh_ptr, const KT* __restrict
   for (int t = 0; t < MAXR; ++t) {
     const int r = wave + NW * t;
     float p = __builtin_fmaf(q0, k0v[t], q1 * k1v[t]);
-    for (int off = 32; off >= 1; off >>= 1) p += __shfl_xor(p, off, 64);
+    p = xor_butterfly(p, lane, AddF());
     if (lane == 0 && r < k) s.score[r] = ((okmask >> t) & 1ull) ? p * scale : -__builtin_inff();
   }
   __syncthreads();
   float m = -__builtin_inff();
   for (int r = lane; r < k; r += 64) m = fmaxf(m, s.score[r]);
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  m = xor_butterfly(m, lane, MaxF());
   float ssum = 0.0f;
   for (int r = lane; r < k; r += 64) ssum += (s.score[r] == -__builtin_inff()) ? 0.0f : __expf(s.score[r] - m);
-  for (int off = 32; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, 64);
+  ssum = xor_butterfly(ssum, lane, AddF());
 
   float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
@@ -1315,14 +1379,10 @@ struct TopkStats {
 template <int NT>
 __device__ __forceinline__ void topk_stats_wave(TopkStats st, TopkShared<NT>& s, int lane, int wave) {
   constexpr int NW = NT / 64;
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t a = __shfl_xor(st.kmax, off, 64), c = __shfl_xor(st.kmin, off, 64);
-    const uint32_t cp = __shfl_xor(st.kminp, off, 64), np = __shfl_xor(st.npos, off, 64);
-    st.kmax = a > st.kmax ? a : st.kmax;
-    st.kmin = c < st.kmin ? c : st.kmin;
-    st.kminp = cp < st.kminp ? cp : st.kminp;
-    st.npos += np;
-  }
+  st.kmax = xor_butterfly_u(st.kmax, lane, MaxU());
+  st.kmin = xor_butterfly_u(st.kmin, lane, MinU());
+  st.kminp = xor_butterfly_u(st.kminp, lane, MinU());
+  st.npos = xor_butterfly_u(st.npos, lane, AddU());
   if (lane == 0) { s.wsum[wave] = st.kmax; s.stat[0][wave] = st.kmin; s.stat[1][wave] = st.kminp; s.stat[2][wave] = st.npos; }
 }
 
@@ -1380,11 +1440,8 @@ __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], in
     uint32_t mine = 0;
 #pragma unroll
     for (int i = 0; i < per; ++i) mine += s.h[per * tid + i];
-    uint32_t suf = mine;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_down(suf, off, 64);
-      if (lane + off < 64) suf += o;
-    }
+    const uint32_t incl = wave_incl_scan(mine);
+    const uint32_t suf = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl + mine;   // lanes >= this one
     if (lane == 0) s.wsum[wave] = suf;
     __syncthreads();
     uint32_t above = suf - mine;
@@ -1468,9 +1525,9 @@ __device__ void topk_block(const uint32_t (&key)[R], const int32_t (&kix)[R], in
     int rank = 0;
 #pragma unroll 4
     for (int j2 = part; j2 < keff; j2 += PARTS) rank += (s.f[j2] > e) ? 1 : 0;
-    if constexpr (PARTS >= 2) rank += __shfl_xor(rank, 1, 64);
-    if constexpr (PARTS >= 4) rank += __shfl_xor(rank, 2, 64);
-    if constexpr (PARTS >= 8) rank += __shfl_xor(rank, 4, 64);
+    if constexpr (PARTS >= 2) rank += (int)lane_xor<1>((uint32_t)rank, lane);
+    if constexpr (PARTS >= 4) rank += (int)lane_xor<2>((uint32_t)rank, lane);
+    if constexpr (PARTS >= 8) rank += (int)lane_xor<4>((uint32_t)rank, lane);
     if (act && part == 0) {
       const int32_t key_index = (int32_t)(0xFFFFFFFFu - (uint32_t)e);
       out_idx[rank] = key_index;
@@ -1548,12 +1605,12 @@ __device__ void attend_rows16(const T* __restrict__ qh_ptr, const T* __restrict_
     float d = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qv[e], kx[pp][e], d);
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) d += __shfl_xor(d, off, 16);
+    d = xor_butterfly16(d, lane, AddF());
     sc[pp] = ok[pp] ? d * scale : -__builtin_inff();
     m = fmaxf(m, sc[pp]);
   }
-  for (int off = 32; off >= 16; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  m = fmaxf(m, lane_xor_f<32>(m, lane));
+  m = fmaxf(m, lane_xor_f<16>(m, lane));
   if (lane == 0) s.red[wave] = m;
   __syncthreads();
   m = s.red[0];
@@ -1572,11 +1629,12 @@ __device__ void attend_rows16(const T* __restrict__ qh_ptr, const T* __restrict_
     for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(pr, vx[pp][e], acc[e]);
   }
   // the four row groups of the wave: every lane of a group holds the group's sum
-  for (int off = 16; off <= 32; off <<= 1) {
-    ssum += __shfl_xor(ssum, off, 64);
+  ssum += lane_xor_f<16>(ssum, lane);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
-  }
+  for (int e = 0; e < 8; ++e) acc[e] += lane_xor_f<16>(acc[e], lane);
+  ssum += lane_xor_f<32>(ssum, lane);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] += lane_xor_f<32>(acc[e], lane);
   if (lane == 0) s.red[wave] = ssum;
   if (lane < 16) {
 #pragma unroll
@@ -1837,8 +1895,7 @@ dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k,
       float d = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qv[e], x[u][e], d);
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) d += __shfl_xor(d, off, 16);
+      d = xor_butterfly16(d, lane, AddF());
       if (ok[u]) {                                // uniform over the row group
         const float sc = d * a.scale;
         const float mn = fmaxf(m, sc);
@@ -1853,7 +1910,8 @@ dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k,
   }
   // workgroup max of the group maxima, then rescale each group's sums to it
   float mw = m;
-  for (int off = 32; off >= 16; off >>= 1) mw = fmaxf(mw, __shfl_xor(mw, off, 64));
+  mw = fmaxf(mw, lane_xor_f<32>(mw, lane));
+  mw = fmaxf(mw, lane_xor_f<16>(mw, lane));
   if (lane == 0) s_red[wave] = mw;
   __syncthreads();
   float M = s_red[0];
@@ -1864,7 +1922,7 @@ dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k,
   float ssum = (part == 0) ? l * f : 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] *= f;
-  for (int off = 32; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, 64);
+  ssum = xor_butterfly(ssum, lane, AddF());
   if (lane == 0) s_red[wave] = ssum;
   __syncthreads();
   ssum = 0.0f;
