@@ -212,6 +212,19 @@ __device__ __forceinline__ void load_key(const KT* __restrict__ src, float (&x)[
   }
 }
 
+// one cross-lane butterfly stage of a key's Walsh-Hadamard transform: the
+// 16 lanes of a key form one DPP row; lanes b and b ^ M exchange coordinates,
+// the lower one keeps the sums, the upper the differences
+template <int M>
+__device__ __forceinline__ void key_stage(float (&x)[SUBD], int b) {
+  const bool upper = (b & M) != 0;
+#pragma unroll
+  for (int j = 0; j < SUBD; ++j) {
+    const float p = __uint_as_float(dpp_xor<M>(__float_as_uint(x[j])));
+    x[j] = upper ? (p - x[j]) : (x[j] + p);
+  }
+}
+
 // code byte, nibbles, weight and partial squared norm of subspace b of one key
 __device__ __forceinline__ void encode_key(float (&x)[SUBD], int b, const Tables& tb, uint32_t& code_out,
                                            uint32_t& nib_out, float& w_out, float& nsq_out) {
@@ -237,15 +250,10 @@ __device__ __forceinline__ void encode_key(float (&x)[SUBD], int b, const Tables
     }
   }
   // cross-lane butterflies (partner lane b ^ m holds coordinate +- 8m)
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    const bool upper = (b & m) != 0;
-#pragma unroll
-    for (int j = 0; j < SUBD; ++j) {
-      const float p = __shfl_xor(x[j], m, 16);
-      x[j] = upper ? (p - x[j]) : (x[j] + p);
-    }
-  }
+  key_stage<1>(x, b);
+  key_stage<2>(x, b);
+  key_stage<4>(x, b);
+  key_stage<8>(x, b);
 
   // per-subspace code, nibbles, weight
   float e = x[0] * x[0];
@@ -327,8 +335,10 @@ encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
     uint32_t* rec = reinterpret_cast<uint32_t*>(records + row * 128);
     rec[b] = nib;
     reinterpret_cast<float*>(rec)[16 + b] = w;
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) nsq += __shfl_xor(nsq, m, 16);
+    nsq += __uint_as_float(dpp_xor<8>(__float_as_uint(nsq)));
+    nsq += __uint_as_float(dpp_xor<4>(__float_as_uint(nsq)));
+    nsq += __uint_as_float(dpp_xor<2>(__float_as_uint(nsq)));
+    nsq += __uint_as_float(dpp_xor<1>(__float_as_uint(nsq)));
     if (b == 0) norms[row] = sqrt_rn(nsq);
   }
   if (ucnt && !direct) {                    // keys per (subspace, centroid)
