@@ -71,9 +71,10 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr int64_t kTargetWG = 512, kMaxKPL = 64;
 constexpr int64_t kFuseTile = 4096;
 // rerank and top-k run as one workgroup per head when there are enough heads to
-// fill the chip, or few enough candidates per head (four per thread)
+// fill the chip, or few enough candidates per head (two per thread); with 32
+// heads the split kernels win from 4096 candidates per head on
 constexpr int kFusedTopkHeads = 128;
-constexpr int kFusedTopkSlots = 4 * pk::RT_THREADS;
+constexpr int kFusedTopkSlots = 2 * pk::RT_THREADS;
 // README "Parameters": candidate / collision ratio (per mille) by retrieval-zone length
 void adaptive_permille(int64_t zone, int* beta, int* rho) {
   if (zone < 5000) { *beta = 500; *rho = 500; }
