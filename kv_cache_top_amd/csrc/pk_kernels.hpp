@@ -1052,7 +1052,7 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
     }
     thp4 = th4 + 0x01010101u;                     // theta + 1 per byte (<= 128: no carry)
   };
-  if constexpr (!FUSED) setup();                  // parameter loads right behind the first group's
+  setup();        // behind the first group's loads; the other groups are requested after it
   uint2* ik = s_ik[wave];
   int nk = 0;
 
@@ -1124,7 +1124,6 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
     uint32_t sg[NG > 1 ? NG - 1 : 1][SEL_GRP];
 #pragma unroll
     for (int g = 1; g < NG; ++g) load_group(g, sg[g - 1]);
-    if constexpr (FUSED) setup();                 // while the scores are in flight
     compact_group(0, sp);
 #pragma unroll
     for (int g = 1; g < NG; ++g) {
