@@ -1029,6 +1029,9 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
   int need[G], run_gt[G], run_eq[G];
   uint32_t th4 = 0x7F7F7F7Fu;                     // absent heads: theta 127, never reached
   uint32_t thp4 = 0;
+  // compaction thresholds: theta, or theta + 1 for a head whose keys at theta
+  // are all taken before this sub-tile (they can no longer be candidates)
+  uint32_t thf4 = 0x7F7F7F7Fu;
   // per head: theta, need_eq, and the counts of keys above / at theta before
   // this wave's sub-tile
   auto setup = [&]() __attribute__((always_inline)) {
@@ -1049,6 +1052,7 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
       }
       need[g] = ne; run_gt[g] = bg; run_eq[g] = be;
       th4 = (th4 & ~(0xFFu << (8 * g))) | ((uint32_t)theta << (8 * g));
+      thf4 = (thf4 & ~(0xFFu << (8 * g))) | ((uint32_t)(be >= ne ? theta + 1 : theta) << (8 * g));
     }
     thp4 = th4 + 0x01010101u;                     // theta + 1 per byte (<= 128: no carry)
   };
@@ -1096,7 +1100,7 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
     for (int r = 0; r < SEL_GRP; ++r) {
       const int i = w0 + (grp * SEL_GRP + r) * 64 + lane;
       const bool valid = i < w1;                  // false for the whole wave past its keys
-      const uint32_t ge4 = ((src[r] | 0x80808080u) - th4) & 0x80808080u;
+      const uint32_t ge4 = ((src[r] | 0x80808080u) - thf4) & 0x80808080u;
       const bool interesting = valid && ge4 != 0u;
       const uint64_t im = __ballot(interesting);
       if (interesting) ik[nk + (int)mbcnt(im)] = make_uint2((uint32_t)i, src[r]);
