@@ -885,7 +885,10 @@ __global__ void __launch_bounds__(256) copy16_kernel(uint4* __restrict__ dst, co
 // key order.  Byte-parallel compares of the packed scores against all heads'
 // theta find the keys at or above some head's theta; only those (about a
 // tenth of the keys) are compacted, in key order, for the per-head ballots,
-// since every other key leaves all counts unchanged.
+// since every other key leaves all counts unchanged.  A head whose need_eq
+// keys at theta all lie before the sub-tile compares against theta + 1 there:
+// its keys at theta can no longer be taken, and its slots only count keys
+// above theta.
 // ===========================================================================
 constexpr int SEL_GRP = 16;             // score chunks per group
 constexpr int SEL_MAXGRP = 4;           // groups of the largest sub-tile (64 chunks of 64 keys)
@@ -1577,7 +1580,7 @@ constexpr int RT_THREADS = 1024;
 // dimensions, so 64 rows are covered per pass; the K and V rows of all P
 // passes are loaded before any is used.  Scores: 16-lane partial dot
 // products; one max and one sum over the workgroup; the value rows are
-// weighted in registers, summed over the four rows of a wave by shuffles and
+// weighted in registers, summed over the four rows of a wave by lane swaps and
 // over the waves in LDS.  fp32; indices < 0 or >= n_rows are skipped.
 template <int NW>
 struct AttRowsShared {
