@@ -1257,7 +1257,7 @@ struct AttendArgs {
 
 template <typename KT, typename QT, typename OT, int MAXR>
 __global__ void __launch_bounds__(256)
-attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k, int n_q_heads, int n_kv_heads, int group) {
+attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k, int n_q_heads, int /*n_kv_heads*/, int group) {
   __shared__ AttShared<4> s_att;
   const int head = blockIdx.x;
   const int seq = head / n_q_heads, qh = head - seq * n_q_heads, kvh = qh / group;
@@ -1394,7 +1394,6 @@ struct TopkStats {
 // topk_block (a barrier must come between)
 template <int NT>
 __device__ __forceinline__ void topk_stats_wave(TopkStats st, TopkShared<NT>& s, int lane, int wave) {
-  constexpr int NW = NT / 64;
   st.kmax = xor_butterfly_u(st.kmax, lane, MaxU());
   st.kmin = xor_butterfly_u(st.kmin, lane, MinU());
   st.kminp = xor_butterfly_u(st.kminp, lane, MinU());
@@ -1839,7 +1838,7 @@ template <typename KT, typename QT, typename OT>
 __global__ void __launch_bounds__(DA_THREADS)
 dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k, const KT* __restrict__ dk,
                            const KT* __restrict__ dv, int64_t dsb, int64_t dsh, int64_t dst, int n_dense,
-                           int n_q_heads, int n_kv_heads, int group) {
+                           int n_q_heads, int /*n_kv_heads*/, int group) {
   __shared__ int32_t s_ix[PK_MAX_TOPK_ATT];                // retrieved rows (-1: skipped)
   __shared__ float s_red[DA_THREADS / 64];
   __shared__ float s_acc[DA_GROUPS][D + 4];
