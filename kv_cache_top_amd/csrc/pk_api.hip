@@ -30,7 +30,7 @@ struct pk_context {
   uint32_t* lut = nullptr;        // [units][16][256]
   float* rq = nullptr;            // [qheads][128]
   uint32_t* scores = nullptr;     // [units][n_cap]
-  uint32_t* tile_hist = nullptr;  // [units][max_subs][4][64]
+  uint32_t* tile_hist = nullptr;  // per unit [4 heads][bins / 4][max_subs][4 bins] (64 or 128 bins)
   SelParams* params = nullptr;    // [units][4]
   int2* sub_base = nullptr;       // [units][max_subs][4]
   int32_t* cand_idx = nullptr;    // [qheads][C]

@@ -620,6 +620,13 @@ __device__ __forceinline__ void xcd_unit_tile(int i, int units, int tiles, int& 
   }
 }
 
+// word of the count of bin `bin` (score bin + 1) of head g in sub-tile `sub` of a
+// unit's histograms; a unit holds max_subs * MAXG * NB words
+template <int NB>
+__device__ __forceinline__ int64_t hist_index(int64_t unit, int max_subs, int sub, int g, int bin) {
+  return (int64_t)unit * max_subs * MAXG * NB + (((int64_t)g * (NB / 4) + (bin >> 2)) * max_subs + sub) * 4 + (bin & 3);
+}
+
 template <int G, int NB>   // NB: histogram bins 1..NB
 __global__ void __launch_bounds__(256)
 collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut,
@@ -694,8 +701,10 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
   }
   __syncthreads();
 
-  // reduce to sub-tile histograms [unit][4 * tile + wave][g][bin - 1]; byte w of
-  // a counter word belongs to wave w
+  // reduce to sub-tile histograms; byte w of a counter word belongs to wave w.
+  // Layout (hist_index): per unit, [head][bin / 4][sub-tile][bin % 4], so that
+  // the readers, one lane per sub-tile, load four bins of consecutive sub-tiles
+  // with one coalesced 16-byte access per lane
   for (int gb = tid; gb < group * NB; gb += 256) {
     const int g = gb / NB, bin = gb % NB;
     const uint32_t* row = s_hist + (g * NB + bin) * HIST_LANES;
@@ -708,7 +717,7 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
     const uint32_t cnt[4] = {lo & 0xFFFFu, hi & 0xFFFFu, lo >> 16, hi >> 16};
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2)
-      tile_hist[(((int64_t)unit * max_subs + 4 * tl + w2) * MAXG + g) * NB + bin] = cnt[w2];
+      tile_hist[hist_index<NB>(unit, max_subs, 4 * tl + w2, g, bin)] = cnt[w2];
   }
 }
 
@@ -738,15 +747,13 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
   __shared__ int2 s_w[4];
   const int unit = blockIdx.x / group, g = blockIdx.x - unit * group;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t* uh = tile_hist + (int64_t)unit * max_subs * MAXG * NB;
-
   uint4 h4[NB / 4];
   auto load_chunk = [&](int base) {
     const int t = base + tid;
     const int tl = t < subs ? t : subs - 1;
-    const uint4* hrow = reinterpret_cast<const uint4*>(uh + ((int64_t)tl * MAXG + g) * NB);
 #pragma unroll
-    for (int q4 = 0; q4 < NB / 4; ++q4) h4[q4] = hrow[q4];
+    for (int q4 = 0; q4 < NB / 4; ++q4)
+      h4[q4] = *reinterpret_cast<const uint4*>(tile_hist + hist_index<NB>(unit, max_subs, tl, g, 4 * q4));
     if (t >= subs) {
 #pragma unroll
       for (int q4 = 0; q4 < NB / 4; ++q4) h4[q4] = make_uint4(0u, 0u, 0u, 0u);
@@ -906,13 +913,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // reduce-scatter over the lanes (lane l ends with the total of bin l + 1).
 // h: this lane's sub-tile histogram (hist_row_load); results go to s_par[g]
 // = (theta, need_eq) and s_base[w][g] = (#gt, #eq) before sub-tile 4 tl + w.
-__device__ __forceinline__ void hist_row_load(const uint32_t* __restrict__ uh, int subs, int g, int lane,
-                                              uint32_t (&h)[64]) {
+__device__ __forceinline__ void hist_row_load(const uint32_t* __restrict__ tile_hist, int unit, int max_subs,
+                                              int subs, int g, int lane, uint32_t (&h)[64]) {
   if (lane < subs) {
-    const uint4* row = reinterpret_cast<const uint4*>(uh + ((int64_t)lane * MAXG + g) * NBIN);
 #pragma unroll
     for (int q4 = 0; q4 < 16; ++q4) {
-      const uint4 x = row[q4];
+      const uint4 x = *reinterpret_cast<const uint4*>(tile_hist + hist_index<NBIN>(unit, max_subs, lane, g, 4 * q4));
       h[4 * q4] = x.x; h[4 * q4 + 1] = x.y; h[4 * q4 + 2] = x.z; h[4 * q4 + 3] = x.w;
     }
   } else {
@@ -1017,7 +1023,7 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
   // in order)
   uint32_t hrow[FUSED ? 64 : 1];
   if constexpr (FUSED) {
-    if (wave < G) hist_row_load(tile_hist + (int64_t)unit * max_subs * MAXG * NBIN, 4 * tiles, wave, lane, hrow);
+    if (wave < G) hist_row_load(tile_hist, unit, max_subs, 4 * tiles, wave, lane, hrow);
   }
 
   // packed scores of keys w0 + r*64 + lane, in groups of SEL_GRP chunks
