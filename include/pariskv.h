@@ -259,11 +259,11 @@ pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype,
 /* Retrieval and sparse attention in one call (README "2. Decode" then
  * "3. Attention"; Slides Sec. 4.2.3 then Eqs. (1)-(3)): the same outputs as
  * pk_retrieve followed by pk_sparse_attend with these arguments on the same
- * stream.  When q, K/V and out share one dtype and rerank + top-k run as one
- * workgroup per head, that workgroup also attends over its head's rows, so the
- * retrieved indices never leave the chip before they are used.  The output
- * may then differ from the separate attention call by fp32 summation order
- * (the softmax and weighted sum are split over 16 instead of 4 waves).
+ * stream.  When q, K/V and out share one dtype, the workgroup that selects a
+ * head's Top-k also attends over that head's rows, so the retrieved indices
+ * never leave the chip before they are used.  The output may then differ from
+ * the separate attention call by fp32 summation order (the softmax and
+ * weighted sum are split over 16 instead of 4 waves).
  * Arguments, layouts, ownership and errors as for the two calls. */
 pk_status pk_retrieve_attend(pk_context* ctx, const void* q, pk_dtype q_dtype,
                              const pk_summaries* sums, const void* k, const void* v,

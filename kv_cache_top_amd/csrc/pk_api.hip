@@ -421,9 +421,10 @@ pk_status check_attend_args(pk_context* ctx, const void* q, pk_dtype q_dtype, co
   return PK_OK;
 }
 
-// The retrieval chain.  With `att` (q, K/V and output of one dtype, the fused
-// rerank + top-k path taken) the last kernel also computes the attention and
-// *attended is set; otherwise the caller still has to attend.
+// The retrieval chain.  With `att` (q, K/V and output of one dtype) the kernel
+// that selects each head's Top-k (rerank + top-k, or top-k after the spread
+// rerank) also computes the attention and *attended is set; otherwise the
+// caller still has to attend.
 pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s,
                         int32_t* topk_idx, float* topk_est, const pk_debug* dbg, hipStream_t stream,
                         const pk::AttendArgs* att, bool* attended) {
@@ -587,15 +588,33 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
     }
     if ((st = check_launch(ctx, "rerank")) != PK_OK) return st;
     {
+      // with attention of matching dtypes, the top-k workgroup attends over its
+      // head's rows as well (no separate attention launch)
       Launch L(ctx, PK_KERNEL_TOPK, stream);
       const int R = (n_sel + pk::TK_THREADS - 1) / pk::TK_THREADS;
-#define PK_TOPK(RR)                                                                                      \
-  hipLaunchKernelGGL(pk::topk_kernel<RR>, dim3(ctx->qheads), dim3(pk::TK_THREADS), 0, stream, ctx->cand_idx,     \
-                     ctx->cand_est, n_sel, C, k, topk_idx, topk_est)
-      if (R <= 2) PK_TOPK(2);
-      else if (R <= 4) PK_TOPK(4);
-      else if (R <= 8) PK_TOPK(8);
-      else PK_TOPK(16);
+      const pk::AttendArgs none{};
+#define PK_TOPK(RR, T, MR, A)                                                                                   \
+  hipLaunchKernelGGL((pk::topk_kernel<RR, T, MR, A>), dim3(ctx->qheads), dim3(pk::TK_THREADS), 0, stream,        \
+                     ctx->cand_idx, ctx->cand_est, n_sel, C, k, topk_idx, topk_est, cfg.n_q_heads, ctx->group,   \
+                     A ? *att : none)
+#define PK_TOPK_R(T, MR, A)                    \
+  do {                                         \
+    if (R <= 2) PK_TOPK(2, T, MR, A);          \
+    else if (R <= 4) PK_TOPK(4, T, MR, A);     \
+    else if (R <= 8) PK_TOPK(8, T, MR, A);     \
+    else PK_TOPK(16, T, MR, A);                \
+  } while (0)
+      if (att) {
+        const int np = k <= 2 * (pk::TK_THREADS / 16) ? 2 : 4;   // passes of 64 rows
+        if (q_dtype == PK_BF16 && np == 2) PK_TOPK_R(uint16_t, 2, true);
+        else if (q_dtype == PK_BF16) PK_TOPK_R(uint16_t, 4, true);
+        else if (np == 2) PK_TOPK_R(float, 2, true);
+        else PK_TOPK_R(float, 4, true);
+        if (attended) *attended = true;
+      } else {
+        PK_TOPK_R(float, 1, false);
+      }
+#undef PK_TOPK_R
 #undef PK_TOPK
     }
     if ((st = check_launch(ctx, "topk")) != PK_OK) return st;

@@ -1789,13 +1789,19 @@ rerank_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot
   }
 }
 
-constexpr int TK_THREADS = 1024;     // top-k workgroup (few heads, many candidates)
+constexpr int TK_THREADS = RT_THREADS;   // top-k workgroup (few heads, many candidates)
 
-template <int R>
+// T, P, ATT: with ATT the workgroup goes on to attend over its head's k rows
+// (q, K, V and the output all of type T; P passes of 64 rows), as
+// rerank_topk_kernel does.
+template <int R, typename T, int P, bool ATT>
 __global__ void __launch_bounds__(TK_THREADS)
 topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_sel,
-            int n_candidates, int k, int32_t* __restrict__ out_idx, float* __restrict__ out_est) {
+            int n_candidates, int k, int32_t* __restrict__ out_idx, float* __restrict__ out_est,
+            int n_q_heads, int group, AttendArgs att) {
   __shared__ TopkShared<TK_THREADS> s_tk;
+  __shared__ int32_t s_idx[ATT ? PK_MAX_TOPK_ATT : 1];
+  __shared__ AttRowsShared<ATT ? TK_THREADS / 64 : 1> s_att;
   const int head = blockIdx.x, tid = threadIdx.x;
   int32_t* ci = cand_idx + (int64_t)head * n_candidates;
   float* ce = cand_est + (int64_t)head * n_candidates;
@@ -1818,7 +1824,15 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
 #pragma unroll
   for (int r = 0; r < R; ++r) key[r] = orderable(ev[r]);
   topk_block<R, TK_THREADS>(key, kix, n_sel, k, out_idx + (int64_t)head * k, out_est ? out_est + (int64_t)head * k : nullptr,
-                     s_tk, tid);
+                     s_tk, tid, ATT ? s_idx : nullptr);
+  if constexpr (ATT) {
+    __syncthreads();
+    const int seq = head / n_q_heads, qh = head - seq * n_q_heads, kvh = qh / group;
+    const T* kb = reinterpret_cast<const T*>(att.k) + seq * att.sb + kvh * att.sh;
+    const T* vb = reinterpret_cast<const T*>(att.v) + seq * att.sb + kvh * att.sh;
+    attend_rows16<T, P>(reinterpret_cast<const T*>(att.q) + (int64_t)head * D, kb, vb, att.st, att.n_rows, s_idx,
+                        k, att.scale, reinterpret_cast<T*>(att.out) + (int64_t)head * D, s_att, tid);
+  }
 }
 
 // ===========================================================================
