@@ -70,11 +70,13 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // units, 256 threads each doing 1..kMaxKPL keys.
 constexpr int64_t kTargetWG = 512, kMaxKPL = 64;
 constexpr int64_t kFuseTile = 4096;
-// rerank and top-k run as one workgroup per head when there are enough heads to
-// fill the chip, or few enough candidates per head (two per thread); with 32
-// heads the split kernels win from 4096 candidates per head on
+// rerank and top-k run as one workgroup per head while its rounds of 1024
+// candidates are few: up to four when there are enough heads to fill the chip
+// (at 256 heads, fused wins at 4096 candidates and the split kernels at 13108),
+// one otherwise (at 32 heads the split kernels win from 2048 on)
 constexpr int kFusedTopkHeads = 128;
-constexpr int kFusedTopkSlots = 2 * pk::RT_THREADS;
+constexpr int kFusedTopkSlotsMany = 4 * pk::RT_THREADS;
+constexpr int kFusedTopkSlots = pk::RT_THREADS;
 // README "Parameters": candidate / collision ratio (per mille) by retrieval-zone length
 void adaptive_permille(int64_t zone, int* beta, int* rho) {
   if (zone < 5000) { *beta = 500; *rho = 500; }
@@ -546,10 +548,10 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
 #undef PK_SELECT
   }
   if ((st = check_launch(ctx, "select")) != PK_OK) return st;
-  if (ctx->qheads >= kFusedTopkHeads || n_sel <= kFusedTopkSlots) {
+  if (n_sel <= (ctx->qheads >= kFusedTopkHeads ? kFusedTopkSlotsMany : kFusedTopkSlots)) {
     // one workgroup per head: rerank and top-k together, estimates in LDS
     Launch L(ctx, PK_KERNEL_RERANK_TOPK, stream);
-    const int R = (n_sel + pk::RT_THREADS - 1) / pk::RT_THREADS;
+    const int R = (n_sel + pk::RT_THREADS - 1) / pk::RT_THREADS;   // <= 4
     float* est_out = (dbg && dbg->cand_est) ? ctx->cand_est : nullptr;
     const pk::AttendArgs none{};
 #define PK_RTK_LAUNCH(RR, T, MR, A)                                                                               \
@@ -560,9 +562,7 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
   do {                                             \
     if (R <= 1) PK_RTK_LAUNCH(1, T, MR, A);        \
     else if (R <= 2) PK_RTK_LAUNCH(2, T, MR, A);   \
-    else if (R <= 4) PK_RTK_LAUNCH(4, T, MR, A);   \
-    else if (R <= 8) PK_RTK_LAUNCH(8, T, MR, A);   \
-    else PK_RTK_LAUNCH(16, T, MR, A);              \
+    else PK_RTK_LAUNCH(4, T, MR, A);               \
   } while (0)
     if (att) {
       const int np = k <= 2 * (pk::RT_THREADS / 16) ? 2 : 4;   // passes of 64 rows

@@ -73,9 +73,9 @@ def test_many_heads_one_workgroup_topk(n, C):
 
 @pytest.mark.parametrize("batch,n_kv,n_q,n", [(1, 1, 4, 20000), (4, 8, 32, 17000)])
 def test_maximum_candidates_and_top_k(batch, n_kv, n_q, n):
-    """C = 16384 and k = 256, the largest the ABI takes: the split rerank /
-    top-k kernels (4 heads) and the one-workgroup-per-head path (128 heads,
-    sixteen candidate slots per thread)."""
+    """C = 16384 and k = 256, the largest the ABI takes, with 4 and with 128
+    query heads: the rerank spread over 1024-candidate workgroups, then one
+    top-k workgroup per head over sixteen slots per thread."""
     from kv_cache_top_amd import pariskv as P
     C, k = P.PK_MAX_CANDIDATES, P.PK_MAX_TOPK
     w = S.custom("llama32k", batch=batch, n_kv_heads=n_kv, n_q_heads=n_q, n=n, n_candidates=C, top_k=k,
