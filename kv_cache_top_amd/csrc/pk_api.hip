@@ -580,11 +580,20 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
   } else {
     // few heads: spread the rerank over several workgroups per head, then select
     {
+      // one candidate per lane while that keeps the grid within ~2048
+      // workgroups, else two or four (fewer tables to build)
       Launch L(ctx, PK_KERNEL_RERANK, stream);
-      const int chunks = (n_sel + pk::RR_PER_WG - 1) / pk::RR_PER_WG;
-      hipLaunchKernelGGL(pk::rerank_kernel, dim3((unsigned)((int64_t)ctx->qheads * chunks)), dim3(256), 0, stream,
-                         s->records, ctx->rq, ctx->cand_idx, ctx->cand_est, s->n_capacity, n_sel, C, chunks,
-                         cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->tb);
+      const int64_t total = (int64_t)ctx->qheads * n_sel;
+      const int rr = total <= (int64_t)1 << 19 ? 1 : (total <= (int64_t)1 << 21 ? 2 : 4);
+      const int chunks = (n_sel + 256 * rr - 1) / (256 * rr);
+#define PK_RR(RRR)                                                                                               \
+  hipLaunchKernelGGL(pk::rerank_kernel<RRR>, dim3((unsigned)((int64_t)ctx->qheads * chunks)), dim3(256), 0, stream, \
+                     s->records, ctx->rq, ctx->cand_idx, ctx->cand_est, s->n_capacity, n_sel, C, chunks,          \
+                     cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->tb)
+      if (rr == 1) PK_RR(1);
+      else if (rr == 2) PK_RR(2);
+      else PK_RR(4);
+#undef PK_RR
     }
     if ((st = check_launch(ctx, "rerank")) != PK_OK) return st;
     {

@@ -1751,10 +1751,9 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
   }
 }
 
-// ---- few heads: rerank spread over RR_PER_WG-candidate workgroups ----------
-constexpr int RR_ROUNDS = 4;                      // candidates per lane
-constexpr int RR_PER_WG = 256 * RR_ROUNDS;
-
+// ---- few heads: rerank spread over workgroups of 256 x RR candidates --------
+// RR: candidates per lane (rounds of 256 per workgroup)
+template <int RR>
 __global__ void __launch_bounds__(256)
 rerank_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot_q,
               int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int64_t n_cap,
@@ -1767,7 +1766,7 @@ rerank_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot
   const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
   int32_t* ci = cand_idx + (int64_t)head * n_candidates;
   float* ce = cand_est + (int64_t)head * n_candidates;
-  const int p0 = ch * RR_PER_WG;
+  const int p0 = ch * 256 * RR;
   const int plast = n_sel - 1;
 
   float rqv[D * 16 / 256];
@@ -1778,14 +1777,17 @@ rerank_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot
   rerank_table<256>(s_T, rqv, tb, tid);
   __syncthreads();
 #pragma unroll 1
-  for (int r = 0; r < RR_ROUNDS; ++r) {
+  for (int r = 0; r < RR; ++r) {
     const int p = p0 + r * 256 + tid;
     if (r) {
       rerank_load(ra, rbase, ixn);
       ixn = ci[p + 256 < plast ? p + 256 : plast];
     }
     const float est = rerank_eval(ra, s_T);
-    if (p < n_sel) ce[p] = est;
+    // every lane stores: past the end a lane holds the last slot's record and
+    // rewrites that slot's estimate with the same value (an unconditional
+    // store keeps the wait for the next key index from covering it)
+    ce[p < n_sel ? p : plast] = est;
   }
 }
 
