@@ -262,6 +262,8 @@ def main():
     nb = algorithmic_bytes(w, w.n)
     if kern["attend"]["launches"] == 0 and kern["rerank_topk"]["launches"] > 0:
         nb["rerank_topk"] += nb["attend"]               # the attention ran inside the rerank + top-k kernel
+    elif kern["attend"]["launches"] == 0 and kern["topk"]["launches"] > 0:
+        nb["topk"] = nb["attend"]                       # the attention ran inside the top-k kernel
     for k in kern:
         if kern[k]["avg_us"] and nb.get(k):
             kern[k]["alg_GBps"] = round(nb[k] / (kern[k]["avg_us"] * 1e-6) / 1e9, 1)
