@@ -1,8 +1,9 @@
 """GPU parity of the single retrieve + attend call (pk_retrieve_attend) against
 the oracle, on the paths it can take: the fused rerank + top-k + attention
-workgroup (many heads, or few candidates; one dtype throughout), the split
-rerank / top-k kernels followed by the attention kernel, mixed dtypes, mapped
-host K/V and the empty key set."""
+workgroup (at most 4096 candidates per head with 128 or more heads, at most
+1024 otherwise), the rerank spread over workgroups followed by one top-k +
+attention workgroup per head (more candidates), the attention kernel after
+either (mixed dtypes), mapped host K/V and the empty key set."""
 import numpy as np
 import pytest
 
@@ -39,7 +40,8 @@ def test_fused_many_heads(n, C, k):
 
 
 def test_split_path_then_attention():
-    """Few heads and many candidates: split rerank / top-k, then the attention kernel."""
+    """Few heads and many candidates: the rerank spread over workgroups, then
+    the top-k workgroup of each head attends over its rows."""
     w = S.custom("llama32k", batch=1, n_kv_heads=2, n_q_heads=8, n=9000, n_candidates=4096, wid=520)
     say("case split path n=9000 C=4096")
     _run(w, [0, 1]).close()
@@ -68,3 +70,28 @@ def test_fused_empty():
     assert (run.topk_idx.cpu().numpy() == -1).all()
     assert (run.out.float().cpu().numpy() == 0).all()
     run.close()
+
+
+@pytest.mark.parametrize("batch,n_kv,n_q,n,C", [(1, 2, 8, 3000, 1024), (1, 2, 8, 3000, 1025),
+                                                 (4, 8, 32, 5000, 4096), (4, 8, 32, 5000, 4097)])
+def test_path_boundaries(batch, n_kv, n_q, n, C):
+    """Candidate counts on both sides of the switch between the fused workgroup
+    and the spread rerank, with few (8) and many (128) query heads."""
+    w = S.custom("llama32k", batch=batch, n_kv_heads=n_kv, n_q_heads=n_q, n=n, n_candidates=C, wid=560 + C % 97)
+    say(f"case path boundary heads={batch * n_q} C={C}")
+    _run(w, [0, 1] if w.units <= 2 else [0, 13, 31]).close()
+
+
+@pytest.mark.parametrize("k", [1, 256])
+def test_spread_path_top_k_extremes(k):
+    """k = 1 and k = 256 on the spread rerank with attention in the top-k workgroup."""
+    w = S.custom("llama32k", batch=1, n_kv_heads=2, n_q_heads=8, n=4000, n_candidates=2000, top_k=k, wid=570 + k)
+    say(f"case spread path k={k}")
+    _run(w, [0, 1]).close()
+
+
+def test_spread_path_fp32():
+    """fp32 q / K / V / output on the spread rerank with attention in the top-k workgroup."""
+    w = S.custom("tiny4k", n=3000, n_candidates=1500, wid=580)
+    say("case spread path fp32")
+    _run(w, [0]).close()
