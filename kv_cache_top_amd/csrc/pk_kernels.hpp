@@ -173,6 +173,34 @@ __device__ __forceinline__ uint32_t xor_butterfly_u(uint32_t x, int lane, Op op)
   x = op(x, lane_xor<2>(x, lane));
   return op(x, lane_xor<1>(x, lane));
 }
+// one stage of reduce_scatter64 below, width W <= 8 (DPP partner lane ^ W)
+template <int W>
+__device__ __forceinline__ void reduce_scatter_stage(uint32_t (&v)[64], int lane) {
+  const bool up = (lane & W) != 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const uint32_t send = up ? v[i] : v[i + W];
+    const uint32_t keep = up ? v[i + W] : v[i];
+    v[i] = keep + dpp_xor<W>(send);
+  }
+}
+
+// Sum of entry l over the wave's 64 lanes, returned in lane l (v is consumed):
+// after the stage of width w, v[i] (i < w) of lane l is the sum, over the
+// 64 / w lanes that share l's bits below w, of entry i + (l & (64 - w));
+// widths 32 and 16 trade register halves between lane halves / rows.
+__device__ __forceinline__ uint32_t reduce_scatter64(uint32_t (&v)[64], int lane) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = swap32_sum(v[i], v[i + 32]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = swap16_sum(v[i], v[i + 16]);
+  reduce_scatter_stage<8>(v, lane);
+  reduce_scatter_stage<4>(v, lane);
+  reduce_scatter_stage<2>(v, lane);
+  reduce_scatter_stage<1>(v, lane);
+  return v[0];
+}
+
 struct AddF { __device__ float operator()(float a, float b) const { return a + b; } };
 struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
 struct MaxU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
@@ -728,8 +756,8 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
 // counts of keys above / at theta.
 //
 // Workgroup = (unit, query head); thread t holds the 64-bin histogram of
-// sub-tile t of each 256-sub-tile chunk in registers.  Bin totals come from an
-// LDS transpose, theta from a suffix scan over the bins, and the per-sub-tile
+// sub-tile t of each 256-sub-tile chunk in registers.  Bin totals come from a
+// register reduce-scatter per wave, theta from a suffix scan over the bins, and the per-sub-tile
 // prefixes from a workgroup scan over the same registers, so a unit with at
 // most 256 sub-tiles reads its histograms once.
 // ===========================================================================
@@ -741,7 +769,6 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
                  int2* __restrict__ sub_base, int64_t n, int subs, int max_subs, int sub_len, int group,
                  int n_candidates) {
   constexpr int NH = NB / 64;                      // 64-bin slices
-  __shared__ uint32_t s_t[TH_THREADS][64 + 1];     // [sub-tile in chunk][bin of a slice], padded
   __shared__ uint32_t s_q[4][64];
   __shared__ int s_par[2];
   __shared__ int2 s_w[4];
@@ -768,19 +795,13 @@ threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__
     load_chunk(base);
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
+      uint32_t v[64];
 #pragma unroll
       for (int q4 = 0; q4 < 16; ++q4) {
-        const uint4 v = h4[16 * h + q4];
-        s_t[tid][4 * q4 + 0] = v.x;
-        s_t[tid][4 * q4 + 1] = v.y;
-        s_t[tid][4 * q4 + 2] = v.z;
-        s_t[tid][4 * q4 + 3] = v.w;
+        const uint4 x = h4[16 * h + q4];
+        v[4 * q4] = x.x; v[4 * q4 + 1] = x.y; v[4 * q4 + 2] = x.z; v[4 * q4 + 3] = x.w;
       }
-      __syncthreads();
-      uint32_t cs = 0;
-#pragma unroll 16
-      for (int r = 0; r < 64; ++r) cs += s_t[wave * 64 + r][lane];
-      s_q[wave][lane] = cs;
+      s_q[wave][lane] = reduce_scatter64(v, lane);   // this wave's 64 sub-tiles, bin 64 h + lane + 1
       __syncthreads();
       if (wave == 0) tot[h] += s_q[0][lane] + s_q[1][lane] + s_q[2][lane] + s_q[3][lane];
       __syncthreads();
@@ -927,36 +948,13 @@ __device__ __forceinline__ void hist_row_load(const uint32_t* __restrict__ tile_
   }
 }
 
-// one stage of the reduce-scatter below, width W <= 8 (DPP partner lane ^ W)
-template <int W>
-__device__ __forceinline__ void reduce_scatter_stage(uint32_t (&v)[64], int lane) {
-  const bool up = (lane & W) != 0;
-#pragma unroll
-  for (int i = 0; i < W; ++i) {
-    const uint32_t send = up ? v[i] : v[i + W];
-    const uint32_t keep = up ? v[i + W] : v[i];
-    v[i] = keep + dpp_xor<W>(send);
-  }
-}
-
 __device__ __forceinline__ void select_params_wave(const uint32_t (&h)[64], int64_t n, int subs, int sub_len,
                                                    int tl, int g, int n_candidates, int lane, int2* s_par,
                                                    int2 (*s_base)[MAXG]) {
   uint32_t v[64];
 #pragma unroll
   for (int i = 0; i < 64; ++i) v[i] = h[i];
-  // after the stage of width w, v[i] (i < w) of lane l is the sum, over the
-  // 64 / w lanes that share l's bits below w, of bin i + (l & (64 - w));
-  // widths 32 and 16 trade register halves between lane halves / rows
-#pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = swap32_sum(v[i], v[i + 32]);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = swap16_sum(v[i], v[i + 16]);
-  reduce_scatter_stage<8>(v, lane);
-  reduce_scatter_stage<4>(v, lane);
-  reduce_scatter_stage<2>(v, lane);
-  reduce_scatter_stage<1>(v, lane);
-  const uint32_t tot = v[0];
+  const uint32_t tot = reduce_scatter64(v, lane);
   // suffix counts: suf at lane l = #{S >= l + 1}; theta = the highest bin
   // whose suffix reaches C (0: every key is taken)
   const uint32_t incl = wave_incl_scan(tot);
