@@ -160,6 +160,8 @@ typedef struct {
   float* cand_est;
 } pk_debug;
 
+
+
 /* Kernels whose launches pk_timing_* can bracket with HIP events. */
 typedef enum {
   PK_KERNEL_ENCODE = 0,
@@ -319,6 +321,16 @@ pk_status pk_timing_begin(pk_context* ctx, int32_t max_launches);
 pk_status pk_timing_end(pk_context* ctx, pk_kernel_timing* timings);
 
 /* ---- diagnostics ---------------------------------------------------------- */
+
+/* Device-side consistency flags of `ctx`, accumulated over its launches since
+ * the last call: PK_DEVICE_ERR_SLOT (a candidate's slot fell outside the list,
+ * i.e. the selection parameters did not match the collision scores; the
+ * candidate is dropped rather than written out of bounds).  Waits for
+ * `hip_stream`, copies the flags to *flags and clears them.  PK_ERR_HIP if a
+ * HIP call fails. */
+#define PK_DEVICE_ERR_SLOT 1u
+pk_status pk_device_errors(pk_context* ctx, uint32_t* flags, void* hip_stream);
+
 const char* pk_status_str(pk_status status);
 /* Last error message of `ctx`, or of the calling thread when ctx is NULL. */
 const char* pk_last_error(const pk_context* ctx);

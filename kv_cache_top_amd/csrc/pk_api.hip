@@ -35,6 +35,7 @@ struct pk_context {
   int2* sub_base = nullptr;       // [units][max_subs][4]
   int32_t* cand_idx = nullptr;    // [qheads][C]
   float* cand_est = nullptr;      // [qheads][C]
+  uint32_t* dev_err = nullptr;    // device error flags (PK_DEVICE_ERR_*)
   std::string err;
   // timing
   int timing_cap = 0;
@@ -126,7 +127,8 @@ pk_status check_launch(pk_context* ctx, const char* what) {
 }
 
 void free_scratch(pk_context* c) {
-  void* ptrs[] = {c->lut, c->rq, c->scores, c->tile_hist, c->params, c->sub_base, c->cand_idx, c->cand_est};
+  void* ptrs[] = {c->lut, c->rq, c->scores, c->tile_hist, c->params, c->sub_base, c->cand_idx, c->cand_est,
+                  c->dev_err};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (int k = 0; k < PK_N_KERNELS; ++k) {
@@ -289,6 +291,7 @@ pk_status pk_create(const pk_config* cfg, pk_context** out) {
       {(void**)&c->sub_base, U * MS * pk::MAXG * sizeof(int2)},
       {(void**)&c->cand_idx, Q * C * 4},
       {(void**)&c->cand_est, Q * C * 4},
+      {(void**)&c->dev_err, 4},
   };
   for (Alloc& a : allocs) {
     e = hipMalloc(a.p, a.bytes);
@@ -301,7 +304,8 @@ pk_status pk_create(const pk_config* cfg, pk_context** out) {
     }
   }
   // LUT bytes of absent query heads stay zero
-  if (hipMemset(c->lut, 0, U * 16 * 256 * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+  if (hipMemset(c->lut, 0, U * 16 * 256 * 4) != hipSuccess || hipMemset(c->dev_err, 0, 4) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
     free_scratch(c);
     delete c;
     return fail(nullptr, PK_ERR_HIP, "scratch initialisation failed");
@@ -402,8 +406,8 @@ pk_status check_retrieve_args(pk_context* ctx, const void* q, pk_dtype q_dtype, 
   if (st != PK_OK) return st;
   if (!q || !topk_idx) return fail(ctx, PK_ERR_INVALID_ARG, "q and topk_idx must be non-NULL");
   if (q_dtype != PK_F32 && q_dtype != PK_BF16) return fail(ctx, PK_ERR_UNSUPPORTED, "q dtype %d", (int)q_dtype);
-  if (!aligned(q, q_dtype == PK_BF16 ? 4 : 8) || !aligned(topk_idx, 4) || (topk_est && !aligned(topk_est, 4)))
-    return fail(ctx, PK_ERR_INVALID_ARG, "misaligned q / output pointer");
+  if (!aligned(q, 16) || !aligned(topk_idx, 4) || (topk_est && !aligned(topk_est, 4)))
+    return fail(ctx, PK_ERR_INVALID_ARG, "q must be 16-byte aligned, topk_idx / topk_est 4-byte aligned");
   return PK_OK;
 }
 
@@ -418,8 +422,8 @@ pk_status check_attend_args(pk_context* ctx, const void* q, pk_dtype q_dtype, co
   if (st != PK_OK) return st;
   if ((st = check_strides(ctx, v, kv_dtype, kv_strides, "v")) != PK_OK) return st;
   if (n_rows < 0) return fail(ctx, PK_ERR_INVALID_ARG, "n_rows < 0");
-  if (!aligned(q, 8) || !aligned(out, 4) || !aligned(topk_idx, 4))
-    return fail(ctx, PK_ERR_INVALID_ARG, "misaligned q / out / topk_idx");
+  if (!aligned(q, 16) || !aligned(out, 4) || !aligned(topk_idx, 4))
+    return fail(ctx, PK_ERR_INVALID_ARG, "q must be 16-byte aligned, out / topk_idx 4-byte aligned");
   return PK_OK;
 }
 
@@ -531,7 +535,7 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
 #define PK_SELECT(GG, F)                                                                                        \
   hipLaunchKernelGGL((pk::select_kernel<GG, F>), dim3(grid), dim3(256), 0, stream, ctx->scores, ctx->params,      \
                      ctx->sub_base, ctx->cand_idx, n, s->n_capacity, tiles, (int)ctx->max_subs, tile,              \
-                     cfg.n_q_heads, cfg.n_kv_heads, C, ctx->tile_hist)
+                     cfg.n_q_heads, cfg.n_kv_heads, C, ctx->tile_hist, ctx->dev_err)
 #define PK_SELECT_G(F)                     \
   switch (ctx->group) {                    \
     case 1: PK_SELECT(1, F); break;        \
@@ -820,6 +824,23 @@ pk_status pk_host_free(void* host_ptr) {
   if (!host_ptr) return PK_OK;
   hipError_t e = hipHostFree(host_ptr);
   if (e != hipSuccess) return fail(nullptr, PK_ERR_HIP, "hipHostFree failed: %s", hipGetErrorString(e));
+  return PK_OK;
+}
+
+pk_status pk_device_errors(pk_context* ctx, uint32_t* flags, void* hip_stream) {
+  static_assert(PK_DEVICE_ERR_SLOT == pk::PK_DEV_ERR_SLOT, "device error flags");
+  if (!ctx || !flags) return fail(ctx, PK_ERR_INVALID_ARG, "NULL argument");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  uint32_t v = 0;
+  PK_HIP(ctx, hipMemcpyAsync(&v, ctx->dev_err, 4, hipMemcpyDeviceToHost, stream));
+  PK_HIP(ctx, hipStreamSynchronize(stream));
+  if (v) {
+    hipLaunchKernelGGL(pk::fill_u32_kernel, dim3(1), dim3(256), 0, stream, ctx->dev_err, 0u, (int64_t)1);
+    pk_status st = check_launch(ctx, "fill");
+    if (st != PK_OK) return st;
+    PK_HIP(ctx, hipStreamSynchronize(stream));
+  }
+  *flags = v;
   return PK_OK;
 }
 

@@ -29,6 +29,9 @@ constexpr int NBIN = 64;     // collision-score bins 1..64 with rank tiers (0 is
 constexpr int NBIN_MAX = 128; // bins with percentile tiers (S <= 16 * 6 = 96)
 constexpr int MAXG = 4;      // query heads per KV head
 
+// device-side error flags (one word of the context's scratch)
+constexpr uint32_t PK_DEV_ERR_SLOT = 1u;   // a candidate slot fell outside the list
+
 // Constant tables passed by value to every kernel that needs them.
 struct Tables {
   uint32_t neg_bits[4];      // bit j of the 128-bit mask set <=> SRHT sign j is -1
@@ -536,6 +539,46 @@ __device__ __forceinline__ void fwht_stage(float& v0, float& v1, int lane) {
   v1 = upper ? (p1 - v1) : (v1 + p1);
 }
 
+// The unnormalised rotation y = H (s * q) of one query head by one wave: lane l
+// ends with coordinates l (v0) and l + 64 (v1).  Butterflies h = 1..32 pair
+// lanes l and l ^ h, h = 64 pairs the two registers.
+template <typename QT>
+__device__ __forceinline__ void rotate_query(const QT* __restrict__ qh, const Tables& tb, int lane, float& v0,
+                                             float& v1) {
+  if constexpr (sizeof(QT) == 2) {
+    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(qh);
+    v0 = __uint_as_float((uint32_t)q16[lane] << 16);
+    v1 = __uint_as_float((uint32_t)q16[lane + 64] << 16);
+  } else {
+    v0 = qh[lane];
+    v1 = qh[lane + 64];
+  }
+  v0 = __uint_as_float(__float_as_uint(v0) ^ (((tb.neg_bits[lane >> 5] >> (lane & 31)) & 1u) << 31));
+  v1 = __uint_as_float(__float_as_uint(v1) ^ (((tb.neg_bits[2 + (lane >> 5)] >> (lane & 31)) & 1u) << 31));
+  fwht_stage<1>(v0, v1, lane);
+  fwht_stage<2>(v0, v1, lane);
+  fwht_stage<4>(v0, v1, lane);
+  fwht_stage<8>(v0, v1, lane);
+  fwht_stage<16>(v0, v1, lane);
+  fwht_stage<32>(v0, v1, lane);
+  const float a0 = v0, a1 = v1;
+  v0 = a0 + a1;
+  v1 = a0 - a1;
+}
+
+// Centroid score keys of subspace b (yb: its 8 rotated coordinates): centroid
+// c = lane + 64 r scores sum_j (bit_j(c) ? +y_j : -y_j), sequential in j.
+__device__ __forceinline__ void centroid_keys(const float (&yb)[SUBD], int lane, uint32_t (&key)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t c = lane + 64 * r;
+    float sc = (c & 1u) ? yb[0] : -yb[0];
+#pragma unroll
+    for (int j = 1; j < SUBD; ++j) sc = sc + (((c >> j) & 1u) ? yb[j] : -yb[j]);
+    key[r] = orderable(sc);
+  }
+}
+
 constexpr int QP_WAVES = 2;
 constexpr int QP_PARTS = NSUB / QP_WAVES;   // workgroups per query head
 
@@ -556,28 +599,8 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
   const int b = part * QP_WAVES + w;        // subspace of this wave
 
   if (w == 0) {
-    // wave 0: lane l holds coordinates l and l + 64; butterflies h = 1..32
-    // pair lanes l and l ^ h, h = 64 pairs the two registers
     float v0, v1;
-    if constexpr (sizeof(QT) == 2) {
-      const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q) + (int64_t)head * D;
-      v0 = __uint_as_float((uint32_t)q16[lane] << 16);
-      v1 = __uint_as_float((uint32_t)q16[lane + 64] << 16);
-    } else {
-      v0 = q[(int64_t)head * D + lane];
-      v1 = q[(int64_t)head * D + lane + 64];
-    }
-    v0 = __uint_as_float(__float_as_uint(v0) ^ (((tb.neg_bits[lane >> 5] >> (lane & 31)) & 1u) << 31));
-    v1 = __uint_as_float(__float_as_uint(v1) ^ (((tb.neg_bits[2 + (lane >> 5)] >> (lane & 31)) & 1u) << 31));
-    fwht_stage<1>(v0, v1, lane);
-    fwht_stage<2>(v0, v1, lane);
-    fwht_stage<4>(v0, v1, lane);
-    fwht_stage<8>(v0, v1, lane);
-    fwht_stage<16>(v0, v1, lane);
-    fwht_stage<32>(v0, v1, lane);
-    const float a0 = v0, a1 = v1;
-    v0 = a0 + a1;
-    v1 = a0 - a1;
+    rotate_query<QT>(q + (int64_t)head * D, tb, lane, v0, v1);
     y[lane] = v0;
     y[lane + 64] = v1;
     if (part == 0) {
@@ -591,15 +614,9 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
 #pragma unroll
   for (int j = 0; j < SUBD; ++j) yb[j] = y[b * SUBD + j];
   uint32_t key[4];
+  centroid_keys(yb, lane, key);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t c = lane + 64 * r;
-    float sc = (c & 1u) ? yb[0] : -yb[0];
-#pragma unroll
-    for (int j = 1; j < SUBD; ++j) sc = sc + (((c >> j) & 1u) ? yb[j] : -yb[j]);
-    key[r] = orderable(sc);
-    lw[w][c] = 0;
-  }
+  for (int r = 0; r < 4; ++r) lw[w][lane + 64 * r] = 0;
 
   if (keep_m > 0) {
     percentile_tiers(key, counts + ((int64_t)unit * NSUB + b) * 256, keep_m, lw[w], lane);
@@ -948,29 +965,32 @@ __device__ __forceinline__ void hist_row_load(const uint32_t* __restrict__ tile_
   }
 }
 
-__device__ __forceinline__ void select_params_wave(const uint32_t (&h)[64], int64_t n, int subs, int sub_len,
-                                                   int tl, int g, int n_candidates, int lane, int2* s_par,
-                                                   int2 (*s_base)[MAXG]) {
-  uint32_t v[64];
-#pragma unroll
-  for (int i = 0; i < 64; ++i) v[i] = h[i];
-  const uint32_t tot = reduce_scatter64(v, lane);
-  // suffix counts: suf at lane l = #{S >= l + 1}; theta = the highest bin
-  // whose suffix reaches C (0: every key is taken)
+// theta and need_eq of one query head from its bin totals (lane l holds the
+// count of keys with S = l + 1 among the unit's n keys): theta = the highest
+// score whose suffix count #{S >= theta} reaches C (0: every key is taken);
+// need_eq = how many keys with S == theta are taken.
+__device__ __forceinline__ void theta_from_totals(uint32_t tot, int64_t n, int n_candidates, int& theta,
+                                                  uint32_t& need_eq) {
   const uint32_t incl = wave_incl_scan(tot);
   const uint32_t all_nz = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-  const uint32_t suf = all_nz - incl + tot;
+  const uint32_t suf = all_nz - incl + tot;          // lane l: #{S >= l + 1}
   const uint64_t ge = __ballot(suf >= (uint32_t)n_candidates);
   const int top = ge ? 63 - __builtin_clzll(ge) : -1;
-  const int theta = top + 1;
+  theta = top + 1;
   const uint32_t n_gt = (top < 0) ? all_nz
                         : (top == 63 ? 0u : (uint32_t)__builtin_amdgcn_readlane((int)suf, (top + 1) & 63));
   const uint32_t eq_tot = (theta > 0) ? (uint32_t)__builtin_amdgcn_readlane((int)tot, (theta - 1) & 63)
                                       : (uint32_t)(n - n_gt);
   const uint32_t want = (uint32_t)n_candidates - n_gt;
-  const uint32_t need_eq = want < eq_tot ? want : eq_tot;
-  // this lane's sub-tile: keys above / at theta, then exclusive prefixes
-  int gt = 0, eq = 0, nz = 0;
+  need_eq = want < eq_tot ? want : eq_tot;
+}
+
+// keys of one histogram (h[b] = count of S = b + 1 among len keys) above and
+// at theta
+__device__ __forceinline__ void counts_at_theta(const uint32_t (&h)[64], int theta, int64_t len, int& gt, int& eq) {
+  int nz = 0;
+  gt = 0;
+  eq = 0;
 #pragma unroll
   for (int b = 0; b < 64; ++b) {
     const int c = (int)h[b];
@@ -978,15 +998,84 @@ __device__ __forceinline__ void select_params_wave(const uint32_t (&h)[64], int6
     gt += (b + 1 > theta) ? c : 0;
     eq = (b + 1 == theta) ? c : eq;
   }
+  if (theta == 0) eq = (int)len - nz;
+}
+
+__device__ __forceinline__ void select_params_wave(const uint32_t (&h)[64], int64_t n, int subs, int sub_len,
+                                                   int tl, int g, int n_candidates, int lane, int2* s_par,
+                                                   int2 (*s_base)[MAXG]) {
+  uint32_t v[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) v[i] = h[i];
+  int theta;
+  uint32_t need_eq;
+  theta_from_totals(reduce_scatter64(v, lane), n, n_candidates, theta, need_eq);
+  // this lane's sub-tile: keys above / at theta, then exclusive prefixes
   int64_t len = n - (int64_t)lane * sub_len;
   len = len < 0 ? 0 : (len > sub_len ? sub_len : len);
-  if (theta == 0) eq = (int)len - nz;
+  int gt, eq;
+  counts_at_theta(h, theta, len, gt, eq);
   if (lane >= subs) { gt = 0; eq = 0; }
   const int pg = (int)wave_incl_scan((uint32_t)gt), pe = (int)wave_incl_scan((uint32_t)eq);
   const int w = lane - 4 * tl;
   if (w >= 0 && w < 4) s_base[w][g] = make_int2(pg - gt, pe - eq);
   if (lane == 0) s_par[g] = make_int2(theta, (int)need_eq);
 }
+
+// Per-head selection state of one wave walking its keys in ascending order:
+// theta, need_eq and the counts of keys above / at theta seen so far (the
+// keys before the wave's first one included).  A key is a candidate of head g
+// iff S > theta, or S == theta and fewer than need_eq keys with S == theta
+// precede it; its slot is (#gt before) + min(#eq before, need_eq), so the list
+// is in ascending key order.  Four heads' scores are the bytes of one u32 and
+// are compared at once.
+template <int G>
+struct HeadSelect {
+  int need[G], run_gt[G], run_eq[G];
+  uint32_t th4 = 0x7F7F7F7Fu;     // absent heads: theta 127, never reached
+  uint32_t thp4 = 0;              // theta + 1 per byte
+  // compaction thresholds: theta, or theta + 1 for a head whose keys at theta
+  // are all taken before the wave's keys (they can no longer be candidates)
+  uint32_t thf4 = 0x7F7F7F7Fu;
+
+  __device__ __forceinline__ void set(int g, int theta, int need_eq, int gt_before, int eq_before) {
+    need[g] = need_eq;
+    run_gt[g] = gt_before;
+    run_eq[g] = eq_before;
+    th4 = (th4 & ~(0xFFu << (8 * g))) | ((uint32_t)theta << (8 * g));
+    thf4 = (thf4 & ~(0xFFu << (8 * g))) | ((uint32_t)(eq_before >= need_eq ? theta + 1 : theta) << (8 * g));
+  }
+  __device__ __forceinline__ void finish() { thp4 = th4 + 0x01010101u; }   // <= 128 per byte: no carry
+
+  // nonzero iff some head may take a key with packed scores s
+  __device__ __forceinline__ uint32_t interesting(uint32_t s) const { return ((s | 0x80808080u) - thf4) & 0x80808080u; }
+
+  // the compacted keys e[0 .. cnt) of the wave, one per lane (cnt <= 64):
+  // per-head ballots give each taken key its slot
+  __device__ __forceinline__ void batch(uint2 e, bool valid, int32_t* __restrict__ cand_idx, int64_t qhead0,
+                                        int n_candidates, uint32_t* err) {
+    const uint32_t m = e.y | 0x80808080u;
+    const uint32_t gt4 = (m - thp4) & 0x80808080u;
+    const uint32_t eq4 = ((m - th4) & 0x80808080u) ^ gt4;
+    bool over = false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const bool isgt = valid && ((gt4 >> (8 * g + 7)) & 1u);
+      const bool iseq = valid && ((eq4 >> (8 * g + 7)) & 1u);
+      const uint64_t gtm = __ballot(isgt), eqm = __ballot(iseq);
+      const int gt_before = run_gt[g] + (int)mbcnt(gtm);
+      const int eq_before = run_eq[g] + (int)mbcnt(eqm);
+      const bool sel = isgt || (iseq && eq_before < need[g]);
+      const int pos = gt_before + (eq_before < need[g] ? eq_before : need[g]);
+      if (sel && pos < n_candidates)              // pos < C whenever the parameters match S
+        cand_idx[(qhead0 + g) * n_candidates + pos] = (int)e.x;
+      over = over || (sel && pos >= n_candidates);
+      run_gt[g] += __popcll(gtm);
+      run_eq[g] += __popcll(eqm);
+    }
+    if (over && err) atomicOr(err, PK_DEV_ERR_SLOT);
+  }
+};
 
 // FUSED: the unit has at most 64 sub-tiles of 64-bin histograms, and each
 // workgroup derives the parameters itself (select_params_wave) instead of
@@ -998,7 +1087,7 @@ __global__ void __launch_bounds__(256)
 select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__ params,
               const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx, int64_t n, int64_t n_cap,
               int tiles, int max_subs, int tile, int n_q_heads, int n_kv_heads, int n_candidates,
-              const uint32_t* __restrict__ tile_hist) {
+              const uint32_t* __restrict__ tile_hist, uint32_t* __restrict__ err) {
   __shared__ uint2 s_ik[4][SEL_QCAP];             // compacted keys: (key, packed S)
   __shared__ int2 s_par[FUSED ? MAXG : 1];
   __shared__ int2 s_base[FUSED ? 4 : 1][MAXG];
@@ -1007,7 +1096,7 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
   xcd_unit_tile(blockIdx.x, gridDim.x / tiles, tiles, unit, tl);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int seq = unit / n_kv_heads, kvh = unit - seq * n_kv_heads;
-  const int qhead0 = seq * n_q_heads + kvh * G;
+  const int64_t qhead0 = (int64_t)seq * n_q_heads + kvh * G;
   // key indices fit in 32 bits (n <= n_capacity < 2^31)
   const int k0 = tl * tile;
   const int k1 = ((int64_t)k0 + tile < n) ? k0 + tile : (int)n;
@@ -1033,12 +1122,7 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
     const int i = w0 + r * 64 + lane;
     sp[r] = srow[i < last ? i : last];
   }
-  int need[G], run_gt[G], run_eq[G];
-  uint32_t th4 = 0x7F7F7F7Fu;                     // absent heads: theta 127, never reached
-  uint32_t thp4 = 0;
-  // compaction thresholds: theta, or theta + 1 for a head whose keys at theta
-  // are all taken before this sub-tile (they can no longer be candidates)
-  uint32_t thf4 = 0x7F7F7F7Fu;
+  HeadSelect<G> hs;
   // per head: theta, need_eq, and the counts of keys above / at theta before
   // this wave's sub-tile
   auto setup = [&]() __attribute__((always_inline)) {
@@ -1048,46 +1132,24 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      int theta, ne, bg, be;
       if constexpr (FUSED) {
         const int2 pr = s_par[g], sb2 = s_base[wave][g];
-        theta = pr.x; ne = pr.y; bg = sb2.x; be = sb2.y;
+        hs.set(g, pr.x, pr.y, sb2.x, sb2.y);
       } else {
         const SelParams p = params[unit * MAXG + g];
         const int2 sb2 = sub_base[((int64_t)unit * max_subs + 4 * tl + wave) * MAXG + g];
-        theta = p.theta; ne = p.need_eq; bg = sb2.x; be = sb2.y;
+        hs.set(g, p.theta, p.need_eq, sb2.x, sb2.y);
       }
-      need[g] = ne; run_gt[g] = bg; run_eq[g] = be;
-      th4 = (th4 & ~(0xFFu << (8 * g))) | ((uint32_t)theta << (8 * g));
-      thf4 = (thf4 & ~(0xFFu << (8 * g))) | ((uint32_t)(be >= ne ? theta + 1 : theta) << (8 * g));
     }
-    thp4 = th4 + 0x01010101u;                     // theta + 1 per byte (<= 128: no carry)
+    hs.finish();
   };
   setup();        // behind the first group's loads; the other groups are requested after it
   uint2* ik = s_ik[wave];
   int nk = 0;
 
-  // per-head selection of the compacted keys b0 .. b0 + cnt - 1 (cnt <= 64)
   auto select_batch = [&](int b0, int cnt) {
     const bool valid = lane < cnt;
-    const uint2 e = ik[b0 + (valid ? lane : 0)];
-    const uint32_t m = e.y | 0x80808080u;
-    const uint32_t gt4 = (m - thp4) & 0x80808080u;
-    const uint32_t eq4 = ((m - th4) & 0x80808080u) ^ gt4;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const bool isgt = valid && ((gt4 >> (8 * g + 7)) & 1u);
-      const bool iseq = valid && ((eq4 >> (8 * g + 7)) & 1u);
-      const uint64_t gtm = __ballot(isgt), eqm = __ballot(iseq);
-      const int gt_before = run_gt[g] + (int)mbcnt(gtm);
-      const int eq_before = run_eq[g] + (int)mbcnt(eqm);
-      const bool sel = isgt || (iseq && eq_before < need[g]);
-      const int pos = gt_before + (eq_before < need[g] ? eq_before : need[g]);
-      if (sel && pos < n_candidates)              // pos < C whenever the parameters match S
-        cand_idx[(int64_t)(qhead0 + g) * n_candidates + pos] = (int)e.x;
-      run_gt[g] += __popcll(gtm);
-      run_eq[g] += __popcll(eqm);
-    }
+    hs.batch(ik[b0 + (valid ? lane : 0)], valid, cand_idx, qhead0, n_candidates, err);
   };
 
   // Every group of the sub-tile is loaded before the first is compacted, and
@@ -1107,8 +1169,7 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
     for (int r = 0; r < SEL_GRP; ++r) {
       const int i = w0 + (grp * SEL_GRP + r) * 64 + lane;
       const bool valid = i < w1;                  // false for the whole wave past its keys
-      const uint32_t ge4 = ((src[r] | 0x80808080u) - thf4) & 0x80808080u;
-      const bool interesting = valid && ge4 != 0u;
+      const bool interesting = valid && hs.interesting(src[r]) != 0u;
       const uint64_t im = __ballot(interesting);
       if (interesting) ik[nk + (int)mbcnt(im)] = make_uint2((uint32_t)i, src[r]);
       nk += __popcll(im);

@@ -33,6 +33,7 @@ PK_TIERS_RANK, PK_TIERS_PERCENTILE = 0, 1
 PK_MAX_CANDIDATES, PK_MAX_TOPK, PK_MAX_DENSE = 16384, 256, 8192
 KERNELS = ["encode", "qprep", "collide", "threshold", "select", "rerank", "topk", "attend", "rerank_topk",
            "dense_attend"]
+PK_DEVICE_ERR_SLOT = 1
 PK_N_KERNELS = len(KERNELS)
 
 
@@ -88,6 +89,7 @@ _SIGS = {
     "pk_host_alloc_mapped": ([ctypes.c_size_t, ctypes.POINTER(_P), ctypes.POINTER(_P)], ctypes.c_int),
     "pk_host_free": ([_P], ctypes.c_int),
     "pk_calibration_copy": ([_P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "pk_device_errors": ([_P, ctypes.POINTER(ctypes.c_uint32), _P], ctypes.c_int),
     "pk_timing_begin": ([_P, ctypes.c_int32], ctypes.c_int),
     "pk_timing_end": ([_P, ctypes.POINTER(pk_kernel_timing)], ctypes.c_int),
     "pk_status_str": ([ctypes.c_int], ctypes.c_char_p),
@@ -142,6 +144,77 @@ def _strides4(t):
     return _I64x3(t.stride(0), t.stride(1), t.stride(2))
 
 
+# configuration of every live context, by handle value: the C ABI sees raw
+# pointers only, so shapes, dtypes and devices are checked here before a call
+_CONFIGS: dict = {}
+
+
+def _handle_value(ctx) -> int:
+    return ctx.value if isinstance(ctx, ctypes.c_void_p) else int(ctx)
+
+
+def _cfg_of(ctx) -> "pk_config":
+    cfg = _CONFIGS.get(_handle_value(ctx) if ctx else 0)
+    if cfg is None:
+        raise ValueError("unknown or destroyed context")
+    return cfg
+
+
+def _need(t, name: str, shape, dtypes, contiguous: bool = True):
+    """Shape, dtype, layout and then device of one tensor argument."""
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    del torch
+
+
+def _need_rows(t, name: str, cfg, dtypes):
+    """[>= batch, >= n_kv_heads, rows, 128] K/V-like tensor on the GPU."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dim() != 4 or t.shape[0] < cfg.batch or t.shape[1] < cfg.n_kv_heads or t.shape[3] != 128:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected [>= {cfg.batch}, >= {cfg.n_kv_heads}, rows, 128]")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+
+
+def _float_types():
+    import torch
+    return (torch.float32, torch.bfloat16)
+
+
+def _check_q(cfg, q):
+    _need(q, "q", (cfg.batch, cfg.n_q_heads, 128), _float_types())
+
+
+def _check_topk(cfg, topk_idx, topk_est):
+    import torch
+    _need(topk_idx, "topk_idx", (cfg.batch, cfg.n_q_heads, cfg.top_k), (torch.int32,))
+    if topk_est is not None:
+        _need(topk_est, "topk_est", (cfg.batch, cfg.n_q_heads, cfg.top_k), (torch.float32,))
+
+
+def _check_out(cfg, out):
+    _need(out, "out", (cfg.batch, cfg.n_q_heads, 128), _float_types())
+
+
+def _check_kv(cfg, k, v):
+    _need_rows(k, "k", cfg, _float_types())
+    _need_rows(v, "v", cfg, _float_types())
+    if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
+        raise ValueError("K and V must share shape, dtype and strides")
+
+
 def make_config(batch, n_kv_heads, n_q_heads, n_capacity, n_candidates, top_k=100, softmax_scale=None,
                 srht_seed=0, tier_top=(1, 4, 16), tier_weight=(4, 2, 1), tier_mode=PK_TIERS_RANK,
                 collision_permille=0, adaptive_ratios=False) -> pk_config:
@@ -184,36 +257,46 @@ def pk_tables(seed: int):
 def pk_create(cfg: pk_config):
     h = ctypes.c_void_p()
     _check(_lib.pk_create(ctypes.byref(cfg), ctypes.byref(h)))
+    keep = pk_config()
+    ctypes.pointer(keep)[0] = cfg
+    _CONFIGS[h.value] = keep
     return h
 
 
 def pk_destroy(ctx) -> None:
+    _CONFIGS.pop(_handle_value(ctx) if ctx else 0, None)
     _lib.pk_destroy(ctx)
 
 
 def pk_encode_keys(ctx, keys, sums: pk_summaries, stream=None):
+    cfg = _cfg_of(ctx)
+    _need_rows(keys, "keys", cfg, _float_types())
     _check(_lib.pk_encode_keys(ctx, _ptr(keys), _dtype(keys), _strides4(keys), keys.shape[2],
                                ctypes.byref(sums), _stream(stream)), ctx)
 
 
 def pk_append_keys(ctx, new_keys, sums: pk_summaries, stream=None):
+    cfg = _cfg_of(ctx)
+    _need_rows(new_keys, "new_keys", cfg, _float_types())
     _check(_lib.pk_append_keys(ctx, _ptr(new_keys), _dtype(new_keys), _strides4(new_keys), new_keys.shape[2],
                                ctypes.byref(sums), _stream(stream)), ctx)
 
 
 def pk_retrieve(ctx, q, sums: pk_summaries, topk_idx, topk_est=None, debug: pk_debug | None = None,
                 stream=None):
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous [batch, n_q_heads, 128]")
+    cfg = _cfg_of(ctx)
+    _check_q(cfg, q)
+    _check_topk(cfg, topk_idx, topk_est)
     _check(_lib.pk_retrieve(ctx, _ptr(q), _dtype(q), ctypes.byref(sums), _ptr(topk_idx), _ptr(topk_est),
                             ctypes.byref(debug) if debug is not None else None, _stream(stream)), ctx)
 
 
 def pk_sparse_attend(ctx, q, k, v, topk_idx, out, stream=None):
-    if k.stride() != v.stride() or k.dtype != v.dtype:
-        raise ValueError("K and V must share dtype and strides")
-    if not q.is_contiguous() or not out.is_contiguous():
-        raise ValueError("q and out must be contiguous")
+    cfg = _cfg_of(ctx)
+    _check_q(cfg, q)
+    _check_kv(cfg, k, v)
+    _check_topk(cfg, topk_idx, None)
+    _check_out(cfg, out)
     _check(_lib.pk_sparse_attend(ctx, _ptr(q), _dtype(q), _ptr(k), _ptr(v), _dtype(k), _strides4(k),
                                  k.shape[2], _ptr(topk_idx), _ptr(out), _dtype(out), _stream(stream)), ctx)
 
@@ -221,6 +304,10 @@ def pk_sparse_attend(ctx, q, k, v, topk_idx, out, stream=None):
 def pk_sparse_attend_raw(ctx, q, k_ptr: int, v_ptr: int, kv_dtype: int, kv_strides, n_rows: int, topk_idx, out,
                          stream=None):
     """Variant for K/V that are not torch tensors (e.g. mapped host memory)."""
+    cfg = _cfg_of(ctx)
+    _check_q(cfg, q)
+    _check_topk(cfg, topk_idx, None)
+    _check_out(cfg, out)
     _check(_lib.pk_sparse_attend(ctx, _ptr(q), _dtype(q), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
                                  kv_dtype, _I64x3(*kv_strides), n_rows, _ptr(topk_idx), _ptr(out), _dtype(out),
                                  _stream(stream)), ctx)
@@ -228,10 +315,11 @@ def pk_sparse_attend_raw(ctx, q, k_ptr: int, v_ptr: int, kv_dtype: int, kv_strid
 
 def pk_retrieve_attend(ctx, q, sums: pk_summaries, k, v, topk_idx, out, topk_est=None,
                        debug: pk_debug | None = None, stream=None):
-    if k.stride() != v.stride() or k.dtype != v.dtype:
-        raise ValueError("K and V must share dtype and strides")
-    if not q.is_contiguous() or not out.is_contiguous():
-        raise ValueError("q and out must be contiguous")
+    cfg = _cfg_of(ctx)
+    _check_q(cfg, q)
+    _check_kv(cfg, k, v)
+    _check_topk(cfg, topk_idx, topk_est)
+    _check_out(cfg, out)
     _check(_lib.pk_retrieve_attend(ctx, _ptr(q), _dtype(q), ctypes.byref(sums), _ptr(k), _ptr(v), _dtype(k),
                                    _strides4(k), k.shape[2], _ptr(topk_idx), _ptr(topk_est), _ptr(out), _dtype(out),
                                    ctypes.byref(debug) if debug is not None else None, _stream(stream)), ctx)
@@ -240,6 +328,10 @@ def pk_retrieve_attend(ctx, q, sums: pk_summaries, k, v, topk_idx, out, topk_est
 def pk_retrieve_attend_raw(ctx, q, sums: pk_summaries, k_ptr: int, v_ptr: int, kv_dtype: int, kv_strides,
                            n_rows: int, topk_idx, out, topk_est=None, debug: pk_debug | None = None, stream=None):
     """Variant for K/V that are not torch tensors (e.g. mapped host memory)."""
+    cfg = _cfg_of(ctx)
+    _check_q(cfg, q)
+    _check_topk(cfg, topk_idx, topk_est)
+    _check_out(cfg, out)
     _check(_lib.pk_retrieve_attend(ctx, _ptr(q), _dtype(q), ctypes.byref(sums), ctypes.c_void_p(k_ptr),
                                    ctypes.c_void_p(v_ptr), kv_dtype, _I64x3(*kv_strides), n_rows, _ptr(topk_idx),
                                    _ptr(topk_est), _ptr(out), _dtype(out),
@@ -248,12 +340,14 @@ def pk_retrieve_attend_raw(ctx, q, sums: pk_summaries, k_ptr: int, v_ptr: int, k
 
 def pk_sparse_dense_attend(ctx, q, k, v, topk_idx, dense_k, dense_v, out, stream=None):
     """Attention over the retrieved rows of k / v and every row of dense_k / dense_v."""
-    if k.stride() != v.stride() or k.dtype != v.dtype or dense_k.stride() != dense_v.stride():
-        raise ValueError("K and V must share dtype and strides")
-    if dense_k.dtype != k.dtype or dense_v.dtype != k.dtype:
+    cfg = _cfg_of(ctx)
+    _check_q(cfg, q)
+    _check_kv(cfg, k, v)
+    _check_kv(cfg, dense_k, dense_v)
+    if dense_k.dtype != k.dtype:
         raise ValueError("dense rows must have the dtype of K / V")
-    if not q.is_contiguous() or not out.is_contiguous():
-        raise ValueError("q and out must be contiguous")
+    _check_topk(cfg, topk_idx, None)
+    _check_out(cfg, out)
     _check(_lib.pk_sparse_dense_attend(ctx, _ptr(q), _dtype(q), _ptr(k), _ptr(v), _dtype(k), _strides4(k),
                                        k.shape[2], _ptr(topk_idx), _ptr(dense_k), _ptr(dense_v),
                                        _strides4(dense_k), dense_k.shape[2], _ptr(out), _dtype(out),
@@ -276,6 +370,13 @@ def pk_calibration_copy(dst, src, stream=None) -> None:
     if dst.numel() * dst.element_size() != n:
         raise ValueError("dst and src differ in size")
     _check(_lib.pk_calibration_copy(_ptr(dst), _ptr(src), n, _stream(stream)))
+
+
+def pk_device_errors(ctx, stream=None) -> int:
+    """Device-side consistency flags since the last call (waits for the stream, then clears them)."""
+    v = ctypes.c_uint32()
+    _check(_lib.pk_device_errors(ctx, ctypes.byref(v), _stream(stream)), ctx)
+    return v.value
 
 
 def pk_timing_begin(ctx, max_launches: int) -> None:

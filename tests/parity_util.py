@@ -157,6 +157,9 @@ class GpuRun:
         torch.cuda.synchronize()
         return self
 
+    def device_errors(self) -> int:
+        return self.P.pk_device_errors(self.ctx.h)
+
     def close(self):
         self.ctx.close()
         for h in self.host_bufs:

@@ -166,3 +166,63 @@ def test_tables_equal_oracle(seed):
     assert np.frombuffer(levels, np.float32).tobytes() == L32.astype(np.float32).tobytes()
     assert np.frombuffer(thr, np.float32).tobytes() == T32.astype(np.float32).tobytes()
     assert P._lib.pk_tables(0, None, levels, thr) == P.PK_ERR_INVALID_ARG
+
+
+@pytest.fixture
+def fake_ctx():
+    """A registered configuration under a handle that is never passed to the
+    library: the binding's checks run, and each case below must raise before
+    any call reaches it."""
+    import torch  # noqa: F401
+    cfg = good_config(batch=2, n_kv_heads=2, n_q_heads=8, top_k=16)
+    h = ctypes.c_void_p(0x5EED0)
+    P._CONFIGS[h.value] = cfg
+    yield h, cfg
+    P._CONFIGS.pop(h.value, None)
+
+
+def test_binding_refuses_misshaped_tensors(fake_ctx):
+    import torch
+    h, cfg = fake_ctx
+    B, Hq, Hk, k = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.top_k
+    q = torch.zeros((B, Hq, 128), dtype=torch.bfloat16)
+    idx = torch.zeros((B, Hq, k), dtype=torch.int32)
+    out = torch.zeros((B, Hq, 128), dtype=torch.bfloat16)
+    kv = torch.zeros((B, Hk, 64, 128), dtype=torch.bfloat16)
+    sums = P.pk_summaries()
+    cases = {
+        "q heads": lambda: P.pk_retrieve(h, torch.zeros((B, Hq - 1, 128), dtype=torch.bfloat16), sums, idx),
+        "q dim": lambda: P.pk_retrieve(h, torch.zeros((B, Hq, 64), dtype=torch.bfloat16), sums, idx),
+        "q dtype": lambda: P.pk_retrieve(h, q.half(), sums, idx),
+        "q strided": lambda: P.pk_retrieve(h, torch.zeros((B, Hq, 256), dtype=torch.bfloat16)[:, :, ::2], sums, idx),
+        "topk_idx int64": lambda: P.pk_retrieve(h, q, sums, idx.long()),
+        "topk_idx short": lambda: P.pk_retrieve(h, q, sums, idx[:, :, :k - 1]),
+        "topk_est shape": lambda: P.pk_retrieve(h, q, sums, idx, torch.zeros((B, Hq, k + 1))),
+        "out too small": lambda: P.pk_sparse_attend(h, q, kv, kv, idx, out[:, :Hq - 1]),
+        "kv too few heads": lambda: P.pk_sparse_attend(h, q, kv[:, :Hk - 1], kv[:, :Hk - 1], idx, out),
+        "kv too few sequences": lambda: P.pk_retrieve_attend(h, q, sums, kv[:B - 1], kv[:B - 1], idx, out),
+        "k / v differ": lambda: P.pk_sparse_attend(h, q, kv, kv[:, :, :32], idx, out),
+        "dense too few heads": lambda: P.pk_sparse_dense_attend(h, q, kv, kv, idx, kv[:, :1], kv[:, :1], out),
+        "keys too few heads": lambda: P.pk_encode_keys(h, kv[:, :1], sums),
+    }
+    for name, call in cases.items():
+        with pytest.raises(ValueError):
+            call()
+        assert name  # every case raised
+
+
+def test_binding_refuses_host_tensors(fake_ctx):
+    import torch
+    h, cfg = fake_ctx
+    q = torch.zeros((cfg.batch, cfg.n_q_heads, 128), dtype=torch.bfloat16)
+    idx = torch.zeros((cfg.batch, cfg.n_q_heads, cfg.top_k), dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        P.pk_retrieve(h, q, P.pk_summaries(), idx)
+
+
+def test_binding_refuses_unknown_context():
+    import torch
+    with pytest.raises(ValueError, match="context"):
+        P.pk_retrieve(ctypes.c_void_p(0x5EED1), torch.zeros((1, 1, 128)), P.pk_summaries(),
+                      torch.zeros((1, 1, 1), dtype=torch.int32))
+

@@ -193,4 +193,16 @@ def test_capacity_and_argument_errors():
     st = P._lib.pk_retrieve(run.ctx.h, ctypes.c_void_p(run.Qt.data_ptr()), P.PK_BF16, ctypes.byref(run.sums.s),
                             None, None, None, None)
     assert st == P.PK_ERR_INVALID_ARG
+    # q is read with 16-byte vector loads: a q that is only 8-byte aligned is refused
+    qbuf = torch.zeros(128 + 8, dtype=torch.bfloat16, device="cuda")
+    for call in (lambda qp: P._lib.pk_retrieve(run.ctx.h, qp, P.PK_BF16, ctypes.byref(run.sums.s),
+                                               ctypes.c_void_p(out.data_ptr()), None, None, None),
+                 lambda qp: P._lib.pk_sparse_attend(run.ctx.h, qp, P.PK_BF16, ctypes.c_void_p(run.Kt.data_ptr()),
+                                                    ctypes.c_void_p(run.Vt.data_ptr()), P.PK_BF16,
+                                                    P._strides4(run.Kt), run.Kt.shape[2],
+                                                    ctypes.c_void_p(out.data_ptr()),
+                                                    ctypes.c_void_p(qbuf.data_ptr()), P.PK_BF16, None)):
+        assert call(ctypes.c_void_p(qbuf.data_ptr() + 8)) == P.PK_ERR_INVALID_ARG
+        assert "16-byte" in P.pk_last_error(run.ctx.h)
+    assert run.device_errors() == 0
     run.close()
