@@ -104,16 +104,17 @@ int64_t max_tiles_for(int units, int64_t n_cap) {
   return (by_min < m ? by_min : m) + 2;
 }
 
+// HIP events around one launch when the context is timing (ctx may be NULL)
 struct Launch {
   pk_context* ctx;
   int kid;
   hipStream_t s;
   Launch(pk_context* c, int k, hipStream_t st) : ctx(c), kid(k), s(st) {
-    if (ctx->timing_cap && ctx->ev_used[kid] < ctx->timing_cap)
+    if (ctx && ctx->timing_cap && ctx->ev_used[kid] < ctx->timing_cap)
       (void)hipEventRecord(ctx->ev[kid][2 * ctx->ev_used[kid]], s);
   }
   ~Launch() {
-    if (ctx->timing_cap && ctx->ev_used[kid] < ctx->timing_cap) {
+    if (ctx && ctx->timing_cap && ctx->ev_used[kid] < ctx->timing_cap) {
       (void)hipEventRecord(ctx->ev[kid][2 * ctx->ev_used[kid] + 1], s);
       ctx->ev_used[kid]++;
     }
@@ -345,18 +346,18 @@ static pk_status fill_words(pk_context* ctx, uint32_t* p, uint32_t value, int64_
   return check_launch(ctx, "fill");
 }
 
-static pk_status check_summaries(pk_context* ctx, const pk_summaries* s) {
+static pk_status check_summaries(pk_context* ctx, const pk_config& cfg, const pk_summaries* s) {
   if (!s) return fail(ctx, PK_ERR_INVALID_ARG, "summaries pointer is NULL");
   if (!s->codes || !s->records || !s->norms) return fail(ctx, PK_ERR_INVALID_ARG, "summary array is NULL");
   if (!aligned(s->codes, 16) || !aligned(s->records, 128) || !aligned(s->norms, 4))
     return fail(ctx, PK_ERR_INVALID_ARG, "codes must be 16-byte and records 128-byte aligned");
-  if (s->n_capacity != ctx->cfg.n_capacity)
+  if (s->n_capacity != cfg.n_capacity)
     return fail(ctx, PK_ERR_INVALID_ARG, "summaries n_capacity (%lld) differs from the context's (%lld)",
-                (long long)s->n_capacity, (long long)ctx->cfg.n_capacity);
+                (long long)s->n_capacity, (long long)cfg.n_capacity);
   if (s->n < 0 || s->n > s->n_capacity)
     return fail(ctx, PK_ERR_INVALID_ARG, "summaries n (%lld) outside 0..n_capacity", (long long)s->n);
   if (s->counts && !aligned(s->counts, 4)) return fail(ctx, PK_ERR_INVALID_ARG, "counts must be 4-byte aligned");
-  if (ctx->cfg.tier_mode == PK_TIERS_PERCENTILE && !s->counts)
+  if (cfg.tier_mode == PK_TIERS_PERCENTILE && !s->counts)
     return fail(ctx, PK_ERR_INVALID_ARG, "percentile tiers need the summaries' centroid counts");
   return PK_OK;
 }
@@ -365,7 +366,7 @@ pk_status pk_encode_keys(pk_context* ctx, const void* keys, pk_dtype dt, const i
                          int64_t n, pk_summaries* inout, void* hip_stream) {
   if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
   if (dt != PK_F32 && dt != PK_BF16) return fail(ctx, PK_ERR_UNSUPPORTED, "key dtype %d", (int)dt);
-  pk_status st = check_summaries(ctx, inout);
+  pk_status st = check_summaries(ctx, ctx->cfg, inout);
   if (st != PK_OK) return st;
   if (n < 0) return fail(ctx, PK_ERR_INVALID_ARG, "n < 0");
   if (n > inout->n_capacity)
@@ -383,7 +384,7 @@ pk_status pk_append_keys(pk_context* ctx, const void* keys, pk_dtype dt, const i
                          int64_t t, pk_summaries* inout, void* hip_stream) {
   if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
   if (dt != PK_F32 && dt != PK_BF16) return fail(ctx, PK_ERR_UNSUPPORTED, "key dtype %d", (int)dt);
-  pk_status st = check_summaries(ctx, inout);
+  pk_status st = check_summaries(ctx, ctx->cfg, inout);
   if (st != PK_OK) return st;
   if (t < 0) return fail(ctx, PK_ERR_INVALID_ARG, "t < 0");
   if (inout->n + t > inout->n_capacity)
@@ -399,10 +400,9 @@ pk_status pk_append_keys(pk_context* ctx, const void* keys, pk_dtype dt, const i
 
 namespace {
 
-pk_status check_retrieve_args(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s,
-                              const int32_t* topk_idx, const float* topk_est) {
-  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
-  pk_status st = check_summaries(ctx, s);
+pk_status check_retrieve_args(pk_context* ctx, const pk_config& cfg, const void* q, pk_dtype q_dtype,
+                              const pk_summaries* s, const int32_t* topk_idx, const float* topk_est) {
+  pk_status st = check_summaries(ctx, cfg, s);
   if (st != PK_OK) return st;
   if (!q || !topk_idx) return fail(ctx, PK_ERR_INVALID_ARG, "q and topk_idx must be non-NULL");
   if (q_dtype != PK_F32 && q_dtype != PK_BF16) return fail(ctx, PK_ERR_UNSUPPORTED, "q dtype %d", (int)q_dtype);
@@ -414,7 +414,6 @@ pk_status check_retrieve_args(pk_context* ctx, const void* q, pk_dtype q_dtype, 
 pk_status check_attend_args(pk_context* ctx, const void* q, pk_dtype q_dtype, const void* k, const void* v,
                             pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows, const int32_t* topk_idx,
                             const void* out, pk_dtype out_dtype) {
-  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
   if (!q || !topk_idx || !out) return fail(ctx, PK_ERR_INVALID_ARG, "q, topk_idx and out must be non-NULL");
   for (pk_dtype d : {q_dtype, kv_dtype, out_dtype})
     if (d != PK_F32 && d != PK_BF16) return fail(ctx, PK_ERR_UNSUPPORTED, "dtype %d", (int)d);
@@ -431,76 +430,145 @@ pk_status check_attend_args(pk_context* ctx, const void* q, pk_dtype q_dtype, co
 // that selects each head's Top-k (rerank + top-k, or top-k after the spread
 // rerank) also computes the attention and *attended is set; otherwise the
 // caller still has to attend.
-pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s,
-                        int32_t* topk_idx, float* topk_est, const pk_debug* dbg, hipStream_t stream,
-                        const pk::AttendArgs* att, bool* attended) {
-  pk_status st = PK_OK;
-  if (attended) *attended = false;
-  const pk_config& cfg = ctx->cfg;
-  const int64_t n = s->n;
-  const int k = cfg.top_k, C_cap = cfg.n_candidates;
-  if (n == 0) {
-    const int64_t cnt = (int64_t)ctx->qheads * k;
-    hipLaunchKernelGGL(pk::fill_empty_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream, topk_idx,
-                       topk_est, cnt);
-    if ((st = check_launch(ctx, "fill")) != PK_OK) return st;
-    if (dbg && dbg->cand_idx) {
-      const int64_t cc = (int64_t)ctx->qheads * C_cap;
-      hipLaunchKernelGGL(pk::fill_empty_kernel, dim3((unsigned)((cc + 255) / 256)), dim3(256), 0, stream,
-                         dbg->cand_idx, dbg->cand_est, cc);
-      if ((st = check_launch(ctx, "fill")) != PK_OK) return st;
-    }
-    return PK_OK;
-  }
-  // candidates C and, with percentile tiers, the kept positions M of this call
-  // (Slides Sec. 4.2.2: C = ceil(beta n); README "Parameters": adaptive ratios)
-  int64_t C64 = C_cap;
+// Sizes of one retrieval over n > 0 keys per unit: candidates C and, with
+// percentile tiers, the kept positions M (Slides Sec. 4.2.2: C = ceil(beta n);
+// README "Parameters": adaptive ratios), and the collide / select tiling.
+struct CallShape {
+  int C = 0, n_sel = 0, tile = 0, tiles = 0;
   uint32_t keep_m = 0;
+  bool pct = false;
+};
+
+pk_status call_shape(pk_context* ctx, const pk_config& cfg, int units, int64_t n, CallShape* cs) {
+  int64_t C64 = cfg.n_candidates;
   if (cfg.adaptive_ratios) {
     int beta = 0, rho = 0;
     adaptive_permille(n, &beta, &rho);
     C64 = ceil_permille(beta, n);
-    if (cfg.tier_mode == PK_TIERS_PERCENTILE) keep_m = (uint32_t)ceil_permille(rho, n);
+    if (cfg.tier_mode == PK_TIERS_PERCENTILE) cs->keep_m = (uint32_t)ceil_permille(rho, n);
   } else if (cfg.tier_mode == PK_TIERS_PERCENTILE) {
-    keep_m = (uint32_t)ceil_permille(cfg.collision_permille, n);
+    cs->keep_m = (uint32_t)ceil_permille(cfg.collision_permille, n);
   }
-  if (C64 > C_cap)
-    return fail(ctx, PK_ERR_CAPACITY, "adaptive candidate count %lld exceeds n_candidates %d", (long long)C64, C_cap);
-  const int C = (int)C64;
-  const bool pct = cfg.tier_mode == PK_TIERS_PERCENTILE;
+  if (C64 > cfg.n_candidates)
+    return fail(ctx, PK_ERR_CAPACITY, "adaptive candidate count %lld exceeds n_candidates %d", (long long)C64,
+                cfg.n_candidates);
+  cs->C = (int)C64;
+  cs->n_sel = (int)(n < C64 ? n : C64);
+  cs->pct = cfg.tier_mode == PK_TIERS_PERCENTILE;
   // 64-bin histograms: with at most 16 tiles (64 sub-tiles) per unit the
   // select workgroups derive theta themselves and no threshold launch is
   // needed; worth a few larger tiles while a tile stays within kFuseTile keys
-  int tile = tile_size(ctx->units, n);
-  if (!pct) {
+  int tile = tile_size(units, n);
+  if (!cs->pct) {
     const int64_t want = ((n + 15) / 16 + 255) / 256 * 256;
     if (want > tile && want <= kFuseTile) tile = (int)want;
   }
-  const int tiles = (int)((n + tile - 1) / tile);
-  if (tiles > ctx->max_tiles)
-    return fail(ctx, PK_ERR_CAPACITY, "internal tiling bound exceeded (%d > %lld)", tiles, (long long)ctx->max_tiles);
-  const unsigned grid = (unsigned)((int64_t)ctx->units * tiles);
-  const int n_sel = (int)(n < C ? n : C);
+  cs->tile = tile;
+  cs->tiles = (int)((n + tile - 1) / tile);
+  return PK_OK;
+}
+
+// What a retrieval runs on: the configuration, constant tables, scratch
+// arrays, and the context (nullable: it only receives timings and error text).
+struct Scratch {
+  uint32_t* lut = nullptr;        // [units][16][256]
+  float* rq = nullptr;            // [qheads][128]
+  uint32_t* scores = nullptr;     // [units][score_stride]
+  int64_t score_stride = 0;
+  uint32_t* tile_hist = nullptr;  // per unit [4][bins / 4][max_subs][4]
+  int64_t max_subs = 0;
+  SelParams* params = nullptr;    // [units][4]
+  int2* sub_base = nullptr;       // [units][max_subs][4]
+  int32_t* cand_idx = nullptr;    // [qheads][C]
+  float* cand_est = nullptr;      // [qheads][C]
+  uint32_t* dev_err = nullptr;    // nullable
+};
+
+struct Plan {
+  const pk_config* cfg;
+  int group, units, qheads;
+  pk::Tables tb;
+  pk::TierSpec tiers;
+  pk_context* ctx;
+};
+
+Plan context_plan(pk_context* ctx) {
+  return Plan{&ctx->cfg, ctx->group, ctx->units, ctx->qheads, ctx->tb, ctx->tiers, ctx};
+}
+
+// Outputs of a retrieval over no keys: every Top-k slot (and candidate slot
+// of the debug copies) -1 / -inf.
+pk_status retrieve_empty(const Plan& pl, int32_t* topk_idx, float* topk_est, const pk_debug* dbg,
+                         hipStream_t stream) {
+  const int64_t cnt = (int64_t)pl.qheads * pl.cfg->top_k;
+  hipLaunchKernelGGL(pk::fill_empty_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream, topk_idx,
+                     topk_est, cnt);
+  pk_status st = check_launch(pl.ctx, "fill");
+  if (st != PK_OK) return st;
+  if (dbg && dbg->cand_idx) {
+    const int64_t cc = (int64_t)pl.qheads * pl.cfg->n_candidates;
+    hipLaunchKernelGGL(pk::fill_empty_kernel, dim3((unsigned)((cc + 255) / 256)), dim3(256), 0, stream,
+                       dbg->cand_idx, dbg->cand_est, cc);
+    st = check_launch(pl.ctx, "fill");
+  }
+  return st;
+}
+
+Scratch context_scratch(pk_context* ctx) {
+  Scratch sc;
+  sc.lut = ctx->lut;
+  sc.rq = ctx->rq;
+  sc.scores = ctx->scores;
+  sc.score_stride = ctx->cfg.n_capacity;
+  sc.tile_hist = ctx->tile_hist;
+  sc.max_subs = ctx->max_subs;
+  sc.params = ctx->params;
+  sc.sub_base = ctx->sub_base;
+  sc.cand_idx = ctx->cand_idx;
+  sc.cand_est = ctx->cand_est;
+  sc.dev_err = ctx->dev_err;
+  return sc;
+}
+
+// The retrieval chain.  With `att` (q, K/V and output of one dtype) the kernel
+// that selects each head's Top-k (rerank + top-k, or top-k after the spread
+// rerank) also computes the attention and *attended is set; otherwise the
+// caller still has to attend.  n > 0; `cs` is call_shape's result for n, and
+// the scratch holds max_subs >= 4 * cs.tiles.
+pk_status retrieve_impl(const Plan& pl, const Scratch& sc, const CallShape& cs, const void* q, pk_dtype q_dtype,
+                        const pk_summaries* s, int32_t* topk_idx, float* topk_est, const pk_debug* dbg,
+                        hipStream_t stream, const pk::AttendArgs* att, bool* attended) {
+  pk_status st = PK_OK;
+  if (attended) *attended = false;
+  pk_context* ctx = pl.ctx;
+  const pk_config& cfg = *pl.cfg;
+  const int64_t n = s->n;
+  const int k = cfg.top_k, C_cap = cfg.n_candidates;
+  const int C = cs.C, tile = cs.tile, tiles = cs.tiles, n_sel = cs.n_sel;
+  const uint32_t keep_m = cs.keep_m;
+  const bool pct = cs.pct;
+  const unsigned grid = (unsigned)((int64_t)pl.units * tiles);
 
   {
     Launch L(ctx, PK_KERNEL_QPREP, stream);
     if (q_dtype == PK_BF16)
-      hipLaunchKernelGGL(pk::qprep_kernel<uint16_t>, dim3(ctx->qheads * pk::QP_PARTS), dim3(64 * pk::QP_WAVES), 0,
-                         stream, (const uint16_t*)q, cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->rq,
-                         (uint8_t*)ctx->lut, ctx->tb, ctx->tiers, s->counts, keep_m);
+      hipLaunchKernelGGL(pk::qprep_kernel<uint16_t>, dim3(pl.qheads * pk::QP_PARTS), dim3(64 * pk::QP_WAVES), 0,
+                         stream, (const uint16_t*)q, cfg.n_q_heads, cfg.n_kv_heads, pl.group, sc.rq,
+                         (uint8_t*)sc.lut, pl.tb, pl.tiers, s->counts, keep_m);
     else
-      hipLaunchKernelGGL(pk::qprep_kernel<float>, dim3(ctx->qheads * pk::QP_PARTS), dim3(64 * pk::QP_WAVES), 0,
-                         stream, (const float*)q, cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->rq,
-                         (uint8_t*)ctx->lut, ctx->tb, ctx->tiers, s->counts, keep_m);
+      hipLaunchKernelGGL(pk::qprep_kernel<float>, dim3(pl.qheads * pk::QP_PARTS), dim3(64 * pk::QP_WAVES), 0,
+                         stream, (const float*)q, cfg.n_q_heads, cfg.n_kv_heads, pl.group, sc.rq,
+                         (uint8_t*)sc.lut, pl.tb, pl.tiers, s->counts, keep_m);
   }
   if ((st = check_launch(ctx, "qprep")) != PK_OK) return st;
   {
     Launch L(ctx, PK_KERNEL_COLLIDE, stream);
 #define PK_COLLIDE(GG, NB)                                                                                    \
   hipLaunchKernelGGL((pk::collide_kernel<GG, NB>), dim3(grid), dim3(256), 0, stream, (const uint4*)s->codes,      \
-                     ctx->lut, ctx->scores, ctx->tile_hist, n, s->n_capacity, tiles, (int)ctx->max_subs, tile)
+                     sc.lut, sc.scores, sc.tile_hist, n, s->n_capacity, sc.score_stride, tiles,      \
+                     (int)sc.max_subs, tile)
 #define PK_COLLIDE_G(NB)                   \
-  switch (ctx->group) {                    \
+  switch (pl.group) {                    \
     case 1: PK_COLLIDE(1, NB); break;      \
     case 2: PK_COLLIDE(2, NB); break;      \
     case 3: PK_COLLIDE(3, NB); break;      \
@@ -521,23 +589,23 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
   if (!fused_params) {
     Launch L(ctx, PK_KERNEL_THRESHOLD, stream);
     if (pct)
-      hipLaunchKernelGGL(pk::threshold_kernel<pk::NBIN_MAX>, dim3(ctx->units * ctx->group), dim3(pk::TH_THREADS), 0,
-                         stream, ctx->tile_hist, ctx->params, ctx->sub_base, n, 4 * tiles, (int)ctx->max_subs,
-                         tile / 4, ctx->group, C);
+      hipLaunchKernelGGL(pk::threshold_kernel<pk::NBIN_MAX>, dim3(pl.units * pl.group), dim3(pk::TH_THREADS), 0,
+                         stream, sc.tile_hist, sc.params, sc.sub_base, n, 4 * tiles, (int)sc.max_subs,
+                         tile / 4, pl.group, C);
     else
-      hipLaunchKernelGGL(pk::threshold_kernel<pk::NBIN>, dim3(ctx->units * ctx->group), dim3(pk::TH_THREADS), 0,
-                         stream, ctx->tile_hist, ctx->params, ctx->sub_base, n, 4 * tiles, (int)ctx->max_subs,
-                         tile / 4, ctx->group, C);
+      hipLaunchKernelGGL(pk::threshold_kernel<pk::NBIN>, dim3(pl.units * pl.group), dim3(pk::TH_THREADS), 0,
+                         stream, sc.tile_hist, sc.params, sc.sub_base, n, 4 * tiles, (int)sc.max_subs,
+                         tile / 4, pl.group, C);
   }
   if ((st = check_launch(ctx, "threshold")) != PK_OK) return st;
   {
     Launch L(ctx, PK_KERNEL_SELECT, stream);
 #define PK_SELECT(GG, F)                                                                                        \
-  hipLaunchKernelGGL((pk::select_kernel<GG, F>), dim3(grid), dim3(256), 0, stream, ctx->scores, ctx->params,      \
-                     ctx->sub_base, ctx->cand_idx, n, s->n_capacity, tiles, (int)ctx->max_subs, tile,              \
-                     cfg.n_q_heads, cfg.n_kv_heads, C, ctx->tile_hist, ctx->dev_err)
+  hipLaunchKernelGGL((pk::select_kernel<GG, F>), dim3(grid), dim3(256), 0, stream, sc.scores, sc.params,      \
+                     sc.sub_base, sc.cand_idx, n, sc.score_stride, tiles, (int)sc.max_subs, tile,            \
+                     cfg.n_q_heads, cfg.n_kv_heads, C, sc.tile_hist, sc.dev_err)
 #define PK_SELECT_G(F)                     \
-  switch (ctx->group) {                    \
+  switch (pl.group) {                    \
     case 1: PK_SELECT(1, F); break;        \
     case 2: PK_SELECT(2, F); break;        \
     case 3: PK_SELECT(3, F); break;        \
@@ -552,16 +620,16 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
 #undef PK_SELECT
   }
   if ((st = check_launch(ctx, "select")) != PK_OK) return st;
-  if (n_sel <= (ctx->qheads >= kFusedTopkHeads ? kFusedTopkSlotsMany : kFusedTopkSlots)) {
+  if (n_sel <= (pl.qheads >= kFusedTopkHeads ? kFusedTopkSlotsMany : kFusedTopkSlots)) {
     // one workgroup per head: rerank and top-k together, estimates in LDS
     Launch L(ctx, PK_KERNEL_RERANK_TOPK, stream);
     const int R = (n_sel + pk::RT_THREADS - 1) / pk::RT_THREADS;   // <= 4
-    float* est_out = (dbg && dbg->cand_est) ? ctx->cand_est : nullptr;
+    float* est_out = (dbg && dbg->cand_est) ? sc.cand_est : nullptr;
     const pk::AttendArgs none{};
 #define PK_RTK_LAUNCH(RR, T, MR, A)                                                                               \
-  hipLaunchKernelGGL((pk::rerank_topk_kernel<RR, T, MR, A>), dim3(ctx->qheads), dim3(pk::RT_THREADS), 0, stream,   \
-                     s->records, ctx->rq, ctx->cand_idx, est_out, s->n_capacity, n_sel, C, cfg.n_q_heads,           \
-                     cfg.n_kv_heads, ctx->group, ctx->tb, k, topk_idx, topk_est, A ? *att : none)
+  hipLaunchKernelGGL((pk::rerank_topk_kernel<RR, T, MR, A>), dim3(pl.qheads), dim3(pk::RT_THREADS), 0, stream,   \
+                     s->records, sc.rq, sc.cand_idx, est_out, s->n_capacity, n_sel, C, cfg.n_q_heads,           \
+                     cfg.n_kv_heads, pl.group, pl.tb, k, topk_idx, topk_est, A ? *att : none)
 #define PK_RTK_R(T, MR, A)                         \
   do {                                             \
     if (R <= 1) PK_RTK_LAUNCH(1, T, MR, A);        \
@@ -587,13 +655,13 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
       // one candidate per lane while that keeps the grid within ~2048
       // workgroups, else two or four (fewer tables to build)
       Launch L(ctx, PK_KERNEL_RERANK, stream);
-      const int64_t total = (int64_t)ctx->qheads * n_sel;
+      const int64_t total = (int64_t)pl.qheads * n_sel;
       const int rr = total <= (int64_t)1 << 19 ? 1 : (total <= (int64_t)1 << 21 ? 2 : 4);
       const int chunks = (n_sel + 256 * rr - 1) / (256 * rr);
 #define PK_RR(RRR)                                                                                               \
-  hipLaunchKernelGGL(pk::rerank_kernel<RRR>, dim3((unsigned)((int64_t)ctx->qheads * chunks)), dim3(256), 0, stream, \
-                     s->records, ctx->rq, ctx->cand_idx, ctx->cand_est, s->n_capacity, n_sel, C, chunks,          \
-                     cfg.n_q_heads, cfg.n_kv_heads, ctx->group, ctx->tb)
+  hipLaunchKernelGGL(pk::rerank_kernel<RRR>, dim3((unsigned)((int64_t)pl.qheads * chunks)), dim3(256), 0, stream, \
+                     s->records, sc.rq, sc.cand_idx, sc.cand_est, s->n_capacity, n_sel, C, chunks,          \
+                     cfg.n_q_heads, cfg.n_kv_heads, pl.group, pl.tb)
       if (rr == 1) PK_RR(1);
       else if (rr == 2) PK_RR(2);
       else PK_RR(4);
@@ -607,8 +675,8 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
       const int R = (n_sel + pk::TK_THREADS - 1) / pk::TK_THREADS;
       const pk::AttendArgs none{};
 #define PK_TOPK(RR, T, MR, A)                                                                                   \
-  hipLaunchKernelGGL((pk::topk_kernel<RR, T, MR, A>), dim3(ctx->qheads), dim3(pk::TK_THREADS), 0, stream,        \
-                     ctx->cand_idx, ctx->cand_est, n_sel, C, k, topk_idx, topk_est, cfg.n_q_heads, ctx->group,   \
+  hipLaunchKernelGGL((pk::topk_kernel<RR, T, MR, A>), dim3(pl.qheads), dim3(pk::TK_THREADS), 0, stream,        \
+                     sc.cand_idx, sc.cand_est, n_sel, C, k, topk_idx, topk_est, cfg.n_q_heads, pl.group,   \
                      A ? *att : none)
 #define PK_TOPK_R(T, MR, A)                    \
   do {                                         \
@@ -634,11 +702,11 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
   }
 
   if (dbg) {
-    const size_t U = ctx->units, Q = ctx->qheads;
-    if (dbg->rot_q) PK_HIP(ctx, hipMemcpyAsync(dbg->rot_q, ctx->rq, Q * 128 * 4, hipMemcpyDeviceToDevice, stream));
-    if (dbg->lut) PK_HIP(ctx, hipMemcpyAsync(dbg->lut, ctx->lut, U * 16 * 256 * 4, hipMemcpyDeviceToDevice, stream));
+    const size_t U = pl.units, Q = pl.qheads;
+    if (dbg->rot_q) PK_HIP(ctx, hipMemcpyAsync(dbg->rot_q, sc.rq, Q * 128 * 4, hipMemcpyDeviceToDevice, stream));
+    if (dbg->lut) PK_HIP(ctx, hipMemcpyAsync(dbg->lut, sc.lut, U * 16 * 256 * 4, hipMemcpyDeviceToDevice, stream));
     if (dbg->scores)
-      PK_HIP(ctx, hipMemcpy2DAsync(dbg->scores, (size_t)n * 4, ctx->scores, (size_t)s->n_capacity * 4, (size_t)n * 4,
+      PK_HIP(ctx, hipMemcpy2DAsync(dbg->scores, (size_t)n * 4, sc.scores, (size_t)sc.score_stride * 4, (size_t)n * 4,
                                    U, hipMemcpyDeviceToDevice, stream));
     // candidate lists are [heads][C] inside, [heads][n_candidates] in the debug copies
     if (C < C_cap && (dbg->cand_idx || dbg->cand_est)) {
@@ -653,25 +721,26 @@ pk_status retrieve_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const 
       if ((st = check_launch(ctx, "fill")) != PK_OK) return st;
     }
     if (dbg->cand_idx)
-      PK_HIP(ctx, hipMemcpy2DAsync(dbg->cand_idx, (size_t)C_cap * 4, ctx->cand_idx, (size_t)C * 4, (size_t)C * 4, Q,
+      PK_HIP(ctx, hipMemcpy2DAsync(dbg->cand_idx, (size_t)C_cap * 4, sc.cand_idx, (size_t)C * 4, (size_t)C * 4, Q,
                                    hipMemcpyDeviceToDevice, stream));
     if (dbg->cand_est)
-      PK_HIP(ctx, hipMemcpy2DAsync(dbg->cand_est, (size_t)C_cap * 4, ctx->cand_est, (size_t)C * 4, (size_t)C * 4, Q,
+      PK_HIP(ctx, hipMemcpy2DAsync(dbg->cand_est, (size_t)C_cap * 4, sc.cand_est, (size_t)C * 4, (size_t)C * 4, Q,
                                    hipMemcpyDeviceToDevice, stream));
   }
   return PK_OK;
 }
 
-pk_status attend_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const void* k, const void* v,
+pk_status attend_impl(const Plan& pl, const void* q, pk_dtype q_dtype, const void* k, const void* v,
                       pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows, const int32_t* topk_idx,
                       void* out, pk_dtype out_dtype, hipStream_t stream) {
-  const pk_config& c = ctx->cfg;
+  pk_context* ctx = pl.ctx;
+  const pk_config& c = *pl.cfg;
   const int kk = c.top_k;
   const pk::AttendArgs a{q, k, v, kv_strides[0], kv_strides[1], kv_strides[2], n_rows, c.softmax_scale, out};
   Launch L(ctx, PK_KERNEL_ATTEND, stream);
 #define PK_ATT(KT, QT, OT, R)                                                                                   \
-  hipLaunchKernelGGL((pk::attend_kernel<KT, QT, OT, R>), dim3(ctx->qheads), dim3(256), 0, stream, a, topk_idx, kk, \
-                     c.n_q_heads, c.n_kv_heads, ctx->group)
+  hipLaunchKernelGGL((pk::attend_kernel<KT, QT, OT, R>), dim3(pl.qheads), dim3(256), 0, stream, a, topk_idx, kk, \
+                     c.n_q_heads, c.n_kv_heads, pl.group)
 #define PK_ATT_R(KT, QT, OT) \
   do {                       \
     if (kk <= 128)           \
@@ -704,23 +773,41 @@ pk_status attend_impl(pk_context* ctx, const void* q, pk_dtype q_dtype, const vo
   return check_launch(ctx, "attend");
 }
 
+// A retrieval with a context's scratch.
+pk_status retrieve_ctx(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s, int32_t* topk_idx,
+                       float* topk_est, const pk_debug* dbg, hipStream_t stream, const pk::AttendArgs* att,
+                       bool* attended) {
+  if (attended) *attended = false;
+  const Plan pl = context_plan(ctx);
+  if (s->n == 0) return retrieve_empty(pl, topk_idx, topk_est, dbg, stream);
+  CallShape cs;
+  pk_status st = call_shape(ctx, ctx->cfg, ctx->units, s->n, &cs);
+  if (st != PK_OK) return st;
+  if (cs.tiles > ctx->max_tiles)
+    return fail(ctx, PK_ERR_CAPACITY, "internal tiling bound exceeded (%d > %lld)", cs.tiles,
+                (long long)ctx->max_tiles);
+  return retrieve_impl(pl, context_scratch(ctx), cs, q, q_dtype, s, topk_idx, topk_est, dbg, stream, att, attended);
+}
+
 }  // namespace
 
 extern "C" {
 
 pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s,
                       int32_t* topk_idx, float* topk_est, const pk_debug* dbg, void* hip_stream) {
-  pk_status st = check_retrieve_args(ctx, q, q_dtype, s, topk_idx, topk_est);
+  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
+  pk_status st = check_retrieve_args(ctx, ctx->cfg, q, q_dtype, s, topk_idx, topk_est);
   if (st != PK_OK) return st;
-  return retrieve_impl(ctx, q, q_dtype, s, topk_idx, topk_est, dbg, (hipStream_t)hip_stream, nullptr, nullptr);
+  return retrieve_ctx(ctx, q, q_dtype, s, topk_idx, topk_est, dbg, (hipStream_t)hip_stream, nullptr, nullptr);
 }
 
 pk_status pk_sparse_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, const void* k, const void* v,
                            pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows,
                            const int32_t* topk_idx, void* out, pk_dtype out_dtype, void* hip_stream) {
+  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
   pk_status st = check_attend_args(ctx, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype);
   if (st != PK_OK) return st;
-  return attend_impl(ctx, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype,
+  return attend_impl(context_plan(ctx), q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype,
                      (hipStream_t)hip_stream);
 }
 
@@ -729,6 +816,7 @@ pk_status pk_sparse_dense_attend(pk_context* ctx, const void* q, pk_dtype q_dtyp
                                  const int32_t* topk_idx, const void* dense_k, const void* dense_v,
                                  const int64_t dense_strides[3], int64_t n_dense, void* out, pk_dtype out_dtype,
                                  void* hip_stream) {
+  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
   pk_status st = check_attend_args(ctx, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype);
   if (st != PK_OK) return st;
   if (n_dense < 0 || n_dense > PK_MAX_DENSE)
@@ -776,7 +864,8 @@ pk_status pk_retrieve_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, c
                              const void* k, const void* v, pk_dtype kv_dtype, const int64_t kv_strides[3],
                              int64_t n_rows, int32_t* topk_idx, float* topk_est, void* out, pk_dtype out_dtype,
                              const pk_debug* dbg, void* hip_stream) {
-  pk_status st = check_retrieve_args(ctx, q, q_dtype, s, topk_idx, topk_est);
+  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
+  pk_status st = check_retrieve_args(ctx, ctx->cfg, q, q_dtype, s, topk_idx, topk_est);
   if (st != PK_OK) return st;
   st = check_attend_args(ctx, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype);
   if (st != PK_OK) return st;
@@ -784,9 +873,10 @@ pk_status pk_retrieve_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, c
   const bool same_dtype = q_dtype == kv_dtype && kv_dtype == out_dtype;
   const pk::AttendArgs a{q, k, v, kv_strides[0], kv_strides[1], kv_strides[2], n_rows, ctx->cfg.softmax_scale, out};
   bool attended = false;
-  st = retrieve_impl(ctx, q, q_dtype, s, topk_idx, topk_est, dbg, stream, same_dtype ? &a : nullptr, &attended);
+  st = retrieve_ctx(ctx, q, q_dtype, s, topk_idx, topk_est, dbg, stream, same_dtype ? &a : nullptr, &attended);
   if (st != PK_OK || attended) return st;
-  return attend_impl(ctx, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype, stream);
+  return attend_impl(context_plan(ctx), q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype,
+                     stream);
 }
 
 pk_status pk_host_alloc_mapped(size_t bytes, void** host_ptr, void** device_ptr) {

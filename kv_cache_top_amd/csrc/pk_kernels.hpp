@@ -392,7 +392,8 @@ encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
 // ranking r < tier_top[last] by (score desc, c asc) are found with a bitwise
 // threshold search over the order-preserving score keys, then ranked among
 // themselves; each gets its tier weight, every other centroid 0.  The weight is
-// written as byte g (query head g of the unit) of the unit's LUT.
+// written as byte g (query head g of the unit) of the unit's LUT; bytes of
+// absent heads (g >= group) are written as 0.
 // ===========================================================================
 // Rank tiers of one subspace (one wave, centroid c = lane + 64 r holds score
 // key key[r]): the centroids ranked r < tiers.top[last] by (score desc, c asc)
@@ -625,10 +626,15 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  // the last query head of a unit also clears the bytes of the absent heads
+  // (g >= group), so the LUT needs no clearing between calls
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint32_t c = lane + 64 * r;
-    lut_bytes[(((int64_t)unit * NSUB + b) * 256 + c) * 4 + g] = lw[w][c];
+    uint8_t* word = lut_bytes + (((int64_t)unit * NSUB + b) * 256 + c) * 4;
+    word[g] = lw[w][c];
+    if (g == group - 1)
+      for (int g2 = group; g2 < MAXG; ++g2) word[g2] = 0;
   }
 }
 
@@ -676,7 +682,7 @@ template <int G, int NB>   // NB: histogram bins 1..NB
 __global__ void __launch_bounds__(256)
 collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut,
                uint32_t* __restrict__ scores, uint32_t* __restrict__ tile_hist,
-               int64_t n, int64_t n_cap, int tiles, int max_subs, int tile) {
+               int64_t n, int64_t n_cap, int64_t s_stride, int tiles, int max_subs, int tile) {
   constexpr int group = G;
   __shared__ uint32_t s_lut[NSUB * 256];
   __shared__ uint32_t s_hist[MAXG * NB * HIST_LANES];
@@ -688,7 +694,7 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
   const int64_t w0 = (int64_t)tl * tile + (int64_t)wave * wkeys;
   const int64_t w1 = (w0 + wkeys < n) ? w0 + wkeys : n;
   const uint4* crow = codes + (int64_t)unit * n_cap;
-  uint32_t* srow = scores + (int64_t)unit * n_cap;
+  uint32_t* srow = scores + (int64_t)unit * s_stride;
 
   // Loads are issued unconditionally from a clamped index (lanes past the end
   // re-read the last key and discard it): conditional loads compile to
@@ -1085,7 +1091,7 @@ struct HeadSelect {
 template <int G, bool FUSED>
 __global__ void __launch_bounds__(256)
 select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__ params,
-              const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx, int64_t n, int64_t n_cap,
+              const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx, int64_t n, int64_t s_stride,
               int tiles, int max_subs, int tile, int n_q_heads, int n_kv_heads, int n_candidates,
               const uint32_t* __restrict__ tile_hist, uint32_t* __restrict__ err) {
   __shared__ uint2 s_ik[4][SEL_QCAP];             // compacted keys: (key, packed S)
@@ -1103,7 +1109,7 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
   const int wkeys = tile >> 2;                    // multiple of 64
   const int w0 = k0 + wave * wkeys;
   const int w1 = (w0 + wkeys < k1) ? w0 + wkeys : k1;
-  const uint32_t* srow = scores + (int64_t)unit * n_cap;
+  const uint32_t* srow = scores + (int64_t)unit * s_stride;
 
   // fused parameters: the histogram rows are requested before the scores, so
   // that waiting for them does not wait for the scores (the memory counter is
