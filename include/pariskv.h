@@ -37,7 +37,9 @@
  *     the default stream).  Outputs are valid after the stream synchronises;
  *     a device fault surfaces at that synchronisation.
  *   - A context owns scratch memory sized at pk_create; no call allocates
- *     device memory after that.  One context serves one stream at a time.
+ *     device memory after that (pk_timing_begin allocates its events).  One
+ *     context serves one stream at a time.  pk_retrieve_attend_noalloc needs
+ *     no context and allocates nothing.
  *   - Outputs must not alias inputs.
  */
 #ifndef PARISKV_H
@@ -272,6 +274,28 @@ pk_status pk_retrieve_attend(pk_context* ctx, const void* q, pk_dtype q_dtype,
                              pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows,
                              int32_t* topk_idx, float* topk_est, void* out, pk_dtype out_dtype,
                              const pk_debug* dbg, void* hip_stream);
+
+/* pk_retrieve_attend without a context, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, results, layouts and errors as
+ * pk_retrieve_attend with a context created from *cfg (no debug copies, no
+ * timings, no device error flags), except that nothing is allocated: the
+ * call's scratch (tier LUT, rotated queries, packed scores, histograms,
+ * selection parameters, candidate lists) lives in a static device array of
+ * PK_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends.  Its size per call is about 4 * units * n + 8 * (query heads)
+ * * C + 16 KiB * units bytes; a call that needs more than the array returns
+ * PK_ERR_CAPACITY (nothing enqueued).  The tables are computed on the host
+ * at each call (no device work).  Every call on a GPU shares that GPU's array
+ * and leaves its contents behind: calls that overlap on one GPU (on different
+ * streams, or from several threads) race and must be serialised by the
+ * caller.  No array needs clearing between calls. */
+#define PK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pk_status pk_retrieve_attend_noalloc(const pk_config* cfg, const void* q, pk_dtype q_dtype,
+                                     const pk_summaries* sums, const void* k, const void* v,
+                                     pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows,
+                                     int32_t* topk_idx, float* topk_est, void* out, pk_dtype out_dtype,
+                                     void* hip_stream);
 
 /* Attention over the retrieved rows and a set of dense rows in one softmax
  * (README "3. Attention": sink, local and retrieved tokens; Slides Fig. 5,

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -247,6 +248,28 @@ pk_status pk_tables(uint64_t seed, int8_t signs[128], float levels[8], float thr
   return PK_OK;
 }
 
+}  // extern "C"
+
+// The constant kernel arguments of a configuration (host only).
+static void kernel_tables(const pk_config& cfg, pk::Tables* tb, pk::TierSpec* tiers) {
+  int8_t signs[128];
+  float L[8], T[7];
+  pk_tables(cfg.srht_seed, signs, L, T);
+  std::memset(tb, 0, sizeof(*tb));
+  for (int j = 0; j < 128; ++j)
+    if (signs[j] < 0) tb->neg_bits[j >> 5] |= 1u << (j & 31);
+  std::memcpy(tb->levels, L, sizeof(L));
+  std::memcpy(tb->thresholds, T, sizeof(T));
+  tb->inv_sqrt_d = (float)(1.0 / std::sqrt(128.0));
+  tiers->n_tiers = cfg.n_tiers;
+  for (int t = 0; t < 4; ++t) {
+    tiers->top[t] = t < cfg.n_tiers ? cfg.tier_top[t] : 0;
+    tiers->weight[t] = t < cfg.n_tiers ? cfg.tier_weight[t] : 0;
+  }
+}
+
+extern "C" {
+
 pk_status pk_create(const pk_config* cfg, pk_context** out) {
   if (!out) return fail(nullptr, PK_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
@@ -259,20 +282,7 @@ pk_status pk_create(const pk_config* cfg, pk_context** out) {
   c->units = cfg->batch * cfg->n_kv_heads;
   c->qheads = cfg->batch * cfg->n_q_heads;
 
-  int8_t signs[128];
-  float L[8], T[7];
-  pk_tables(cfg->srht_seed, signs, L, T);
-  std::memset(&c->tb, 0, sizeof(c->tb));
-  for (int j = 0; j < 128; ++j)
-    if (signs[j] < 0) c->tb.neg_bits[j >> 5] |= 1u << (j & 31);
-  std::memcpy(c->tb.levels, L, sizeof(L));
-  std::memcpy(c->tb.thresholds, T, sizeof(T));
-  c->tb.inv_sqrt_d = (float)(1.0 / std::sqrt(128.0));
-  c->tiers.n_tiers = cfg->n_tiers;
-  for (int t = 0; t < 4; ++t) {
-    c->tiers.top[t] = t < cfg->n_tiers ? cfg->tier_top[t] : 0;
-    c->tiers.weight[t] = t < cfg->n_tiers ? cfg->tier_weight[t] : 0;
-  }
+  kernel_tables(*cfg, &c->tb, &c->tiers);
   c->max_tiles = max_tiles_for(c->units, cfg->n_capacity);
   c->max_subs = 4 * c->max_tiles;
 
@@ -877,6 +887,108 @@ pk_status pk_retrieve_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, c
   if (st != PK_OK || attended) return st;
   return attend_impl(context_plan(ctx), q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype,
                      stream);
+}
+
+}  // extern "C"
+
+// ---- retrieval without a context: scratch in a static device array ----------
+// Each GPU the library runs on holds its own copy of `scratch` until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is a stand-in, not a device address): it uses the per-device
+// address from hipGetSymbolAddress, taken once per device on first use.
+static __device__ __align__(256) unsigned char scratch[PK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[kMaxDevices] = {};
+
+pk_status device_scratch(int dev, unsigned char** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(nullptr, PK_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(nullptr, PK_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<unsigned char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return PK_OK;
+}
+
+// Carves the arrays of one call out of `base` (256-byte aligned each); with
+// base NULL only the total is computed.
+size_t carve_scratch(unsigned char* base, const pk_config& cfg, int units, int qheads, int64_t n,
+                     const CallShape& cs, Scratch* sc) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    unsigned char* p = base ? base + off : nullptr;
+    off += (bytes + 255) / 256 * 256;
+    return p;
+  };
+  const size_t U = units, Q = qheads, MS = 4 * (size_t)cs.tiles, C = cs.C;
+  const size_t bins = cs.pct ? pk::NBIN_MAX : pk::NBIN;
+  sc->lut = reinterpret_cast<uint32_t*>(take(U * 16 * 256 * 4));
+  sc->rq = reinterpret_cast<float*>(take(Q * 128 * 4));
+  sc->scores = reinterpret_cast<uint32_t*>(take(U * (size_t)n * 4));
+  sc->score_stride = n;
+  sc->tile_hist = reinterpret_cast<uint32_t*>(take(U * MS * pk::MAXG * bins * 4));
+  sc->max_subs = (int64_t)MS;
+  sc->params = reinterpret_cast<SelParams*>(take(U * pk::MAXG * sizeof(SelParams)));
+  sc->sub_base = reinterpret_cast<int2*>(take(U * MS * pk::MAXG * sizeof(int2)));
+  sc->cand_idx = reinterpret_cast<int32_t*>(take(Q * C * 4));
+  sc->cand_est = reinterpret_cast<float*>(take(Q * C * 4));
+  sc->dev_err = nullptr;
+  (void)cfg;
+  return off;
+}
+
+}  // namespace
+
+extern "C" {
+
+pk_status pk_retrieve_attend_noalloc(const pk_config* cfg, const void* q, pk_dtype q_dtype, const pk_summaries* s,
+                                     const void* k, const void* v, pk_dtype kv_dtype, const int64_t kv_strides[3],
+                                     int64_t n_rows, int32_t* topk_idx, float* topk_est, void* out,
+                                     pk_dtype out_dtype, void* hip_stream) {
+  pk_status st = pk_validate_config(cfg);
+  if (st != PK_OK) return st;
+  if ((st = check_retrieve_args(nullptr, *cfg, q, q_dtype, s, topk_idx, topk_est)) != PK_OK) return st;
+  if ((st = check_attend_args(nullptr, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype)) !=
+      PK_OK)
+    return st;
+  Plan pl{cfg, cfg->n_q_heads / cfg->n_kv_heads, cfg->batch * cfg->n_kv_heads, cfg->batch * cfg->n_q_heads, {}, {},
+          nullptr};
+  kernel_tables(*cfg, &pl.tb, &pl.tiers);
+  hipStream_t stream = (hipStream_t)hip_stream;
+  const pk::AttendArgs a{q, k, v, kv_strides[0], kv_strides[1], kv_strides[2], n_rows, cfg->softmax_scale, out};
+  const bool same_dtype = q_dtype == kv_dtype && kv_dtype == out_dtype;
+  bool attended = false;
+  if (s->n == 0) {
+    st = retrieve_empty(pl, topk_idx, topk_est, nullptr, stream);
+  } else {
+    CallShape cs;
+    if ((st = call_shape(nullptr, *cfg, pl.units, s->n, &cs)) != PK_OK) return st;
+    Scratch sc;
+    const size_t need = carve_scratch(nullptr, *cfg, pl.units, pl.qheads, s->n, cs, &sc);
+    if (need > PK_NOALLOC_SCRATCH_BYTES)
+      return fail(nullptr, PK_ERR_CAPACITY,
+                  "this call needs %zu bytes of scratch; the static scratch of the no-allocation call holds %zu "
+                  "(fewer keys, units or candidates per call fit)",
+                  need, (size_t)PK_NOALLOC_SCRATCH_BYTES);
+    int dev = 0;
+    PK_HIP(nullptr, hipGetDevice(&dev));
+    unsigned char* base = nullptr;
+    if ((st = device_scratch(dev, &base)) != PK_OK) return st;
+    carve_scratch(base, *cfg, pl.units, pl.qheads, s->n, cs, &sc);
+    st = retrieve_impl(pl, sc, cs, q, q_dtype, s, topk_idx, topk_est, nullptr, stream, same_dtype ? &a : nullptr,
+                       &attended);
+  }
+  if (st != PK_OK || attended) return st;
+  return attend_impl(pl, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype, stream);
 }
 
 pk_status pk_host_alloc_mapped(size_t bytes, void** host_ptr, void** device_ptr) {

@@ -31,6 +31,7 @@ PK_OK, PK_ERR_INVALID_ARG, PK_ERR_UNSUPPORTED, PK_ERR_CAPACITY, PK_ERR_OUT_OF_ME
 PK_F32, PK_BF16 = 0, 1
 PK_TIERS_RANK, PK_TIERS_PERCENTILE = 0, 1
 PK_MAX_CANDIDATES, PK_MAX_TOPK, PK_MAX_DENSE = 16384, 256, 8192
+PK_NOALLOC_SCRATCH_BYTES = 64 << 20
 KERNELS = ["encode", "qprep", "collide", "threshold", "select", "rerank", "topk", "attend", "rerank_topk",
            "dense_attend"]
 PK_DEVICE_ERR_SLOT = 1
@@ -84,6 +85,9 @@ _SIGS = {
                          ctypes.c_int),
     "pk_retrieve_attend": ([_P, _P, ctypes.c_int, ctypes.POINTER(pk_summaries), _P, _P, ctypes.c_int, _I64x3,
                             ctypes.c_int64, _P, _P, _P, ctypes.c_int, ctypes.POINTER(pk_debug), _P], ctypes.c_int),
+    "pk_retrieve_attend_noalloc": ([ctypes.POINTER(pk_config), _P, ctypes.c_int, ctypes.POINTER(pk_summaries), _P,
+                                    _P, ctypes.c_int, _I64x3, ctypes.c_int64, _P, _P, _P, ctypes.c_int, _P],
+                                   ctypes.c_int),
     "pk_sparse_dense_attend": ([_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _I64x3, ctypes.c_int64, _P, _P, _P,
                                 _I64x3, ctypes.c_int64, _P, ctypes.c_int, _P], ctypes.c_int),
     "pk_host_alloc_mapped": ([ctypes.c_size_t, ctypes.POINTER(_P), ctypes.POINTER(_P)], ctypes.c_int),
@@ -336,6 +340,18 @@ def pk_retrieve_attend_raw(ctx, q, sums: pk_summaries, k_ptr: int, v_ptr: int, k
                                    ctypes.c_void_p(v_ptr), kv_dtype, _I64x3(*kv_strides), n_rows, _ptr(topk_idx),
                                    _ptr(topk_est), _ptr(out), _dtype(out),
                                    ctypes.byref(debug) if debug is not None else None, _stream(stream)), ctx)
+
+
+def pk_retrieve_attend_noalloc(cfg: pk_config, q, sums: pk_summaries, k, v, topk_idx, out, topk_est=None,
+                               stream=None):
+    """pk_retrieve_attend with no context: the scratch is the library's static device array."""
+    _check_q(cfg, q)
+    _check_kv(cfg, k, v)
+    _check_topk(cfg, topk_idx, topk_est)
+    _check_out(cfg, out)
+    _check(_lib.pk_retrieve_attend_noalloc(ctypes.byref(cfg), _ptr(q), _dtype(q), ctypes.byref(sums), _ptr(k),
+                                           _ptr(v), _dtype(k), _strides4(k), k.shape[2], _ptr(topk_idx),
+                                           _ptr(topk_est), _ptr(out), _dtype(out), _stream(stream)))
 
 
 def pk_sparse_dense_attend(ctx, q, k, v, topk_idx, dense_k, dense_v, out, stream=None):
