@@ -36,6 +36,7 @@ struct pk_context {
   int2* sub_base = nullptr;       // [units][max_subs][4]
   int32_t* cand_idx = nullptr;    // [qheads][C]
   float* cand_est = nullptr;      // [qheads][C]
+  uint32_t* unit_tot = nullptr;   // [units][4][64] bin totals of the collision scores
   uint32_t* dev_err = nullptr;    // device error flags (PK_DEVICE_ERR_*)
   std::string err;
   // timing
@@ -130,7 +131,7 @@ pk_status check_launch(pk_context* ctx, const char* what) {
 
 void free_scratch(pk_context* c) {
   void* ptrs[] = {c->lut, c->rq, c->scores, c->tile_hist, c->params, c->sub_base, c->cand_idx, c->cand_est,
-                  c->dev_err};
+                  c->unit_tot, c->dev_err};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (int k = 0; k < PK_N_KERNELS; ++k) {
@@ -302,6 +303,7 @@ pk_status pk_create(const pk_config* cfg, pk_context** out) {
       {(void**)&c->sub_base, U * MS * pk::MAXG * sizeof(int2)},
       {(void**)&c->cand_idx, Q * C * 4},
       {(void**)&c->cand_est, Q * C * 4},
+      {(void**)&c->unit_tot, U * pk::MAXG * pk::NBIN * 4},
       {(void**)&c->dev_err, 4},
   };
   for (Alloc& a : allocs) {
@@ -465,9 +467,8 @@ pk_status call_shape(pk_context* ctx, const pk_config& cfg, int units, int64_t n
   cs->C = (int)C64;
   cs->n_sel = (int)(n < C64 ? n : C64);
   cs->pct = cfg.tier_mode == PK_TIERS_PERCENTILE;
-  // 64-bin histograms: with at most 16 tiles (64 sub-tiles) per unit the
-  // select workgroups derive theta themselves and no threshold launch is
-  // needed; worth a few larger tiles while a tile stays within kFuseTile keys
+  // rank tiers: tiles of up to kFuseTile keys when a unit has few keys
+  // (at most 16 tiles), fewer sub-tiles for the selection parameters to sum
   int tile = tile_size(units, n);
   if (!cs->pct) {
     const int64_t want = ((n + 15) / 16 + 255) / 256 * 256;
@@ -485,8 +486,9 @@ struct Scratch {
   float* rq = nullptr;            // [qheads][128]
   uint32_t* scores = nullptr;     // [units][score_stride]
   int64_t score_stride = 0;
-  uint32_t* tile_hist = nullptr;  // per unit [4][bins / 4][max_subs][4]
+  uint32_t* tile_hist = nullptr;  // per unit: histograms (128 bins) or suffix counts (64 bins)
   int64_t max_subs = 0;
+  uint32_t* unit_tot = nullptr;   // [units][4][64]
   SelParams* params = nullptr;    // [units][4]
   int2* sub_base = nullptr;       // [units][max_subs][4]
   int32_t* cand_idx = nullptr;    // [qheads][C]
@@ -536,6 +538,7 @@ Scratch context_scratch(pk_context* ctx) {
   sc.sub_base = ctx->sub_base;
   sc.cand_idx = ctx->cand_idx;
   sc.cand_est = ctx->cand_est;
+  sc.unit_tot = ctx->unit_tot;
   sc.dev_err = ctx->dev_err;
   return sc;
 }
@@ -564,18 +567,18 @@ pk_status retrieve_impl(const Plan& pl, const Scratch& sc, const CallShape& cs, 
     if (q_dtype == PK_BF16)
       hipLaunchKernelGGL(pk::qprep_kernel<uint16_t>, dim3(pl.qheads * pk::QP_PARTS), dim3(64 * pk::QP_WAVES), 0,
                          stream, (const uint16_t*)q, cfg.n_q_heads, cfg.n_kv_heads, pl.group, sc.rq,
-                         (uint8_t*)sc.lut, pl.tb, pl.tiers, s->counts, keep_m);
+                         (uint8_t*)sc.lut, pl.tb, pl.tiers, s->counts, keep_m, pct ? nullptr : sc.unit_tot);
     else
       hipLaunchKernelGGL(pk::qprep_kernel<float>, dim3(pl.qheads * pk::QP_PARTS), dim3(64 * pk::QP_WAVES), 0,
                          stream, (const float*)q, cfg.n_q_heads, cfg.n_kv_heads, pl.group, sc.rq,
-                         (uint8_t*)sc.lut, pl.tb, pl.tiers, s->counts, keep_m);
+                         (uint8_t*)sc.lut, pl.tb, pl.tiers, s->counts, keep_m, pct ? nullptr : sc.unit_tot);
   }
   if ((st = check_launch(ctx, "qprep")) != PK_OK) return st;
   {
     Launch L(ctx, PK_KERNEL_COLLIDE, stream);
 #define PK_COLLIDE(GG, NB)                                                                                    \
   hipLaunchKernelGGL((pk::collide_kernel<GG, NB>), dim3(grid), dim3(256), 0, stream, (const uint4*)s->codes,      \
-                     sc.lut, sc.scores, sc.tile_hist, n, s->n_capacity, sc.score_stride, tiles,      \
+                     sc.lut, sc.scores, sc.tile_hist, sc.unit_tot, n, s->n_capacity, sc.score_stride, tiles,      \
                      (int)sc.max_subs, tile)
 #define PK_COLLIDE_G(NB)                   \
   switch (pl.group) {                    \
@@ -593,9 +596,9 @@ pk_status retrieve_impl(const Plan& pl, const Scratch& sc, const CallShape& cs, 
 #undef PK_COLLIDE
   }
   if ((st = check_launch(ctx, "collide")) != PK_OK) return st;
-  // at most 64 sub-tiles of 64-bin histograms per unit: each select workgroup
-  // derives theta and its prefix counts itself
-  const bool fused_params = !pct && 4 * tiles <= 64;
+  // rank tiers: each select workgroup derives theta and its prefix counts
+  // itself; percentile tiers (128 bins): the threshold kernel does
+  const bool fused_params = !pct;
   if (!fused_params) {
     Launch L(ctx, PK_KERNEL_THRESHOLD, stream);
     if (pct)
@@ -613,7 +616,7 @@ pk_status retrieve_impl(const Plan& pl, const Scratch& sc, const CallShape& cs, 
 #define PK_SELECT(GG, F)                                                                                        \
   hipLaunchKernelGGL((pk::select_kernel<GG, F>), dim3(grid), dim3(256), 0, stream, sc.scores, sc.params,      \
                      sc.sub_base, sc.cand_idx, n, sc.score_stride, tiles, (int)sc.max_subs, tile,            \
-                     cfg.n_q_heads, cfg.n_kv_heads, C, sc.tile_hist, sc.dev_err)
+                     cfg.n_q_heads, cfg.n_kv_heads, C, sc.unit_tot, sc.tile_hist, sc.dev_err)
 #define PK_SELECT_G(F)                     \
   switch (pl.group) {                    \
     case 1: PK_SELECT(1, F); break;        \
@@ -930,7 +933,7 @@ size_t carve_scratch(unsigned char* base, const pk_config& cfg, int units, int q
     return p;
   };
   const size_t U = units, Q = qheads, MS = 4 * (size_t)cs.tiles, C = cs.C;
-  const size_t bins = cs.pct ? pk::NBIN_MAX : pk::NBIN;
+  const size_t bins = cs.pct ? pk::NBIN_MAX : pk::NBIN + 1;   // histograms, or suffix counts s = 1..65
   sc->lut = reinterpret_cast<uint32_t*>(take(U * 16 * 256 * 4));
   sc->rq = reinterpret_cast<float*>(take(Q * 128 * 4));
   sc->scores = reinterpret_cast<uint32_t*>(take(U * (size_t)n * 4));
@@ -941,6 +944,7 @@ size_t carve_scratch(unsigned char* base, const pk_config& cfg, int units, int q
   sc->sub_base = reinterpret_cast<int2*>(take(U * MS * pk::MAXG * sizeof(int2)));
   sc->cand_idx = reinterpret_cast<int32_t*>(take(Q * C * 4));
   sc->cand_est = reinterpret_cast<float*>(take(Q * C * 4));
+  sc->unit_tot = reinterpret_cast<uint32_t*>(take(U * pk::MAXG * pk::NBIN * 4));
   sc->dev_err = nullptr;
   (void)cfg;
   return off;

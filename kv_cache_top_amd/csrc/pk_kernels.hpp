@@ -587,7 +587,7 @@ template <typename QT>
 __global__ void __launch_bounds__(64 * QP_WAVES)
 qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
              float* __restrict__ rot_q, uint8_t* __restrict__ lut_bytes, Tables tb,
-             TierSpec tiers, const uint32_t* __restrict__ counts, uint32_t keep_m) {
+             TierSpec tiers, const uint32_t* __restrict__ counts, uint32_t keep_m, uint32_t* __restrict__ unit_tot) {
   __shared__ float y[D];
   __shared__ uint64_t sel[QP_WAVES][256];   // (score key, 255 - centroid) of the selected centroids
   __shared__ uint8_t lw[QP_WAVES][256];     // tier weight per centroid
@@ -607,6 +607,8 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
     if (part == 0) {
       rot_q[(int64_t)head * D + lane] = v0 * tb.inv_sqrt_d;
       rot_q[(int64_t)head * D + lane + 64] = v1 * tb.inv_sqrt_d;
+      // the collide kernel that follows adds this head's bin counts here
+      if (unit_tot) unit_tot[((int64_t)unit * MAXG + g) * NBIN + lane] = 0u;
     }
   }
   __syncthreads();
@@ -678,10 +680,17 @@ __device__ __forceinline__ int64_t hist_index(int64_t unit, int max_subs, int su
   return (int64_t)unit * max_subs * MAXG * NB + (((int64_t)g * (NB / 4) + (bin >> 2)) * max_subs + sub) * 4 + (bin & 3);
 }
 
+// word of the suffix count #{S >= s} (s = 1..65; s = 65 is always 0) of
+// head g in sub-tile `sub` of a unit: rows of max_subs sub-tiles, a unit holds
+// MAXG * 65 rows
+__device__ __forceinline__ int64_t suf_index(int64_t unit, int max_subs, int g, int s, int sub) {
+  return (((int64_t)unit * MAXG + g) * (NBIN + 1) + (s - 1)) * max_subs + sub;
+}
+
 template <int G, int NB>   // NB: histogram bins 1..NB
 __global__ void __launch_bounds__(256)
 collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut,
-               uint32_t* __restrict__ scores, uint32_t* __restrict__ tile_hist,
+               uint32_t* __restrict__ scores, uint32_t* __restrict__ tile_hist, uint32_t* __restrict__ unit_tot,
                int64_t n, int64_t n_cap, int64_t s_stride, int tiles, int max_subs, int tile) {
   constexpr int group = G;
   __shared__ uint32_t s_lut[NSUB * 256];
@@ -752,10 +761,15 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
   }
   __syncthreads();
 
-  // reduce to sub-tile histograms; byte w of a counter word belongs to wave w.
-  // Layout (hist_index): per unit, [head][bin / 4][sub-tile][bin % 4], so that
-  // the readers, one lane per sub-tile, load four bins of consecutive sub-tiles
-  // with one coalesced 16-byte access per lane
+  // Byte w of a counter word belongs to wave w.  With 128 bins (percentile
+  // tiers) the sub-tile histograms are stored for the threshold kernel, in
+  // the hist_index layout: per unit, [head][bin / 4][sub-tile][bin % 4], so
+  // that its readers, one lane per sub-tile, load four bins of consecutive
+  // sub-tiles with one coalesced 16-byte access.  With 64 bins each sub-tile
+  // publishes its suffix counts #{S >= s} (suf_index layout) and the bin
+  // counts are added to the unit's totals, from which every select workgroup
+  // derives the parameters itself; thread (g, s - 1) owns bin s of head g, so
+  // wave g holds head g.
   for (int gb = tid; gb < group * NB; gb += 256) {
     const int g = gb / NB, bin = gb % NB;
     const uint32_t* row = s_hist + (g * NB + bin) * HIST_LANES;
@@ -766,9 +780,23 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
       hi += (v >> 8) & 0x00FF00FFu;   // waves 1 and 3
     }
     const uint32_t cnt[4] = {lo & 0xFFFFu, hi & 0xFFFFu, lo >> 16, hi >> 16};
+    if constexpr (NB == NBIN) {
+      // 16-bit fields: sub-tiles 0 and 1 in c01, 2 and 3 in c23 (counts <= tile / 4 < 2^16)
+      const uint32_t c01 = cnt[0] | (cnt[1] << 16), c23 = cnt[2] | (cnt[3] << 16);
+      const uint32_t i01 = wave_incl_scan(c01), i23 = wave_incl_scan(c23);
+      const uint32_t s01 = (uint32_t)__builtin_amdgcn_readlane((int)i01, 63) - i01 + c01;   // #{S >= bin + 1}
+      const uint32_t s23 = (uint32_t)__builtin_amdgcn_readlane((int)i23, 63) - i23 + c23;
+      *reinterpret_cast<uint4*>(tile_hist + suf_index(unit, max_subs, g, bin + 1, 4 * tl)) =
+          make_uint4(s01 & 0xFFFFu, s01 >> 16, s23 & 0xFFFFu, s23 >> 16);
+      if (bin == 0)   // #{S >= 65} = 0
+        *reinterpret_cast<uint4*>(tile_hist + suf_index(unit, max_subs, g, NBIN + 1, 4 * tl)) = make_uint4(0, 0, 0, 0);
+      const uint32_t c = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+      if (c) atomicAdd(&unit_tot[((int64_t)unit * MAXG + g) * NBIN + bin], c);
+    } else {
 #pragma unroll
-    for (int w2 = 0; w2 < 4; ++w2)
-      tile_hist[hist_index<NB>(unit, max_subs, 4 * tl + w2, g, bin)] = cnt[w2];
+      for (int w2 = 0; w2 < 4; ++w2)
+        tile_hist[hist_index<NB>(unit, max_subs, 4 * tl + w2, g, bin)] = cnt[w2];
+    }
   }
 }
 
@@ -950,27 +978,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Selection parameters of query head g from the unit's 64-bin sub-tile
-// histograms when the unit has at most 64 sub-tiles (one per lane): the same
-// theta / need_eq / prefix counts as the threshold kernel, for the sub-tiles
-// 4 tl .. 4 tl + 3 of one select workgroup.  Bin totals come from a register
-// reduce-scatter over the lanes (lane l ends with the total of bin l + 1).
-// h: this lane's sub-tile histogram (hist_row_load); results go to s_par[g]
-// = (theta, need_eq) and s_base[w][g] = (#gt, #eq) before sub-tile 4 tl + w.
-__device__ __forceinline__ void hist_row_load(const uint32_t* __restrict__ tile_hist, int unit, int max_subs,
-                                              int subs, int g, int lane, uint32_t (&h)[64]) {
-  if (lane < subs) {
-#pragma unroll
-    for (int q4 = 0; q4 < 16; ++q4) {
-      const uint4 x = *reinterpret_cast<const uint4*>(tile_hist + hist_index<NBIN>(unit, max_subs, lane, g, 4 * q4));
-      h[4 * q4] = x.x; h[4 * q4 + 1] = x.y; h[4 * q4 + 2] = x.z; h[4 * q4 + 3] = x.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) h[i] = 0;
-  }
-}
-
 // theta and need_eq of one query head from its bin totals (lane l holds the
 // count of keys with S = l + 1 among the unit's n keys): theta = the highest
 // score whose suffix count #{S >= theta} reaches C (0: every key is taken);
@@ -991,41 +998,59 @@ __device__ __forceinline__ void theta_from_totals(uint32_t tot, int64_t n, int n
   need_eq = want < eq_tot ? want : eq_tot;
 }
 
-// keys of one histogram (h[b] = count of S = b + 1 among len keys) above and
-// at theta
-__device__ __forceinline__ void counts_at_theta(const uint32_t (&h)[64], int theta, int64_t len, int& gt, int& eq) {
-  int nz = 0;
-  gt = 0;
-  eq = 0;
-#pragma unroll
-  for (int b = 0; b < 64; ++b) {
-    const int c = (int)h[b];
-    nz += c;
-    gt += (b + 1 > theta) ? c : 0;
-    eq = (b + 1 == theta) ? c : eq;
-  }
-  if (theta == 0) eq = (int)len - nz;
-}
-
-__device__ __forceinline__ void select_params_wave(const uint32_t (&h)[64], int64_t n, int subs, int sub_len,
-                                                   int tl, int g, int n_candidates, int lane, int2* s_par,
-                                                   int2 (*s_base)[MAXG]) {
-  uint32_t v[64];
-#pragma unroll
-  for (int i = 0; i < 64; ++i) v[i] = h[i];
+// Selection parameters of query head g (wave g) for the sub-tiles 4 tl ..
+// 4 tl + 3 of one select workgroup, from the unit's bin totals (tot at lane
+// l: keys with S = l + 1) and the sub-tiles' suffix counts: theta / need_eq as
+// theta_from_totals, then the keys above / at theta in every earlier
+// sub-tile, 64 sub-tiles (one per lane) per step.  Results go to s_par[g] =
+// (theta, need_eq) and s_base[w][g] = (#gt, #eq) before sub-tile 4 tl + w.
+__device__ __forceinline__ void select_params_suffix(uint32_t tot, const uint32_t* __restrict__ suf, int unit,
+                                                     int max_subs, int sub_len, int64_t n, int tl, int g,
+                                                     int n_candidates, int lane, int2* s_par,
+                                                     int2 (*s_base)[MAXG]) {
   int theta;
   uint32_t need_eq;
-  theta_from_totals(reduce_scatter64(v, lane), n, n_candidates, theta, need_eq);
-  // this lane's sub-tile: keys above / at theta, then exclusive prefixes
-  int64_t len = n - (int64_t)lane * sub_len;
-  len = len < 0 ? 0 : (len > sub_len ? sub_len : len);
-  int gt, eq;
-  counts_at_theta(h, theta, len, gt, eq);
-  if (lane >= subs) { gt = 0; eq = 0; }
-  const int pg = (int)wave_incl_scan((uint32_t)gt), pe = (int)wave_incl_scan((uint32_t)eq);
-  const int w = lane - 4 * tl;
-  if (w >= 0 && w < 4) s_base[w][g] = make_int2(pg - gt, pe - eq);
-  if (lane == 0) s_par[g] = make_int2(theta, (int)need_eq);
+  theta_from_totals(tot, n, n_candidates, theta, need_eq);
+  const uint32_t* row_gt = suf + suf_index(unit, max_subs, g, theta + 1, 0);             // #{S > theta}
+  const uint32_t* row_ge = suf + suf_index(unit, max_subs, g, theta > 0 ? theta : 1, 0);  // #{S >= theta}
+  const int first = 4 * tl;
+  int pre_gt = 0, pre_eq = 0;
+  int in_gt[4] = {0, 0, 0, 0}, in_eq[4] = {0, 0, 0, 0};
+  for (int c0 = 0; c0 < first + 4; c0 += 64) {   // uniform
+    const int sub = c0 + lane;
+    int gt = 0, eq = 0;
+    if (sub < first + 4) {
+      gt = (int)row_gt[sub];
+      int ge;
+      if (theta > 0) {
+        ge = (int)row_ge[sub];
+      } else {                                    // every key has S >= 0
+        int64_t len = n - (int64_t)sub * sub_len;
+        ge = (int)(len < 0 ? 0 : (len > sub_len ? sub_len : len));
+      }
+      eq = ge - gt;
+    }
+    const bool before = sub < first;
+    pre_gt += (int)xor_butterfly_u(before ? (uint32_t)gt : 0u, lane, AddU());
+    pre_eq += (int)xor_butterfly_u(before ? (uint32_t)eq : 0u, lane, AddU());
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int sw = first + w - c0;              // uniform
+      if (sw >= 0 && sw < 64) {
+        in_gt[w] = __builtin_amdgcn_readlane(gt, sw);
+        in_eq[w] = __builtin_amdgcn_readlane(eq, sw);
+      }
+    }
+  }
+  if (lane == 0) {
+    s_par[g] = make_int2(theta, (int)need_eq);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      s_base[w][g] = make_int2(pre_gt, pre_eq);
+      pre_gt += in_gt[w];
+      pre_eq += in_eq[w];
+    }
+  }
 }
 
 // Per-head selection state of one wave walking its keys in ascending order:
@@ -1083,17 +1108,17 @@ struct HeadSelect {
   }
 };
 
-// FUSED: the unit has at most 64 sub-tiles of 64-bin histograms, and each
-// workgroup derives the parameters itself (select_params_wave) instead of
-// reading the threshold kernel's.  The tiles of one unit share an XCD where
-// they can (xcd_unit_tile), so the unit's histograms are fetched into its L2
-// once.
+// FUSED (64 bins, rank tiers): each workgroup derives the parameters itself
+// from the unit's totals and the sub-tiles' suffix counts
+// (select_params_suffix); otherwise it reads the threshold kernel's.  The
+// tiles of one unit share an XCD where they can (xcd_unit_tile), so the
+// unit's counts are fetched into its L2 once.
 template <int G, bool FUSED>
 __global__ void __launch_bounds__(256)
 select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__ params,
               const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx, int64_t n, int64_t s_stride,
               int tiles, int max_subs, int tile, int n_q_heads, int n_kv_heads, int n_candidates,
-              const uint32_t* __restrict__ tile_hist, uint32_t* __restrict__ err) {
+              const uint32_t* __restrict__ unit_tot, const uint32_t* __restrict__ suf, uint32_t* __restrict__ err) {
   __shared__ uint2 s_ik[4][SEL_QCAP];             // compacted keys: (key, packed S)
   __shared__ int2 s_par[FUSED ? MAXG : 1];
   __shared__ int2 s_base[FUSED ? 4 : 1][MAXG];
@@ -1111,12 +1136,12 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
   const int w1 = (w0 + wkeys < k1) ? w0 + wkeys : k1;
   const uint32_t* srow = scores + (int64_t)unit * s_stride;
 
-  // fused parameters: the histogram rows are requested before the scores, so
-  // that waiting for them does not wait for the scores (the memory counter is
-  // in order)
-  uint32_t hrow[FUSED ? 64 : 1];
+  // fused parameters: the head's bin totals are requested before the scores,
+  // so that waiting for them does not wait for the scores (the memory
+  // counter is in order)
+  uint32_t tot = 0;
   if constexpr (FUSED) {
-    if (wave < G) hist_row_load(tile_hist, unit, max_subs, 4 * tiles, wave, lane, hrow);
+    if (wave < G) tot = unit_tot[((int64_t)unit * MAXG + wave) * NBIN + lane];
   }
 
   // packed scores of keys w0 + r*64 + lane, in groups of SEL_GRP chunks
@@ -1133,7 +1158,8 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
   // this wave's sub-tile
   auto setup = [&]() __attribute__((always_inline)) {
     if constexpr (FUSED) {
-      if (wave < G) select_params_wave(hrow, n, 4 * tiles, tile >> 2, tl, wave, n_candidates, lane, s_par, s_base);
+      if (wave < G)
+        select_params_suffix(tot, suf, unit, max_subs, tile >> 2, n, tl, wave, n_candidates, lane, s_par, s_base);
       __syncthreads();
     }
 #pragma unroll
