@@ -1,16 +1,22 @@
 """Decode-step benchmark of the ParisKV retrieval + sparse-attention path on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched128k]
-                    [--layers L] [--no-cpu] [--copy-calibration]
+                    [--layers L] [--no-cpu] [--no-recall] [--no-extra] [--copy-calibration]
 
 A step is one pass of the whole hot path for one layer: one pk_retrieve_attend
 call (query rotation, collision votes, candidate selection, 4-bit rerank,
 Top-k, sparse attention) for every (sequence, query head) of the workload,
-plus pk_append_keys of one key per KV head on the drift workload.  Inputs are seeded
-synthetic Llama-3.1-8B-shaped tensors already resident in HBM (or, for the
-1M-token workload, K/V in pinned host memory read through mapped pointers).
-Consecutive steps rotate over `--layers` distinct summary buffers and a pool
-of queries, so the codes are not served from the 256 MB last-level cache.
+plus pk_append_keys of one key per KV head on the drift workload.  Inputs are
+seeded synthetic Llama-3.1-8B-shaped tensors already resident in HBM (or, for
+the 1M-token workload, K/V in pinned host memory read through mapped
+pointers).  Consecutive steps rotate over distinct per-layer summary buffers
+(enough that one rotation touches >= 1 GiB of codes and records, four times
+the 256 MB last-level cache) and a pool of queries; the drift workload
+appends each step's key to the layer it retrieves from.
+
+The headline line is the batched 128K workload; with the default workload
+the 1M-token offload and the 128K drift stream are run after it and reported
+under "workloads" (the metric is quoted at 128K and 1M context).
 
 Prints one JSON line.
 """
@@ -33,6 +39,7 @@ METRIC = "retrieval+sparse-attn decode steps/s per layer at 128K/1M ctx; % HBM p
 HBM_PEAK_GBS = 8000.0
 CODE_BYTES = 16
 RECORD_BYTES = 128
+STAGE12 = ("qprep", "collide", "threshold", "select", "rerank", "rerank_topk", "topk")
 
 
 def log(*a):
@@ -48,8 +55,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="distinct summary buffers rotated (0 = auto)")
     ap.add_argument("--queries", type=int, default=8, help="query sets in the pool")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-workers", type=int, default=0, help="oracle worker processes (0 = min(16, cores))")
     ap.add_argument("--no-recall", action="store_true", help="skip the recall@k check after the timed steps")
+    ap.add_argument("--no-extra", action="store_true", help="only the named workload (no 1M / drift entries)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM traffic counter calibration)")
     return ap.parse_args()
@@ -84,75 +93,98 @@ def algorithmic_bytes(w, n: int) -> dict:
     }
 
 
-def cpu_baseline(w, K, V, Q_pool, seconds: float) -> dict:
-    """The oracle's decode step on the host, on a bounded sample of the workload."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle's decode step, one unit per task, in worker processes
+# ---------------------------------------------------------------------------
+def _oracle_worker(task):
+    """Runs in a spawned process (single-threaded numpy): encode one unit with
+    the oracle (untimed), then time decode steps of its query heads for
+    `seconds`.  Returns (unit-steps, seconds)."""
+    wname, u, seconds = task
     from threadpoolctl import threadpool_limits
 
     from oracle import pariskv_oracle as O
     from workloads import synthetic as S
-    signs = O.srht_signs(w.srht_seed)
-    L32, T32 = O.magnitude_tables_f32()
-    units = [0] if w.units == 1 else [0, w.units - 1]
-    encs = {}
-    for u in units:                                   # prefill summaries: not timed
-        b, h = divmod(u, w.n_kv_heads)
-        kf = S.as_f32(K[b, h])
-        encs[u] = (kf, S.as_f32(V[b, h]),
-                   {k: np.concatenate([O.encode_f32(kf[i:i + 65536], signs, L32, T32)[k]
-                                       for i in range(0, kf.shape[0], 65536)])
-                    for k in ("codes", "nibbles", "weights", "norms")})
-    done = 0
-    t0 = time.perf_counter()
+    w = S.WORKLOADS[wname]
+    b, h = divmod(u, w.n_kv_heads)
     with threadpool_limits(limits=1):
+        keys = S.unit_keys(w, b, h)
+        kf = S.as_f32(keys)
+        vf = S.as_f32(S.unit_values(w, b, h))
+        signs = O.srht_signs(w.srht_seed)
+        L32, T32 = O.magnitude_tables_f32()
+        parts = [O.encode_f32(kf[i:i + 65536], signs, L32, T32) for i in range(0, kf.shape[0], 65536)]
+        enc = {k: np.concatenate([p[k] for p in parts]) for k in ("codes", "nibbles", "weights", "norms")}
+        qs = [S.as_f32(np.stack([S.query(w, b, h * w.group + g, keys, step=s) for g in range(w.group)]))
+              for s in range(4)]
+        M = None
+        if w.tier_mode == "percentile":
+            rho = O.adaptive_ratios_permille(w.n)[1] if w.adaptive else w.collision_permille
+            M = O.ratio_count(rho, w.n)
+        done = 0
+        t0 = time.perf_counter()
         while True:
-            for u in units:
-                b, h = divmod(u, w.n_kv_heads)
-                kf, vf, enc = encs[u]
-                q = Q_pool[done % len(Q_pool)]
-                qs = S.as_f32(q[b, h * w.group:(h + 1) * w.group])
-                M = None
-                if w.tier_mode == "percentile":
-                    rho = O.adaptive_ratios_permille(w.n)[1] if w.adaptive else w.collision_permille
-                    M = O.ratio_count(rho, w.n)
-                O.decode_unit(qs, kf, vf, enc, signs, L32, w.tier_top, w.tier_weight, candidates_per_call(w, w.n),
-                              w.top_k, w.softmax_scale, percentile_M=M)
-                done += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-    el = time.perf_counter() - t0
-    per_unit = el / done
-    return {"value": 1.0 / (per_unit * w.units), "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} unit-steps (units {units}, {w.group} query heads each, full n={w.n}) "
-                      f"in {el:.1f} s; one step = {w.units} units"}
+            O.decode_unit(qs[done % len(qs)], kf, vf, enc, signs, L32, w.tier_top, w.tier_weight,
+                          candidates_per_call(w, w.n), w.top_k, w.softmax_scale, percentile_M=M)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return done, el
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this path has no multi-GPU mode; "
-              "units shard across GPUs with no exchange, see the design notes.", file=sys.stderr)
-        sys.exit(2)
+def cpu_baseline(w, seconds: float, workers: int) -> dict:
+    """The oracle on the host's cores, on a bounded sample of the workload's units."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    cores = os.cpu_count() or 1
+    n_proc = workers or max(1, min(16, cores, w.units))
+    units = sorted({int(round(i * (w.units - 1) / max(1, n_proc - 1))) for i in range(n_proc)})
+    t0 = time.perf_counter()
+    # fresh interpreters (spawn): the workers never touch the GPU; a failing
+    # worker ends the pool with an error instead of being restarted
+    with ProcessPoolExecutor(len(units), mp_context=mp.get_context("spawn")) as pool:
+        res = list(pool.map(_oracle_worker, [(w.name, u, seconds) for u in units]))
+    wall = time.perf_counter() - t0
+    unit_steps_per_s = sum(d / el for d, el in res)
+    done = sum(d for d, _ in res)
+    return {"value": unit_steps_per_s / w.units, "unit": "steps/s", "cores": len(units), "kind": "oracle",
+            "sample": f"{done} unit-steps of the full-size units {units} ({w.group} query heads each, "
+                      f"n={w.n}), one single-threaded worker process per unit for {seconds:.0f} s each; "
+                      f"one step = {w.units} units (rate summed over the workers)",
+            "host_cores": cores, "cpu_model": cpu_model(), "wall_s": round(wall, 1)}
+
+
+# ---------------------------------------------------------------------------
+def run_workload(w, args, steps: int, warmup: int, want_recall: bool) -> dict:
     import torch
 
     from kv_cache_top_amd import pariskv as P
+    from kv_cache_top_amd.profiling import load_trace_avg_us, load_traffic
+    from kv_cache_top_amd.studies import exact_topk_fp64
     from workloads import synthetic as S
+    dev = torch.device("cuda")
 
     def to_torch(a: np.ndarray):
         if a.dtype == np.uint16:
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    w = S.WORKLOADS[args.workload]
-    if w.sink_tokens or w.local_tokens:
-        return run_layout(args, w)
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda")
     t0 = time.time()
-    log(f"[bench] generating {w.name}: units={w.units} n={w.n} C={w.n_candidates}")
+    log(f"[bench] {w.name}: generating units={w.units} n={w.n} C={w.n_candidates}")
     K = S.all_keys(w)
     V = S.all_values(w)
     Q_pool = [S.all_queries(w, K, step=s) for s in range(args.queries)]
-    log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
+    log(f"[bench] {w.name}: inputs ready in {time.time() - t0:.1f} s")
 
     cap = w.n_capacity
     cfg = P.make_config(w.batch, w.n_kv_heads, w.n_q_heads, cap, w.n_candidates, w.top_k, w.softmax_scale,
@@ -162,6 +194,13 @@ def main():
     ctx = P.Context(cfg)
     kv_dt = P.PK_BF16 if w.kv_dtype == "bf16" else P.PK_F32
     host_bufs = []
+    app = bool(w.append_steps)
+    ak = av = None
+    if app:
+        ak = np.stack([np.stack([np.stack([S.appended_key(w, b, h, t) for t in range(w.append_steps)])
+                                 for h in range(w.n_kv_heads)]) for b in range(w.batch)])
+        av = np.stack([np.stack([np.stack([S.appended_value(w, b, h, t) for t in range(w.append_steps)])
+                                 for h in range(w.n_kv_heads)]) for b in range(w.batch)])
     if w.kv_home == "host":
         def mapped(A):
             shape = (w.batch, w.n_kv_heads, cap, 128)
@@ -175,12 +214,14 @@ def main():
         kv_strides = (w.n_kv_heads * cap * 128, cap * 128, 128)
         Kt = Vt = None
     else:
-        def dev_full(A):
+        def dev_full(A, extra):
             t = torch.empty((w.batch, w.n_kv_heads, cap, 128),
                             dtype=torch.bfloat16 if A.dtype == np.uint16 else torch.float32, device=dev)
             t[:, :, :A.shape[2]] = to_torch(A)
+            if extra is not None:
+                t[:, :, A.shape[2]:] = to_torch(extra)
             return t
-        Kt, Vt = dev_full(K), dev_full(V)
+        Kt, Vt = dev_full(K, ak), dev_full(V, av)
         kptr, vptr = Kt.data_ptr(), Vt.data_ptr()
         kv_strides = (Kt.stride(0), Kt.stride(1), Kt.stride(2))
 
@@ -189,44 +230,32 @@ def main():
     P._check(P._lib.pk_encode_keys(ctx.h, ctypes.c_void_p(kptr), kv_dt, st3, w.n, ctypes.byref(sums0.s),
                                    P._stream(None)), ctx.h)
     torch.cuda.synchronize()
-    # distinct summary buffers per layer so a step's codes are not LLC-resident
-    step_bytes = algorithmic_bytes(w, w.n)
-    touched = step_bytes["collide"] + step_bytes["rerank"]
-    layers = args.layers or max(1, min(8, int(np.ceil(1.0 * 2 ** 30 / max(touched, 1)))))
+    # distinct summary buffers per layer, so that one rotation touches >= 1 GiB
+    # of codes and gathered records (the step's own reads are not LLC hits)
+    nb0 = algorithmic_bytes(w, w.n)
+    touched = nb0["collide"] + nb0["rerank"]
+    summary_bytes = sums0.codes.numel() + sums0.records.numel() + 4 * sums0.norms.numel()
+    layers = args.layers or max(1, min(64, int(np.ceil(2 ** 30 / max(touched, 1))),
+                                       int((16 << 30) // max(summary_bytes, 1))))
     sums = [sums0] + [sums0.clone(cfg) for _ in range(layers - 1)]
     Qd = [to_torch(q) for q in Q_pool]
-    H = w.batch * w.n_q_heads
     idx = torch.empty((w.batch, w.n_q_heads, w.top_k), dtype=torch.int32, device=dev)
     est = torch.empty((w.batch, w.n_q_heads, w.top_k), dtype=torch.float32, device=dev)
     out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.bfloat16 if kv_dt == P.PK_BF16 else torch.float32,
                       device=dev)
     stream = torch.cuda.current_stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
-
-    # drift stream: appended keys per step (rows n0 + t of K/V)
-    app = None
-    if w.append_steps:
-        total = args.warmup + 2 * args.steps
-        if total > w.append_steps:
-            raise SystemExit(f"drift workload holds {w.append_steps} appended steps; warmup + 2*steps = {total}")
-        ak = np.stack([np.stack([np.stack([S.appended_key(w, b, h, t) for t in range(w.append_steps)])
-                                 for h in range(w.n_kv_heads)]) for b in range(w.batch)])
-        av = np.stack([np.stack([np.stack([S.appended_value(w, b, h, t) for t in range(w.append_steps)])
-                                 for h in range(w.n_kv_heads)]) for b in range(w.batch)])
-        if Kt is not None:
-            Kt[:, :, w.n:] = to_torch(ak)
-            Vt[:, :, w.n:] = to_torch(av)
-        app = True
-        layers = 1
-        sums = [sums0]
+    if app:
+        per_layer = -(-(warmup + 2 * steps) // layers)
+        if per_layer > w.append_steps:
+            raise SystemExit(f"{w.name} holds {w.append_steps} appended keys per layer; needs {per_layer}")
+    row_bytes = kv_strides[2] * (2 if kv_dt == P.PK_BF16 else 4)
 
     def step(i):
         s = sums[i % layers]
-        if app:
-            t = s.s.n - w.n
-            off = (w.n + t) * kv_strides[2] * (2 if kv_dt == P.PK_BF16 else 4)
-            P._check(P._lib.pk_append_keys(ctx.h, ctypes.c_void_p(kptr + off), kv_dt, st3, 1, ctypes.byref(s.s),
-                                           sptr), ctx.h)
+        if app:   # this layer's next key (row n of K/V) joins its summaries
+            P._check(P._lib.pk_append_keys(ctx.h, ctypes.c_void_p(kptr + s.s.n * row_bytes), kv_dt, st3, 1,
+                                           ctypes.byref(s.s), sptr), ctx.h)
         q = Qd[i % len(Qd)]
         P._check(P._lib.pk_retrieve_attend(ctx.h, ctypes.c_void_p(q.data_ptr()), kv_dt, ctypes.byref(s.s),
                                            ctypes.c_void_p(kptr), ctypes.c_void_p(vptr), kv_dt, st3,
@@ -234,48 +263,188 @@ def main():
                                            ctypes.c_void_p(est.data_ptr()), ctypes.c_void_p(out.data_ptr()), kv_dt,
                                            None, sptr), ctx.h)
 
-    log(f"[bench] warmup {args.warmup} steps, {layers} rotated layer buffers")
-    for i in range(args.warmup):
+    log(f"[bench] {w.name}: warmup {warmup} steps, {layers} rotated layer buffers")
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
     # timed region 1: the step rate (no per-kernel events)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    for i in range(steps):
+        step(warmup + i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t1
-    ms = 1e3 * el / args.steps
-    log(f"[bench] {args.steps} steps in {el * 1e3:.1f} ms: {ms * 1e3:.1f} us/step")
+    ms = 1e3 * el / steps
+    log(f"[bench] {w.name}: {steps} steps in {el * 1e3:.1f} ms: {ms * 1e3:.1f} us/step")
 
     # timed region 2: the same steps with HIP events around every kernel launch
-    P.pk_timing_begin(ctx.h, args.steps)
+    P.pk_timing_begin(ctx.h, steps)
     torch.cuda.synchronize()
     t2 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + args.steps + i if app else i)
+    for i in range(steps):
+        step(warmup + steps + i)
     torch.cuda.synchronize()
     el2 = time.perf_counter() - t2
     tim = P.pk_timing_end(ctx.h)
     kern = {k: {"launches": c, "avg_us": (1e3 * t / c if c else None)} for k, (c, t) in tim.items()}
-    nb = algorithmic_bytes(w, w.n)
+    n_now = sums[0].s.n
+    nb = algorithmic_bytes(w, n_now)
+    att_in = None
     if kern["attend"]["launches"] == 0 and kern["rerank_topk"]["launches"] > 0:
+        att_in = "rerank_topk"
         nb["rerank_topk"] += nb["attend"]               # the attention ran inside the rerank + top-k kernel
     elif kern["attend"]["launches"] == 0 and kern["topk"]["launches"] > 0:
+        att_in = "topk"
         nb["topk"] = nb["attend"]                       # the attention ran inside the top-k kernel
+    host_kv = w.kv_home == "host"
     for k in kern:
         if kern[k]["avg_us"] and nb.get(k):
             kern[k]["alg_GBps"] = round(nb[k] / (kern[k]["avg_us"] * 1e-6) / 1e9, 1)
-    timed = {k: v for k, v in kern.items() if v["avg_us"]}
-    dom = max(timed, key=lambda k: timed[k]["avg_us"])
+        tr = load_trace_avg_us(k, w.name)
+        if tr is not None and kern[k]["launches"]:
+            kern[k]["trace_avg_us"] = tr
+    # the dominant HBM kernel (a kernel whose bytes cross the host link is
+    # reported under host_link instead)
+    hbm_kernels = {k: v for k, v in kern.items() if v["avg_us"] and not (host_kv and k == att_in)}
+    dom = max(hbm_kernels, key=lambda k: hbm_kernels[k]["avg_us"])
     achieved = nb.get(dom, 0) / (kern[dom]["avg_us"] * 1e-6) / 1e9
-    log("[bench] per-kernel: " + json.dumps(kern))
+    trace_us = kern[dom].get("trace_avg_us")
+    log(f"[bench] {w.name}: per-kernel: " + json.dumps(kern))
+    traffic_b = load_traffic(dom, w.name)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic_b is None else round(traffic_b / (kern[dom]["avg_us"] * 1e-6) / 1e9, 1),
+                "alg_bytes_per_launch": nb.get(dom, 0), "hbm_bytes_per_launch": traffic_b,
+                "avg_launch_us": round(kern[dom]["avg_us"], 3),
+                "trace_avg_us": trace_us,
+                "frac_trace": (round(nb.get(dom, 0) / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if trace_us else None)}
+
+    # Stage I + II: the retrieval kernels (with the attention when it runs
+    # inside them over HBM rows; a kernel that reads its rows over the host
+    # link is reported under host_link instead)
+    s12 = [k for k in STAGE12 if kern[k]["launches"] and not (host_kv and k == att_in)]
+    s12_us = sum(kern[k]["avg_us"] for k in s12)
+    s12_tr = (sum(kern[k]["trace_avg_us"] for k in s12) if all("trace_avg_us" in kern[k] for k in s12) else None)
+    codes_b, rec_b = CODE_BYTES * n_now * w.units, nb["rerank"]
+    att_b = nb["attend"] if (att_in and not host_kv) else 0
+    s12_b = codes_b + rec_b + att_b
+    stage12 = {"kernels": s12, "event_us": round(s12_us, 3), "trace_us": None if s12_tr is None else round(s12_tr, 3),
+               "alg_bytes": s12_b, "codes_bytes": codes_b, "records_bytes": rec_b, "attention_bytes_hbm": att_b,
+               "GBps": round(s12_b / (s12_us * 1e-6) / 1e9, 1),
+               "frac": round(s12_b / (s12_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+               "frac_trace": None if s12_tr is None else round(s12_b / (s12_tr * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    # records of the union of each unit's query heads' candidate sets (what a
+    # per-unit gather would need), from one untimed call with debug copies
+    s_last = sums[0]
+    C_now = candidates_per_call(w, n_now)
+    cand = torch.empty((w.batch * w.n_q_heads, w.n_candidates), dtype=torch.int32, device=dev)
+    dbg = P.pk_debug(0, 0, 0, cand.data_ptr(), 0)
+    P._check(P._lib.pk_retrieve(ctx.h, ctypes.c_void_p(Qd[0].data_ptr()), kv_dt, ctypes.byref(s_last.s),
+                                ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(est.data_ptr()), ctypes.byref(dbg),
+                                sptr), ctx.h)
+    torch.cuda.synchronize()
+    cu = cand.view(w.units, w.group, -1)[:, :, :min(C_now, n_now)]
+    union = sum(int(torch.unique(cu[u]).numel()) for u in range(w.units))
+    stage12["records_union_bytes"] = RECORD_BYTES * union
+    stage12["frac_union"] = round((codes_b + RECORD_BYTES * union + att_b) / (s12_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+
+    res = {"value": round(1e3 / ms, 2), "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
+           "ms_per_step_with_kernel_events": round(1e3 * el2 / steps, 4),
+           "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads, "n_q_heads": w.n_q_heads,
+                      "n": w.n, "n_at_end": int(n_now), "n_candidates": candidates_per_call(w, w.n),
+                      "top_k": w.top_k, "kv_dtype": w.kv_dtype, "tiers": w.tier_mode, "adaptive_ratios": w.adaptive,
+                      "kv_home": w.kv_home, "layers_rotated": layers, "query_pool": len(Qd),
+                      "append_per_step": 1 if app else 0,
+                      "llc_resident": bool(layers * touched <= 256 * 2 ** 20)},
+           "roofline": roofline, "stage12": stage12,
+           "step": {"alg_bytes": nb["collide"] + nb["rerank"] + nb["attend"] + nb["encode"],
+                    "frac_of_peak": round((nb["collide"] + nb["rerank"] + nb["attend"] + nb["encode"])
+                                          / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "kernels": kern}
+
+    if host_kv:
+        # the K/V rows cross the host link: their kernel against a measured
+        # ceiling, a plain 16-byte-per-lane copy out of mapped host memory
+        probe_n = 64 << 20
+        hsrc, dsrc = P.pk_host_alloc_mapped(probe_n)
+        dst = torch.empty(probe_n, dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            P._check(P._lib.pk_calibration_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(dsrc), probe_n, sptr))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            P._check(P._lib.pk_calibration_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(dsrc), probe_n, sptr))
+        e1.record()
+        torch.cuda.synchronize()
+        ceil_gbs = 5 * probe_n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        P.pk_host_free(hsrc)
+        del dst
+        hk = att_in or "attend"
+        hb = nb["attend"]
+        hus = kern[hk]["avg_us"]
+        res["host_link"] = {"kernel": hk, "bytes_per_step": hb, "avg_launch_us": round(hus, 3),
+                            "GBps": round(hb / (hus * 1e-6) / 1e9, 2),
+                            "mapped_read_ceiling_GBps": round(ceil_gbs, 2),
+                            "frac_of_ceiling": round(hb / (hus * 1e-6) / 1e9 / ceil_gbs, 4),
+                            "note": "the kernel also selects the Top-k before it reads the rows"}
+
+    if want_recall:
+        # recall@k of every query head: the retrieved rows against the exact
+        # Top-k of <k_i, q> (fp64, ties to the lower index) over all current keys
+        P._check(P._lib.pk_retrieve(ctx.h, ctypes.c_void_p(Qd[0].data_ptr()), kv_dt, ctypes.byref(s_last.s),
+                                    ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(est.data_ptr()), None, sptr),
+                 ctx.h)
+        got = idx.cpu().numpy()
+        qf = Qd[0].float()
+        hits = []
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                if Kt is not None:
+                    kf = Kt[b, h, :n_now]
+                else:
+                    rows = [K[b, h, :min(n_now, w.n)]] + ([ak[b, h, :n_now - w.n]] if n_now > w.n else [])
+                    kf = torch.from_numpy(S.as_f32(np.concatenate(rows))).to(dev)
+                ex = exact_topk_fp64(kf, qf[b, h * w.group:(h + 1) * w.group], w.top_k)
+                for g in range(w.group):
+                    hits.append(len(np.intersect1d(ex[g], got[b, h * w.group + g])) / ex.shape[1])
+                del kf
+        recall = float(np.mean(hits))
+        log(f"[bench] {w.name}: recall@{w.top_k} over {len(hits)} query heads at n={n_now}: {recall:.3f}")
+        res["recall_at_k"] = {"value": round(recall, 4), "k": w.top_k, "n": int(n_now), "query_heads": len(hits),
+                              "reference": "exact Top-k of <k_i, q> in fp64 over all current keys, ties to the "
+                                           "lower key index"}
+    ctx.close()
+    for hb_ in host_bufs:
+        P.pk_host_free(hb_)
+    del sums, Kt, Vt
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this path has no multi-GPU mode; "
+              "(sequence, KV head) units shard across GPUs with no exchange (see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from workloads import synthetic as S
+    torch.cuda.set_device(0)
+    w = S.WORKLOADS[args.workload]
+    if w.sink_tokens or w.local_tokens:
+        return run_layout(args, w)
+    head = run_workload(w, args, args.steps, args.warmup, not args.no_recall)
 
     if args.copy_calibration:
         # 1 GiB each way through the library's 16-byte-per-lane copy: the counter
         # runs divide by what FETCH_SIZE / WRITE_SIZE read for it
-        a = torch.ones(2 ** 30, dtype=torch.uint8, device=dev)
+        from kv_cache_top_amd import pariskv as P
+        a = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda")
         b2 = torch.empty_like(a)
         for _ in range(3):
             P.pk_calibration_copy(b2, a)
@@ -284,74 +453,40 @@ def main():
             raise SystemExit("calibration copy mismatch")
         del a, b2
 
-    # retrieval quality of the final state: recall@k of every query head against
-    # the exact Top-k of <k_i, q> over all current keys (fp32 on the GPU, untimed)
-    recall_info = None
-    s_last = sums[0]
-    n_now = s_last.s.n
-    if not args.no_recall:
-        qi = 0
-        P._check(P._lib.pk_retrieve(ctx.h, ctypes.c_void_p(Qd[qi].data_ptr()), kv_dt, ctypes.byref(s_last.s),
-                                    ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(est.data_ptr()), None, sptr), ctx.h)
-        got = idx.cpu().numpy()
-        qf = Qd[qi].float()
-        hits = []
-        for b in range(w.batch):
-            for h in range(w.n_kv_heads):
-                if Kt is not None:
-                    kf = Kt[b, h, :n_now].float()
-                else:
-                    kf = torch.from_numpy(S.as_f32(K[b, h, :n_now])).to(dev)
-                sc = kf @ qf[b, h * w.group:(h + 1) * w.group].T          # [n, G]
-                ex = torch.topk(sc, min(w.top_k, n_now), dim=0).indices.T.cpu().numpy()
-                for g in range(w.group):
-                    hits.append(len(np.intersect1d(ex[g], got[b, h * w.group + g])) / ex.shape[1])
-                del kf, sc
-        recall = float(np.mean(hits))
-        log(f"[bench] recall@{w.top_k} over {len(hits)} query heads at n={n_now}: {recall:.3f}")
-        recall_info = {"value": round(recall, 4), "k": w.top_k, "n": int(n_now), "query_heads": len(hits),
-                       "reference": "exact Top-k of <k_i, q> in fp32 over all current keys"}
-
-    from kv_cache_top_amd.profiling import load_traffic
-    traffic_b = load_traffic(dom, w.name)
-    traffic = None if traffic_b is None else round(traffic_b / (kern[dom]["avg_us"] * 1e-6) / 1e9, 1)
-
-    step_alg = nb["collide"] + nb["rerank"] + nb["attend"] + nb["encode"]
     res = {
         "metric": METRIC,
-        "value": round(1e3 / ms, 2),
+        "value": head["value"],
         "unit": "steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads, "n_q_heads": w.n_q_heads,
-                   "n": w.n, "n_candidates": candidates_per_call(w, w.n), "top_k": w.top_k, "kv_dtype": w.kv_dtype,
-                   "tiers": w.tier_mode, "adaptive_ratios": w.adaptive,
-                   "kv_home": w.kv_home, "layers_rotated": layers, "query_pool": len(Qd),
-                   "append_per_step": 1 if app else 0},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "alg_bytes_per_launch": nb.get(dom, 0), "hbm_bytes_per_launch": traffic_b,
-                     "avg_launch_us": round(kern[dom]["avg_us"], 3)},
-        "step": {"alg_bytes": step_alg, "alg_GBps": round(step_alg / (ms * 1e-3) / 1e9, 1),
-                 "frac_of_peak": round(step_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "ms_per_step_with_kernel_events": round(1e3 * el2 / args.steps, 4)},
-        "kernels": kern,
-        "recall_at_k": recall_info,
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "stage12": head["stage12"],
+        "step": dict(head["step"], ms_per_step_with_kernel_events=head["ms_per_step_with_kernel_events"]),
+        "kernels": head["kernels"],
+        "recall_at_k": head.get("recall_at_k"),
     }
+    if args.workload == "batched128k" and not args.no_extra:
+        extra = {}
+        for name, steps in (("offload1m", max(20, args.steps // 4)), ("drift128k", max(20, args.steps // 2))):
+            r = run_workload(S.WORKLOADS[name], args, steps, min(args.warmup, 20), not args.no_recall)
+            extra[name] = {k: r[k] for k in ("value", "ms_per_step", "steps", "config", "roofline", "stage12",
+                                             "kernels") if k in r}
+            for k in ("host_link", "recall_at_k"):
+                if k in r:
+                    extra[name][k] = r[k]
+        res["workloads"] = extra
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(w, K, V, Q_pool, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.cpu_workers)
     print(json.dumps(res), flush=True)
-    ctx.close()
-    for h in host_bufs:
-        P.pk_host_free(h)
 
 
 def run_layout(args, w):
@@ -365,7 +500,6 @@ def run_layout(args, w):
     from kv_cache_top_amd import pariskv as P
     from workloads import synthetic as S
     dev = torch.device("cuda")
-    torch.cuda.set_device(0)
 
     def to_torch(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -464,7 +598,8 @@ def run_layout(args, w):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads, "n_q_heads": w.n_q_heads,
                    "prefill": w.n, "zone_keys_end": int(n_zone), "sink": sink, "local": local, "update": upd,
-                   "n_candidates": w.n_candidates, "top_k": w.top_k, "kv_dtype": w.kv_dtype},
+                   "n_candidates": w.n_candidates, "top_k": w.top_k, "kv_dtype": w.kv_dtype,
+                   "llc_resident": True},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "alg_bytes_per_launch": alg, "avg_launch_us": round(kern[dom]["avg_us"], 3)},

@@ -131,6 +131,28 @@ def load_traffic(kernel: str, workload: str):
     return int(kv["hbm_bytes_per_launch"])
 
 
+def load_trace_avg_us(kernel: str, workload: str):
+    """Average rocprofv3 trace duration (us) of `kernel` (the pk_timing name) on
+    `workload` from profiles/kernels_<workload>.md, or None (no summary, no
+    such kernel, or stale: the summary's source digest differs)."""
+    path = os.path.join(PROFILES, f"kernels_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if f"kernel source digest: {kernel_source_digest()}" not in text:
+        return None
+    hits = []
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 3 and "_kernel" in cells[0]:
+            if cells[0].split("_kernel")[0] == kernel:
+                hits.append((int(cells[1]), float(cells[2])))
+    if not hits:
+        return None
+    calls = sum(c for c, _ in hits)
+    return round(sum(c * us for c, us in hits) / calls, 3)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)

@@ -14,7 +14,8 @@ final two-stage result; Fig. 9, recall against the candidate ratio):
   together, i.e. the tighter Stage II byte count 128 B x |union of the G
   candidate sets| per unit, against the per-head sum 128 B x G x C.
 
-The exact Top-k is <k_i, q> in fp32 over all current keys (torch on the GPU).
+The exact Top-k is the definition: <k_i, q> in fp64 over all current keys,
+ties to the lower key index (torch, on the device that holds the keys).
 Each result is printed as one JSON line, then a markdown table.
 
     python -m kv_cache_top_amd.studies drift [--every 64]
@@ -49,27 +50,50 @@ def _config(P, w, cap):
                          w.collision_permille, w.adaptive)
 
 
+def exact_topk_fp64(K, Q, k: int) -> np.ndarray:
+    """Exact Top-k of <k_i, q> for each row q of Q: fp64 inner products over
+    the keys K [n, 128] (torch tensors, any dtype and device), ordered by
+    (score desc, key index asc).  Returns numpy [G, min(k, n)]."""
+    import torch
+    sc = K.double() @ Q.double().T                                  # [n, G]
+    order = torch.sort(-sc, dim=0, stable=True).indices             # equal scores keep ascending index
+    return order[:min(k, K.shape[0])].T.cpu().numpy()
+
+
+def stage1_topk(S: np.ndarray, k: int) -> np.ndarray:
+    """The k keys with the largest collision score S, ties to the lower index."""
+    return np.lexsort((np.arange(S.shape[0]), -S.astype(np.int64)))[:k]
+
+
+def head_recalls(exact, S, cand, top):
+    """Recall of one query head's exact Top-k by (Stage I alone: the k keys
+    with the largest S; the candidate set; the final Top-k)."""
+    ex = set(np.asarray(exact).tolist())
+    k = len(ex)
+    by_s = stage1_topk(np.asarray(S), k)
+    c = np.asarray(cand)
+    t = np.asarray(top)
+    return (len(ex & set(by_s.tolist())) / k, len(ex & set(c[c >= 0].tolist())) / k,
+            len(ex & set(t[t >= 0].tolist())) / k)
+
+
 def _recalls(Kt, q, cand, top, scores, n, G, k):
     """Mean recall@k over the query heads of one retrieval, of: the k keys with
     the largest collision score S (Stage I alone, ties to the lower index), the
     candidate set (an upper bound for the final result) and the final Top-k."""
-    import torch
     s_top, coarse, final = [], [], []
     B, Hq, Hkv = q.shape[0], q.shape[1], Kt.shape[1]
-    qf = q.float()
     for b in range(B):
         for h in range(Hkv):
-            sc = Kt[b, h, :n].float() @ qf[b, h * G:(h + 1) * G].T
-            ex = torch.topk(sc, min(k, n), dim=0).indices.T.cpu().numpy()
+            ex = exact_topk_fp64(Kt[b, h, :n], q[b, h * G:(h + 1) * G], k)
             packed = scores[b * Hkv + h, :n]
             for g in range(G):
                 hid = b * Hq + h * G + g
-                exact = set(ex[g].tolist())
                 S = (packed >> np.uint32(8 * g)) & np.uint32(0xFF)
-                by_s = np.lexsort((np.arange(n), -S.astype(np.int64)))[:k]
-                s_top.append(len(exact & set(by_s.tolist())) / len(exact))
-                coarse.append(len(exact & set(cand[hid].tolist())) / len(exact))
-                final.append(len(exact & set(top[b, h * G + g].tolist())) / len(exact))
+                r = head_recalls(ex[g], S, cand[hid], top[b, h * G + g])
+                s_top.append(r[0])
+                coarse.append(r[1])
+                final.append(r[2])
     return float(np.mean(s_top)), float(np.mean(coarse)), float(np.mean(final))
 
 
@@ -85,41 +109,53 @@ def _retrieve(P, ctx, sums, q, w, cfg_c, dev):
     return cand.cpu().numpy(), idx.cpu().numpy(), scores.cpu().numpy().view(np.uint32)
 
 
-def drift(every: int, modes):
+def drift_stream(w, every: int, T: int | None = None, dev=None):
+    """Recall rows of one drift stream: encode the w.n prefill keys, then
+    append T keys per KV head one step at a time; every `every`-th step (and
+    the last) retrieve with queries planted on the current keys."""
     import torch
 
     from kv_cache_top_amd import pariskv as P
     from workloads import synthetic as S
-    dev = torch.device("cuda")
+    dev = dev or torch.device("cuda")
+    T = w.append_steps if T is None else T
+    K = S.all_keys(w)
+    ak = np.stack([np.stack([np.stack([S.appended_key(w, b, h, t) for t in range(T)])
+                             for h in range(w.n_kv_heads)]) for b in range(w.batch)])
+    Kall = np.concatenate([K, ak], axis=2)
+    Kt = _torch(Kall, dev)
+    cfg = _config(P, w, w.n + T)
+    ctx = P.Context(cfg)
+    sums = P.Summaries(cfg)
+    P.pk_encode_keys(ctx.h, Kt[:, :, :w.n], sums.s)
+    rows = []
+    for t in range(T + 1):
+        if t % every == 0 or t == T:
+            n_t = w.n + t
+            Q = S.all_queries(w, lambda bb, hh, J: Kall[bb, hh, J], step=t, n_t=n_t)
+            cand, top, scores = _retrieve(P, ctx, sums, _torch(Q, dev), w, cfg.n_candidates, dev)
+            st, c, f = _recalls(Kt, _torch(Q, dev), cand, top, scores, n_t, w.group, w.top_k)
+            rows.append({"study": "drift", "tiers": w.tier_mode, "step": t, "n": n_t,
+                         "stage1_top_k_recall": round(st, 4), "candidate_recall": round(c, 4),
+                         "final_recall": round(f, 4), "_Q": Q})
+        if t < T:
+            P.pk_append_keys(ctx.h, Kt[:, :, w.n + t:w.n + t + 1], sums.s)
+    ctx.close()
+    return rows, Kall
+
+
+def drift(every: int, modes):
+    from workloads import synthetic as S
     rows = []
     for mode in modes:
         base = S.WORKLOADS["drift128k"]
         # adaptive candidates: C = ceil(0.1 n) grows with the stream up to n + T keys
         w = base if mode == "rank" else S.custom("drift128k", tier_mode="percentile", adaptive=True,
                                                   n_candidates=(100 * (base.n + base.append_steps) + 999) // 1000)
-        T = w.append_steps
-        K = S.all_keys(w)
-        ak = np.stack([np.stack([np.stack([S.appended_key(w, b, h, t) for t in range(T)])
-                                 for h in range(w.n_kv_heads)]) for b in range(w.batch)])
-        Kall = np.concatenate([K, ak], axis=2)
-        Kt = _torch(Kall, dev)
-        cfg = _config(P, w, w.n + T)
-        ctx = P.Context(cfg)
-        sums = P.Summaries(cfg)
-        P.pk_encode_keys(ctx.h, Kt[:, :, :w.n], sums.s)
-        for t in range(T + 1):
-            if t % every == 0 or t == T:
-                n_t = w.n + t
-                Q = S.all_queries(w, lambda bb, hh, J: Kall[bb, hh, J], step=t, n_t=n_t)
-                cand, top, scores = _retrieve(P, ctx, sums, _torch(Q, dev), w, cfg.n_candidates, dev)
-                st, c, f = _recalls(Kt, _torch(Q, dev), cand, top, scores, n_t, w.group, w.top_k)
-                row = {"study": "drift", "tiers": mode, "step": t, "n": n_t, "stage1_top_k_recall": round(st, 4),
-                       "candidate_recall": round(c, 4), "final_recall": round(f, 4)}
-                print(json.dumps(row), flush=True)
-                rows.append(row)
-            if t < T:
-                P.pk_append_keys(ctx.h, Kt[:, :, w.n + t:w.n + t + 1], sums.s)
-        ctx.close()
+        for row in drift_stream(w, every)[0]:
+            row.pop("_Q")
+            print(json.dumps(row), flush=True)
+            rows.append(row)
     return rows
 
 

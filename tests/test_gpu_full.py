@@ -3,12 +3,13 @@ benchmark times (one pk_retrieve_attend call per step): the whole workload
 runs on the GPU; the oracle recomputes sampled units (every intermediate bit
 for bit, attention within 2e-2).
 
-  llama32k     1 x 8 KV / 32 q heads, n = 32768, C = 2048
-  batched128k  8 x 8 KV / 32 q heads, n = 131072, C = 4096
+  llama32k     1 x 8 KV / 32 q heads, n = 32768, C = 2048; 4 of 8 units checked
+  batched128k  8 x 8 KV / 32 q heads, n = 131072, C = 4096; 8 of 64 units checked
   offload1m    1 x 8 KV / 32 q heads, n = 1048576, C = 8192, K/V in pinned
-               host memory read through mapped device pointers
+               host memory read through mapped device pointers; 4 of 8 units
   drift128k    n = 131072 prefill + 1024 decode steps appending one key per KV
-               head with a drifting mean; sampled steps checked, recall reported
+               head with a drifting mean; 8 steps over the run checked on 2
+               units, recall reported
   batched128k_pct  batched128k with the pages' percentile tiers and adaptive
                ratios (C = 13108)
   drift128k_layout the sink / local / update-buffer layout over the drift stream
@@ -52,11 +53,12 @@ def _run_full(name, units, kv_host=False):
 
 
 def test_full_llama32k():
-    _run_full("llama32k", units=[0, 5])
+    _run_full("llama32k", units=[0, 3, 5, 7])
 
 
 def test_full_batched128k():
-    _run_full("batched128k", units=[0, 37, 63])
+    """One unit in every eighth: 0, 9, ..., 63 (units 8 apart run on one XCD)."""
+    _run_full("batched128k", units=[0, 9, 18, 27, 36, 45, 54, 63])
 
 
 def test_full_batched128k_percentile_adaptive():
@@ -65,7 +67,7 @@ def test_full_batched128k_percentile_adaptive():
 
 
 def test_full_offload1m_mapped_host_kv():
-    _run_full("offload1m", units=[6], kv_host=True)
+    _run_full("offload1m", units=[0, 2, 5, 7], kv_host=True)
 
 
 def test_full_drift_stream():
@@ -85,12 +87,13 @@ def test_full_drift_stream():
     Vall = np.concatenate([V0, av], axis=2)
     Q0 = S.all_queries(w, K0)
     run = GpuRun(w, Kall, Vall, Q0, n=w.n, capacity=w.n + T)
-    check_steps = {0, 1, 511, T - 1}
-    unit = 3
-    b, h = divmod(unit, w.n_kv_heads)
-    kf_all = S.as_f32(Kall[b, h])
-    vf_all = S.as_f32(Vall[b, h])
-    enc_all = oracle_encode(kf_all)
+    check_steps = {0, 1, 127, 255, 511, 767, 895, T - 1}
+    units = (3, 6)
+    ref = {}
+    for unit in units:
+        b, h = divmod(unit, w.n_kv_heads)
+        kf_all = S.as_f32(Kall[b, h])
+        ref[unit] = (kf_all, S.as_f32(Vall[b, h]), oracle_encode(kf_all))
     recalls = []
     for t in range(T):
         P.pk_append_keys(run.ctx.h, to_torch(Kall[:, :, w.n + t:w.n + t + 1]), run.sums.s)
@@ -101,12 +104,15 @@ def test_full_drift_stream():
         run.debug = t in check_steps
         run.retrieve_attend()
         if t in check_steps:
-            say(f"case drift128k: step {t}, oracle unit {unit}")
-            enc = {k: v[:n_t] for k, v in enc_all.items()}
-            check_encode_unit(run, unit, kf_all[:n_t], enc=enc, rows=slice(w.n - 8, n_t))
-            st = {}
-            check_retrieve_unit(run, b, h, kf_all[:n_t], vf_all[:n_t], enc, stats=st)
-            recalls += st["recall"]
+            for unit in units:
+                say(f"case drift128k: step {t}, oracle unit {unit}")
+                b, h = divmod(unit, w.n_kv_heads)
+                kf_all, vf_all, enc_all = ref[unit]
+                enc = {k: v[:n_t] for k, v in enc_all.items()}
+                check_encode_unit(run, unit, kf_all[:n_t], enc=enc, rows=slice(w.n - 8, n_t))
+                st = {}
+                check_retrieve_unit(run, b, h, kf_all[:n_t], vf_all[:n_t], enc, stats=st)
+                recalls += st["recall"]
     assert run.n == w.n + T
     run.close()
     say(f"case drift128k: recall@100 at checked steps {np.round(recalls, 3).tolist()}")
