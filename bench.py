@@ -544,7 +544,20 @@ def run_layout(args, w):
     idx = torch.empty((w.batch, w.n_q_heads, w.top_k), dtype=torch.int32, device=dev)
     out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
-    state = {"window": local, "next": local}          # tokens in the window; next stream token
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    state = {"window": local, "next": local, "offloaded": None}   # tokens in the window; next stream token
+    host = w.kv_home == "host"
+    zst = (w.n_kv_heads * cap * 128, cap * 128, 128)
+    if host:
+        # the zone's full-precision rows in pinned host memory: the prefill
+        # zone now, flushed window rows as they are offloaded
+        hz = []
+        for A in (Kz, Vz):
+            h, d = P.pk_host_alloc_mapped(int(np.prod(A.shape)) * 2)
+            hz.append((h, d))
+            P.pk_offload_rows(A[:, :, :zone0], d, zst)
+        torch.cuda.synchronize()
+        copy_stream = torch.cuda.Stream()
 
     def step(i):
         s_ = state
@@ -556,10 +569,28 @@ def run_layout(args, w):
         s_["next"] += 1
         q = Qd[i % len(Qd)]
         P.pk_retrieve(ctx.h, q, sums.s, idx, None, None, stream)
-        P.pk_sparse_dense_attend(ctx.h, q, Kz, Vz, idx, Kd[:, :, :sink + s_["window"]],
-                                 Vd[:, :, :sink + s_["window"]], out, stream)
+        nd = sink + s_["window"]
+        if host:
+            if s_["offloaded"] is not None:           # rows the attention may read are in the host zone
+                stream.wait_event(s_["offloaded"])
+                s_["offloaded"] = None
+            P._check(P._lib.pk_sparse_dense_attend(
+                ctx.h, P._ptr(q), P.PK_BF16, ctypes.c_void_p(hz[0][1]), ctypes.c_void_p(hz[1][1]), P.PK_BF16,
+                P._I64x3(*zst), sums.n, P._ptr(idx), P._ptr(Kd), P._ptr(Vd), P._strides4(Kd), nd, P._ptr(out),
+                P.PK_BF16, sptr), ctx.h)
+        else:
+            P.pk_sparse_dense_attend(ctx.h, q, Kz, Vz, idx, Kd[:, :, :nd], Vd[:, :, :nd], out, stream)
         if s_["window"] == local + upd:                # full update buffer: oldest upd tokens join the zone
-            P.pk_append_keys(ctx.h, Kz[:, :, sums.n:sums.n + upd], sums.s, stream)
+            n0 = sums.n
+            if host:                                   # offloaded on a second stream meanwhile
+                ready = torch.cuda.Event()
+                ready.record(stream)
+                copy_stream.wait_event(ready)
+                for (hh, dd), A in zip(hz, (Kz, Vz)):
+                    P.pk_offload_rows(A[:, :, n0:n0 + upd], dd + n0 * 256, zst, stream=copy_stream)
+                s_["offloaded"] = torch.cuda.Event()
+                s_["offloaded"].record(copy_stream)
+            P.pk_append_keys(ctx.h, Kz[:, :, n0:n0 + upd], sums.s, stream)
             Kd[:, :, sink:sink + local] = Kd[:, :, sink + upd:sink + upd + local].clone()
             Vd[:, :, sink:sink + local] = Vd[:, :, sink + upd:sink + upd + local].clone()
             s_["window"] = local
@@ -599,7 +630,7 @@ def run_layout(args, w):
         "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads, "n_q_heads": w.n_q_heads,
                    "prefill": w.n, "zone_keys_end": int(n_zone), "sink": sink, "local": local, "update": upd,
                    "n_candidates": w.n_candidates, "top_k": w.top_k, "kv_dtype": w.kv_dtype,
-                   "llc_resident": True},
+                   "zone_kv_home": w.kv_home, "llc_resident": True},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "alg_bytes_per_launch": alg, "avg_launch_us": round(kern[dom]["avg_us"], 3)},
@@ -607,6 +638,9 @@ def run_layout(args, w):
     }
     print(json.dumps(res), flush=True)
     ctx.close()
+    if host:
+        for hh, _ in hz:
+            P.pk_host_free(hh)
 
 
 if __name__ == "__main__":

@@ -325,6 +325,22 @@ pk_status pk_sparse_dense_attend(pk_context* ctx, const void* q, pk_dtype q_dtyp
 pk_status pk_host_alloc_mapped(size_t bytes, void** host_ptr, void** device_ptr);
 pk_status pk_host_free(void* host_ptr);
 
+/* Offload of full-precision K or V rows into the host tier (README "1. Prefill":
+ * K/V asynchronously offloaded to CPU memory; Slides Fig. 5, Sec. 4.2.1: a
+ * full update buffer is encoded and its old local tokens are moved out):
+ * copies rows [0, rows) of every (sequence, KV head) of src [batch][n_kv_heads]
+ * [rows][128] to dst with the same shape.  src, dst: device pointers (dst
+ * typically the device view of pk_host_alloc_mapped memory, at the zone row
+ * where the rows belong), element strides {batch, head, token}, last dim
+ * contiguous, rows 16-byte aligned; both of `dtype`.  Enqueued on hip_stream,
+ * which may be a second stream beside the retrieval's: the caller orders any
+ * attention that may read the rows after it (an event), and keeps src
+ * unchanged until it completes.  PK_ERR_INVALID_ARG / _UNSUPPORTED on bad
+ * arguments (nothing enqueued). */
+pk_status pk_offload_rows(const void* src, const int64_t src_strides[3], void* dst,
+                          const int64_t dst_strides[3], pk_dtype dtype, int32_t batch,
+                          int32_t n_kv_heads, int64_t rows, void* hip_stream);
+
 /* ---- measurement aids ------------------------------------------------------ */
 
 /* Plain device-to-device copy of `bytes` (a multiple of 16; both pointers

@@ -1013,6 +1013,27 @@ pk_status pk_host_alloc_mapped(size_t bytes, void** host_ptr, void** device_ptr)
   return PK_OK;
 }
 
+pk_status pk_offload_rows(const void* src, const int64_t src_strides[3], void* dst, const int64_t dst_strides[3],
+                          pk_dtype dtype, int32_t batch, int32_t n_kv_heads, int64_t rows, void* hip_stream) {
+  if (dtype != PK_F32 && dtype != PK_BF16) return fail(nullptr, PK_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+  if (batch < 1 || n_kv_heads < 1 || rows < 0)
+    return fail(nullptr, PK_ERR_INVALID_ARG, "batch and n_kv_heads must be >= 1 and rows >= 0");
+  pk_status st = check_strides(nullptr, src, dtype, src_strides, "src");
+  if (st != PK_OK) return st;
+  if ((st = check_strides(nullptr, dst, dtype, dst_strides, "dst")) != PK_OK) return st;
+  if (rows == 0) return PK_OK;
+  const int64_t vec = dtype == PK_BF16 ? 8 : 4;   // elements per 16 bytes
+  const int row_vec = (int)(PK_HEAD_DIM / vec);
+  const int64_t total = (int64_t)batch * n_kv_heads * rows * row_vec;
+  hipLaunchKernelGGL(pk::copy_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)hip_stream, reinterpret_cast<const uint4*>(src), src_strides[0] / vec,
+                     src_strides[1] / vec, src_strides[2] / vec, reinterpret_cast<uint4*>(dst), dst_strides[0] / vec,
+                     dst_strides[1] / vec, dst_strides[2] / vec, (int)n_kv_heads, rows, row_vec, total);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(nullptr, PK_ERR_HIP, "offload launch failed: %s", hipGetErrorString(e));
+  return PK_OK;
+}
+
 pk_status pk_calibration_copy(void* dst, const void* src, size_t bytes, void* hip_stream) {
   if (!dst || !src || bytes % 16 != 0 || !aligned(dst, 16) || !aligned(src, 16))
     return fail(nullptr, PK_ERR_INVALID_ARG, "calibration copy needs non-NULL 16-byte aligned pointers and size");

@@ -2072,6 +2072,20 @@ dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k,
   }
 }
 
+// rows [0, rows) of every (sequence, KV head) from src to dst, 16 bytes per
+// lane (row_vec 16-byte pieces per row); dst may be the device view of mapped
+// host memory, so the stores cross the host link
+__global__ void __launch_bounds__(256) copy_rows_kernel(const uint4* __restrict__ src, int64_t ssb, int64_t ssh,
+                                                      int64_t sst, uint4* __restrict__ dst, int64_t dsb,
+                                                      int64_t dsh, int64_t dst_, int n_kv_heads, int64_t rows,
+                                                      int row_vec, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t v = i % row_vec, r = (i / row_vec) % rows, uh = i / (row_vec * rows);
+  const int64_t b = uh / n_kv_heads, h = uh - b * n_kv_heads;
+  dst[b * dsb + h * dsh + r * dst_ + v] = src[b * ssb + h * ssh + r * sst + v];
+}
+
 // set `count` words to `value`
 __global__ void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t value, int64_t count) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;

@@ -92,6 +92,8 @@ _SIGS = {
                                 _I64x3, ctypes.c_int64, _P, ctypes.c_int, _P], ctypes.c_int),
     "pk_host_alloc_mapped": ([ctypes.c_size_t, ctypes.POINTER(_P), ctypes.POINTER(_P)], ctypes.c_int),
     "pk_host_free": ([_P], ctypes.c_int),
+    "pk_offload_rows": ([_P, _I64x3, _P, _I64x3, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _P],
+                        ctypes.c_int),
     "pk_calibration_copy": ([_P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "pk_device_errors": ([_P, ctypes.POINTER(ctypes.c_uint32), _P], ctypes.c_int),
     "pk_timing_begin": ([_P, ctypes.c_int32], ctypes.c_int),
@@ -378,6 +380,16 @@ def pk_host_alloc_mapped(nbytes: int):
 
 def pk_host_free(host_ptr: int) -> None:
     _check(_lib.pk_host_free(ctypes.c_void_p(host_ptr)))
+
+
+def pk_offload_rows(src, dst_ptr: int, dst_strides, stream=None) -> None:
+    """Copy every row of src [batch, heads, rows, 128] (a GPU tensor) to the
+    device pointer dst_ptr (e.g. the device view of mapped host memory, at the
+    first destination row) with element strides dst_strides."""
+    if src.device.type != "cuda":
+        raise ValueError("src must be a GPU tensor")
+    _check(_lib.pk_offload_rows(_ptr(src), _strides4(src), ctypes.c_void_p(dst_ptr), _I64x3(*dst_strides),
+                                _dtype(src), src.shape[0], src.shape[1], src.shape[2], _stream(stream)))
 
 
 def pk_calibration_copy(dst, src, stream=None) -> None:

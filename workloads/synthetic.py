@@ -110,6 +110,10 @@ WORKLOADS = {
         # the zone (the rest of the 128K prefill) is retrieved from
         Workload("drift128k_layout", 7, 1, 8, 32, 131072, "bf16", 4096, append_steps=1024, sink_tokens=64,
                  local_tokens=512, update_tokens=256),
+        # the same with the zone's K/V in pinned host memory: flushed rows are
+        # offloaded there and read back through mapped pointers
+        Workload("drift128k_layout_host", 7, 1, 8, 32, 131072, "bf16", 4096, append_steps=1024, sink_tokens=64,
+                 local_tokens=512, update_tokens=256, kv_home="host"),
     ]
 }
 
