@@ -58,10 +58,21 @@ typedef enum {
   PK_ERR_UNSUPPORTED = -2,   /* valid in principle, not supported by this build */
   PK_ERR_CAPACITY = -3,      /* keys would exceed the summaries' capacity      */
   PK_ERR_OUT_OF_MEMORY = -4, /* device or pinned host allocation failed        */
-  PK_ERR_HIP = -5            /* a HIP runtime call failed (no GPU, launch error) */
+  PK_ERR_HIP = -5,           /* a HIP runtime call failed (no GPU, launch error) */
+  /* never returned: they make every int32 value a valid pk_status, so that a
+     caller's out-of-range value (e.g. to pk_status_str) is defined behaviour */
+  PK_STATUS_MIN_ENUM_ = -0x7FFFFFFF - 1,
+  PK_STATUS_MAX_ENUM_ = 0x7FFFFFFF
 } pk_status;
 
-typedef enum { PK_F32 = 0, PK_BF16 = 1 } pk_dtype;
+typedef enum {
+  PK_F32 = 0,
+  PK_BF16 = 1,
+  /* not dtypes: every int32 value is a pk_dtype, so that an invalid one is
+     refused (PK_ERR_UNSUPPORTED) rather than undefined */
+  PK_DTYPE_MIN_ENUM_ = -0x7FFFFFFF - 1,
+  PK_DTYPE_MAX_ENUM_ = 0x7FFFFFFF
+} pk_dtype;
 
 /* Fixed geometry of this build. */
 #define PK_HEAD_DIM 128      /* D */

@@ -1,6 +1,6 @@
 """Build libpariskv.so (HIP for gfx950) in-tree.
 
-    python -m kv_cache_top_amd.build [--verbose]
+    python -m kv_cache_top_amd.build [--verbose] [--sanitize]
 """
 from __future__ import annotations
 
@@ -36,10 +36,27 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpariskv.so)")
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compile every source into kv_cache_top_amd/libpariskv.so; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *(extra or []), "-I", INCLUDE, "-I", CSRC,
+# host code only: AddressSanitizer and UndefinedBehaviorSanitizer on the
+# runtime's C++ (argument checks, tables, launch plans); device code is built
+# as usual.  Load the result with PARISKV_LIB and the sanitizer runtime
+# preloaded (see sanitizer_runtime()).
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+LIB_SANITIZED = os.path.join(PKG, "libpariskv_hostsan.so")
+
+
+def sanitizer_runtime() -> str:
+    """Path of clang's shared AddressSanitizer runtime (to LD_PRELOAD into python)."""
+    out = subprocess.run([hipcc(), "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return out.stdout.strip()
+
+
+def build(verbose: bool = False, extra: list[str] | None = None, sanitize: bool = False) -> str:
+    """Compile every source into kv_cache_top_amd/libpariskv.so (with sanitize:
+    libpariskv_hostsan.so, host code sanitized); returns its path."""
+    out_lib = LIB_SANITIZED if sanitize else LIB
+    tmp = out_lib + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, *(SANITIZE_FLAGS if sanitize else []), *(extra or []), "-I", INCLUDE, "-I", CSRC,
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -50,9 +67,9 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
     if verbose and errs:
         print("\n".join(errs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out_lib)
+    return out_lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    print(build(verbose="--verbose" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -168,6 +168,7 @@ const char* pk_status_str(pk_status s) {
     case PK_ERR_CAPACITY: return "PK_ERR_CAPACITY";
     case PK_ERR_OUT_OF_MEMORY: return "PK_ERR_OUT_OF_MEMORY";
     case PK_ERR_HIP: return "PK_ERR_HIP";
+    default: break;
   }
   return "PK_ERR_UNKNOWN";
 }

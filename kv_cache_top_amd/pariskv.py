@@ -16,7 +16,8 @@ import os
 import torch  # noqa: F401
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpariskv.so")
+# PARISKV_LIB selects another build of the same library (e.g. the host-sanitized one)
+LIB_PATH = os.environ.get("PARISKV_LIB") or os.path.join(PKG, "libpariskv.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_top_amd.build` "

@@ -226,3 +226,30 @@ def test_binding_refuses_unknown_context():
         P.pk_retrieve(ctypes.c_void_p(0x5EED1), torch.zeros((1, 1, 128)), P.pk_summaries(),
                       torch.zeros((1, 1, 1), dtype=torch.int32))
 
+
+
+def test_invalid_enum_values_are_refused():
+    """Out-of-range dtypes and statuses from a caller are defined behaviour:
+    refused or named unknown (the host-sanitized build checks that no
+    undefined enum load happens)."""
+    src = ctypes.create_string_buffer(4096 + 16)
+    base = (ctypes.addressof(src) + 15) // 16 * 16
+    st3 = P._I64x3(128, 128, 128)
+    for bad in (7, -1, 2 ** 31 - 1, -2 ** 31):
+        assert P._lib.pk_offload_rows(ctypes.c_void_p(base), st3, ctypes.c_void_p(base), st3, bad, 1, 1, 1,
+                                      None) == P.PK_ERR_UNSUPPORTED
+    for bad in (1, -6, -99, 2 ** 31 - 1, -2 ** 31):
+        assert P._lib.pk_status_str(bad).decode() == "PK_ERR_UNKNOWN"
+
+
+def test_offload_rows_rejects_before_launch():
+    st3 = P._I64x3(128, 128, 128)
+    assert P._lib.pk_offload_rows(None, st3, ctypes.c_void_p(256), st3, P.PK_BF16, 1, 1, 1, None) == \
+        P.PK_ERR_INVALID_ARG
+    assert P._lib.pk_offload_rows(ctypes.c_void_p(256), st3, ctypes.c_void_p(264), st3, P.PK_BF16, 1, 1, 1,
+                                  None) == P.PK_ERR_INVALID_ARG          # misaligned destination
+    assert P._lib.pk_offload_rows(ctypes.c_void_p(256), st3, ctypes.c_void_p(512), st3, P.PK_BF16, 0, 1, 1,
+                                  None) == P.PK_ERR_INVALID_ARG          # no sequences
+    # zero rows: valid, nothing to copy, no device touched
+    assert P._lib.pk_offload_rows(ctypes.c_void_p(256), st3, ctypes.c_void_p(512), st3, P.PK_BF16, 1, 1, 0,
+                                  None) == P.PK_OK
