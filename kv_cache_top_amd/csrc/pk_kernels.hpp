@@ -395,10 +395,71 @@ encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
 // written as byte g (query head g of the unit) of the unit's LUT; bytes of
 // absent heads (g >= group) are written as 0.
 // ===========================================================================
+// Bitonic sort of one u32 per lane over the wave, descending (lane 0 ends
+// with the largest): stage (K, J) compare-exchanges lanes l and l ^ J; blocks
+// of K lanes with (l & K) == 0 keep the larger value at the lower lane.
+template <int K, int J>
+__device__ __forceinline__ uint32_t bitonic64_step(uint32_t v, int lane) {
+  const uint32_t p = lane_xor<J>(v, lane);
+  const bool keep_max = ((lane & K) == 0) == ((lane & J) == 0);
+  const uint32_t hi = v > p ? v : p, lo = v > p ? p : v;
+  return keep_max ? hi : lo;
+}
+template <int K, int J>
+__device__ __forceinline__ uint32_t bitonic64_j(uint32_t v, int lane) {
+  v = bitonic64_step<K, J>(v, lane);
+  if constexpr (J > 1) return bitonic64_j<K, J / 2>(v, lane);
+  else return v;
+}
+template <int K>
+__device__ __forceinline__ uint32_t bitonic64_k(uint32_t v, int lane) {
+  v = bitonic64_j<K, K / 2>(v, lane);
+  if constexpr (K < 64) return bitonic64_k<K * 2>(v, lane);
+  else return v;
+}
+
+// Rank tiers of one subspace (one wave, centroid c = lane + 64 r holds score
+// key key[r]) when the last tier ends at T <= 64: the T-th largest of the 64
+// per-lane maxima is a lower bound of the T-th largest key (at least T keys
+// reach it), so only keys at or above it can rank below T.  Those (typically
+// a few dozen) are compacted as (score key << 32 | 255 - c), which orders by
+// (score desc, c asc), and ranked among themselves; each centroid ranked
+// below T gets its tier weight in lw[c].
+__device__ __forceinline__ void rank_tiers_bound(const uint32_t (&key)[4], const TierSpec& tiers, uint64_t* sel,
+                                                 uint8_t* lw, int lane) {
+  const int T = tiers.top[tiers.n_tiers - 1];
+  uint32_t m = key[0] > key[1] ? key[0] : key[1];
+  m = m > key[2] ? m : key[2];
+  m = m > key[3] ? m : key[3];
+  const uint32_t sorted = bitonic64_k<2>(m, lane);
+  const uint32_t bound = (uint32_t)__builtin_amdgcn_readlane((int)sorted, T - 1);   // T <= 64
+  int cnt = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const bool take = key[r] >= bound;
+    const uint64_t tm = __ballot(take);
+    if (take) sel[cnt + (int)mbcnt(tm)] = ((uint64_t)key[r] << 32) | (uint64_t)(255 - (lane + 64 * r));
+    cnt += __popcll(tm);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  for (int j = lane; j < cnt; j += 64) {
+    const uint64_t e = sel[j];
+    int rank = 0;
+    for (int j2 = 0; j2 < cnt; ++j2) rank += (sel[j2] > e) ? 1 : 0;
+    uint32_t wgt = 0;
+    for (int tt = 0; tt < tiers.n_tiers; ++tt) {
+      if (rank < tiers.top[tt]) { wgt = (uint32_t)tiers.weight[tt]; break; }
+    }
+    lw[255 - (int)(e & 0xFFu)] = (uint8_t)wgt;   // rank >= T: weight 0, as the cleared entry
+  }
+}
+
 // Rank tiers of one subspace (one wave, centroid c = lane + 64 r holds score
 // key key[r]): the centroids ranked r < tiers.top[last] by (score desc, c asc)
 // are found with a bitwise threshold search over the score keys, then ranked
-// among themselves; each gets its tier weight in lw[c].
+// among themselves; each gets its tier weight in lw[c].  (rank_tiers_bound
+// is used when the last tier ends within 64.)
 __device__ __forceinline__ void rank_tiers(const uint32_t (&key)[4], const TierSpec& tiers, uint64_t* sel,
                                            uint8_t* lw, int lane) {
   const int T = tiers.top[tiers.n_tiers - 1];
@@ -623,6 +684,8 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
 
   if (keep_m > 0) {
     percentile_tiers(key, counts + ((int64_t)unit * NSUB + b) * 256, keep_m, lw[w], lane);
+  } else if (tiers.top[tiers.n_tiers - 1] <= 64) {
+    rank_tiers_bound(key, tiers, sel[w], lw[w], lane);
   } else {
     rank_tiers(key, tiers, sel[w], lw[w], lane);
   }

@@ -3,6 +3,7 @@ calls of different sizes on one context, many repeated calls (identical
 results), one key, fewer keys than one wave's share of a tile, and n <= C
 (every key a candidate).  Every result is compared with the oracle bit for
 bit, and the device-side consistency flags stay clear."""
+import numpy as np
 import pytest
 
 from workloads import synthetic as S
@@ -71,3 +72,33 @@ def test_repeated_calls_identical():
             assert torch.equal(a, b)
     assert run.device_errors() == 0
     run.close()
+
+
+def test_two_launch_geometries_same_results():
+    """Units (0, 0) and (0, 1) alone (2 units, 8 query heads: small tiles, the
+    rerank spread over workgroups, then a top-k kernel) and inside a batch of
+    64 units (256 query heads: large tiles, rerank and top-k in one workgroup
+    per head) see the same keys and queries: candidates, estimates and Top-k
+    are bit-identical, attention within the fp32 summation-order tolerance."""
+    import torch
+    from tests.parity_util import attention_ok
+    small = S.custom("llama32k", batch=1, n_kv_heads=2, n_q_heads=8, n=20000, n_candidates=1024, wid=1420)
+    big = S.custom("llama32k", batch=8, n_kv_heads=8, n_q_heads=32, n=20000, n_candidates=1024, wid=1420)
+    runs = []
+    for w in (small, big):
+        say(f"case geometry units={w.units}")
+        K = S.all_keys(w)
+        V = S.all_values(w)
+        Q = S.all_queries(w, K)
+        runs.append(GpuRun(w, K, V, Q).retrieve_attend())
+    a, b = runs
+    np.testing.assert_array_equal(a.Q[0, :8], b.Q[0, :8])          # same inputs for these heads
+    for t_a, t_b in ((a.cand_idx, b.cand_idx), (a.cand_est, b.cand_est)):
+        assert torch.equal(t_a[:8], t_b[:8])
+    assert torch.equal(a.topk_idx[0, :8], b.topk_idx[0, :8])
+    assert torch.equal(a.topk_est[0, :8], b.topk_est[0, :8])
+    for qh in range(8):
+        assert attention_ok(a.out[0, qh].float().cpu().numpy(), b.out[0, qh].float().cpu().numpy())
+    for r in runs:
+        assert r.device_errors() == 0
+        r.close()
