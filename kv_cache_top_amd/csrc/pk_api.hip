@@ -73,6 +73,9 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // units, 256 threads each doing 1..kMaxKPL keys.
 constexpr int64_t kTargetWG = 512, kMaxKPL = 64;
 constexpr int64_t kFuseTile = 4096;
+// select runs one workgroup per sub-tile from this many 64-key rows per wave
+// (sub-tiles of >= 4 * 64 * kSelectSubMinRows keys) on
+constexpr int kSelectSubMinRows = 4;
 // rerank and top-k run as one workgroup per head while its rounds of 1024
 // candidates are few: up to four when there are enough heads to fill the chip
 // (at 256 heads, fused wins at 4096 candidates and the split kernels at 13108),
@@ -625,7 +628,38 @@ pk_status retrieve_impl(const Plan& pl, const Scratch& sc, const CallShape& cs, 
     case 3: PK_SELECT(3, F); break;        \
     default: PK_SELECT(4, F); break;       \
   }
-    if (fused_params) {
+    // one workgroup per sub-tile once a sub-tile is long enough to split
+    // over the four waves (more resident waves hide the score loads)
+    const int rpw = (tile / 256 + 3) / 4;         // 64-key rows per wave
+    if (rpw >= kSelectSubMinRows) {
+      const int subs = 4 * tiles;
+      const unsigned sgrid = (unsigned)((int64_t)pl.units * subs);
+#define PK_SELSUB(GG, F, RW)                                                                                     \
+  hipLaunchKernelGGL((pk::select_sub_kernel<GG, F, RW>), dim3(sgrid), dim3(256), 0, stream, sc.scores, sc.params, \
+                     sc.sub_base, sc.cand_idx, n, sc.score_stride, subs, (int)sc.max_subs, tile / 4,          \
+                     cfg.n_q_heads, cfg.n_kv_heads, C, sc.unit_tot, sc.tile_hist, sc.dev_err)
+#define PK_SELSUB_R(GG, F)                   \
+  do {                                       \
+    if (rpw <= 4) PK_SELSUB(GG, F, 4);       \
+    else if (rpw <= 8) PK_SELSUB(GG, F, 8);  \
+    else PK_SELSUB(GG, F, 16);               \
+  } while (0)
+#define PK_SELSUB_G(F)                        \
+  switch (pl.group) {                       \
+    case 1: PK_SELSUB_R(1, F); break;         \
+    case 2: PK_SELSUB_R(2, F); break;         \
+    case 3: PK_SELSUB_R(3, F); break;         \
+    default: PK_SELSUB_R(4, F); break;        \
+  }
+      if (fused_params) {
+        PK_SELSUB_G(true);
+      } else {
+        PK_SELSUB_G(false);
+      }
+#undef PK_SELSUB_G
+#undef PK_SELSUB_R
+#undef PK_SELSUB
+    } else if (fused_params) {
       PK_SELECT_G(true);
     } else {
       PK_SELECT_G(false);

@@ -1306,6 +1306,172 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
 }
 
 // ===========================================================================
+// select, one workgroup per sub-tile (the collide kernel's per-wave key
+// range): the candidate set of every query head (Slides Sec. 4.2.2).
+//
+// The sub-tile's rows of 64 keys are split over the four waves (ROWS rows
+// each at most).  The keys above / at theta before the sub-tile come from
+// the unit's bin totals and the sub-tiles' suffix counts (FUSED, rank tiers)
+// or from the threshold kernel; the waves' own prefixes inside the sub-tile
+// from byte-parallel counts of their registers.  Then each wave compacts its
+// keys at or above some head's theta and gives them their slots
+// (HeadSelect), as select_kernel does.  Four times as many workgroups as
+// select_kernel keep more waves per compute unit to overlap the score loads
+// with the slot ballots.
+// ===========================================================================
+constexpr int SS_DRAIN_ROWS = 8;                          // rows compacted between queue drains
+constexpr int SS_QCAP = SS_DRAIN_ROWS * 64 + 64;          // queue entries per wave
+
+// theta / need_eq of head g (wave g) and the keys above / at theta in the
+// unit's sub-tiles before `sub` (64 sub-tiles per step); lane 0 writes them
+__device__ __forceinline__ void select_params_sub(uint32_t tot, const uint32_t* __restrict__ suf, int unit,
+                                                  int max_subs, int sub_len, int64_t n, int sub, int g,
+                                                  int n_candidates, int lane, int2* s_par, int2* s_sb) {
+  int theta;
+  uint32_t need_eq;
+  theta_from_totals(tot, n, n_candidates, theta, need_eq);
+  const uint32_t* row_gt = suf + suf_index(unit, max_subs, g, theta + 1, 0);             // #{S > theta}
+  const uint32_t* row_ge = suf + suf_index(unit, max_subs, g, theta > 0 ? theta : 1, 0);  // #{S >= theta}
+  int pre_gt = 0, pre_eq = 0;
+  for (int c0 = 0; c0 < sub; c0 += 64) {          // uniform
+    const int t = c0 + lane;
+    int gt = 0, eq = 0;
+    if (t < sub) {
+      gt = (int)row_gt[t];
+      int ge;
+      if (theta > 0) {
+        ge = (int)row_ge[t];
+      } else {                                    // every key has S >= 0
+        int64_t len = n - (int64_t)t * sub_len;
+        ge = (int)(len < 0 ? 0 : (len > sub_len ? sub_len : len));
+      }
+      eq = ge - gt;
+    }
+    pre_gt += (int)xor_butterfly_u((uint32_t)gt, lane, AddU());
+    pre_eq += (int)xor_butterfly_u((uint32_t)eq, lane, AddU());
+  }
+  if (lane == 0) {
+    s_par[g] = make_int2(theta, (int)need_eq);
+    s_sb[g] = make_int2(pre_gt, pre_eq);
+  }
+}
+
+template <int G, bool FUSED, int ROWS>
+__global__ void __launch_bounds__(256)
+select_sub_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__ params,
+                  const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx, int64_t n, int64_t s_stride,
+                  int subs, int max_subs, int sub_len, int n_q_heads, int n_kv_heads, int n_candidates,
+                  const uint32_t* __restrict__ unit_tot, const uint32_t* __restrict__ suf,
+                  uint32_t* __restrict__ err) {
+  __shared__ uint2 s_ik[4][SS_QCAP];               // compacted keys: (key, packed S)
+  __shared__ int2 s_par[MAXG], s_sb[MAXG];
+  __shared__ uint32_t s_wc[4][4];                  // per wave: #gt heads 0/2, 1/3, #eq heads 0/2, 1/3 (16-bit)
+
+  int unit, sub;
+  xcd_unit_tile(blockIdx.x, gridDim.x / subs, subs, unit, sub);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int seq = unit / n_kv_heads, kvh = unit - seq * n_kv_heads;
+  const int64_t qhead0 = (int64_t)seq * n_q_heads + kvh * G;
+  // key indices fit in 32 bits (n <= n_capacity < 2^31)
+  const int rows_total = sub_len >> 6;
+  const int rpw = (rows_total + 3) >> 2;           // rows per wave, <= ROWS
+  const int r0 = wave * rpw;
+  const int nrows = (r0 + rpw <= rows_total) ? rpw : (rows_total > r0 ? rows_total - r0 : 0);
+  const int w0 = sub * sub_len + r0 * 64;
+  const int wlen = (int)((int64_t)w0 + nrows * 64 <= n ? nrows * 64 : (n > w0 ? n - w0 : 0));
+  const int jlast = wlen > 0 ? wlen - 1 : -w0;    // clamped loads re-read key w0 + jlast (>= 0)
+  const uint32_t* srow = scores + (int64_t)unit * s_stride + w0;
+
+  uint32_t tot = 0;
+  if constexpr (FUSED) {                           // requested before the scores (in-order memory counter)
+    if (wave < G) tot = unit_tot[((int64_t)unit * MAXG + wave) * NBIN + lane];
+  }
+  uint32_t sp[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const int j = r * 64 + lane;
+    sp[r] = srow[j < jlast ? j : jlast];
+  }
+  if constexpr (FUSED) {
+    if (wave < G) select_params_sub(tot, suf, unit, max_subs, sub_len, n, sub, wave, n_candidates, lane, s_par, s_sb);
+  } else {
+    if (tid < G) {
+      const SelParams p = params[unit * MAXG + tid];
+      s_par[tid] = make_int2(p.theta, p.need_eq);
+      s_sb[tid] = sub_base[((int64_t)unit * max_subs + sub) * MAXG + tid];
+    }
+  }
+  __syncthreads();
+  // this wave's keys above / at each head's theta: byte g of the flag words
+  // counts head g (at most ROWS <= 16 per lane), then 16-bit wave sums
+  uint32_t th4 = 0x7F7F7F7Fu;
+#pragma unroll
+  for (int g = 0; g < G; ++g) th4 = (th4 & ~(0xFFu << (8 * g))) | ((uint32_t)s_par[g].x << (8 * g));
+  const uint32_t thp4 = th4 + 0x01010101u;
+  uint32_t cgt = 0, ceq = 0;
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    if (r * 64 + lane < wlen) {
+      const uint32_t m = sp[r] | 0x80808080u;
+      const uint32_t gt4 = (m - thp4) & 0x80808080u;
+      const uint32_t eq4 = ((m - th4) & 0x80808080u) ^ gt4;
+      cgt += gt4 >> 7;
+      ceq += eq4 >> 7;
+    }
+  }
+  const uint32_t g02 = xor_butterfly_u(cgt & 0x00FF00FFu, lane, AddU());
+  const uint32_t g13 = xor_butterfly_u((cgt >> 8) & 0x00FF00FFu, lane, AddU());
+  const uint32_t e02 = xor_butterfly_u(ceq & 0x00FF00FFu, lane, AddU());
+  const uint32_t e13 = xor_butterfly_u((ceq >> 8) & 0x00FF00FFu, lane, AddU());
+  if (lane == 0) {
+    s_wc[wave][0] = g02; s_wc[wave][1] = g13; s_wc[wave][2] = e02; s_wc[wave][3] = e13;
+  }
+  __syncthreads();
+  HeadSelect<G> hs;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int word = g & 1, shift = 16 * (g >> 1);
+    int bg = s_sb[g].x, be = s_sb[g].y;
+    for (int w2 = 0; w2 < wave; ++w2) {
+      bg += (int)((s_wc[w2][word] >> shift) & 0xFFFFu);
+      be += (int)((s_wc[w2][2 + word] >> shift) & 0xFFFFu);
+    }
+    hs.set(g, s_par[g].x, s_par[g].y, bg, be);
+  }
+  hs.finish();
+
+  uint2* ik = s_ik[wave];
+  int nk = 0;
+  auto drain = [&]() {                            // whole batches; the remainder (< 64) moves to the front
+    wave_lds_sync();
+    int b0 = 0;
+    for (; b0 + 64 <= nk; b0 += 64) hs.batch(ik[b0 + lane], true, cand_idx, qhead0, n_candidates, err);
+    if (b0 > 0) {
+      const int rem = nk - b0;
+      uint2 e = make_uint2(0u, 0u);
+      if (lane < rem) e = ik[b0 + lane];
+      wave_lds_sync();
+      if (lane < rem) ik[lane] = e;
+      nk = rem;
+    }
+    wave_lds_sync();
+  };
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    if (r % SS_DRAIN_ROWS == 0 && r > 0 && nk > SS_QCAP - SS_DRAIN_ROWS * 64) drain();   // uniform
+    const bool take = r * 64 + lane < wlen && hs.interesting(sp[r]) != 0u;
+    const uint64_t im = __ballot(take);
+    if (take) ik[nk + (int)mbcnt(im)] = make_uint2((uint32_t)(w0 + r * 64 + lane), sp[r]);
+    nk += __popcll(im);
+  }
+  drain();
+  {
+    const bool valid = lane < nk;
+    hs.batch(ik[valid ? lane : 0], valid, cand_idx, qhead0, n_candidates, err);
+  }
+}
+
+// ===========================================================================
 // sparse attention over the retrieved rows (Slides Sec. 3, Eqs. (1)-(3);
 // README "3. Attention"; UVA fetch of host-resident rows, Slides Sec. 4.2.3).
 //
