@@ -5,8 +5,9 @@
 
 A step is one pass of the whole hot path for one layer: one pk_retrieve_attend
 call (query rotation, collision votes, candidate selection, 4-bit rerank,
-Top-k, sparse attention) for every (sequence, query head) of the workload,
-plus pk_append_keys of one key per KV head on the drift workload.  Inputs are
+Top-k, sparse attention) for every (sequence, query head) of the workload; on
+the drift workload one pk_append_retrieve_attend call, which also encodes that
+step's new key per KV head (inside the query-prep launch).  Inputs are
 seeded synthetic Llama-3.1-8B-shaped tensors already resident in HBM (or, for
 the 1M-token workload, K/V in pinned host memory read through mapped
 pointers).  Consecutive steps rotate over distinct per-layer summary buffers
@@ -253,10 +254,14 @@ def run_workload(w, args, steps: int, warmup: int, want_recall: bool) -> dict:
 
     def step(i):
         s = sums[i % layers]
-        if app:   # this layer's next key (row n of K/V) joins its summaries
-            P._check(P._lib.pk_append_keys(ctx.h, ctypes.c_void_p(kptr + s.s.n * row_bytes), kv_dt, st3, 1,
-                                           ctypes.byref(s.s), sptr), ctx.h)
         q = Qd[i % len(Qd)]
+        if app:   # this layer's next key (row n of K/V) joins its summaries, then the retrieval
+            P._check(P._lib.pk_append_retrieve_attend(
+                ctx.h, ctypes.c_void_p(kptr + s.s.n * row_bytes), kv_dt, st3, 1, ctypes.byref(s.s),
+                ctypes.c_void_p(q.data_ptr()), kv_dt, ctypes.c_void_p(kptr), ctypes.c_void_p(vptr), kv_dt, st3,
+                ctypes.c_int64(cap), ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(est.data_ptr()),
+                ctypes.c_void_p(out.data_ptr()), kv_dt, sptr), ctx.h)
+            return
         P._check(P._lib.pk_retrieve_attend(ctx.h, ctypes.c_void_p(q.data_ptr()), kv_dt, ctypes.byref(s.s),
                                            ctypes.c_void_p(kptr), ctypes.c_void_p(vptr), kv_dt, st3,
                                            ctypes.c_int64(cap), ctypes.c_void_p(idx.data_ptr()),

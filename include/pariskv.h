@@ -286,6 +286,27 @@ pk_status pk_retrieve_attend(pk_context* ctx, const void* q, pk_dtype q_dtype,
                              int32_t* topk_idx, float* topk_est, void* out, pk_dtype out_dtype,
                              const pk_debug* dbg, void* hip_stream);
 
+/* One decode step: the step's new keys join the summaries, then retrieval and
+ * sparse attention over all n + t keys (README "2. Decode": new tokens are
+ * encoded with the fixed codebook as they arrive, then the query retrieves;
+ * Slides Sec. 4.2.3).  The results equal pk_append_keys(new_keys, t, inout)
+ * followed by pk_retrieve_attend(q, inout, ...) on the same stream, and
+ * inout->n advances by t when the call returns PK_OK.  With rank tiers and
+ * t <= 64 the new rows are encoded by extra workgroups of the query-prep
+ * launch, which saves a launch per step (percentile tiers need the new rows'
+ * centroid counts before the query prep, so there the encode runs first).
+ * new_keys, key_dtype, key_strides, t: as for pk_append_keys (the rows may be
+ * rows n .. n + t - 1 of the k argument); the other arguments as for
+ * pk_retrieve_attend, with no debug copies.  Errors as for the two calls; on
+ * an error nothing is enqueued if it is an argument error, and inout->n is
+ * unchanged in every case. */
+pk_status pk_append_retrieve_attend(pk_context* ctx, const void* new_keys, pk_dtype key_dtype,
+                                    const int64_t key_strides[3], int64_t t, pk_summaries* inout,
+                                    const void* q, pk_dtype q_dtype, const void* k, const void* v,
+                                    pk_dtype kv_dtype, const int64_t kv_strides[3], int64_t n_rows,
+                                    int32_t* topk_idx, float* topk_est, void* out, pk_dtype out_dtype,
+                                    void* hip_stream);
+
 /* pk_retrieve_attend without a context, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  Same arguments, results, layouts and errors as

@@ -47,6 +47,16 @@ struct pk_context {
 
 namespace {
 
+// encode launch arguments for rows [row0, row0 + t) of every unit
+template <typename KT>
+pk::EncodeArgs<KT> encode_args(const pk_config& cfg, const void* keys, const int64_t* st, int64_t t,
+                                      int64_t row0, const pk_summaries* s) {
+  return pk::EncodeArgs<KT>{(const KT*)keys, st[0], st[1], st[2], cfg.n_kv_heads, t,
+                            (int)((t + pk::ENC_KEYS - 1) / pk::ENC_KEYS), row0, s->n_capacity,
+                            s->codes, s->records, s->norms, s->counts};
+}
+
+
 thread_local std::string g_err;
 
 pk_status fail(pk_context* ctx, pk_status st, const char* fmt, ...) {
@@ -346,12 +356,10 @@ static pk_status encode_rows(pk_context* ctx, const void* keys, pk_dtype dt, con
   Launch L(ctx, PK_KERNEL_ENCODE, stream);
   if (dt == PK_BF16)
     hipLaunchKernelGGL(pk::encode_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint16_t*)keys, st[0], st[1], st[2], ctx->cfg.n_kv_heads, t, (int)chunks, row0,
-                       s->n_capacity, s->codes, s->records, s->norms, s->counts, ctx->tb);
+                       encode_args<uint16_t>(ctx->cfg, keys, st, t, row0, s), ctx->tb);
   else
     hipLaunchKernelGGL(pk::encode_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const float*)keys, st[0], st[1], st[2], ctx->cfg.n_kv_heads, t, (int)chunks, row0,
-                       s->n_capacity, s->codes, s->records, s->norms, s->counts, ctx->tb);
+                       encode_args<float>(ctx->cfg, keys, st, t, row0, s), ctx->tb);
   return check_launch(ctx, "encode");
 }
 
@@ -500,6 +508,16 @@ struct Scratch {
   uint32_t* dev_err = nullptr;    // nullable
 };
 
+// Rows of one decode step that the retrieval's first launch also encodes
+// (pk_append_retrieve_attend): rank tiers, 1..ENC_DIRECT rows per unit,
+// written at row0 of the summaries.
+struct PendingAppend {
+  const void* keys;
+  pk_dtype dt;
+  const int64_t* strides;
+  int64_t t, row0;
+};
+
 struct Plan {
   const pk_config* cfg;
   int group, units, qheads;
@@ -554,7 +572,8 @@ Scratch context_scratch(pk_context* ctx) {
 // the scratch holds max_subs >= 4 * cs.tiles.
 pk_status retrieve_impl(const Plan& pl, const Scratch& sc, const CallShape& cs, const void* q, pk_dtype q_dtype,
                         const pk_summaries* s, int32_t* topk_idx, float* topk_est, const pk_debug* dbg,
-                        hipStream_t stream, const pk::AttendArgs* att, bool* attended) {
+                        hipStream_t stream, const pk::AttendArgs* att, bool* attended,
+                        const PendingAppend* app = nullptr) {
   pk_status st = PK_OK;
   if (attended) *attended = false;
   pk_context* ctx = pl.ctx;
@@ -568,14 +587,31 @@ pk_status retrieve_impl(const Plan& pl, const Scratch& sc, const CallShape& cs, 
 
   {
     Launch L(ctx, PK_KERNEL_QPREP, stream);
-    if (q_dtype == PK_BF16)
-      hipLaunchKernelGGL(pk::qprep_kernel<uint16_t>, dim3(pl.qheads * pk::QP_PARTS), dim3(64 * pk::QP_WAVES), 0,
-                         stream, (const uint16_t*)q, cfg.n_q_heads, cfg.n_kv_heads, pl.group, sc.rq,
-                         (uint8_t*)sc.lut, pl.tb, pl.tiers, s->counts, keep_m, pct ? nullptr : sc.unit_tot);
-    else
-      hipLaunchKernelGGL(pk::qprep_kernel<float>, dim3(pl.qheads * pk::QP_PARTS), dim3(64 * pk::QP_WAVES), 0,
-                         stream, (const float*)q, cfg.n_q_heads, cfg.n_kv_heads, pl.group, sc.rq,
-                         (uint8_t*)sc.lut, pl.tb, pl.tiers, s->counts, keep_m, pct ? nullptr : sc.unit_tot);
+    const int qblocks = pl.qheads * pk::QP_PARTS;
+#define PK_QA(QT)                                                                                             \
+  pk::QprepArgs<QT>{(const QT*)q, cfg.n_q_heads, cfg.n_kv_heads, pl.group, sc.rq, (uint8_t*)sc.lut, s->counts, \
+                    keep_m, pct ? nullptr : sc.unit_tot}
+    if (app) {
+      // the step's appended rows are encoded by extra workgroups of the same
+      // launch (one per unit: t <= ENC_DIRECT)
+      const unsigned blocks = (unsigned)(qblocks + pl.units);
+#define PK_AQ(QT, KT)                                                                                         \
+  hipLaunchKernelGGL((pk::append_qprep_kernel<QT, KT>), dim3(blocks), dim3(64 * pk::QP_WAVES), 0, stream,    \
+                     PK_QA(QT), encode_args<KT>(cfg, app->keys, app->strides, app->t, app->row0, s), pl.tb,  \
+                     pl.tiers, qblocks)
+      if (q_dtype == PK_BF16 && app->dt == PK_BF16) PK_AQ(uint16_t, uint16_t);
+      else if (q_dtype == PK_BF16) PK_AQ(uint16_t, float);
+      else if (app->dt == PK_BF16) PK_AQ(float, uint16_t);
+      else PK_AQ(float, float);
+#undef PK_AQ
+    } else if (q_dtype == PK_BF16) {
+      hipLaunchKernelGGL(pk::qprep_kernel<uint16_t>, dim3(qblocks), dim3(64 * pk::QP_WAVES), 0, stream,
+                         PK_QA(uint16_t), pl.tb, pl.tiers);
+    } else {
+      hipLaunchKernelGGL(pk::qprep_kernel<float>, dim3(qblocks), dim3(64 * pk::QP_WAVES), 0, stream,
+                         PK_QA(float), pl.tb, pl.tiers);
+    }
+#undef PK_QA
   }
   if ((st = check_launch(ctx, "qprep")) != PK_OK) return st;
   {
@@ -824,7 +860,7 @@ pk_status attend_impl(const Plan& pl, const void* q, pk_dtype q_dtype, const voi
 // A retrieval with a context's scratch.
 pk_status retrieve_ctx(pk_context* ctx, const void* q, pk_dtype q_dtype, const pk_summaries* s, int32_t* topk_idx,
                        float* topk_est, const pk_debug* dbg, hipStream_t stream, const pk::AttendArgs* att,
-                       bool* attended) {
+                       bool* attended, const PendingAppend* app = nullptr) {
   if (attended) *attended = false;
   const Plan pl = context_plan(ctx);
   if (s->n == 0) return retrieve_empty(pl, topk_idx, topk_est, dbg, stream);
@@ -834,7 +870,8 @@ pk_status retrieve_ctx(pk_context* ctx, const void* q, pk_dtype q_dtype, const p
   if (cs.tiles > ctx->max_tiles)
     return fail(ctx, PK_ERR_CAPACITY, "internal tiling bound exceeded (%d > %lld)", cs.tiles,
                 (long long)ctx->max_tiles);
-  return retrieve_impl(pl, context_scratch(ctx), cs, q, q_dtype, s, topk_idx, topk_est, dbg, stream, att, attended);
+  return retrieve_impl(pl, context_scratch(ctx), cs, q, q_dtype, s, topk_idx, topk_est, dbg, stream, att, attended,
+                       app);
 }
 
 }  // namespace
@@ -925,6 +962,47 @@ pk_status pk_retrieve_attend(pk_context* ctx, const void* q, pk_dtype q_dtype, c
   if (st != PK_OK || attended) return st;
   return attend_impl(context_plan(ctx), q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype,
                      stream);
+}
+
+pk_status pk_append_retrieve_attend(pk_context* ctx, const void* new_keys, pk_dtype key_dtype,
+                                    const int64_t key_strides[3], int64_t t, pk_summaries* inout, const void* q,
+                                    pk_dtype q_dtype, const void* k, const void* v, pk_dtype kv_dtype,
+                                    const int64_t kv_strides[3], int64_t n_rows, int32_t* topk_idx,
+                                    float* topk_est, void* out, pk_dtype out_dtype, void* hip_stream) {
+  if (!ctx) return fail(nullptr, PK_ERR_INVALID_ARG, "context is NULL");
+  if (key_dtype != PK_F32 && key_dtype != PK_BF16)
+    return fail(ctx, PK_ERR_UNSUPPORTED, "key dtype %d", (int)key_dtype);
+  pk_status st = check_summaries(ctx, ctx->cfg, inout);
+  if (st != PK_OK) return st;
+  if (t < 0) return fail(ctx, PK_ERR_INVALID_ARG, "t < 0");
+  if (inout->n + t > inout->n_capacity)
+    return fail(ctx, PK_ERR_CAPACITY, "n + t (%lld) exceeds n_capacity (%lld)", (long long)(inout->n + t),
+                (long long)inout->n_capacity);
+  if (t > 0 && (st = check_strides(ctx, new_keys, key_dtype, key_strides, "new_keys")) != PK_OK) return st;
+  pk_summaries after = *inout;
+  after.n += t;
+  if ((st = check_retrieve_args(ctx, ctx->cfg, q, q_dtype, &after, topk_idx, topk_est)) != PK_OK) return st;
+  if ((st = check_attend_args(ctx, q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype)) !=
+      PK_OK)
+    return st;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  // rank tiers: qprep reads no centroid counts, so a few new rows per unit are
+  // encoded by the first launch of the retrieval; otherwise by their own
+  const bool fuse = t > 0 && t <= pk::ENC_DIRECT && ctx->cfg.tier_mode == PK_TIERS_RANK;
+  if (t > 0 && !fuse &&
+      (st = encode_rows(ctx, new_keys, key_dtype, key_strides, t, inout->n, inout, stream)) != PK_OK)
+    return st;
+  const PendingAppend app{new_keys, key_dtype, key_strides, t, inout->n};
+  const bool same_dtype = q_dtype == kv_dtype && kv_dtype == out_dtype;
+  const pk::AttendArgs a{q, k, v, kv_strides[0], kv_strides[1], kv_strides[2], n_rows, ctx->cfg.softmax_scale, out};
+  bool attended = false;
+  st = retrieve_ctx(ctx, q, q_dtype, &after, topk_idx, topk_est, nullptr, stream, same_dtype ? &a : nullptr,
+                    &attended, fuse ? &app : nullptr);
+  if (st == PK_OK && !attended)
+    st = attend_impl(context_plan(ctx), q, q_dtype, k, v, kv_dtype, kv_strides, n_rows, topk_idx, out, out_dtype,
+                     stream);
+  if (st == PK_OK) inout->n = after.n;
+  return st;
 }
 
 }  // extern "C"

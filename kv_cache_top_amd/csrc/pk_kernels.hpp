@@ -325,33 +325,54 @@ __device__ __forceinline__ void encode_key(float (&x)[SUBD], int b, const Tables
   nsq_out = nsq;
 }
 
+// Where the rows a launch encodes come from and go to.
 template <typename KT>
-__global__ void __launch_bounds__(256)
-encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
-              int n_kv_heads, int64_t t, int chunks, int64_t row0, int64_t n_cap,
-              uint8_t* __restrict__ codes, uint8_t* __restrict__ records,
-              float* __restrict__ norms, uint32_t* __restrict__ counts, Tables tb) {
-  __shared__ uint32_t s_cnt[NSUB * 256];
-  const int64_t unit = blockIdx.x / chunks;
-  const int64_t r0 = (int64_t)(blockIdx.x - unit * chunks) * ENC_KEYS;
+struct EncodeArgs {
+  const KT* keys;
+  int64_t sb, sh, st;      // element strides of batch, KV head, token
+  int n_kv_heads;
+  int64_t t;               // rows per unit
+  int chunks;              // workgroups per unit: ceil(t / ENC_KEYS)
+  int64_t row0, n_cap;     // first row written, rows per unit of the summaries
+  uint8_t* codes;
+  uint8_t* records;
+  float* norms;
+  uint32_t* counts;        // nullable
+};
+
+// Workgroup `block` of NT threads (16 per key) encodes its rows.  DIRECT:
+// every launch has t <= ENC_DIRECT, so the counts are added directly and no
+// LDS counters are needed.
+template <typename KT, int NT, bool DIRECT>
+__device__ __forceinline__ void encode_body(const EncodeArgs<KT>& a, const Tables& tb, int block) {
+  __shared__ uint32_t s_cnt[DIRECT ? 1 : NSUB * 256];
+  const int64_t t = a.t, n_cap = a.n_cap, row0 = a.row0, st = a.st;
+  const int64_t unit = block / a.chunks;
+  const int64_t r0 = (int64_t)(block - unit * a.chunks) * ENC_KEYS;
   const int64_t r1 = (r0 + ENC_KEYS < t) ? r0 + ENC_KEYS : t;
   const int tid = threadIdx.x, b = tid & 15;
-  const int64_t seq = unit / n_kv_heads, head = unit - seq * n_kv_heads;
-  const KT* ubase = keys + seq * sb + head * sh + b * SUBD;
-  const bool direct = t <= ENC_DIRECT;
-  uint32_t* ucnt = counts ? counts + unit * NSUB * 256 : nullptr;
-  if (ucnt && !direct) {
-    for (int i = tid; i < NSUB * 256; i += 256) s_cnt[i] = 0;
-    __syncthreads();
+  const int64_t seq = unit / a.n_kv_heads, head = unit - seq * a.n_kv_heads;
+  const KT* ubase = a.keys + seq * a.sb + head * a.sh + b * SUBD;
+  const bool direct = DIRECT || t <= ENC_DIRECT;
+  uint32_t* ucnt = a.counts ? a.counts + unit * NSUB * 256 : nullptr;
+  uint8_t* codes = a.codes;
+  uint8_t* records = a.records;
+  float* norms = a.norms;
+  if constexpr (!DIRECT) {
+    if (ucnt && !direct) {
+      for (int i = tid; i < NSUB * 256; i += NT) s_cnt[i] = 0;
+      __syncthreads();
+    }
   }
 
   // whole 16-lane groups; the next key's load is in flight while one is encoded
+  constexpr int GROUPS = NT / 16;
   int64_t r = r0 + (tid >> 4);
   float xa[SUBD];
   if (r < r1) load_key<KT>(ubase + r * st, xa);
-  for (; r < r1; r += 16) {
+  for (; r < r1; r += GROUPS) {
     float xb[SUBD];
-    if (r + 16 < r1) load_key<KT>(ubase + (r + 16) * st, xb);
+    if (r + GROUPS < r1) load_key<KT>(ubase + (r + GROUPS) * st, xb);
     uint32_t code, nib;
     float w, nsq;
     encode_key(xa, b, tb, code, nib, w, nsq);
@@ -361,7 +382,7 @@ encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
     codes[row * 16 + b] = (uint8_t)code;
     if (ucnt) {
       if (direct) atomicAdd(&ucnt[b * 256 + code], 1u);
-      else atomicAdd(&s_cnt[b * 256 + code], 1u);
+      else if constexpr (!DIRECT) atomicAdd(&s_cnt[b * 256 + code], 1u);
     }
     uint32_t* rec = reinterpret_cast<uint32_t*>(records + row * 128);
     rec[b] = nib;
@@ -372,11 +393,19 @@ encode_kernel(const KT* __restrict__ keys, int64_t sb, int64_t sh, int64_t st,
     nsq += __uint_as_float(dpp_xor<1>(__float_as_uint(nsq)));
     if (b == 0) norms[row] = sqrt_rn(nsq);
   }
-  if (ucnt && !direct) {                    // keys per (subspace, centroid)
-    __syncthreads();
-    for (int i = tid; i < NSUB * 256; i += 256)
-      if (s_cnt[i]) atomicAdd(&ucnt[i], s_cnt[i]);
+  if constexpr (!DIRECT) {
+    if (ucnt && !direct) {                  // keys per (subspace, centroid)
+      __syncthreads();
+      for (int i = tid; i < NSUB * 256; i += NT)
+        if (s_cnt[i]) atomicAdd(&ucnt[i], s_cnt[i]);
+    }
   }
+}
+
+template <typename KT>
+__global__ void __launch_bounds__(256)
+encode_kernel(EncodeArgs<KT> a, Tables tb) {
+  encode_body<KT, 256, false>(a, tb, blockIdx.x);
 }
 
 // ===========================================================================
@@ -645,16 +674,32 @@ constexpr int QP_WAVES = 2;
 constexpr int QP_PARTS = NSUB / QP_WAVES;   // workgroups per query head
 
 template <typename QT>
-__global__ void __launch_bounds__(64 * QP_WAVES)
-qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
-             float* __restrict__ rot_q, uint8_t* __restrict__ lut_bytes, Tables tb,
-             TierSpec tiers, const uint32_t* __restrict__ counts, uint32_t keep_m, uint32_t* __restrict__ unit_tot) {
+struct QprepArgs {
+  const QT* q;
+  int n_q_heads, n_kv_heads, group;
+  float* rot_q;
+  uint8_t* lut_bytes;
+  const uint32_t* counts;  // percentile tiers
+  uint32_t keep_m;         // percentile tiers: kept positions M (0: rank tiers)
+  uint32_t* unit_tot;      // nullable: bin totals cleared for the collide kernel
+};
+
+template <typename QT>
+__device__ __forceinline__ void qprep_body(const QprepArgs<QT>& a, const Tables& tb, const TierSpec& tiers,
+                                           int block) {
   __shared__ float y[D];
   __shared__ uint64_t sel[QP_WAVES][256];   // (score key, 255 - centroid) of the selected centroids
   __shared__ uint8_t lw[QP_WAVES][256];     // tier weight per centroid
 
-  const int head = blockIdx.x / QP_PARTS;   // sequence * n_q_heads + query head
-  const int part = blockIdx.x - head * QP_PARTS;
+  const QT* __restrict__ q = a.q;
+  const int n_q_heads = a.n_q_heads, n_kv_heads = a.n_kv_heads, group = a.group;
+  float* __restrict__ rot_q = a.rot_q;
+  uint8_t* __restrict__ lut_bytes = a.lut_bytes;
+  const uint32_t* __restrict__ counts = a.counts;
+  const uint32_t keep_m = a.keep_m;
+  uint32_t* __restrict__ unit_tot = a.unit_tot;
+  const int head = block / QP_PARTS;        // sequence * n_q_heads + query head
+  const int part = block - head * QP_PARTS;
   const int seq = head / n_q_heads, qh = head - seq * n_q_heads;
   const int unit = seq * n_kv_heads + qh / group, g = qh % group;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -701,6 +746,23 @@ qprep_kernel(const QT* __restrict__ q, int n_q_heads, int n_kv_heads, int group,
     if (g == group - 1)
       for (int g2 = group; g2 < MAXG; ++g2) word[g2] = 0;
   }
+}
+
+template <typename QT>
+__global__ void __launch_bounds__(64 * QP_WAVES)
+qprep_kernel(QprepArgs<QT> a, Tables tb, TierSpec tiers) {
+  qprep_body<QT>(a, tb, tiers, blockIdx.x);
+}
+
+// One decode step's appended keys and the query preparation in one launch:
+// workgroups [0, qprep_blocks) run qprep, the rest encode the new rows (at
+// most ENC_DIRECT per unit).  The two touch disjoint data with rank tiers
+// (qprep reads no centroid counts), so nothing orders them.
+template <typename QT, typename KT>
+__global__ void __launch_bounds__(64 * QP_WAVES)
+append_qprep_kernel(QprepArgs<QT> qa, EncodeArgs<KT> ea, Tables tb, TierSpec tiers, int qprep_blocks) {
+  if ((int)blockIdx.x < qprep_blocks) qprep_body<QT>(qa, tb, tiers, blockIdx.x);
+  else encode_body<KT, 64 * QP_WAVES, true>(ea, tb, blockIdx.x - qprep_blocks);
 }
 
 

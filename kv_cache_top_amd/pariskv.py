@@ -86,6 +86,9 @@ _SIGS = {
                          ctypes.c_int),
     "pk_retrieve_attend": ([_P, _P, ctypes.c_int, ctypes.POINTER(pk_summaries), _P, _P, ctypes.c_int, _I64x3,
                             ctypes.c_int64, _P, _P, _P, ctypes.c_int, ctypes.POINTER(pk_debug), _P], ctypes.c_int),
+    "pk_append_retrieve_attend": ([_P, _P, ctypes.c_int, _I64x3, ctypes.c_int64, ctypes.POINTER(pk_summaries), _P,
+                                   ctypes.c_int, _P, _P, ctypes.c_int, _I64x3, ctypes.c_int64, _P, _P, _P,
+                                   ctypes.c_int, _P], ctypes.c_int),
     "pk_retrieve_attend_noalloc": ([ctypes.POINTER(pk_config), _P, ctypes.c_int, ctypes.POINTER(pk_summaries), _P,
                                     _P, ctypes.c_int, _I64x3, ctypes.c_int64, _P, _P, _P, ctypes.c_int, _P],
                                    ctypes.c_int),
@@ -330,6 +333,22 @@ def pk_retrieve_attend(ctx, q, sums: pk_summaries, k, v, topk_idx, out, topk_est
     _check(_lib.pk_retrieve_attend(ctx, _ptr(q), _dtype(q), ctypes.byref(sums), _ptr(k), _ptr(v), _dtype(k),
                                    _strides4(k), k.shape[2], _ptr(topk_idx), _ptr(topk_est), _ptr(out), _dtype(out),
                                    ctypes.byref(debug) if debug is not None else None, _stream(stream)), ctx)
+
+
+def pk_append_retrieve_attend(ctx, new_keys, q, sums: pk_summaries, k, v, topk_idx, out, topk_est=None,
+                              stream=None):
+    """One decode step: new_keys [batch][n_kv_heads][t][128] join the summaries,
+    then retrieval + attention over all keys (k, v hold every row)."""
+    cfg = _cfg_of(ctx)
+    _need_rows(new_keys, "new_keys", cfg, _float_types())
+    _check_q(cfg, q)
+    _check_kv(cfg, k, v)
+    _check_topk(cfg, topk_idx, topk_est)
+    _check_out(cfg, out)
+    _check(_lib.pk_append_retrieve_attend(ctx, _ptr(new_keys), _dtype(new_keys), _strides4(new_keys),
+                                          new_keys.shape[2], ctypes.byref(sums), _ptr(q), _dtype(q), _ptr(k),
+                                          _ptr(v), _dtype(k), _strides4(k), k.shape[2], _ptr(topk_idx),
+                                          _ptr(topk_est), _ptr(out), _dtype(out), _stream(stream)), ctx)
 
 
 def pk_retrieve_attend_raw(ctx, q, sums: pk_summaries, k_ptr: int, v_ptr: int, kv_dtype: int, kv_strides,
