@@ -71,7 +71,11 @@ def test_full_offload1m_mapped_host_kv():
 
 
 def test_full_drift_stream():
-    """1024 decode steps: append one drifting key per KV head, retrieve, attend."""
+    """1024 decode steps, each one pk_append_retrieve_attend call (the call the
+    benchmark times): append one drifting key per KV head, retrieve, attend.
+    At the checked steps the same retrieval also runs with debug copies, its
+    intermediates are compared with the oracle, and the decode-step call's
+    Top-k, estimates and output must equal it bit for bit."""
     import torch
     from kv_cache_top_amd import pariskv as P
     w = S.WORKLOADS["drift128k"]
@@ -95,15 +99,21 @@ def test_full_drift_stream():
         kf_all = S.as_f32(Kall[b, h])
         ref[unit] = (kf_all, S.as_f32(Vall[b, h]), oracle_encode(kf_all))
     recalls = []
+    idx = torch.empty((w.batch, w.n_q_heads, w.top_k), dtype=torch.int32, device="cuda")
+    est = torch.empty((w.batch, w.n_q_heads, w.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.bfloat16, device="cuda")
     for t in range(T):
-        P.pk_append_keys(run.ctx.h, to_torch(Kall[:, :, w.n + t:w.n + t + 1]), run.sums.s)
         n_t = w.n + t + 1
         Qt = S.all_queries(w, lambda bb, hh, J: Kall[bb, hh, J], step=t, n_t=n_t)
         run.Q = Qt
         run.Qt = to_torch(Qt)
-        run.debug = t in check_steps
-        run.retrieve_attend()
+        P.pk_append_retrieve_attend(run.ctx.h, run.Kt[:, :, n_t - 1:n_t], run.Qt, run.sums.s, run.Kt, run.Vt, idx,
+                                    out, est)
         if t in check_steps:
+            run.debug = True
+            run.retrieve_attend()
+            for a, r in zip((idx, est, out), (run.topk_idx, run.topk_est, run.out)):
+                assert torch.equal(a, r), f"decode-step call differs from the retrieval at step {t}"
             for unit in units:
                 say(f"case drift128k: step {t}, oracle unit {unit}")
                 b, h = divmod(unit, w.n_kv_heads)
