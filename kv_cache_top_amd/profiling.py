@@ -46,7 +46,7 @@ def short_name(full: str) -> str:
 
 
 # kernels that pk_timing brackets under another kernel's name
-KEY_ALIASES = {"select_sub": "select"}
+KEY_ALIASES = {"select_sub": "select", "append_qprep": "qprep"}
 
 
 def kernel_key(full: str) -> str:

@@ -54,4 +54,5 @@ def test_kernel_keys_follow_pk_timing_names():
     from kv_cache_top_amd.profiling import kernel_key
     assert kernel_key("void pk::collide_kernel<4, 64>(HIP_vector_type<unsigned int, 4u> const*)") == "collide"
     assert kernel_key("void pk::select_sub_kernel<4, true, 16>(unsigned int const*)") == "select"
+    assert kernel_key("void pk::append_qprep_kernel<unsigned short, unsigned short>(pk::QprepArgs)") == "qprep"
     assert kernel_key("void pk::rerank_topk_kernel<4, unsigned short, 2, true>(unsigned char const*)") == "rerank_topk"
