@@ -1384,38 +1384,53 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
 constexpr int SS_DRAIN_ROWS = 8;                          // rows compacted between queue drains
 constexpr int SS_QCAP = SS_DRAIN_ROWS * 64 + 64;          // queue entries per wave
 
-// theta / need_eq of head g (wave g) and the keys above / at theta in the
-// unit's sub-tiles before `sub` (64 sub-tiles per step); lane 0 writes them
-__device__ __forceinline__ void select_params_sub(uint32_t tot, const uint32_t* __restrict__ suf, int unit,
-                                                  int max_subs, int sub_len, int64_t n, int sub, int g,
-                                                  int n_candidates, int lane, int2* s_par, int2* s_sb) {
-  int theta;
+// The selection parameters of head g (wave g) in two parts, so that the
+// wave's score rows can be counted in between.  select_theta_sub: theta /
+// need_eq from the unit's bin totals (to s_par[g]), and requests for the
+// suffix counts of up to 64 earlier sub-tiles (they arrive behind the score
+// rows).  select_prefix_sub: the keys above / at theta in the sub-tiles before
+// `sub` (to s_sb[g]), 64 sub-tiles per step.
+struct SubPrefix {
+  int theta = 0, gt0 = 0, ge0 = 0;
+};
+
+__device__ __forceinline__ int keys_in_sub(int64_t n, int t, int sub_len) {
+  const int64_t len = n - (int64_t)t * sub_len;
+  return (int)(len < 0 ? 0 : (len > sub_len ? sub_len : len));
+}
+
+__device__ __forceinline__ SubPrefix select_theta_sub(uint32_t tot, const uint32_t* __restrict__ suf, int unit,
+                                                      int max_subs, int sub_len, int64_t n, int sub, int g,
+                                                      int n_candidates, int lane, int2* s_par) {
+  SubPrefix sp;
   uint32_t need_eq;
-  theta_from_totals(tot, n, n_candidates, theta, need_eq);
-  const uint32_t* row_gt = suf + suf_index(unit, max_subs, g, theta + 1, 0);             // #{S > theta}
-  const uint32_t* row_ge = suf + suf_index(unit, max_subs, g, theta > 0 ? theta : 1, 0);  // #{S >= theta}
-  int pre_gt = 0, pre_eq = 0;
-  for (int c0 = 0; c0 < sub; c0 += 64) {          // uniform
+  theta_from_totals(tot, n, n_candidates, sp.theta, need_eq);
+  if (lane < sub) {
+    sp.gt0 = (int)suf[suf_index(unit, max_subs, g, sp.theta + 1, lane)];                        // #{S > theta}
+    sp.ge0 = sp.theta > 0 ? (int)suf[suf_index(unit, max_subs, g, sp.theta, lane)]              // #{S >= theta}
+                          : keys_in_sub(n, lane, sub_len);                                      // every key
+  }
+  if (lane == 0) s_par[g] = make_int2(sp.theta, (int)need_eq);
+  return sp;
+}
+
+__device__ __forceinline__ void select_prefix_sub(const SubPrefix& sp, const uint32_t* __restrict__ suf, int unit,
+                                                  int max_subs, int sub_len, int64_t n, int sub, int g, int lane,
+                                                  int2* s_sb) {
+  int pre_gt = (int)xor_butterfly_u((uint32_t)sp.gt0, lane, AddU());
+  int pre_eq = (int)xor_butterfly_u((uint32_t)(sp.ge0 - sp.gt0), lane, AddU());
+  for (int c0 = 64; c0 < sub; c0 += 64) {          // uniform
     const int t = c0 + lane;
     int gt = 0, eq = 0;
     if (t < sub) {
-      gt = (int)row_gt[t];
-      int ge;
-      if (theta > 0) {
-        ge = (int)row_ge[t];
-      } else {                                    // every key has S >= 0
-        int64_t len = n - (int64_t)t * sub_len;
-        ge = (int)(len < 0 ? 0 : (len > sub_len ? sub_len : len));
-      }
+      gt = (int)suf[suf_index(unit, max_subs, g, sp.theta + 1, t)];
+      const int ge = sp.theta > 0 ? (int)suf[suf_index(unit, max_subs, g, sp.theta, t)] : keys_in_sub(n, t, sub_len);
       eq = ge - gt;
     }
     pre_gt += (int)xor_butterfly_u((uint32_t)gt, lane, AddU());
     pre_eq += (int)xor_butterfly_u((uint32_t)eq, lane, AddU());
   }
-  if (lane == 0) {
-    s_par[g] = make_int2(theta, (int)need_eq);
-    s_sb[g] = make_int2(pre_gt, pre_eq);
-  }
+  if (lane == 0) s_sb[g] = make_int2(pre_gt, pre_eq);
 }
 
 template <int G, bool FUSED, int ROWS>
@@ -1444,9 +1459,18 @@ select_sub_kernel(const uint32_t* __restrict__ scores, const SelParams* __restri
   const int jlast = wlen > 0 ? wlen - 1 : -w0;    // clamped loads re-read key w0 + jlast (>= 0)
   const uint32_t* srow = scores + (int64_t)unit * s_stride + w0;
 
+  // the parameters' inputs are requested before the scores (the memory
+  // counter is in order, so waiting for them does not wait for the scores)
   uint32_t tot = 0;
-  if constexpr (FUSED) {                           // requested before the scores (in-order memory counter)
+  SelParams prm{};
+  int2 sbase = make_int2(0, 0);
+  if constexpr (FUSED) {
     if (wave < G) tot = unit_tot[((int64_t)unit * MAXG + wave) * NBIN + lane];
+  } else {
+    if (tid < G) {
+      prm = params[unit * MAXG + tid];
+      sbase = sub_base[((int64_t)unit * max_subs + sub) * MAXG + tid];
+    }
   }
   uint32_t sp[ROWS];
 #pragma unroll
@@ -1454,13 +1478,13 @@ select_sub_kernel(const uint32_t* __restrict__ scores, const SelParams* __restri
     const int j = r * 64 + lane;
     sp[r] = srow[j < jlast ? j : jlast];
   }
+  SubPrefix pfx;
   if constexpr (FUSED) {
-    if (wave < G) select_params_sub(tot, suf, unit, max_subs, sub_len, n, sub, wave, n_candidates, lane, s_par, s_sb);
+    if (wave < G) pfx = select_theta_sub(tot, suf, unit, max_subs, sub_len, n, sub, wave, n_candidates, lane, s_par);
   } else {
     if (tid < G) {
-      const SelParams p = params[unit * MAXG + tid];
-      s_par[tid] = make_int2(p.theta, p.need_eq);
-      s_sb[tid] = sub_base[((int64_t)unit * max_subs + sub) * MAXG + tid];
+      s_par[tid] = make_int2(prm.theta, prm.need_eq);
+      s_sb[tid] = sbase;
     }
   }
   __syncthreads();
@@ -1487,6 +1511,9 @@ select_sub_kernel(const uint32_t* __restrict__ scores, const SelParams* __restri
   const uint32_t e13 = xor_butterfly_u((ceq >> 8) & 0x00FF00FFu, lane, AddU());
   if (lane == 0) {
     s_wc[wave][0] = g02; s_wc[wave][1] = g13; s_wc[wave][2] = e02; s_wc[wave][3] = e13;
+  }
+  if constexpr (FUSED) {                           // the earlier sub-tiles' counts arrived behind the rows
+    if (wave < G) select_prefix_sub(pfx, suf, unit, max_subs, sub_len, n, sub, wave, lane, s_sb);
   }
   __syncthreads();
   HeadSelect<G> hs;
