@@ -180,8 +180,8 @@ typedef enum {
   PK_KERNEL_ENCODE = 0,
   PK_KERNEL_QPREP = 1,
   PK_KERNEL_COLLIDE = 2,
-  PK_KERNEL_THRESHOLD = 3,     /* selection parameters; not launched when a unit's
-                                  histograms fit one wave (select derives them) */
+  PK_KERNEL_THRESHOLD = 3,     /* reserved: no longer launched (every select
+                                  workgroup derives the selection parameters) */
   PK_KERNEL_SELECT = 4,
   PK_KERNEL_RERANK = 5,        /* 4-bit rerank, several workgroups per head (few heads) */
   PK_KERNEL_TOPK = 6,          /* final top-k after PK_KERNEL_RERANK */

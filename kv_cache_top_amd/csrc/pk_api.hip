@@ -17,7 +17,6 @@
 #include "pk_kernels.hpp"
 #include "pk_tables.hpp"
 
-using pk::SelParams;
 
 struct pk_context {
   pk_config cfg;
@@ -31,12 +30,10 @@ struct pk_context {
   uint32_t* lut = nullptr;        // [units][16][256]
   float* rq = nullptr;            // [qheads][128]
   uint32_t* scores = nullptr;     // [units][n_cap]
-  uint32_t* tile_hist = nullptr;  // per unit [4 heads][bins / 4][max_subs][4 bins] (64 or 128 bins)
-  SelParams* params = nullptr;    // [units][4]
-  int2* sub_base = nullptr;       // [units][max_subs][4]
+  uint32_t* tile_hist = nullptr;  // per unit [4 heads][bins + 1][max_subs] sub-tile suffix counts (64 or 128 bins)
   int32_t* cand_idx = nullptr;    // [qheads][C]
   float* cand_est = nullptr;      // [qheads][C]
-  uint32_t* unit_tot = nullptr;   // [units][4][64] bin totals of the collision scores
+  uint32_t* unit_tot = nullptr;   // [units][4][bins] bin totals of the collision scores
   uint32_t* dev_err = nullptr;    // device error flags (PK_DEVICE_ERR_*)
   std::string err;
   // timing
@@ -143,8 +140,7 @@ pk_status check_launch(pk_context* ctx, const char* what) {
 }
 
 void free_scratch(pk_context* c) {
-  void* ptrs[] = {c->lut, c->rq, c->scores, c->tile_hist, c->params, c->sub_base, c->cand_idx, c->cand_est,
-                  c->unit_tot, c->dev_err};
+  void* ptrs[] = {c->lut, c->rq, c->scores, c->tile_hist, c->cand_idx, c->cand_est, c->unit_tot, c->dev_err};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (int k = 0; k < PK_N_KERNELS; ++k) {
@@ -312,12 +308,10 @@ pk_status pk_create(const pk_config* cfg, pk_context** out) {
       {(void**)&c->lut, U * 16 * 256 * 4},
       {(void**)&c->rq, Q * 128 * 4},
       {(void**)&c->scores, U * N * 4},
-      {(void**)&c->tile_hist, U * MS * pk::MAXG * pk::NBIN_MAX * 4},
-      {(void**)&c->params, U * pk::MAXG * sizeof(SelParams)},
-      {(void**)&c->sub_base, U * MS * pk::MAXG * sizeof(int2)},
+      {(void**)&c->tile_hist, U * MS * pk::MAXG * (pk::NBIN_MAX + 1) * 4},
       {(void**)&c->cand_idx, Q * C * 4},
       {(void**)&c->cand_est, Q * C * 4},
-      {(void**)&c->unit_tot, U * pk::MAXG * pk::NBIN * 4},
+      {(void**)&c->unit_tot, U * pk::MAXG * pk::NBIN_MAX * 4},
       {(void**)&c->dev_err, 4},
   };
   for (Alloc& a : allocs) {
@@ -498,11 +492,9 @@ struct Scratch {
   float* rq = nullptr;            // [qheads][128]
   uint32_t* scores = nullptr;     // [units][score_stride]
   int64_t score_stride = 0;
-  uint32_t* tile_hist = nullptr;  // per unit: histograms (128 bins) or suffix counts (64 bins)
+  uint32_t* tile_hist = nullptr;  // per unit: sub-tile suffix counts
   int64_t max_subs = 0;
-  uint32_t* unit_tot = nullptr;   // [units][4][64]
-  SelParams* params = nullptr;    // [units][4]
-  int2* sub_base = nullptr;       // [units][max_subs][4]
+  uint32_t* unit_tot = nullptr;   // [units][4][bins]
   int32_t* cand_idx = nullptr;    // [qheads][C]
   float* cand_est = nullptr;      // [qheads][C]
   uint32_t* dev_err = nullptr;    // nullable
@@ -556,8 +548,6 @@ Scratch context_scratch(pk_context* ctx) {
   sc.score_stride = ctx->cfg.n_capacity;
   sc.tile_hist = ctx->tile_hist;
   sc.max_subs = ctx->max_subs;
-  sc.params = ctx->params;
-  sc.sub_base = ctx->sub_base;
   sc.cand_idx = ctx->cand_idx;
   sc.cand_est = ctx->cand_est;
   sc.unit_tot = ctx->unit_tot;
@@ -590,7 +580,7 @@ pk_status retrieve_impl(const Plan& pl, const Scratch& sc, const CallShape& cs, 
     const int qblocks = pl.qheads * pk::QP_PARTS;
 #define PK_QA(QT)                                                                                             \
   pk::QprepArgs<QT>{(const QT*)q, cfg.n_q_heads, cfg.n_kv_heads, pl.group, sc.rq, (uint8_t*)sc.lut, s->counts, \
-                    keep_m, pct ? nullptr : sc.unit_tot}
+                    keep_m, sc.unit_tot}
     if (app) {
       // the step's appended rows are encoded by extra workgroups of the same
       // launch (one per unit: t <= ENC_DIRECT)
@@ -636,33 +626,20 @@ pk_status retrieve_impl(const Plan& pl, const Scratch& sc, const CallShape& cs, 
 #undef PK_COLLIDE
   }
   if ((st = check_launch(ctx, "collide")) != PK_OK) return st;
-  // rank tiers: each select workgroup derives theta and its prefix counts
-  // itself; percentile tiers (128 bins): the threshold kernel does
-  const bool fused_params = !pct;
-  if (!fused_params) {
-    Launch L(ctx, PK_KERNEL_THRESHOLD, stream);
-    if (pct)
-      hipLaunchKernelGGL(pk::threshold_kernel<pk::NBIN_MAX>, dim3(pl.units * pl.group), dim3(pk::TH_THREADS), 0,
-                         stream, sc.tile_hist, sc.params, sc.sub_base, n, 4 * tiles, (int)sc.max_subs,
-                         tile / 4, pl.group, C);
-    else
-      hipLaunchKernelGGL(pk::threshold_kernel<pk::NBIN>, dim3(pl.units * pl.group), dim3(pk::TH_THREADS), 0,
-                         stream, sc.tile_hist, sc.params, sc.sub_base, n, 4 * tiles, (int)sc.max_subs,
-                         tile / 4, pl.group, C);
-  }
-  if ((st = check_launch(ctx, "threshold")) != PK_OK) return st;
   {
+    // every select workgroup derives theta and its prefix counts itself from
+    // the unit's bin totals and the sub-tiles' suffix counts
     Launch L(ctx, PK_KERNEL_SELECT, stream);
-#define PK_SELECT(GG, F)                                                                                        \
-  hipLaunchKernelGGL((pk::select_kernel<GG, F>), dim3(grid), dim3(256), 0, stream, sc.scores, sc.params,      \
-                     sc.sub_base, sc.cand_idx, n, sc.score_stride, tiles, (int)sc.max_subs, tile,            \
-                     cfg.n_q_heads, cfg.n_kv_heads, C, sc.unit_tot, sc.tile_hist, sc.dev_err)
-#define PK_SELECT_G(F)                     \
+#define PK_SELECT(GG, NB)                                                                                      \
+  hipLaunchKernelGGL((pk::select_kernel<GG, NB>), dim3(grid), dim3(256), 0, stream, sc.scores, sc.cand_idx, n, \
+                     sc.score_stride, tiles, (int)sc.max_subs, tile, cfg.n_q_heads, cfg.n_kv_heads, C,        \
+                     sc.unit_tot, sc.tile_hist, sc.dev_err)
+#define PK_SELECT_G(NB)                    \
   switch (pl.group) {                    \
-    case 1: PK_SELECT(1, F); break;        \
-    case 2: PK_SELECT(2, F); break;        \
-    case 3: PK_SELECT(3, F); break;        \
-    default: PK_SELECT(4, F); break;       \
+    case 1: PK_SELECT(1, NB); break;       \
+    case 2: PK_SELECT(2, NB); break;       \
+    case 3: PK_SELECT(3, NB); break;       \
+    default: PK_SELECT(4, NB); break;      \
   }
     // one workgroup per sub-tile once a sub-tile is long enough to split
     // over the four waves (more resident waves hide the score loads)
@@ -670,35 +647,35 @@ pk_status retrieve_impl(const Plan& pl, const Scratch& sc, const CallShape& cs, 
     if (rpw >= kSelectSubMinRows) {
       const int subs = 4 * tiles;
       const unsigned sgrid = (unsigned)((int64_t)pl.units * subs);
-#define PK_SELSUB(GG, F, RW)                                                                                     \
-  hipLaunchKernelGGL((pk::select_sub_kernel<GG, F, RW>), dim3(sgrid), dim3(256), 0, stream, sc.scores, sc.params, \
-                     sc.sub_base, sc.cand_idx, n, sc.score_stride, subs, (int)sc.max_subs, tile / 4,          \
-                     cfg.n_q_heads, cfg.n_kv_heads, C, sc.unit_tot, sc.tile_hist, sc.dev_err)
-#define PK_SELSUB_R(GG, F)                   \
+#define PK_SELSUB(GG, NB, RW)                                                                                    \
+  hipLaunchKernelGGL((pk::select_sub_kernel<GG, NB, RW>), dim3(sgrid), dim3(256), 0, stream, sc.scores,        \
+                     sc.cand_idx, n, sc.score_stride, subs, (int)sc.max_subs, tile / 4, cfg.n_q_heads,       \
+                     cfg.n_kv_heads, C, sc.unit_tot, sc.tile_hist, sc.dev_err)
+#define PK_SELSUB_R(GG, NB)                  \
   do {                                       \
-    if (rpw <= 4) PK_SELSUB(GG, F, 4);       \
-    else if (rpw <= 8) PK_SELSUB(GG, F, 8);  \
-    else PK_SELSUB(GG, F, 16);               \
+    if (rpw <= 4) PK_SELSUB(GG, NB, 4);      \
+    else if (rpw <= 8) PK_SELSUB(GG, NB, 8); \
+    else PK_SELSUB(GG, NB, 16);              \
   } while (0)
-#define PK_SELSUB_G(F)                        \
+#define PK_SELSUB_G(NB)                       \
   switch (pl.group) {                       \
-    case 1: PK_SELSUB_R(1, F); break;         \
-    case 2: PK_SELSUB_R(2, F); break;         \
-    case 3: PK_SELSUB_R(3, F); break;         \
-    default: PK_SELSUB_R(4, F); break;        \
+    case 1: PK_SELSUB_R(1, NB); break;        \
+    case 2: PK_SELSUB_R(2, NB); break;        \
+    case 3: PK_SELSUB_R(3, NB); break;        \
+    default: PK_SELSUB_R(4, NB); break;       \
   }
-      if (fused_params) {
-        PK_SELSUB_G(true);
+      if (pct) {
+        PK_SELSUB_G(pk::NBIN_MAX);
       } else {
-        PK_SELSUB_G(false);
+        PK_SELSUB_G(pk::NBIN);
       }
 #undef PK_SELSUB_G
 #undef PK_SELSUB_R
 #undef PK_SELSUB
-    } else if (fused_params) {
-      PK_SELECT_G(true);
+    } else if (pct) {
+      PK_SELECT_G(pk::NBIN_MAX);
     } else {
-      PK_SELECT_G(false);
+      PK_SELECT_G(pk::NBIN);
     }
 #undef PK_SELECT_G
 #undef PK_SELECT
@@ -1046,18 +1023,16 @@ size_t carve_scratch(unsigned char* base, const pk_config& cfg, int units, int q
     return p;
   };
   const size_t U = units, Q = qheads, MS = 4 * (size_t)cs.tiles, C = cs.C;
-  const size_t bins = cs.pct ? pk::NBIN_MAX : pk::NBIN + 1;   // histograms, or suffix counts s = 1..65
+  const size_t bins = cs.pct ? pk::NBIN_MAX : pk::NBIN;       // suffix counts s = 1..bins + 1
   sc->lut = reinterpret_cast<uint32_t*>(take(U * 16 * 256 * 4));
   sc->rq = reinterpret_cast<float*>(take(Q * 128 * 4));
   sc->scores = reinterpret_cast<uint32_t*>(take(U * (size_t)n * 4));
   sc->score_stride = n;
-  sc->tile_hist = reinterpret_cast<uint32_t*>(take(U * MS * pk::MAXG * bins * 4));
+  sc->tile_hist = reinterpret_cast<uint32_t*>(take(U * MS * pk::MAXG * (bins + 1) * 4));
   sc->max_subs = (int64_t)MS;
-  sc->params = reinterpret_cast<SelParams*>(take(U * pk::MAXG * sizeof(SelParams)));
-  sc->sub_base = reinterpret_cast<int2*>(take(U * MS * pk::MAXG * sizeof(int2)));
   sc->cand_idx = reinterpret_cast<int32_t*>(take(Q * C * 4));
   sc->cand_est = reinterpret_cast<float*>(take(Q * C * 4));
-  sc->unit_tot = reinterpret_cast<uint32_t*>(take(U * pk::MAXG * pk::NBIN * 4));
+  sc->unit_tot = reinterpret_cast<uint32_t*>(take(U * pk::MAXG * bins * 4));
   sc->dev_err = nullptr;
   (void)cfg;
   return off;

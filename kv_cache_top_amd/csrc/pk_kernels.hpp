@@ -46,14 +46,6 @@ struct TierSpec {
   int weight[4];
 };
 
-// per-(unit, head) selection parameters written by the collide kernel
-struct SelParams {
-  int theta;     // threshold score
-  int need_eq;   // keys with S == theta that are taken (lowest indices first)
-  int n_gt;      // keys with S > theta
-  int n_sel;     // n_gt + need_eq = min(n, C)
-};
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -714,7 +706,11 @@ __device__ __forceinline__ void qprep_body(const QprepArgs<QT>& a, const Tables&
       rot_q[(int64_t)head * D + lane] = v0 * tb.inv_sqrt_d;
       rot_q[(int64_t)head * D + lane + 64] = v1 * tb.inv_sqrt_d;
       // the collide kernel that follows adds this head's bin counts here
-      if (unit_tot) unit_tot[((int64_t)unit * MAXG + g) * NBIN + lane] = 0u;
+      if (unit_tot) {
+        const int nb = keep_m > 0 ? NBIN_MAX : NBIN;
+        unit_tot[((int64_t)unit * MAXG + g) * nb + lane] = 0u;
+        if (keep_m > 0) unit_tot[((int64_t)unit * MAXG + g) * nb + 64 + lane] = 0u;
+      }
     }
   }
   __syncthreads();
@@ -768,14 +764,15 @@ append_qprep_kernel(QprepArgs<QT> qa, EncodeArgs<KT> ea, Tables tb, TierSpec tie
 
 // ===========================================================================
 // collide: tier-weighted collision votes (Slides Eq. (15), Sec. 4.2.2;
-// README "2. Decode") and per-tile score histograms.
+// README "2. Decode"), per-sub-tile suffix counts of the scores and the
+// unit's score histogram.
 //
 // Workgroup = (unit, tile of `tile` keys).  The unit's LUT (16 x 256 u32, byte
 // g = weight for query head g) sits in LDS; a key's 16 code bytes index it
-// and the 16 words are summed: four 8-bit lanes of at most 64 never carry, so
+// and the 16 words are summed: four 8-bit lanes of at most 96 never carry, so
 // one u32 add serves all query heads of the KV head.  S is stored packed.
 // Wave w scores the w-th quarter ("sub-tile") of the tile.  Histogram bins
-// 1..64 are counted in LDS words of HIST_LANES per (head, bin): lanes l and
+// 1..NB (64 with rank tiers, 128 with percentile tiers) are counted in LDS words of HIST_LANES per (head, bin): lanes l and
 // l + 32 share a word, and byte w of it belongs to wave w (a byte counts at
 // most 2 * keys per lane <= 128), which gives one histogram per sub-tile; bin
 // 0 is implied by the sub-tile length.  Each lane keeps COLLIDE_UNROLL code
@@ -798,18 +795,12 @@ __device__ __forceinline__ void xcd_unit_tile(int i, int units, int tiles, int& 
   }
 }
 
-// word of the count of bin `bin` (score bin + 1) of head g in sub-tile `sub` of a
-// unit's histograms; a unit holds max_subs * MAXG * NB words
+// word of the suffix count #{S >= s} (s = 1..NB + 1; s = NB + 1 is always 0)
+// of head g in sub-tile `sub` of a unit: rows of max_subs sub-tiles, a unit
+// holds MAXG * (NB + 1) rows
 template <int NB>
-__device__ __forceinline__ int64_t hist_index(int64_t unit, int max_subs, int sub, int g, int bin) {
-  return (int64_t)unit * max_subs * MAXG * NB + (((int64_t)g * (NB / 4) + (bin >> 2)) * max_subs + sub) * 4 + (bin & 3);
-}
-
-// word of the suffix count #{S >= s} (s = 1..65; s = 65 is always 0) of
-// head g in sub-tile `sub` of a unit: rows of max_subs sub-tiles, a unit holds
-// MAXG * 65 rows
 __device__ __forceinline__ int64_t suf_index(int64_t unit, int max_subs, int g, int s, int sub) {
-  return (((int64_t)unit * MAXG + g) * (NBIN + 1) + (s - 1)) * max_subs + sub;
+  return (((int64_t)unit * MAXG + g) * (NB + 1) + (s - 1)) * max_subs + sub;
 }
 
 template <int G, int NB>   // NB: histogram bins 1..NB
@@ -886,184 +877,58 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
   }
   __syncthreads();
 
-  // Byte w of a counter word belongs to wave w.  With 128 bins (percentile
-  // tiers) the sub-tile histograms are stored for the threshold kernel, in
-  // the hist_index layout: per unit, [head][bin / 4][sub-tile][bin % 4], so
-  // that its readers, one lane per sub-tile, load four bins of consecutive
-  // sub-tiles with one coalesced 16-byte access.  With 64 bins each sub-tile
-  // publishes its suffix counts #{S >= s} (suf_index layout) and the bin
-  // counts are added to the unit's totals, from which every select workgroup
-  // derives the parameters itself; thread (g, s - 1) owns bin s of head g, so
-  // wave g holds head g.
-  for (int gb = tid; gb < group * NB; gb += 256) {
+  // Byte w of a counter word belongs to wave w.  Each sub-tile publishes its
+  // suffix counts #{S >= s} (suf_index layout) and the bin counts are added to
+  // the unit's totals, from which every select workgroup derives its
+  // parameters.  Thread (g, s - 1) owns bin s of head g: a wave holds 64 bins
+  // of one head, and with 128 bins the lower half adds the totals of the
+  // upper half (the next wave).  The LUT's LDS words carry the upper halves'
+  // totals (no lookup is left after the barrier above; a separate array
+  // would take the 128-bin kernel past two workgroups per CU).
+  uint32_t* s_upper = s_lut;
+  for (int b0 = 0; b0 < group * NB; b0 += 256) {   // uniform; a wave is active or not as a whole
+    const int gb = b0 + tid;
+    const bool act = gb < group * NB;
     const int g = gb / NB, bin = gb % NB;
-    const uint32_t* row = s_hist + (g * NB + bin) * HIST_LANES;
-    uint32_t lo = 0, hi = 0;
-    for (int i = 0; i < HIST_LANES; ++i) {
-      const uint32_t v = row[(i + tid) & (HIST_LANES - 1)];
-      lo += v & 0x00FF00FFu;          // waves 0 and 2
-      hi += (v >> 8) & 0x00FF00FFu;   // waves 1 and 3
-    }
-    const uint32_t cnt[4] = {lo & 0xFFFFu, hi & 0xFFFFu, lo >> 16, hi >> 16};
-    if constexpr (NB == NBIN) {
+    uint32_t s01 = 0, s23 = 0, c = 0;
+    if (act) {
+      const uint32_t* row = s_hist + (g * NB + bin) * HIST_LANES;
+      uint32_t lo = 0, hi = 0;
+      for (int i = 0; i < HIST_LANES; ++i) {
+        const uint32_t v = row[(i + tid) & (HIST_LANES - 1)];
+        lo += v & 0x00FF00FFu;          // waves 0 and 2
+        hi += (v >> 8) & 0x00FF00FFu;   // waves 1 and 3
+      }
+      const uint32_t cnt[4] = {lo & 0xFFFFu, hi & 0xFFFFu, lo >> 16, hi >> 16};
+      c = cnt[0] + cnt[1] + cnt[2] + cnt[3];
       // 16-bit fields: sub-tiles 0 and 1 in c01, 2 and 3 in c23 (counts <= tile / 4 < 2^16)
       const uint32_t c01 = cnt[0] | (cnt[1] << 16), c23 = cnt[2] | (cnt[3] << 16);
       const uint32_t i01 = wave_incl_scan(c01), i23 = wave_incl_scan(c23);
-      const uint32_t s01 = (uint32_t)__builtin_amdgcn_readlane((int)i01, 63) - i01 + c01;   // #{S >= bin + 1}
-      const uint32_t s23 = (uint32_t)__builtin_amdgcn_readlane((int)i23, 63) - i23 + c23;
-      *reinterpret_cast<uint4*>(tile_hist + suf_index(unit, max_subs, g, bin + 1, 4 * tl)) =
+      const uint32_t t01 = (uint32_t)__builtin_amdgcn_readlane((int)i01, 63);
+      const uint32_t t23 = (uint32_t)__builtin_amdgcn_readlane((int)i23, 63);
+      s01 = t01 - i01 + c01;             // #{S >= bin + 1} among this wave's bins
+      s23 = t23 - i23 + c23;
+      if (NB > 64 && lane == 0) {
+        s_upper[2 * wave] = t01;
+        s_upper[2 * wave + 1] = t23;
+      }
+    }
+    if constexpr (NB > 64) {
+      static_assert(NB == 128, "64 or 128 bins");
+      __syncthreads();
+      if (act && bin < 64) {
+        s01 += s_upper[2 * wave + 2];
+        s23 += s_upper[2 * wave + 3];
+      }
+      __syncthreads();
+    }
+    if (act) {
+      *reinterpret_cast<uint4*>(tile_hist + suf_index<NB>(unit, max_subs, g, bin + 1, 4 * tl)) =
           make_uint4(s01 & 0xFFFFu, s01 >> 16, s23 & 0xFFFFu, s23 >> 16);
-      if (bin == 0)   // #{S >= 65} = 0
-        *reinterpret_cast<uint4*>(tile_hist + suf_index(unit, max_subs, g, NBIN + 1, 4 * tl)) = make_uint4(0, 0, 0, 0);
-      const uint32_t c = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-      if (c) atomicAdd(&unit_tot[((int64_t)unit * MAXG + g) * NBIN + bin], c);
-    } else {
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2)
-        tile_hist[hist_index<NB>(unit, max_subs, 4 * tl + w2, g, bin)] = cnt[w2];
+      if (bin == 0)   // #{S >= NB + 1} = 0
+        *reinterpret_cast<uint4*>(tile_hist + suf_index<NB>(unit, max_subs, g, NB + 1, 4 * tl)) = make_uint4(0, 0, 0, 0);
+      if (c) atomicAdd(&unit_tot[((int64_t)unit * MAXG + g) * NB + bin], c);
     }
-  }
-}
-
-// ===========================================================================
-// threshold: per (unit, head) the score theta of the C-th best key, how many
-// keys with S == theta are taken (the lowest indices, Slides Sec. 4.2.2
-// histogram + prefix-scan selection), and per sub-tile the exclusive prefix
-// counts of keys above / at theta.
-//
-// Workgroup = (unit, query head); thread t holds the 64-bin histogram of
-// sub-tile t of each 256-sub-tile chunk in registers.  Bin totals come from a
-// register reduce-scatter per wave, theta from a suffix scan over the bins, and the per-sub-tile
-// prefixes from a workgroup scan over the same registers, so a unit with at
-// most 256 sub-tiles reads its histograms once.
-// ===========================================================================
-constexpr int TH_THREADS = 256;
-
-template <int NB>   // histogram bins 1..NB, a multiple of 64
-__global__ void __launch_bounds__(TH_THREADS)
-threshold_kernel(const uint32_t* __restrict__ tile_hist, SelParams* __restrict__ params,
-                 int2* __restrict__ sub_base, int64_t n, int subs, int max_subs, int sub_len, int group,
-                 int n_candidates) {
-  constexpr int NH = NB / 64;                      // 64-bin slices
-  __shared__ uint32_t s_q[4][64];
-  __shared__ int s_par[2];
-  __shared__ int2 s_w[4];
-  const int unit = blockIdx.x / group, g = blockIdx.x - unit * group;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  uint4 h4[NB / 4];
-  auto load_chunk = [&](int base) {
-    const int t = base + tid;
-    const int tl = t < subs ? t : subs - 1;
-#pragma unroll
-    for (int q4 = 0; q4 < NB / 4; ++q4)
-      h4[q4] = *reinterpret_cast<const uint4*>(tile_hist + hist_index<NB>(unit, max_subs, tl, g, 4 * q4));
-    if (t >= subs) {
-#pragma unroll
-      for (int q4 = 0; q4 < NB / 4; ++q4) h4[q4] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-
-  // pass 1: bin totals (wave 0, lane l holds bin 64 h + l + 1 in tot[h])
-  uint32_t tot[NH];
-#pragma unroll
-  for (int h = 0; h < NH; ++h) tot[h] = 0;
-  for (int base = 0; base < subs; base += TH_THREADS) {
-    load_chunk(base);
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      uint32_t v[64];
-#pragma unroll
-      for (int q4 = 0; q4 < 16; ++q4) {
-        const uint4 x = h4[16 * h + q4];
-        v[4 * q4] = x.x; v[4 * q4 + 1] = x.y; v[4 * q4 + 2] = x.z; v[4 * q4 + 3] = x.w;
-      }
-      s_q[wave][lane] = reduce_scatter64(v, lane);   // this wave's 64 sub-tiles, bin 64 h + lane + 1
-      __syncthreads();
-      if (wave == 0) tot[h] += s_q[0][lane] + s_q[1][lane] + s_q[2][lane] + s_q[3][lane];
-      __syncthreads();
-    }
-  }
-
-  if (wave == 0) {
-    // suffix sums over bins: suf[h] at lane l = #{S >= 64 h + l + 1}
-    uint32_t suf[NH];
-    uint32_t above = 0;                             // keys in higher slices
-#pragma unroll
-    for (int h = NH - 1; h >= 0; --h) {
-      const uint32_t incl = wave_incl_scan(tot[h]);
-      const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl + tot[h];   // lanes >= l
-      suf[h] = x + above;
-      above = (uint32_t)__builtin_amdgcn_readlane((int)suf[h], 0);
-    }
-    int theta = 0;
-    uint32_t n_gt = above;                          // every key with S >= 1
-    bool found = false;
-#pragma unroll
-    for (int h = NH - 1; h >= 0; --h) {
-      const uint64_t ge = __ballot(suf[h] >= (uint32_t)n_candidates);
-      if (!found && ge) {
-        const int top = 63 - __builtin_clzll(ge);   // highest bin of the slice with suffix >= C
-        theta = 64 * h + top + 1;
-        const uint32_t next_in_slice = (uint32_t)__builtin_amdgcn_readlane((int)suf[h], (top + 1) & 63);
-        const uint32_t next_slice = (h + 1 < NH) ? (uint32_t)__builtin_amdgcn_readlane((int)suf[(h + 1) % NH], 0) : 0u;
-        n_gt = (top == 63) ? next_slice : next_in_slice;
-        found = true;
-      }
-    }
-    uint32_t eq_tot = (uint32_t)(n - n_gt);
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)tot[h], (theta - 1) & 63);
-      if (theta > 0 && (theta - 1) / 64 == h) eq_tot = v;
-    }
-    const uint32_t want = (uint32_t)n_candidates - n_gt;
-    const uint32_t need_eq = want < eq_tot ? want : eq_tot;
-    if (lane == 0) {
-      params[unit * MAXG + g] = SelParams{theta, (int)need_eq, (int)n_gt, (int)(n_gt + need_eq)};
-      s_par[0] = theta;
-    }
-  }
-  __syncthreads();
-  const int theta = s_par[0];
-
-  // pass 2: per-sub-tile exclusive prefixes of (#gt, #eq)
-  int run_gt = 0, run_eq = 0;
-  for (int base = 0; base < subs; base += TH_THREADS) {
-    if (subs > TH_THREADS) load_chunk(base);      // else the registers still hold chunk 0
-    const int t = base + tid;
-    int gt = 0, eq = 0, nz = 0;
-#pragma unroll
-    for (int q4 = 0; q4 < NB / 4; ++q4) {
-      const int c4[4] = {(int)h4[q4].x, (int)h4[q4].y, (int)h4[q4].z, (int)h4[q4].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int sbin = 4 * q4 + e + 1;
-        nz += c4[e];
-        gt += (sbin > theta) ? c4[e] : 0;
-        eq = (sbin == theta) ? c4[e] : eq;
-      }
-    }
-    int64_t len = n - (int64_t)t * sub_len;
-    len = len < 0 ? 0 : (len > sub_len ? sub_len : len);
-    if (theta == 0) eq = (int)len - nz;
-    if (t >= subs) { gt = 0; eq = 0; }
-    const int pg = (int)wave_incl_scan((uint32_t)gt);   // inclusive scans within the wave
-    const int pe = (int)wave_incl_scan((uint32_t)eq);
-    if (lane == 63) s_w[wave] = make_int2(pg, pe);
-    __syncthreads();
-    int wg = 0, we = 0, cg = 0, ce = 0;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int2 x = s_w[v];
-      if (v < wave) { wg += x.x; we += x.y; }
-      cg += x.x; ce += x.y;
-    }
-    __syncthreads();                               // s_w is rewritten by the next chunk
-    if (t < subs)
-      sub_base[((int64_t)unit * max_subs + t) * MAXG + g] =
-          make_int2(run_gt + wg + pg - gt, run_eq + we + pe - eq);
-    run_gt += cg;
-    run_eq += ce;
   }
 }
 
@@ -1082,8 +947,9 @@ __global__ void __launch_bounds__(256) copy16_kernel(uint4* __restrict__ dst, co
 // Sec. 4.3: C = ceil(beta n)).
 //
 // Workgroup = (unit, tile), same tiling as collide; wave w owns sub-tile w and
-// starts from the counts of earlier keys above / at theta supplied by the
-// threshold kernel.  A key is a candidate of head g iff S > theta, or S ==
+// starts from the counts of earlier keys above / at theta, which it derives
+// from the unit's bin totals and the earlier sub-tiles' suffix counts (both
+// written by collide).  A key is a candidate of head g iff S > theta, or S ==
 // theta and fewer than need_eq keys with S == theta precede it; its slot is
 // (#gt before) + min(#eq before, need_eq), which lists candidates in ascending
 // key order.  Byte-parallel compares of the packed scores against all heads'
@@ -1103,24 +969,46 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// theta and need_eq of one query head from its bin totals (lane l holds the
-// count of keys with S = l + 1 among the unit's n keys): theta = the highest
-// score whose suffix count #{S >= theta} reaches C (0: every key is taken);
-// need_eq = how many keys with S == theta are taken.
-__device__ __forceinline__ void theta_from_totals(uint32_t tot, int64_t n, int n_candidates, int& theta,
-                                                  uint32_t& need_eq) {
-  const uint32_t incl = wave_incl_scan(tot);
-  const uint32_t all_nz = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-  const uint32_t suf = all_nz - incl + tot;          // lane l: #{S >= l + 1}
-  const uint64_t ge = __ballot(suf >= (uint32_t)n_candidates);
-  const int top = ge ? 63 - __builtin_clzll(ge) : -1;
-  theta = top + 1;
-  const uint32_t n_gt = (top < 0) ? all_nz
-                        : (top == 63 ? 0u : (uint32_t)__builtin_amdgcn_readlane((int)suf, (top + 1) & 63));
-  const uint32_t eq_tot = (theta > 0) ? (uint32_t)__builtin_amdgcn_readlane((int)tot, (theta - 1) & 63)
-                                      : (uint32_t)(n - n_gt);
+// theta and need_eq of one query head from its bin totals (tot[h] at lane l:
+// the count of keys with S = 64 h + l + 1 among the unit's n keys): theta =
+// the highest score whose suffix count #{S >= theta} reaches C (0: every key
+// is taken); need_eq = how many keys with S == theta are taken.
+template <int NB>
+__device__ __forceinline__ void theta_from_totals(const uint32_t (&tot)[NB / 64], int64_t n, int n_candidates,
+                                                  int& theta, uint32_t& need_eq) {
+  constexpr int H = NB / 64;
+  uint32_t suf[H];                                   // suf[h] at lane l: #{S >= 64 h + l + 1}
+  uint32_t above = 0;                                // keys in the higher halves
+#pragma unroll
+  for (int h = H - 1; h >= 0; --h) {
+    const uint32_t incl = wave_incl_scan(tot[h]);
+    const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    suf[h] = all - incl + tot[h] + above;
+    above += all;
+  }
+  theta = 0;
+  uint32_t n_gt = above, eq_tot = (uint32_t)(n - above);   // theta 0: every key with S >= 1 is above
+#pragma unroll
+  for (int h = 0; h < H; ++h) {                      // a higher half overrides a lower one
+    const uint64_t ge = __ballot(suf[h] >= (uint32_t)n_candidates);
+    if (ge) {
+      const int top = 63 - __builtin_clzll(ge);
+      theta = 64 * h + top + 1;
+      if (top < 63) n_gt = (uint32_t)__builtin_amdgcn_readlane((int)suf[h], top + 1);
+      else n_gt = (h + 1 < H) ? (uint32_t)__builtin_amdgcn_readlane((int)suf[h + 1 < H ? h + 1 : h], 0) : 0u;
+      eq_tot = (uint32_t)__builtin_amdgcn_readlane((int)tot[h], top);
+    }
+  }
   const uint32_t want = (uint32_t)n_candidates - n_gt;
   need_eq = want < eq_tot ? want : eq_tot;
+}
+
+// the bin totals of head g for theta_from_totals
+template <int NB>
+__device__ __forceinline__ void load_totals(const uint32_t* __restrict__ unit_tot, int unit, int g, int lane,
+                                            uint32_t (&tot)[NB / 64]) {
+#pragma unroll
+  for (int h = 0; h < NB / 64; ++h) tot[h] = unit_tot[((int64_t)unit * MAXG + g) * NB + 64 * h + lane];
 }
 
 // Selection parameters of query head g (wave g) for the sub-tiles 4 tl ..
@@ -1129,15 +1017,16 @@ __device__ __forceinline__ void theta_from_totals(uint32_t tot, int64_t n, int n
 // theta_from_totals, then the keys above / at theta in every earlier
 // sub-tile, 64 sub-tiles (one per lane) per step.  Results go to s_par[g] =
 // (theta, need_eq) and s_base[w][g] = (#gt, #eq) before sub-tile 4 tl + w.
-__device__ __forceinline__ void select_params_suffix(uint32_t tot, const uint32_t* __restrict__ suf, int unit,
+template <int NB>
+__device__ __forceinline__ void select_params_suffix(const uint32_t (&tot)[NB / 64], const uint32_t* __restrict__ suf, int unit,
                                                      int max_subs, int sub_len, int64_t n, int tl, int g,
                                                      int n_candidates, int lane, int2* s_par,
                                                      int2 (*s_base)[MAXG]) {
   int theta;
   uint32_t need_eq;
-  theta_from_totals(tot, n, n_candidates, theta, need_eq);
-  const uint32_t* row_gt = suf + suf_index(unit, max_subs, g, theta + 1, 0);             // #{S > theta}
-  const uint32_t* row_ge = suf + suf_index(unit, max_subs, g, theta > 0 ? theta : 1, 0);  // #{S >= theta}
+  theta_from_totals<NB>(tot, n, n_candidates, theta, need_eq);
+  const uint32_t* row_gt = suf + suf_index<NB>(unit, max_subs, g, theta + 1, 0);             // #{S > theta}
+  const uint32_t* row_ge = suf + suf_index<NB>(unit, max_subs, g, theta > 0 ? theta : 1, 0);  // #{S >= theta}
   const int first = 4 * tl;
   int pre_gt = 0, pre_eq = 0;
   int in_gt[4] = {0, 0, 0, 0}, in_eq[4] = {0, 0, 0, 0};
@@ -1233,20 +1122,18 @@ struct HeadSelect {
   }
 };
 
-// FUSED (64 bins, rank tiers): each workgroup derives the parameters itself
-// from the unit's totals and the sub-tiles' suffix counts
-// (select_params_suffix); otherwise it reads the threshold kernel's.  The
-// tiles of one unit share an XCD where they can (xcd_unit_tile), so the
+// Each workgroup derives the parameters itself from the unit's bin totals
+// and the sub-tiles' suffix counts (select_params_suffix; NB: bins 1..NB).
+// The tiles of one unit share an XCD where they can (xcd_unit_tile), so the
 // unit's counts are fetched into its L2 once.
-template <int G, bool FUSED>
+template <int G, int NB>
 __global__ void __launch_bounds__(256)
-select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__ params,
-              const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx, int64_t n, int64_t s_stride,
+select_kernel(const uint32_t* __restrict__ scores, int32_t* __restrict__ cand_idx, int64_t n, int64_t s_stride,
               int tiles, int max_subs, int tile, int n_q_heads, int n_kv_heads, int n_candidates,
               const uint32_t* __restrict__ unit_tot, const uint32_t* __restrict__ suf, uint32_t* __restrict__ err) {
   __shared__ uint2 s_ik[4][SEL_QCAP];             // compacted keys: (key, packed S)
-  __shared__ int2 s_par[FUSED ? MAXG : 1];
-  __shared__ int2 s_base[FUSED ? 4 : 1][MAXG];
+  __shared__ int2 s_par[MAXG];
+  __shared__ int2 s_base[4][MAXG];
 
   int unit, tl;
   xcd_unit_tile(blockIdx.x, gridDim.x / tiles, tiles, unit, tl);
@@ -1261,13 +1148,10 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
   const int w1 = (w0 + wkeys < k1) ? w0 + wkeys : k1;
   const uint32_t* srow = scores + (int64_t)unit * s_stride;
 
-  // fused parameters: the head's bin totals are requested before the scores,
-  // so that waiting for them does not wait for the scores (the memory
-  // counter is in order)
-  uint32_t tot = 0;
-  if constexpr (FUSED) {
-    if (wave < G) tot = unit_tot[((int64_t)unit * MAXG + wave) * NBIN + lane];
-  }
+  // the head's bin totals are requested before the scores, so that waiting
+  // for them does not wait for the scores (the memory counter is in order)
+  uint32_t tot[NB / 64] = {};
+  if (wave < G) load_totals<NB>(unit_tot, unit, wave, lane, tot);
 
   // packed scores of keys w0 + r*64 + lane, in groups of SEL_GRP chunks
   // (clamped, unconditional loads; the next group is in flight while one is used)
@@ -1282,21 +1166,13 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
   // per head: theta, need_eq, and the counts of keys above / at theta before
   // this wave's sub-tile
   auto setup = [&]() __attribute__((always_inline)) {
-    if constexpr (FUSED) {
-      if (wave < G)
-        select_params_suffix(tot, suf, unit, max_subs, tile >> 2, n, tl, wave, n_candidates, lane, s_par, s_base);
-      __syncthreads();
-    }
+    if (wave < G)
+      select_params_suffix<NB>(tot, suf, unit, max_subs, tile >> 2, n, tl, wave, n_candidates, lane, s_par, s_base);
+    __syncthreads();
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      if constexpr (FUSED) {
-        const int2 pr = s_par[g], sb2 = s_base[wave][g];
-        hs.set(g, pr.x, pr.y, sb2.x, sb2.y);
-      } else {
-        const SelParams p = params[unit * MAXG + g];
-        const int2 sb2 = sub_base[((int64_t)unit * max_subs + 4 * tl + wave) * MAXG + g];
-        hs.set(g, p.theta, p.need_eq, sb2.x, sb2.y);
-      }
+      const int2 pr = s_par[g], sb2 = s_base[wave][g];
+      hs.set(g, pr.x, pr.y, sb2.x, sb2.y);
     }
     hs.finish();
   };
@@ -1373,8 +1249,8 @@ select_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__
 //
 // The sub-tile's rows of 64 keys are split over the four waves (ROWS rows
 // each at most).  The keys above / at theta before the sub-tile come from
-// the unit's bin totals and the sub-tiles' suffix counts (FUSED, rank tiers)
-// or from the threshold kernel; the waves' own prefixes inside the sub-tile
+// the unit's bin totals and the sub-tiles' suffix counts; the waves' own
+// prefixes inside the sub-tile
 // from byte-parallel counts of their registers.  Then each wave compacts its
 // keys at or above some head's theta and gives them their slots
 // (HeadSelect), as select_kernel does.  Four times as many workgroups as
@@ -1399,21 +1275,23 @@ __device__ __forceinline__ int keys_in_sub(int64_t n, int t, int sub_len) {
   return (int)(len < 0 ? 0 : (len > sub_len ? sub_len : len));
 }
 
-__device__ __forceinline__ SubPrefix select_theta_sub(uint32_t tot, const uint32_t* __restrict__ suf, int unit,
+template <int NB>
+__device__ __forceinline__ SubPrefix select_theta_sub(const uint32_t (&tot)[NB / 64], const uint32_t* __restrict__ suf, int unit,
                                                       int max_subs, int sub_len, int64_t n, int sub, int g,
                                                       int n_candidates, int lane, int2* s_par) {
   SubPrefix sp;
   uint32_t need_eq;
-  theta_from_totals(tot, n, n_candidates, sp.theta, need_eq);
+  theta_from_totals<NB>(tot, n, n_candidates, sp.theta, need_eq);
   if (lane < sub) {
-    sp.gt0 = (int)suf[suf_index(unit, max_subs, g, sp.theta + 1, lane)];                        // #{S > theta}
-    sp.ge0 = sp.theta > 0 ? (int)suf[suf_index(unit, max_subs, g, sp.theta, lane)]              // #{S >= theta}
+    sp.gt0 = (int)suf[suf_index<NB>(unit, max_subs, g, sp.theta + 1, lane)];                        // #{S > theta}
+    sp.ge0 = sp.theta > 0 ? (int)suf[suf_index<NB>(unit, max_subs, g, sp.theta, lane)]              // #{S >= theta}
                           : keys_in_sub(n, lane, sub_len);                                      // every key
   }
   if (lane == 0) s_par[g] = make_int2(sp.theta, (int)need_eq);
   return sp;
 }
 
+template <int NB>
 __device__ __forceinline__ void select_prefix_sub(const SubPrefix& sp, const uint32_t* __restrict__ suf, int unit,
                                                   int max_subs, int sub_len, int64_t n, int sub, int g, int lane,
                                                   int2* s_sb) {
@@ -1423,8 +1301,8 @@ __device__ __forceinline__ void select_prefix_sub(const SubPrefix& sp, const uin
     const int t = c0 + lane;
     int gt = 0, eq = 0;
     if (t < sub) {
-      gt = (int)suf[suf_index(unit, max_subs, g, sp.theta + 1, t)];
-      const int ge = sp.theta > 0 ? (int)suf[suf_index(unit, max_subs, g, sp.theta, t)] : keys_in_sub(n, t, sub_len);
+      gt = (int)suf[suf_index<NB>(unit, max_subs, g, sp.theta + 1, t)];
+      const int ge = sp.theta > 0 ? (int)suf[suf_index<NB>(unit, max_subs, g, sp.theta, t)] : keys_in_sub(n, t, sub_len);
       eq = ge - gt;
     }
     pre_gt += (int)xor_butterfly_u((uint32_t)gt, lane, AddU());
@@ -1433,10 +1311,9 @@ __device__ __forceinline__ void select_prefix_sub(const SubPrefix& sp, const uin
   if (lane == 0) s_sb[g] = make_int2(pre_gt, pre_eq);
 }
 
-template <int G, bool FUSED, int ROWS>
+template <int G, int NB, int ROWS>
 __global__ void __launch_bounds__(256)
-select_sub_kernel(const uint32_t* __restrict__ scores, const SelParams* __restrict__ params,
-                  const int2* __restrict__ sub_base, int32_t* __restrict__ cand_idx, int64_t n, int64_t s_stride,
+select_sub_kernel(const uint32_t* __restrict__ scores, int32_t* __restrict__ cand_idx, int64_t n, int64_t s_stride,
                   int subs, int max_subs, int sub_len, int n_q_heads, int n_kv_heads, int n_candidates,
                   const uint32_t* __restrict__ unit_tot, const uint32_t* __restrict__ suf,
                   uint32_t* __restrict__ err) {
@@ -1461,17 +1338,8 @@ select_sub_kernel(const uint32_t* __restrict__ scores, const SelParams* __restri
 
   // the parameters' inputs are requested before the scores (the memory
   // counter is in order, so waiting for them does not wait for the scores)
-  uint32_t tot = 0;
-  SelParams prm{};
-  int2 sbase = make_int2(0, 0);
-  if constexpr (FUSED) {
-    if (wave < G) tot = unit_tot[((int64_t)unit * MAXG + wave) * NBIN + lane];
-  } else {
-    if (tid < G) {
-      prm = params[unit * MAXG + tid];
-      sbase = sub_base[((int64_t)unit * max_subs + sub) * MAXG + tid];
-    }
-  }
+  uint32_t tot[NB / 64] = {};
+  if (wave < G) load_totals<NB>(unit_tot, unit, wave, lane, tot);
   uint32_t sp[ROWS];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
@@ -1479,14 +1347,7 @@ select_sub_kernel(const uint32_t* __restrict__ scores, const SelParams* __restri
     sp[r] = srow[j < jlast ? j : jlast];
   }
   SubPrefix pfx;
-  if constexpr (FUSED) {
-    if (wave < G) pfx = select_theta_sub(tot, suf, unit, max_subs, sub_len, n, sub, wave, n_candidates, lane, s_par);
-  } else {
-    if (tid < G) {
-      s_par[tid] = make_int2(prm.theta, prm.need_eq);
-      s_sb[tid] = sbase;
-    }
-  }
+  if (wave < G) pfx = select_theta_sub<NB>(tot, suf, unit, max_subs, sub_len, n, sub, wave, n_candidates, lane, s_par);
   __syncthreads();
   // this wave's keys above / at each head's theta: byte g of the flag words
   // counts head g (at most ROWS <= 16 per lane), then 16-bit wave sums
@@ -1512,9 +1373,8 @@ select_sub_kernel(const uint32_t* __restrict__ scores, const SelParams* __restri
   if (lane == 0) {
     s_wc[wave][0] = g02; s_wc[wave][1] = g13; s_wc[wave][2] = e02; s_wc[wave][3] = e13;
   }
-  if constexpr (FUSED) {                           // the earlier sub-tiles' counts arrived behind the rows
-    if (wave < G) select_prefix_sub(pfx, suf, unit, max_subs, sub_len, n, sub, wave, lane, s_sb);
-  }
+  // the earlier sub-tiles' counts arrived behind the rows
+  if (wave < G) select_prefix_sub<NB>(pfx, suf, unit, max_subs, sub_len, n, sub, wave, lane, s_sb);
   __syncthreads();
   HeadSelect<G> hs;
 #pragma unroll
