@@ -550,26 +550,31 @@ __device__ __forceinline__ void rank_tiers(const uint32_t (&key)[4], const TierS
 // holds v[r].  Stage (K, J) compare-exchanges positions x and x ^ J (in the
 // lane for J < 4, else with lane l ^ J / 4); blocks of K with (x & K) == 0
 // keep the larger value at the lower position.
+// Each value is kept or replaced by its partner: one compare and two selects
+// per value across lanes, one compare and four selects per pair in a lane.
 template <int K, int J>
 __device__ __forceinline__ void bitonic_step(uint64_t (&v)[4], int lane) {
-  uint64_t pv[4];
+  if constexpr (J >= 4) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if constexpr (J >= 4) {
-      pv[r] = ((uint64_t)lane_xor<J / 4>((uint32_t)(v[r] >> 32), lane) << 32) |
-              (uint64_t)lane_xor<J / 4>((uint32_t)v[r], lane);
-    } else {
-      pv[r] = v[r ^ J];
+    for (int r = 0; r < 4; ++r) {
+      const uint64_t pv = ((uint64_t)lane_xor<J / 4>((uint32_t)(v[r] >> 32), lane) << 32) |
+                          (uint64_t)lane_xor<J / 4>((uint32_t)v[r], lane);
+      const int x = 4 * lane + r;
+      const bool want_max = ((x & K) == 0) == ((x & J) == 0);
+      v[r] = ((pv > v[r]) == want_max) ? pv : v[r];
     }
-  }
+  } else {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int x = 4 * lane + r;
-    const bool desc_block = (x & K) == 0;
-    const bool lower = (x & J) == 0;
-    const uint64_t hi = v[r] > pv[r] ? v[r] : pv[r];
-    const uint64_t lo = v[r] > pv[r] ? pv[r] : v[r];
-    v[r] = (lower == desc_block) ? hi : lo;
+    for (int a = 0; a < 4; ++a) {
+      if ((a & J) == 0) {                          // the pair (a, a | J); a is the lower position
+        const int b = a | J;
+        const bool desc = ((4 * lane + a) & K) == 0;
+        const uint64_t va = v[a], vb = v[b];
+        const bool sw = desc ? (vb > va) : (va > vb);
+        v[a] = sw ? vb : va;
+        v[b] = sw ? va : vb;
+      }
+    }
   }
 }
 template <int K, int J>
@@ -587,18 +592,24 @@ __device__ __forceinline__ void bitonic_k(uint64_t (&v)[4], int lane) {
 // centroids are sorted by (score desc, c asc) with a bitonic network over the
 // wave (position x = 4 lane + r), their key counts are prefix-summed in that
 // order, and a centroid whose first key sits at position P < keep_m gets the
-// bonus 6 - floor(6 P / keep_m) (tiers 0..5 -> 6..1) in lw[c].
-__device__ __forceinline__ void percentile_tiers(const uint32_t (&key)[4], const uint32_t* __restrict__ cnt_row,
-                                                 uint32_t keep_m, uint8_t* lw, int lane) {
+// bonus 6 - floor(6 P / keep_m) (tiers 0..5 -> 6..1) in lw[c].  cnt holds
+// the counts of centroids lane + 64 r, loaded before the scores were known;
+// they go through the wave's LDS row s_cnt once the sort is done.
+__device__ __forceinline__ void percentile_tiers(const uint32_t (&key)[4], const uint32_t (&cnt)[4],
+                                                 uint32_t* s_cnt, uint32_t keep_m, uint8_t* lw, int lane) {
   uint64_t v[4];                                  // (score key, 255 - c): larger = earlier
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = ((uint64_t)key[r] << 8) | (uint64_t)(255u - (uint32_t)(lane + 64 * r));
   bitonic_k<2>(v, lane);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s_cnt[lane + 64 * r] = cnt[r];
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
   uint32_t c[4], nk[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     c[r] = 255u - (uint32_t)(v[r] & 0xFFu);
-    nk[r] = cnt_row[c[r]];
+    nk[r] = s_cnt[c[r]];
   }
   const uint32_t tot = nk[0] + nk[1] + nk[2] + nk[3];
   const uint32_t incl = wave_incl_scan(tot);     // keys in this and lower lanes
@@ -682,6 +693,7 @@ __device__ __forceinline__ void qprep_body(const QprepArgs<QT>& a, const Tables&
   __shared__ float y[D];
   __shared__ uint64_t sel[QP_WAVES][256];   // (score key, 255 - centroid) of the selected centroids
   __shared__ uint8_t lw[QP_WAVES][256];     // tier weight per centroid
+  __shared__ uint32_t s_cnt[QP_WAVES][256]; // percentile tiers: centroid key counts
 
   const QT* __restrict__ q = a.q;
   const int n_q_heads = a.n_q_heads, n_kv_heads = a.n_kv_heads, group = a.group;
@@ -697,6 +709,14 @@ __device__ __forceinline__ void qprep_body(const QprepArgs<QT>& a, const Tables&
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int b = part * QP_WAVES + w;        // subspace of this wave
 
+  // percentile tiers: this subspace's centroid counts, requested first (they
+  // do not depend on the query) and used after the centroid sort
+  uint32_t cnt[4] = {0, 0, 0, 0};
+  if (keep_m > 0) {
+    const uint32_t* cr = counts + ((int64_t)unit * NSUB + b) * 256;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cnt[r] = cr[lane + 64 * r];
+  }
   if (w == 0) {
     float v0, v1;
     rotate_query<QT>(q + (int64_t)head * D, tb, lane, v0, v1);
@@ -724,7 +744,7 @@ __device__ __forceinline__ void qprep_body(const QprepArgs<QT>& a, const Tables&
   for (int r = 0; r < 4; ++r) lw[w][lane + 64 * r] = 0;
 
   if (keep_m > 0) {
-    percentile_tiers(key, counts + ((int64_t)unit * NSUB + b) * 256, keep_m, lw[w], lane);
+    percentile_tiers(key, cnt, s_cnt[w], keep_m, lw[w], lane);
   } else if (tiers.top[tiers.n_tiers - 1] <= 64) {
     rank_tiers_bound(key, tiers, sel[w], lw[w], lane);
   } else {
