@@ -40,7 +40,7 @@ METRIC = "retrieval+sparse-attn decode steps/s per layer at 128K/1M ctx; % HBM p
 HBM_PEAK_GBS = 8000.0
 CODE_BYTES = 16
 RECORD_BYTES = 128
-STAGE12 = ("qprep", "collide", "threshold", "select", "rerank", "rerank_topk", "topk")
+STAGE12 = ("qprep", "collide", "select", "rerank", "rerank_topk", "topk")
 
 
 def log(*a):
