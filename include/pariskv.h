@@ -312,8 +312,8 @@ pk_status pk_append_retrieve_attend(pk_context* ctx, const void* new_keys, pk_dt
  * that forbid hipMalloc.  Same arguments, results, layouts and errors as
  * pk_retrieve_attend with a context created from *cfg (no debug copies, no
  * timings, no device error flags), except that nothing is allocated: the
- * call's scratch (tier LUT, rotated queries, packed scores, histograms,
- * selection parameters, candidate lists) lives in a static device array of
+ * call's scratch (tier LUT, rotated queries, packed scores, score bin
+ * totals and sub-tile suffix counts, candidate lists) lives in a static device array of
  * PK_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the
  * process ends.  Its size per call is about 4 * units * n + 8 * (query heads)
  * * C + 16 KiB * units bytes; a call that needs more than the array returns
