@@ -228,7 +228,13 @@ void pk_destroy(pk_context* ctx);
 /* Encode keys [batch][n_kv_heads][n][128] (element strides `key_strides` =
  * {batch, head, token}; the last dimension is contiguous) into rows [0, n) of
  * every unit and set inout->n = n.  keys: device pointer, PK_F32 or PK_BF16.
- * When inout->counts is non-NULL it is recounted over the n keys. */
+ * When inout->counts is non-NULL it is recounted over the n keys.
+ * What a row holds (README "1. Prefill": keys normalised, SRHT-rotated and
+ * summarised twice): the 16 sign-pattern centroid IDs of the rotated key's
+ * 8-dim blocks, one byte each (Slides Eqs. (5)-(6)); the 4-bit codes of its
+ * coordinates, a sign bit and a 3-bit Lloyd-Max magnitude level (Slides frame
+ * "The codebook is data-independent; the quantizer uses a prior"), with one
+ * fp32 weight per block (Slides Eqs. (7)-(10)); and the key's norm. */
 pk_status pk_encode_keys(pk_context* ctx, const void* keys, pk_dtype key_dtype,
                          const int64_t key_strides[3], int64_t n,
                          pk_summaries* inout, void* hip_stream);
@@ -244,7 +250,13 @@ pk_status pk_append_keys(pk_context* ctx, const void* new_keys, pk_dtype key_dty
 
 /* ---- decode step ------------------------------------------------------------ */
 
-/* Retrieve the Top-k keys of every query head.
+/* Retrieve the Top-k keys of every query head (README "2. Decode"): the query
+ * is rotated and scored against each block's centroids (Slides Eqs. (5)-(6));
+ * every key gets the tier-weighted collision vote S_i of Slides Eq. (15)
+ * (Sec. 4.2.2, Stage I); the C keys with the largest S_i (ties to the lower
+ * index) are reranked with the 4-bit inner-product estimate of Slides Eqs.
+ * (7)-(10) (Stage II); the k largest estimates (ties to the lower index) are
+ * returned (Slides Sec. 4.2.3).
  * q          device [batch][n_q_heads][128], PK_F32 or PK_BF16, contiguous;
  * sums       summaries with sums->n >= 0 valid keys per unit;
  * topk_idx   device i32 [batch][n_q_heads][k]: key indices sorted by
@@ -255,7 +267,11 @@ pk_status pk_retrieve(pk_context* ctx, const void* q, pk_dtype q_dtype,
                       const pk_summaries* sums, int32_t* topk_idx, float* topk_est,
                       const pk_debug* dbg, void* hip_stream);
 
-/* Sparse attention over the retrieved rows of every query head.
+/* Sparse attention over the retrieved rows of every query head (Slides Sec. 3,
+ * Eqs. (1)-(3); README "3. Attention"): s_i = softmax_scale * <k_i, q> over the
+ * retrieved indices only, o = sum_i softmax(s)_i v_i, in fp32.  The rows may
+ * sit in mapped host memory and are then read one by one over the host link
+ * (README "Key Insight").
  * q          device [batch][n_q_heads][128], contiguous;
  * k, v       [batch][n_kv_heads][n][128] with element strides kv_strides =
  *            {batch, head, token} shared by K and V, last dim contiguous, rows
