@@ -55,7 +55,7 @@ extern "C" {
 typedef enum {
   PK_OK = 0,
   PK_ERR_INVALID_ARG = -1,   /* bad pointer, size, stride or config field     */
-  PK_ERR_UNSUPPORTED = -2,   /* valid in principle, not supported by this build */
+  PK_ERR_UNSUPPORTED = -2,   /* valid in principle, not supported by this library */
   PK_ERR_CAPACITY = -3,      /* keys would exceed the summaries' capacity      */
   PK_ERR_OUT_OF_MEMORY = -4, /* device or pinned host allocation failed        */
   PK_ERR_HIP = -5,           /* a HIP runtime call failed (no GPU, launch error) */
@@ -74,7 +74,7 @@ typedef enum {
   PK_DTYPE_MAX_ENUM_ = 0x7FFFFFFF
 } pk_dtype;
 
-/* Fixed geometry of this build. */
+/* Fixed geometry of this library. */
 #define PK_HEAD_DIM 128      /* D */
 #define PK_N_SUB 16          /* B subspaces (Slides, App. Table 4: B = 16, m = 8) */
 #define PK_SUB_DIM 8         /* m: one byte of sign bits per subspace          */

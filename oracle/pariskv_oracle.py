@@ -19,7 +19,7 @@ Two precisions are kept apart:
     the fp32 rerank estimate, so that a GPU implementation taking the same
     decisions in the same precision can be compared bit for bit.
 
-Readings taken where the pages are silent (all also listed in the design doc):
+Readings taken where the pages are silent:
   R1  SRHT: R = (1/sqrt(D)) * H * diag(s), H the Sylvester-ordered Hadamard
       matrix, s a vector of +-1 drawn from Philox4x64-10 with key (seed, 0):
       sign j = +1 iff the top bit of the j-th 64-bit output is 0, counters

@@ -44,7 +44,7 @@ def oracle_encode(keys_f32: np.ndarray, chunk: int = 65536):
     return {k: np.concatenate([p[k] for p in parts]) for k in ("codes", "nibbles", "weights", "norms")}
 
 
-class GpuRun:
+class HipRun:
     """One workload run through the library: encode, retrieve (with debug copies), attend."""
 
     def __init__(self, w: S.Workload, K: np.ndarray, V: np.ndarray, Q: np.ndarray, n: int | None = None,
@@ -170,7 +170,7 @@ class GpuRun:
 # ---------------------------------------------------------------------------
 # comparisons
 # ---------------------------------------------------------------------------
-def check_encode_unit(run: GpuRun, u: int, keys_f32: np.ndarray, enc=None, rows=None):
+def check_encode_unit(run: HipRun, u: int, keys_f32: np.ndarray, enc=None, rows=None):
     """Codes, nibbles and weights bit-exact, norms to 1e-6 relative, for unit u."""
     enc = oracle_encode(keys_f32) if enc is None else enc
     n = keys_f32.shape[0]
@@ -206,7 +206,7 @@ def attention_ok(o_gpu: np.ndarray, o_ref: np.ndarray, rel: float = 2e-2) -> boo
     return bool(np.all(np.abs(o_gpu.astype(np.float64) - o_ref) <= rel * (np.abs(o_ref) + rms)))
 
 
-def check_retrieve_unit(run: GpuRun, b: int, h: int, keys_f32, values_f32, enc, heads=None,
+def check_retrieve_unit(run: HipRun, b: int, h: int, keys_f32, values_f32, enc, heads=None,
                         check_attention=True, stats=None):
     """Every intermediate of the unit's query heads against the oracle."""
     signs, L32_, _ = tables()

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from workloads import synthetic as S
-from tests.parity_util import GpuRun, check_encode_unit, check_retrieve_unit, oracle_encode, say
+from tests.parity_util import HipRun, check_encode_unit, check_retrieve_unit, oracle_encode, say
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +29,7 @@ def test_degenerate_sizes(case):
         w = S.custom("llama32k", batch=1, n_kv_heads=2, n_q_heads=8, n=900, n_candidates=1024, wid=1402)
     say(f"case {case} units={w.units} n={w.n} C={w.n_candidates}")
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q).retrieve_attend()
+    run = HipRun(w, K, V, Q).retrieve_attend()
     for u in range(w.units):
         b, h = divmod(u, w.n_kv_heads)
         kf, vf = S.as_f32(K[b, h]), S.as_f32(V[b, h])
@@ -43,7 +43,7 @@ def test_back_to_back_calls_of_different_sizes():
     selection parameters change with n): every call matches the oracle."""
     w = S.custom("llama32k", batch=2, n_kv_heads=4, n_q_heads=16, n=9000, n_candidates=512, wid=1410)
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q, n=9000)
+    run = HipRun(w, K, V, Q, n=9000)
     for n in (9000, 2049, 9000, 64, 5000):
         say(f"case back-to-back n={n}")
         run.sums.s.n = n
@@ -64,7 +64,7 @@ def test_repeated_calls_identical():
     w = S.custom("llama32k", batch=2, n_kv_heads=8, n_q_heads=32, n=20000, n_candidates=1024, wid=1411)
     say(f"case repeated units={w.units} n={w.n}")
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q).retrieve()
+    run = HipRun(w, K, V, Q).retrieve()
     ref = [t.clone() for t in (run.cand_idx, run.cand_est, run.topk_idx, run.topk_est)]
     for _ in range(50):
         run.retrieve()
@@ -90,7 +90,7 @@ def test_two_launch_geometries_same_results():
         K = S.all_keys(w)
         V = S.all_values(w)
         Q = S.all_queries(w, K)
-        runs.append(GpuRun(w, K, V, Q).retrieve_attend())
+        runs.append(HipRun(w, K, V, Q).retrieve_attend())
     a, b = runs
     np.testing.assert_array_equal(a.Q[0, :8], b.Q[0, :8])          # same inputs for these heads
     for t_a, t_b in ((a.cand_idx, b.cand_idx), (a.cand_est, b.cand_est)):

@@ -19,7 +19,7 @@ import pytest
 
 from oracle import pariskv_oracle as O
 from workloads import synthetic as S
-from tests.parity_util import GpuRun, check_encode_unit, check_retrieve_unit, oracle_encode, say, tables, to_torch
+from tests.parity_util import HipRun, check_encode_unit, check_retrieve_unit, oracle_encode, say, tables, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def _run_full(name, units, kv_host=False):
     V = S.all_values(w)
     Q = S.all_queries(w, K)
     say(f"case {name}: GPU run")
-    run = GpuRun(w, K, V, Q, kv_host=kv_host).retrieve_attend()
+    run = HipRun(w, K, V, Q, kv_host=kv_host).retrieve_attend()
     stats = {}
     for u in units:
         b, h = divmod(u, w.n_kv_heads)
@@ -90,7 +90,7 @@ def test_full_drift_stream():
     Kall = np.concatenate([K0, ak], axis=2)
     Vall = np.concatenate([V0, av], axis=2)
     Q0 = S.all_queries(w, K0)
-    run = GpuRun(w, Kall, Vall, Q0, n=w.n, capacity=w.n + T)
+    run = HipRun(w, Kall, Vall, Q0, n=w.n, capacity=w.n + T)
     check_steps = {0, 1, 127, 255, 511, 767, 895, T - 1}
     units = (3, 6)
     ref = {}
@@ -149,7 +149,7 @@ def test_full_layout_stream():
     Kz = np.concatenate([K[:, :, sink:], ak], axis=2)
     Vz = np.concatenate([V[:, :, sink:], av], axis=2)
     Q = S.all_queries(w, K)
-    run = GpuRun(w, Kz, Vz, Q, n=zone0, capacity=Kz.shape[2])
+    run = HipRun(w, Kz, Vz, Q, n=zone0, capacity=Kz.shape[2])
     window = local                                     # stream tokens 0..local-1 are in the window
     for t in range(steps):
         window += 1                                   # token local + t joins the window

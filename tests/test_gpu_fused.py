@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from workloads import synthetic as S
-from tests.parity_util import GpuRun, check_encode_unit, check_retrieve_unit, say
+from tests.parity_util import HipRun, check_encode_unit, check_retrieve_unit, say
 
 pytestmark = pytest.mark.gpu
 
@@ -17,7 +17,7 @@ def _run(w, units, kv_host=False, out_dtype="match", n=None):
     K = S.all_keys(w)
     V = S.all_values(w)
     Q = S.all_queries(w, K)
-    run = GpuRun(w, K, V, Q, kv_host=kv_host, n=n).retrieve_attend(out_dtype=out_dtype)
+    run = HipRun(w, K, V, Q, kv_host=kv_host, n=n).retrieve_attend(out_dtype=out_dtype)
     for u in units:
         b, h = divmod(u, w.n_kv_heads)
         kf = S.as_f32(K[b, h, :run.n])
@@ -66,7 +66,7 @@ def test_fused_empty():
     K = S.all_keys(w)
     V = S.all_values(w)
     Q = S.all_queries(w, K)
-    run = GpuRun(w, K, V, Q, n=0).retrieve_attend()
+    run = HipRun(w, K, V, Q, n=0).retrieve_attend()
     assert (run.topk_idx.cpu().numpy() == -1).all()
     assert (run.out.float().cpu().numpy() == 0).all()
     run.close()

@@ -8,7 +8,7 @@ eager call's indices, estimates and attention outputs."""
 import pytest
 
 from workloads import synthetic as S
-from tests.parity_util import GpuRun, say, to_torch
+from tests.parity_util import HipRun, say, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -21,7 +21,7 @@ def test_captured_retrieval_replays_equal_eager(entry):
     K = S.all_keys(w)
     V = S.all_values(w)
     Qs = [S.all_queries(w, K, step=s) for s in range(3)]
-    run = GpuRun(w, K, V, Qs[0], debug=False)
+    run = HipRun(w, K, V, Qs[0], debug=False)
     q = to_torch(Qs[0]).contiguous()
     idx = torch.full((w.batch, w.n_q_heads, w.top_k), -7, dtype=torch.int32, device="cuda")
     est = torch.zeros((w.batch, w.n_q_heads, w.top_k), dtype=torch.float32, device="cuda")

@@ -9,7 +9,7 @@ import pytest
 
 from oracle import pariskv_oracle as O
 from workloads import synthetic as S
-from tests.parity_util import GpuRun, attention_ok, check_encode_unit, check_retrieve_unit, say, to_torch
+from tests.parity_util import HipRun, attention_ok, check_encode_unit, check_retrieve_unit, say, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +57,7 @@ def test_sink_local_and_retrieved(sink, zone, local, k):
     Kz, Vz = K[:, :, sink:sink + zone], V[:, :, sink:sink + zone]
     Kd = np.concatenate([K[:, :, :sink], K[:, :, sink + zone:]], axis=2)
     Vd = np.concatenate([V[:, :, :sink], V[:, :, sink + zone:]], axis=2)
-    run = GpuRun(w, np.ascontiguousarray(Kz), np.ascontiguousarray(Vz), Q).retrieve()
+    run = HipRun(w, np.ascontiguousarray(Kz), np.ascontiguousarray(Vz), Q).retrieve()
     out = _dense_attend(run, to_torch(Kd), to_torch(Vd))
     for u in (0, 3):
         b, h = divmod(u, w.n_kv_heads)
@@ -73,12 +73,12 @@ def test_dense_only_and_empty_dense():
     K, V, Q = _split(w, 0, 600, 300)
     Kz, Vz, Kd, Vd = K[:, :, :600], V[:, :, :600], K[:, :, 600:], V[:, :, 600:]
     # empty zone: only the dense rows are attended
-    run = GpuRun(w, np.ascontiguousarray(Kz), np.ascontiguousarray(Vz), Q, n=0).retrieve()
+    run = HipRun(w, np.ascontiguousarray(Kz), np.ascontiguousarray(Vz), Q, n=0).retrieve()
     out = _dense_attend(run, to_torch(np.ascontiguousarray(Kd)), to_torch(np.ascontiguousarray(Vd)))
     _check_layout(run, Kz, Vz, Kd, Vd, out, [0])
     run.close()
     # no dense rows: the retrieved rows alone
-    run = GpuRun(w, np.ascontiguousarray(Kz), np.ascontiguousarray(Vz), Q).retrieve()
+    run = HipRun(w, np.ascontiguousarray(Kz), np.ascontiguousarray(Vz), Q).retrieve()
     out = _dense_attend(run, to_torch(np.ascontiguousarray(Kd[:, :, :0])), to_torch(np.ascontiguousarray(Vd[:, :, :0])))
     _check_layout(run, Kz, Vz, Kd[:, :, :0], Vd[:, :, :0], out, [0])
     run.close()
@@ -92,7 +92,7 @@ def test_zone_buffer_without_rows():
     say("case layout with a zero-row zone tensor")
     K, V, Q = _split(w, 0, 300, 150)
     Kd, Vd = np.ascontiguousarray(K[:, :, 300:]), np.ascontiguousarray(V[:, :, 300:])
-    run = GpuRun(w, np.ascontiguousarray(K[:, :, :300]), np.ascontiguousarray(V[:, :, :300]), Q).retrieve()
+    run = HipRun(w, np.ascontiguousarray(K[:, :, :300]), np.ascontiguousarray(V[:, :, :300]), Q).retrieve()
     empty = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
     out = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
     Kdt, Vdt = to_torch(Kd), to_torch(Vd)
@@ -122,7 +122,7 @@ def test_many_dense_rows_and_limit():
     K, V, Q = _split(w, 0, 1000, 8192)
     Kz, Vz = np.ascontiguousarray(K[:, :, :1000]), np.ascontiguousarray(V[:, :, :1000])
     Kd, Vd = np.ascontiguousarray(K[:, :, 1000:]), np.ascontiguousarray(V[:, :, 1000:])
-    run = GpuRun(w, Kz, Vz, Q).retrieve()
+    run = HipRun(w, Kz, Vz, Q).retrieve()
     out = _dense_attend(run, to_torch(Kd), to_torch(Vd))
     _check_layout(run, Kz, Vz, Kd, Vd, out, [0])
     import torch
@@ -148,7 +148,7 @@ def test_update_buffer_flushes_into_the_zone():
     zone_cap = zone0 + upd * flushes
     Kz = np.ascontiguousarray(K[:, :, sink:sink + zone_cap])
     Vz = np.ascontiguousarray(V[:, :, sink:sink + zone_cap])
-    run = GpuRun(w, Kz, Vz, Q, n=zone0, capacity=zone_cap)
+    run = HipRun(w, Kz, Vz, Q, n=zone0, capacity=zone_cap)
     for f in range(flushes + 1):
         zn = zone0 + upd * f                          # zone rows so far
         lo = sink + zn                                # first dense row after the zone
@@ -203,7 +203,7 @@ def test_flushes_offload_into_mapped_host_zone():
     row_b = 128 * 2
     # the stream's tokens on the GPU (the source of the window rows and of the flushes)
     Kt_all, Vt_all = to_torch(Kz), to_torch(Vz)
-    run = GpuRun(w, Kz[:, :, :zone0], Vz[:, :, :zone0], Q, n=zone0, capacity=zone_cap)
+    run = HipRun(w, Kz[:, :, :zone0], Vz[:, :, :zone0], Q, n=zone0, capacity=zone_cap)
     copy_stream = torch.cuda.Stream()
     compute = torch.cuda.current_stream()
     offloaded = None

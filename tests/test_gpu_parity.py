@@ -8,7 +8,7 @@ import pytest
 
 from oracle import pariskv_oracle as O
 from workloads import synthetic as S
-from tests.parity_util import GpuRun, check_encode_unit, check_retrieve_unit, oracle_encode, say, tables
+from tests.parity_util import HipRun, check_encode_unit, check_retrieve_unit, oracle_encode, say, tables
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ def test_tiny_single_head_fp32():
     w = S.WORKLOADS["tiny4k"]
     say("case tiny4k fp32 n=4096 C=512")
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q).retrieve().attend()
+    run = HipRun(w, K, V, Q).retrieve().attend()
     _check_all_units(run, K, V)
     run.close()
 
@@ -44,7 +44,7 @@ def test_gqa_ragged_bf16(n):
     w = S.custom("llama32k", batch=2, n_kv_heads=2, n_q_heads=8, n=n, n_candidates=256, wid=100 + n)
     say(f"case gqa bf16 n={n}")
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q).retrieve().attend()
+    run = HipRun(w, K, V, Q).retrieve().attend()
     _check_all_units(run, K, V)
     run.close()
 
@@ -55,7 +55,7 @@ def test_group_sizes(group):
                  wid=200 + group)
     say(f"case group={group}")
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q).retrieve().attend()
+    run = HipRun(w, K, V, Q).retrieve().attend()
     _check_all_units(run, K, V)
     run.close()
 
@@ -66,7 +66,7 @@ def test_many_heads_one_workgroup_topk(n, C):
     w = S.custom("llama32k", batch=4, n_kv_heads=8, n_q_heads=32, n=n, n_candidates=C, wid=260 + C)
     say(f"case 128 heads n={n} C={C}")
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q).retrieve().attend()
+    run = HipRun(w, K, V, Q).retrieve().attend()
     _check_all_units(run, K, V, units=[0, 13, 31])
     run.close()
 
@@ -82,7 +82,7 @@ def test_maximum_candidates_and_top_k(batch, n_kv, n_q, n):
                  wid=270 + n_q)
     say(f"case maximum C={C} k={k} heads={batch * n_q} n={n}")
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q).retrieve().attend()
+    run = HipRun(w, K, V, Q).retrieve().attend()
     _check_all_units(run, K, V, units=None if w.units == 1 else [0, 31])
     run.close()
 
@@ -93,7 +93,7 @@ def test_many_subtiles_single_unit():
     w = S.custom("llama32k", batch=1, n_kv_heads=1, n_q_heads=4, n=70001, n_candidates=1024, wid=250)
     say("case single unit n=70001 C=1024")
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q).retrieve().attend()
+    run = HipRun(w, K, V, Q).retrieve().attend()
     _check_all_units(run, K, V)
     run.close()
 
@@ -103,7 +103,7 @@ def test_small_n_edges(n, C, k):
     w = S.custom("llama32k", batch=1, n_kv_heads=2, n_q_heads=4, n=n, n_candidates=C, top_k=k, wid=300 + n)
     say(f"case small n={n} C={C} k={k}")
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q).retrieve().attend()
+    run = HipRun(w, K, V, Q).retrieve().attend()
     _check_all_units(run, K, V)
     run.close()
 
@@ -112,7 +112,7 @@ def test_empty_key_set():
     w = S.custom("llama32k", batch=1, n_kv_heads=2, n_q_heads=4, n=16, n_candidates=64, top_k=10, wid=400)
     say("case empty")
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q, n=0).retrieve().attend()
+    run = HipRun(w, K, V, Q, n=0).retrieve().attend()
     assert run.n == 0
     assert (run.topk_idx.cpu().numpy() == -1).all()
     assert np.isneginf(run.topk_est.cpu().numpy()).all()
@@ -126,7 +126,7 @@ def test_zero_keys_and_zero_query():
     K, V, Q = _inputs(w)
     K[0, 0, 10:20] = 0          # bf16 +0
     Q[0, 1] = 0                 # a zero query: all centroid scores tie
-    run = GpuRun(w, K, V, Q).retrieve().attend()
+    run = HipRun(w, K, V, Q).retrieve().attend()
     _check_all_units(run, K, V)
     run.close()
 
@@ -135,7 +135,7 @@ def test_deterministic_repeat():
     w = S.custom("llama32k", batch=2, n_kv_heads=2, n_q_heads=8, n=5000, n_candidates=400, wid=600)
     say("case determinism")
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q).retrieve().attend()
+    run = HipRun(w, K, V, Q).retrieve().attend()
     a = [t.cpu().numpy().copy() for t in (run.topk_idx, run.topk_est, run.cand_idx, run.cand_est, run.out.float())]
     run.retrieve().attend()
     b = [t.cpu().numpy() for t in (run.topk_idx, run.topk_est, run.cand_idx, run.cand_est, run.out.float())]
@@ -148,9 +148,9 @@ def test_append_equals_full_encode():
     w = S.custom("llama32k", batch=1, n_kv_heads=2, n_q_heads=8, n=3000, n_candidates=256, wid=700)
     say("case append")
     K, V, Q = _inputs(w)
-    full = GpuRun(w, K, V, Q)
+    full = HipRun(w, K, V, Q)
     # encode the first 2000 rows; attention later reads all 3000 rows of K / V
-    part = GpuRun(w, K, V, Q, n=2000, capacity=3000)
+    part = HipRun(w, K, V, Q, n=2000, capacity=3000)
     from kv_cache_top_amd import pariskv as P
     from tests.parity_util import to_torch
     P.pk_append_keys(part.ctx.h, to_torch(K[:, :, 2000:2990]), part.sums.s)
@@ -177,7 +177,7 @@ def test_capacity_and_argument_errors():
     from kv_cache_top_amd import pariskv as P
     w = S.custom("llama32k", batch=1, n_kv_heads=1, n_q_heads=1, n=64, n_candidates=32, top_k=8, wid=800)
     K, V, Q = _inputs(w)
-    run = GpuRun(w, K, V, Q)
+    run = HipRun(w, K, V, Q)
     from tests.parity_util import to_torch
     with pytest.raises(P.PkError) as ei:
         P.pk_append_keys(run.ctx.h, to_torch(K[:, :, :1]), run.sums.s)

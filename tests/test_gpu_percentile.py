@@ -8,7 +8,7 @@ import pytest
 
 from oracle import pariskv_oracle as O
 from workloads import synthetic as S
-from tests.parity_util import GpuRun, check_encode_unit, check_retrieve_unit, say, to_torch
+from tests.parity_util import HipRun, check_encode_unit, check_retrieve_unit, say, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -17,7 +17,7 @@ def _run(w, units, n=None, fused=False):
     K = S.all_keys(w)
     V = S.all_values(w)
     Q = S.all_queries(w, K)
-    run = GpuRun(w, K, V, Q, n=n)
+    run = HipRun(w, K, V, Q, n=n)
     run = run.retrieve_attend() if fused else run.retrieve().attend()
     for u in units:
         b, h = divmod(u, w.n_kv_heads)
@@ -65,7 +65,7 @@ def test_adaptive_candidates_over_capacity_is_an_error():
     K = S.all_keys(w)
     V = S.all_values(w)
     Q = S.all_queries(w, K)
-    run = GpuRun(w, K, V, Q)
+    run = HipRun(w, K, V, Q)
     with pytest.raises(P.PkError) as e:
         run.retrieve()                              # ceil(0.5 * 4000) = 2000 > 1000
     assert e.value.status == P.PK_ERR_CAPACITY
@@ -81,7 +81,7 @@ def test_percentile_counts_follow_appends():
     K = S.all_keys(w)
     V = S.all_values(w)
     Q = S.all_queries(w, K)
-    run = GpuRun(w, K, V, Q, n=2000, capacity=2600)
+    run = HipRun(w, K, V, Q, n=2000, capacity=2600)
     for t0 in range(2000, 2600, 150):
         P.pk_append_keys(run.ctx.h, to_torch(K[:, :, t0:t0 + 150]), run.sums.s)
     assert run.n == 2600

@@ -7,7 +7,7 @@ static array is refused before anything is enqueued."""
 import pytest
 
 from workloads import synthetic as S
-from tests.parity_util import GpuRun, check_retrieve_unit, oracle_encode, say
+from tests.parity_util import HipRun, check_retrieve_unit, oracle_encode, say
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +19,7 @@ def test_noalloc_matches_context_call_twice():
     K = S.all_keys(w)
     V = S.all_values(w)
     Q = S.all_queries(w, K)
-    run = GpuRun(w, K, V, Q, debug=False)
+    run = HipRun(w, K, V, Q, debug=False)
     for n in (9000, 3001):                       # the second call over fewer keys
         say(f"case noalloc n={n}")
         run.sums.s.n = n
