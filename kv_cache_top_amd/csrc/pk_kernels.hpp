@@ -1597,6 +1597,19 @@ __device__ __forceinline__ uint64_t topk_item(uint32_t key, int32_t ix) {
   return ((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)ix);
 }
 
+// Wave priority for round r of `rounds` over which the waves of a workgroup
+// gather records: a wave that is rounds behind the others issues first when
+// both are ready, so that the waves finish their gathers close together (the
+// workgroup's next step waits for the last one).  The last round, and a
+// single round, run at the normal priority.
+__device__ __forceinline__ void set_prio_behind(int r, int rounds) {
+  const int left = rounds - 1 - r;          // rounds still to come after this one
+  if (left >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (left == 2) __builtin_amdgcn_s_setprio(2);
+  else if (left == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // LDS table T[j][nib] = fl(v(nib) * Rq[j]) of one query head; thread tid
 // fills entries tid + k NT.  The Rq values are loaded first (rerank_rq_load),
 // ahead of the record loads, so that building the table does not wait for
@@ -2009,11 +2022,13 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
       rerank_load(ra, rbase, ixn);
       ixn = ci[p + RT_THREADS < plast ? p + RT_THREADS : plast];
     }
+    set_prio_behind(r, rounds);     // the top-k waits for the last wave
     const float est = rerank_eval(ra, s_T);
     s_est[p] = est;
     if (p < n_sel) st.add(orderable(est));
     if (ce && p < n_sel) ce[p] = est;
   }
+  __builtin_amdgcn_s_setprio(0);
   int32_t kix[R];                   // the slots' key indices (L2), in flight during the first top-k steps
 #pragma unroll
   for (int r = 0; r < R; ++r) {
