@@ -1,7 +1,8 @@
 """Decode-step benchmark of the ParisKV retrieval + sparse-attention path on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched128k]
-                    [--layers L] [--no-cpu] [--no-recall] [--no-extra] [--copy-calibration]
+                    [--layers L] [--no-cpu] [--no-recall] [--no-extra] [--no-warm]
+                    [--copy-calibration]
 
 A step is one pass of the whole hot path for one layer: one pk_retrieve_attend
 call (query rotation, collision votes, candidate selection, 4-bit rerank,
@@ -61,6 +62,8 @@ def parse():
     ap.add_argument("--cpu-workers", type=int, default=0, help="oracle worker processes (0 = min(16, cores))")
     ap.add_argument("--no-recall", action="store_true", help="skip the recall@k check after the timed steps")
     ap.add_argument("--no-extra", action="store_true", help="only the named workload (no 1M / drift entries)")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the warm single-buffer context timing (profiles then see cold steps only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM traffic counter calibration)")
     return ap.parse_args()
@@ -509,7 +512,7 @@ def main():
     w = S.WORKLOADS[args.workload]
     if w.sink_tokens or w.local_tokens:
         return run_layout(args, w)
-    head = run_workload(w, args, args.steps, args.warmup, not args.no_recall, want_warm=True)
+    head = run_workload(w, args, args.steps, args.warmup, not args.no_recall, want_warm=not args.no_warm)
     hbm_copy = hbm_copy_rate()
 
     if args.copy_calibration:
