@@ -2209,7 +2209,9 @@ dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k,
   float m = -__builtin_inff(), l = 0.0f, acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  const int passes = (total + DA_UNROLL * DA_GROUPS - 1) / (DA_UNROLL * DA_GROUPS);
   for (int r0 = 0; r0 < total; r0 += DA_UNROLL * DA_GROUPS) {   // uniform
+    set_prio_behind(r0 / (DA_UNROLL * DA_GROUPS), passes);       // the merge waits for the last wave
     float x[DA_UNROLL][8], y[DA_UNROLL][8];
     bool ok[DA_UNROLL];
 #pragma unroll
@@ -2249,6 +2251,7 @@ dense_sparse_attend_kernel(AttendArgs a, const int32_t* __restrict__ idx, int k,
       }
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   // workgroup max of the group maxima, then rescale each group's sums to it
   float mw = m;
   mw = fmaxf(mw, lane_xor_f<32>(mw, lane));
