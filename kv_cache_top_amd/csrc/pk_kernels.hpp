@@ -912,12 +912,16 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
     const int g = gb / NB, bin = gb % NB;
     uint32_t s01 = 0, s23 = 0, c = 0;
     if (act) {
-      const uint32_t* row = s_hist + (g * NB + bin) * HIST_LANES;
+      // the row's words four at a time, from a start rotated by thread
+      // (neighbouring threads read neighbouring rows)
+      const uint4* row = reinterpret_cast<const uint4*>(s_hist + (g * NB + bin) * HIST_LANES);
       uint32_t lo = 0, hi = 0;
-      for (int i = 0; i < HIST_LANES; ++i) {
-        const uint32_t v = row[(i + tid) & (HIST_LANES - 1)];
-        lo += v & 0x00FF00FFu;          // waves 0 and 2
-        hi += (v >> 8) & 0x00FF00FFu;   // waves 1 and 3
+#pragma unroll
+      for (int i = 0; i < HIST_LANES / 4; ++i) {
+        const uint4 v = row[(i + tid) & (HIST_LANES / 4 - 1)];
+        lo += (v.x & 0x00FF00FFu) + (v.y & 0x00FF00FFu) + (v.z & 0x00FF00FFu) + (v.w & 0x00FF00FFu);   // waves 0, 2
+        hi += ((v.x >> 8) & 0x00FF00FFu) + ((v.y >> 8) & 0x00FF00FFu) + ((v.z >> 8) & 0x00FF00FFu) +
+              ((v.w >> 8) & 0x00FF00FFu);                                                              // waves 1, 3
       }
       const uint32_t cnt[4] = {lo & 0xFFFFu, hi & 0xFFFFu, lo >> 16, hi >> 16};
       c = cnt[0] + cnt[1] + cnt[2] + cnt[3];
