@@ -1035,11 +1035,15 @@ __device__ __forceinline__ void load_totals(const uint32_t* __restrict__ unit_to
   for (int h = 0; h < NB / 64; ++h) tot[h] = unit_tot[((int64_t)unit * MAXG + g) * NB + 64 * h + lane];
 }
 
+// chunks of 64 sub-tiles' suffix counts requested together when selection
+// parameters need the counts of more than 64 earlier sub-tiles
+constexpr int PFX_CH = 4;
+
 // Selection parameters of query head g (wave g) for the sub-tiles 4 tl ..
 // 4 tl + 3 of one select workgroup, from the unit's bin totals (tot at lane
 // l: keys with S = l + 1) and the sub-tiles' suffix counts: theta / need_eq as
 // theta_from_totals, then the keys above / at theta in every earlier
-// sub-tile, 64 sub-tiles (one per lane) per step.  Results go to s_par[g] =
+// sub-tile, 64 sub-tiles (one per lane) per chunk.  Results go to s_par[g] =
 // (theta, need_eq) and s_base[w][g] = (#gt, #eq) before sub-tile 4 tl + w.
 template <int NB>
 __device__ __forceinline__ void select_params_suffix(const uint32_t (&tot)[NB / 64], const uint32_t* __restrict__ suf, int unit,
@@ -1054,29 +1058,46 @@ __device__ __forceinline__ void select_params_suffix(const uint32_t (&tot)[NB / 
   const int first = 4 * tl;
   int pre_gt = 0, pre_eq = 0;
   int in_gt[4] = {0, 0, 0, 0}, in_eq[4] = {0, 0, 0, 0};
-  for (int c0 = 0; c0 < first + 4; c0 += 64) {   // uniform
-    const int sub = c0 + lane;
-    int gt = 0, eq = 0;
-    if (sub < first + 4) {
-      gt = (int)row_gt[sub];
-      int ge;
-      if (theta > 0) {
-        ge = (int)row_ge[sub];
-      } else {                                    // every key has S >= 0
-        int64_t len = n - (int64_t)sub * sub_len;
-        ge = (int)(len < 0 ? 0 : (len > sub_len ? sub_len : len));
-      }
-      eq = ge - gt;
-    }
-    const bool before = sub < first;
-    pre_gt += (int)xor_butterfly_u(before ? (uint32_t)gt : 0u, lane, AddU());
-    pre_eq += (int)xor_butterfly_u(before ? (uint32_t)eq : 0u, lane, AddU());
+  // chunks of 64 sub-tiles (one per lane), PFX_CH chunks requested together
+  for (int c00 = 0; c00 < first + 4; c00 += 64 * PFX_CH) {   // uniform
+    int gtv[PFX_CH], gev[PFX_CH];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int sw = first + w - c0;              // uniform
-      if (sw >= 0 && sw < 64) {
-        in_gt[w] = __builtin_amdgcn_readlane(gt, sw);
-        in_eq[w] = __builtin_amdgcn_readlane(eq, sw);
+    for (int c = 0; c < PFX_CH; ++c) {
+      const int sub = c00 + 64 * c + lane;
+      gtv[c] = 0;
+      gev[c] = 0;
+      if (sub < first + 4) {
+        gtv[c] = (int)row_gt[sub];
+        if (theta > 0) gev[c] = (int)row_ge[sub];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < PFX_CH; ++c) {
+      const int c0 = c00 + 64 * c;
+      if (c0 >= first + 4) break;                 // uniform
+      const int sub = c0 + lane;
+      int gt = 0, eq = 0;
+      if (sub < first + 4) {
+        gt = gtv[c];
+        int ge;
+        if (theta > 0) {
+          ge = gev[c];
+        } else {                                  // every key has S >= 0
+          int64_t len = n - (int64_t)sub * sub_len;
+          ge = (int)(len < 0 ? 0 : (len > sub_len ? sub_len : len));
+        }
+        eq = ge - gt;
+      }
+      const bool before = sub < first;
+      pre_gt += (int)xor_butterfly_u(before ? (uint32_t)gt : 0u, lane, AddU());
+      pre_eq += (int)xor_butterfly_u(before ? (uint32_t)eq : 0u, lane, AddU());
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int sw = first + w - c0;            // uniform
+        if (sw >= 0 && sw < 64) {
+          in_gt[w] = __builtin_amdgcn_readlane(gt, sw);
+          in_eq[w] = __builtin_amdgcn_readlane(eq, sw);
+        }
       }
     }
   }
@@ -1321,16 +1342,25 @@ __device__ __forceinline__ void select_prefix_sub(const SubPrefix& sp, const uin
                                                   int2* s_sb) {
   int pre_gt = (int)xor_butterfly_u((uint32_t)sp.gt0, lane, AddU());
   int pre_eq = (int)xor_butterfly_u((uint32_t)(sp.ge0 - sp.gt0), lane, AddU());
-  for (int c0 = 64; c0 < sub; c0 += 64) {          // uniform
-    const int t = c0 + lane;
-    int gt = 0, eq = 0;
-    if (t < sub) {
-      gt = (int)suf[suf_index<NB>(unit, max_subs, g, sp.theta + 1, t)];
-      const int ge = sp.theta > 0 ? (int)suf[suf_index<NB>(unit, max_subs, g, sp.theta, t)] : keys_in_sub(n, t, sub_len);
-      eq = ge - gt;
+  // the later chunks of 64 sub-tiles, PFX_CH chunks requested together
+  for (int c0 = 64; c0 < sub; c0 += 64 * PFX_CH) {   // uniform
+    int gt[PFX_CH], ge[PFX_CH];
+#pragma unroll
+    for (int c = 0; c < PFX_CH; ++c) {
+      const int t = c0 + 64 * c + lane;
+      gt[c] = 0;
+      ge[c] = 0;
+      if (t < sub) {
+        gt[c] = (int)suf[suf_index<NB>(unit, max_subs, g, sp.theta + 1, t)];
+        ge[c] = sp.theta > 0 ? (int)suf[suf_index<NB>(unit, max_subs, g, sp.theta, t)] : keys_in_sub(n, t, sub_len);
+      }
     }
-    pre_gt += (int)xor_butterfly_u((uint32_t)gt, lane, AddU());
-    pre_eq += (int)xor_butterfly_u((uint32_t)eq, lane, AddU());
+#pragma unroll
+    for (int c = 0; c < PFX_CH; ++c) {
+      if (c0 + 64 * c >= sub) break;                // uniform
+      pre_gt += (int)xor_butterfly_u((uint32_t)gt[c], lane, AddU());
+      pre_eq += (int)xor_butterfly_u((uint32_t)(ge[c] - gt[c]), lane, AddU());
+    }
   }
   if (lane == 0) s_sb[g] = make_int2(pre_gt, pre_eq);
 }
