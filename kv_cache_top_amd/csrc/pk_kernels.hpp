@@ -2022,7 +2022,10 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
   __shared__ int32_t s_idx[ATT ? PK_MAX_TOPK_ATT : 1];
   __shared__ AttRowsShared<ATT ? RT_THREADS / 64 : 1> s_att;
 
-  const int head = blockIdx.x, tid = threadIdx.x;
+  // the query heads of one KV head on one XCD (their common records meet in its L2)
+  int unit_x, g_x;
+  xcd_unit_tile(blockIdx.x, gridDim.x / group, group, unit_x, g_x);
+  const int head = unit_x * group + g_x, tid = threadIdx.x;
   const int seq = head / n_q_heads, qh = head - seq * n_q_heads;
   const int unit = seq * n_kv_heads + qh / group;
   const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
