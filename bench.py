@@ -98,6 +98,16 @@ def algorithmic_bytes(w, n: int) -> dict:
     }
 
 
+def secondary_counts(w, n: int) -> dict:
+    """Work per step that is not HBM bytes: table lookups of the collision
+    votes (one per code byte, all query heads of a KV head served by one
+    packed lookup) and the rerank's multiply-adds (one per coordinate of each
+    candidate record, per query head)."""
+    n_sel = min(n, candidates_per_call(w, n))
+    return {"collision_lut_lookups": 16 * n * w.units,
+            "rerank_macs": 128 * n_sel * w.batch * w.n_q_heads}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -401,6 +411,7 @@ def run_workload(w, args, steps: int, warmup: int, want_recall: bool, want_warm:
            "step": {"alg_bytes": nb["collide"] + nb["rerank"] + nb["attend"] + nb["encode"],
                     "frac_of_peak": round((nb["collide"] + nb["rerank"] + nb["attend"] + nb["encode"])
                                           / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "secondary": secondary_counts(w, n_now),
            "kernels": kern}
     if warm_ms is not None:
         res["warm_single_buffer"] = {
@@ -546,6 +557,7 @@ def main():
         "roofline": head["roofline"],
         "stage12": head["stage12"],
         "step": dict(head["step"], ms_per_step_with_kernel_events=head["ms_per_step_with_kernel_events"]),
+        "secondary": head["secondary"],
         "kernels": head["kernels"],
         "recall_at_k": head.get("recall_at_k"),
         "warm_single_buffer": head.get("warm_single_buffer"),
@@ -557,7 +569,7 @@ def main():
                             ("llama32k", max(20, args.steps // 2))):
             r = run_workload(S.WORKLOADS[name], args, steps, min(args.warmup, 20), not args.no_recall)
             extra[name] = {k: r[k] for k in ("value", "ms_per_step", "repetitions", "steps", "config", "roofline",
-                                             "stage12", "kernels") if k in r}
+                                             "stage12", "secondary", "kernels") if k in r}
             for k in ("host_link", "recall_at_k"):
                 if k in r:
                     extra[name][k] = r[k]

@@ -66,3 +66,14 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_secondary_counts_per_step():
+    # batched 128K: 16 code-byte lookups per key over 64 units (134 M), and
+    # 128 multiply-adds per candidate record over 256 query heads (134 M)
+    w = S.WORKLOADS["batched128k"]
+    sec = bench.secondary_counts(w, w.n)
+    assert sec == {"collision_lut_lookups": 134_217_728, "rerank_macs": 134_217_728}
+    # fewer keys than candidates: every key is a candidate
+    t = bench.secondary_counts(w, 1000)
+    assert t["rerank_macs"] == 128 * 1000 * w.batch * w.n_q_heads
