@@ -102,3 +102,18 @@ def test_two_launch_geometries_same_results():
     for r in runs:
         assert r.device_errors() == 0
         r.close()
+
+
+def test_many_short_sub_tiles():
+    """One unit of 300,000 keys: short tiles (768 keys at one unit), about
+    1,560 sub-tiles, so a select workgroup near the end sums the suffix counts
+    of 25 chunks of 64 earlier sub-tiles, requested four chunks at a time;
+    every intermediate and the Top-k match the oracle bit for bit."""
+    w = S.custom("llama32k", batch=1, n_kv_heads=1, n_q_heads=4, n=300000, n_candidates=4096, wid=1430)
+    say(f"case many sub-tiles units={w.units} n={w.n} C={w.n_candidates}")
+    K, V, Q = _inputs(w)
+    run = HipRun(w, K, V, Q).retrieve_attend()
+    kf, vf = S.as_f32(K[0, 0]), S.as_f32(V[0, 0])
+    check_retrieve_unit(run, 0, 0, kf, vf, check_encode_unit(run, 0, kf))
+    assert run.device_errors() == 0
+    run.close()
