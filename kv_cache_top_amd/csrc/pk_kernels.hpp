@@ -46,6 +46,32 @@ struct TierSpec {
   int weight[4];
 };
 
+// Table entries picked by a per-lane index through selects over scalar
+// registers: an indexed read of a kernel-argument array is a vector memory
+// load, and waiting for it also waits for every load issued before it (the
+// record gathers in the rerank, the key loads in the encoder).  The entries
+// pass through readfirstlane so that the selects are not turned back into
+// such a load.
+__device__ __forceinline__ uint32_t sreg(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ float level_of(const Tables& tb, int i) {
+  uint32_t lv[NLEV];
+#pragma unroll
+  for (int l = 0; l < NLEV; ++l) lv[l] = sreg(__float_as_uint(tb.levels[l]));
+  uint32_t v = lv[0];
+#pragma unroll
+  for (int l = 1; l < NLEV; ++l) v = (i == l) ? lv[l] : v;
+  return __uint_as_float(v);
+}
+__device__ __forceinline__ uint32_t neg_word(const Tables& tb, int i) {
+  uint32_t nw[4];
+#pragma unroll
+  for (int l = 0; l < 4; ++l) nw[l] = sreg(tb.neg_bits[l]);
+  uint32_t v = nw[0];
+#pragma unroll
+  for (int l = 1; l < 4; ++l) v = (i == l) ? nw[l] : v;
+  return v;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -255,7 +281,7 @@ __device__ __forceinline__ void encode_key(float (&x)[SUBD], int b, const Tables
 #pragma unroll
   for (int j = 0; j < SUBD; ++j) nsq += x[j] * x[j];
 
-  const uint32_t neg = (tb.neg_bits[b >> 2] >> ((b & 3) * 8)) & 0xFFu;
+  const uint32_t neg = (neg_word(tb, b >> 2) >> ((b & 3) * 8)) & 0xFFu;
 #pragma unroll
   for (int j = 0; j < SUBD; ++j)
     x[j] = __uint_as_float(__float_as_uint(x[j]) ^ (((neg >> j) & 1u) << 31));
@@ -1660,7 +1686,7 @@ __device__ __forceinline__ void rerank_table(float* s_T, const float (&rqv)[D * 
 #pragma unroll
   for (int k = 0; k < D * 16 / NT; ++k) {
     const int e = tid + k * NT, nb = e & 15;
-    const float lv = tb.levels[nb & 7];
+    const float lv = level_of(tb, nb & 7);
     const float v = (nb & 8) ? lv : -lv;
     s_T[e] = v * rqv[k];
   }
@@ -2038,12 +2064,11 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
   // round waits for one memory trip (its records), not two
   float rqv[D * 16 / RT_THREADS];
   rerank_rq_load<RT_THREADS>(rot_q + (int64_t)head * D, tid, rqv);
+  // unconditional (clamped) loads: a branch around them would make the
+  // table below wait for the records as well
   uint4 ra[8];
-  int ixn = 0;
-  if (n_sel > 0) {
-    rerank_load(ra, rbase, ci[tid < plast ? tid : plast]);
-    ixn = ci[RT_THREADS + tid < plast ? RT_THREADS + tid : plast];
-  }
+  rerank_load(ra, rbase, ci[tid < plast ? tid : plast]);
+  int ixn = ci[RT_THREADS + tid < plast ? RT_THREADS + tid : plast];
   rerank_table<RT_THREADS>(s_T, rqv, tb, tid);
   topk_shared_init<RT_THREADS>(s_tk, tid);
   for (int p = n_sel + tid; p < n_candidates; p += RT_THREADS) {   // invalid tail slots (n < C)
@@ -2117,6 +2142,9 @@ rerank_kernel(const uint8_t* __restrict__ records, const float* __restrict__ rot
   int ixn = ci[p0 + 256 + tid < plast ? p0 + 256 + tid : plast];   // next round's key index
   rerank_table<256>(s_T, rqv, tb, tid);
   __syncthreads();
+  // nothing that reads the records is scheduled above the table build (it
+  // would make the table wait for the record loads)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 1
   for (int r = 0; r < RR; ++r) {
     const int p = p0 + r * 256 + tid;
