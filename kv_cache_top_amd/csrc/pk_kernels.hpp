@@ -871,7 +871,8 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
   // re-read the last key and discard it): conditional loads compile to
   // exec-masked blocks that serialise on the memory counter.
   const int64_t last = (w1 > w0) ? w1 - 1 : 0;
-  // first batch of codes in flight while the tables are staged
+  // first batch of codes in flight while the tables are staged; the LUT is
+  // requested all at once (a load-wait-store loop would wait once per part)
   uint4 c[COLLIDE_UNROLL];
 #pragma unroll
   for (int u = 0; u < COLLIDE_UNROLL; ++u) {
@@ -879,11 +880,16 @@ collide_kernel(const uint4* __restrict__ codes, const uint32_t* __restrict__ lut
     c[u] = crow[i < last ? i : last];
   }
   {
+    constexpr int LUT_PER_THREAD = NSUB * 256 / 4 / 256;   // uint4 of the LUT per thread
     const uint4* src = reinterpret_cast<const uint4*>(lut + (int64_t)unit * NSUB * 256);
-    uint4* dst = reinterpret_cast<uint4*>(s_lut);
-    for (int i = tid; i < NSUB * 256 / 4; i += 256) dst[i] = src[i];
+    uint4 lt[LUT_PER_THREAD];
+#pragma unroll
+    for (int k = 0; k < LUT_PER_THREAD; ++k) lt[k] = src[tid + 256 * k];
     uint4* h4 = reinterpret_cast<uint4*>(s_hist);
     for (int i = tid; i < group * NB * HIST_LANES / 4; i += 256) h4[i] = make_uint4(0, 0, 0, 0);
+    uint4* dst = reinterpret_cast<uint4*>(s_lut);
+#pragma unroll
+    for (int k = 0; k < LUT_PER_THREAD; ++k) dst[tid + 256 * k] = lt[k];
   }
   __syncthreads();
 
