@@ -62,6 +62,16 @@ __device__ __forceinline__ float level_of(const Tables& tb, int i) {
   for (int l = 1; l < NLEV; ++l) v = (i == l) ? lv[l] : v;
   return __uint_as_float(v);
 }
+// weight of the first tier whose top exceeds `rank` (0 past the last tier),
+// by selects over the tiers in scalar registers: a loop that stops at a
+// per-lane tier would index the argument array per lane (a vector load)
+__device__ __forceinline__ uint32_t tier_weight_of(const TierSpec& tiers, int rank) {
+  uint32_t wgt = 0;
+#pragma unroll
+  for (int tt = 3; tt >= 0; --tt)
+    if (tt < tiers.n_tiers) wgt = rank < (int)sreg((uint32_t)tiers.top[tt]) ? sreg((uint32_t)tiers.weight[tt]) : wgt;
+  return wgt;
+}
 __device__ __forceinline__ uint32_t neg_word(const Tables& tb, int i) {
   uint32_t nw[4];
 #pragma unroll
@@ -494,11 +504,7 @@ __device__ __forceinline__ void rank_tiers_bound(const uint32_t (&key)[4], const
     const uint64_t e = sel[j];
     int rank = 0;
     for (int j2 = 0; j2 < cnt; ++j2) rank += (sel[j2] > e) ? 1 : 0;
-    uint32_t wgt = 0;
-    for (int tt = 0; tt < tiers.n_tiers; ++tt) {
-      if (rank < tiers.top[tt]) { wgt = (uint32_t)tiers.weight[tt]; break; }
-    }
-    lw[255 - (int)(e & 0xFFu)] = (uint8_t)wgt;   // rank >= T: weight 0, as the cleared entry
+    lw[255 - (int)(e & 0xFFu)] = (uint8_t)tier_weight_of(tiers, rank);   // rank >= T: weight 0, as the cleared entry
   }
 }
 
@@ -564,11 +570,7 @@ __device__ __forceinline__ void rank_tiers(const uint32_t (&key)[4], const TierS
     int rank = 0;
 #pragma unroll 16
     for (int j2 = 0; j2 < T; ++j2) rank += (sel[j2] > e) ? 1 : 0;
-    uint32_t wgt = 0;
-    for (int tt = 0; tt < tiers.n_tiers; ++tt) {
-      if (rank < tiers.top[tt]) { wgt = (uint32_t)tiers.weight[tt]; break; }
-    }
-    lw[255 - (int)(e & 0xFFu)] = (uint8_t)wgt;
+    lw[255 - (int)(e & 0xFFu)] = (uint8_t)tier_weight_of(tiers, rank);
   }
 }
 
