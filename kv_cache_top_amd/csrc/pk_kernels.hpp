@@ -1947,6 +1947,37 @@ __device__ __forceinline__ void load8(const KT* __restrict__ row, int part, floa
   }
 }
 
+// One thread's 8 dimensions of q, as loaded (bf16: one 16-byte word; fp32:
+// two): requested at the start of a kernel that attends at its end, and
+// converted only there, so that no wait for q sits in front of the rows'
+// requests.
+struct QRaw {
+  uint4 a, b;
+};
+template <typename T>
+__device__ __forceinline__ QRaw q_raw_load(const T* __restrict__ qh, int part) {
+  QRaw r;
+  if constexpr (sizeof(T) == 2) {
+    r.a = reinterpret_cast<const uint4*>(qh)[part];
+    r.b = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    r.a = reinterpret_cast<const uint4*>(qh)[2 * part];
+    r.b = reinterpret_cast<const uint4*>(qh)[2 * part + 1];
+  }
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ void q_raw_cvt(const QRaw& r, float (&x)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    x[0] = bf16_lo(r.a.x); x[1] = bf16_hi(r.a.x); x[2] = bf16_lo(r.a.y); x[3] = bf16_hi(r.a.y);
+    x[4] = bf16_lo(r.a.z); x[5] = bf16_hi(r.a.z); x[6] = bf16_lo(r.a.w); x[7] = bf16_hi(r.a.w);
+  } else {
+    x[0] = __uint_as_float(r.a.x); x[1] = __uint_as_float(r.a.y); x[2] = __uint_as_float(r.a.z);
+    x[3] = __uint_as_float(r.a.w); x[4] = __uint_as_float(r.b.x); x[5] = __uint_as_float(r.b.y);
+    x[6] = __uint_as_float(r.b.z); x[7] = __uint_as_float(r.b.w);
+  }
+}
+
 // ---- many heads: rerank and top-k of one head in one workgroup -------------
 constexpr int RT_THREADS = 1024;
 
@@ -1964,7 +1995,7 @@ struct AttRowsShared {
 };
 
 template <typename T, int P>
-__device__ void attend_rows16(const T* __restrict__ qh_ptr, const T* __restrict__ kb, const T* __restrict__ vb,
+__device__ void attend_rows16(const QRaw& qraw, const T* __restrict__ kb, const T* __restrict__ vb,
                               int64_t st, int64_t n_rows, const int32_t* hidx, int k, float scale,
                               T* __restrict__ out_head, AttRowsShared<RT_THREADS / 64>& s, int tid) {
   constexpr int NW = RT_THREADS / 64, RG = RT_THREADS / 16;
@@ -1976,8 +2007,6 @@ __device__ void attend_rows16(const T* __restrict__ qh_ptr, const T* __restrict_
     }
     return;
   }
-  float qv[8];
-  load8(qh_ptr, part, qv);
   float kx[P][8], vx[P][8];
   bool ok[P];
 #pragma unroll
@@ -1989,6 +2018,8 @@ __device__ void attend_rows16(const T* __restrict__ qh_ptr, const T* __restrict_
     load8(kb + row * st, part, kx[pp]);
     load8(vb + row * st, part, vx[pp]);
   }
+  float qv[8];
+  q_raw_cvt<T>(qraw, qv);
   float sc[P];
   float m = -__builtin_inff();
 #pragma unroll
@@ -2060,6 +2091,8 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
   int unit_x, g_x;
   xcd_unit_tile(blockIdx.x, gridDim.x / group, group, unit_x, g_x);
   const int head = unit_x * group + g_x, tid = threadIdx.x;
+  QRaw qraw{};
+  if constexpr (ATT) qraw = q_raw_load<T>(reinterpret_cast<const T*>(att.q) + (int64_t)head * D, tid & 15);
   const int seq = head / n_q_heads, qh = head - seq * n_q_heads;
   const int unit = seq * n_kv_heads + qh / group;
   const uint8_t* rbase = records + (int64_t)unit * n_cap * 128;
@@ -2120,7 +2153,7 @@ rerank_topk_kernel(const uint8_t* __restrict__ records, const float* __restrict_
     const int kvh = qh / group;
     const T* kb = reinterpret_cast<const T*>(att.k) + seq * att.sb + kvh * att.sh;
     const T* vb = reinterpret_cast<const T*>(att.v) + seq * att.sb + kvh * att.sh;
-    attend_rows16<T, P>(reinterpret_cast<const T*>(att.q) + (int64_t)head * D, kb, vb, att.st, att.n_rows, s_idx,
+    attend_rows16<T, P>(qraw, kb, vb, att.st, att.n_rows, s_idx,
                         k, att.scale, reinterpret_cast<T*>(att.out) + (int64_t)head * D, s_att, tid);
   }
 }
@@ -2182,6 +2215,8 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
   __shared__ int32_t s_idx[ATT ? PK_MAX_TOPK_ATT : 1];
   __shared__ AttRowsShared<ATT ? TK_THREADS / 64 : 1> s_att;
   const int head = blockIdx.x, tid = threadIdx.x;
+  QRaw qraw{};
+  if constexpr (ATT) qraw = q_raw_load<T>(reinterpret_cast<const T*>(att.q) + (int64_t)head * D, tid & 15);
   int32_t* ci = cand_idx + (int64_t)head * n_candidates;
   float* ce = cand_est + (int64_t)head * n_candidates;
   // candidate estimates: clamped unconditional loads, all in flight together
@@ -2209,7 +2244,7 @@ topk_kernel(int32_t* __restrict__ cand_idx, float* __restrict__ cand_est, int n_
     const int seq = head / n_q_heads, qh = head - seq * n_q_heads, kvh = qh / group;
     const T* kb = reinterpret_cast<const T*>(att.k) + seq * att.sb + kvh * att.sh;
     const T* vb = reinterpret_cast<const T*>(att.v) + seq * att.sb + kvh * att.sh;
-    attend_rows16<T, P>(reinterpret_cast<const T*>(att.q) + (int64_t)head * D, kb, vb, att.st, att.n_rows, s_idx,
+    attend_rows16<T, P>(qraw, kb, vb, att.st, att.n_rows, s_idx,
                         k, att.scale, reinterpret_cast<T*>(att.out) + (int64_t)head * D, s_att, tid);
   }
 }
